@@ -1,0 +1,51 @@
+"""Oracle: a plain, slow, fp64 CPU definition of the block-denoising step.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares no code,
+constant table or helper with the HIP library under
+``block_mask_diffusion_tt_amd/`` and never imports it; the product path never
+imports this package.
+
+Every function states the passage of the pages it follows.  Citation tags:
+
+  [keyframe]  "Diffusion Nemotron: Nvidia's "Two Brain" Diffusion Model"
+              (keyframe.defihacklabs.io video summary)
+  [news]      "NVIDIA发布Nemotron两塔模型，实现2.42倍文本生成吞吐并保持98.7%质量"
+              (889990.xyz)
+  [telegram]  "NVIDIA, возможно, решила главный компромисс современных LLM"
+              (tgviewer.app post)
+  [dothoosh]  "فرآیند انتشار در برابر رمزگشایی متوالی در مدل جدید انویدیا"
+              (dothoosh.com)
+  [modelcard] "Nemotron-Labs-TwoTower-30B-A3B-Base-BF16" model-card digest
+              (aitrends.kr)
+
+What is pinned, and how (tests/test_oracle_*.py):
+  attention      -- empty context reduces to torch's fp64 scaled-dot-product
+                    attention; equals a dense block-causal masked attention over
+                    the concatenated sequence; probability rows sum to one;
+                    closed forms (single key, equal keys, planted key, zero
+                    query); GQA == MHA with repeated heads; permutation
+                    invariances; scalar-loop brute force on tiny shapes.
+  unmasking      -- closed forms for p on hand-built logits (V=2, one planted
+                    logit, temperature), the gamma threshold (inclusive), the
+                    one-commit rule with lowest-position ties, lowest-id argmax
+                    ties, monotonicity in gamma, loop invariants, scalar-loop
+                    brute force.
+  adaLN-single   -- SiLU(0)=0, sinusoid special values, scalar-loop brute
+                    force of the affine map.  The PLACEMENT of scale/shift/gate
+                    and the timestep definition are readings the pages do not
+                    fix: parity unpinned for those two choices.
+"""
+
+from .attention import (  # noqa: F401
+    timestep_embedding,
+    adaln_single,
+    modulate_q,
+    block_attn,
+    dense_block_causal_attn,
+)
+from .unmask import (  # noqa: F401
+    row_confidence,
+    confidence_unmask,
+    denoise_block,
+)

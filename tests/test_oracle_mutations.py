@@ -1,0 +1,123 @@
+"""Planted mistakes: each mutant of the oracle's source (a dropped term, a wrong
+sign or index, a swapped operand) must make at least one pin test fail.  The
+mutations are applied to the oracle on the CPU only."""
+import inspect
+import types
+
+import pytest
+
+import oracle
+import oracle.attention as attention_src
+import oracle.unmask as unmask_src
+
+from . import test_oracle_attention as TA
+from . import test_oracle_unmask as TU
+
+ATTN_PINS = [TA.test_p1_empty_context_is_library_attention,
+             TA.test_p2_concat_block_causal_equivalence,
+             TA.test_p3_rows_sum_to_one, TA.test_p4_single_key_returns_value,
+             TA.test_p5_equal_keys_give_mean_value,
+             lambda: TA.test_p6_planted_key_weight(3.0),
+             TA.test_p7_adaln_special_cases, TA.test_p8_permutations,
+             TA.test_p9_gqa_is_repeated_mha, TA.test_brute_force_tiny,
+             TA.test_timestep_embedding_special_values, TA.test_adaln_single_pins]
+
+UNMASK_PINS = [TU.test_u1_exact_half_and_inclusive_threshold,
+               lambda: TU.test_u2_planted_logit_closed_form(1024),
+               TU.test_u3_one_commit_rule, TU.test_u4_lowest_id_on_ties,
+               lambda: TU.test_u5_u8_loop_invariants(0), TU.test_u6_monotone_in_gamma,
+               lambda: TU.test_u7_temperature_closed_form(0.1),
+               TU.test_mask_id_prediction_commits, TU.test_nothing_masked_is_a_noop,
+               lambda: TU.test_u9_brute_force(1)]
+
+ATTN_MUTANTS = [
+    ("g = h // group", "g = h % Hkv"),                          # wrong GQA head map
+    ("@ keys.T / np.sqrt(d)", "@ keys.T"),                      # dropped 1/sqrt(d)
+    ("(1.0 + _f64(scale)", "(_f64(scale)"),                     # dropped the 1 in (1+scale)
+    ("q = q + _f64(shift)", "q = q - _f64(shift)"),             # wrong sign of shift
+    ("kc[st:st + n, g, :], kb[b, :, g, :]", "kc[st:st + n, g, :]"),   # dropped block keys
+    ("o = o + _f64(residual)[b, :, h, :]", "o = o"),            # dropped residual
+    ("mx[:, 0] + np.log(z[:, 0])\n            if gate", "np.log(z[:, 0])\n            if gate"),  # lse without max
+    ("[np.cos(args), np.sin(args)]", "[np.sin(args), np.cos(args)]"),  # swapped sinusoid halves
+    ("silu = e / (1.0 + np.exp(-e))", "silu = e"),              # dropped SiLU
+    ("u[None, :, :, :] + table[:, :, None, :]", "u[None, :, :, :] + 0 * table[:, :, None, :]"),
+    ("u.reshape(e.shape[0], 3, width).transpose(1, 0, 2)",
+     "u.reshape(e.shape[0], width, 3).transpose(2, 0, 1)"),     # interleaved chunks
+]
+
+UNMASK_MUTANTS = [
+    ("conf[b, s] >= g]", "conf[b, s] > g]"),                    # exclusive threshold
+    ("np.flatnonzero(x == m)[0]", "np.flatnonzero(x == m)[-1]"),  # highest id on ties
+    ("/ float(temperature)", ""),                               # ignored temperature
+    ("top = min(s for s", "top = max(s for s"),                 # highest slot on ties
+    ("tok[b, s] = mask_token_id", "pass"),                      # no re-mask
+    ("chosen = [top]", "chosen = []"),                          # no one-commit rule
+    ("n_m.astype(np.float64) / S", "1.0 - n_m.astype(np.float64) / S"),
+]
+
+
+def _mutant(module, old, new):
+    src = inspect.getsource(module)
+    assert old in src, old
+    mod = types.ModuleType(module.__name__ + "_mutant")
+    mod.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(old, new, 1), module.__name__ + "_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def _caught(pins):
+    for pin in pins:
+        try:
+            pin()
+        except Exception:
+            return True
+    return False
+
+
+@pytest.mark.parametrize("old,new", ATTN_MUTANTS)
+def test_attention_mutant_is_caught(monkeypatch, old, new):
+    mod = _mutant(attention_src, old, new)
+    for name in ("timestep_embedding", "adaln_single", "modulate_q", "block_attn",
+                 "dense_block_causal_attn"):
+        monkeypatch.setattr(oracle, name, getattr(mod, name))
+    assert _caught(ATTN_PINS)
+
+
+@pytest.mark.parametrize("old,new", UNMASK_MUTANTS)
+def test_unmask_mutant_is_caught(monkeypatch, old, new):
+    mod = _mutant(unmask_src, old, new)
+    for name in ("row_confidence", "confidence_unmask", "denoise_block"):
+        monkeypatch.setattr(oracle, name, getattr(mod, name))
+    assert _caught(UNMASK_PINS + [_loop_timestep_pin])
+
+
+def _loop_timestep_pin():
+    """The loop's timestep is the masked fraction: with adaLN weights that map
+    the embedding's first channel straight into the gate, the first step's
+    gate equals SiLU(cos(1000 * n_masked / S)) (the embedding at frequency 1)."""
+    import math
+
+    import numpy as np
+    B, S, Hq, d = 1, 4, 1, 2
+    W = Hq * d
+    w = np.zeros((256, 3 * W))
+    w[0, 2 * W:3 * W] = 1.0                       # gate <- SiLU(emb[0])
+    masked = np.array([[1, 1, 1, 0]], np.uint8)
+    q = np.zeros((B, S, Hq, d))
+    kv = np.ones((B, S, Hq, d))
+    ctx = np.zeros((1, 1, d))
+    lg = np.zeros((B, S, 4))
+    lg[..., 0] = 50.0
+    r = oracle.denoise_block(lambda k, l: (q, kv, kv), lambda k: lg, [ctx], [ctx],
+                             np.zeros(B, np.int64), np.zeros(B, np.int32),
+                             np.full((B, S), 3), masked, 0.8, 1.0, 3, max_steps=1,
+                             ada_w=w, ada_bias=np.zeros(3 * W),
+                             ada_table=np.zeros((1, 3, W)))
+    e0 = math.cos(1000.0 * 3 / 4)
+    gate = e0 / (1 + math.exp(-e0))
+    out = r["outputs"][0][0][0]
+    assert np.allclose(out[0, 0, 0], gate * 1.0, atol=1e-12)
+
+
+def test_loop_timestep_is_masked_fraction():
+    _loop_timestep_pin()
