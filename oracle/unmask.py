@@ -32,8 +32,11 @@ import numpy as np
 
 from .attention import adaln_single, block_attn, timestep_embedding
 
-# Decisions whose fp64 margin is below this are reported as ambiguous: two
-# correct fp64 evaluations could take them either way.
+# Decisions whose fp64 margin is nonzero but below this are reported as
+# ambiguous: two correct fp64 evaluations could take them either way.  Exact
+# equalities (identical rows, p exactly equal to gamma) are not ambiguous:
+# every deterministic evaluation reproduces them, and the stated rules
+# (inclusive threshold, lowest slot) settle them.
 AMBIGUOUS_MARGIN = 1e-12
 
 
@@ -64,7 +67,8 @@ def confidence_unmask(logits, tokens, masked, gamma, temperature,
     Returns a dict of new arrays: tokens, masked (uint8), committed_now
     (uint8), conf (float64, NaN where not masked on entry), pred (int64, -1
     where not masked on entry), commit_step (or None), n_masked [B], and
-    ambiguous (number of decisions within AMBIGUOUS_MARGIN in fp64).
+    ambiguous (number of decisions whose nonzero fp64 margin is below
+    AMBIGUOUS_MARGIN).
     """
     lg = np.asarray(logits)
     B, S, _ = lg.shape
@@ -81,13 +85,13 @@ def confidence_unmask(logits, tokens, masked, gamma, temperature,
         for s in slots:
             pred[b, s], conf[b, s] = row_confidence(lg[b, s], temperature)
         chosen = [s for s in slots if conf[b, s] >= g]
-        ambiguous += sum(1 for s in slots if abs(conf[b, s] - g) < AMBIGUOUS_MARGIN)
+        ambiguous += sum(1 for s in slots if 0.0 < abs(conf[b, s] - g) < AMBIGUOUS_MARGIN)
         if not chosen and slots:
             best = max(conf[b, s] for s in slots)
             top = min(s for s in slots if conf[b, s] == best)
             chosen = [top]
             ambiguous += sum(1 for s in slots
-                             if s != top and best - conf[b, s] < AMBIGUOUS_MARGIN)
+                             if 0.0 < best - conf[b, s] < AMBIGUOUS_MARGIN)
         for s in slots:
             if s in chosen:
                 tok[b, s] = pred[b, s]
