@@ -1,0 +1,227 @@
+"""Benchmark of the block-denoising step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: timestep embedding
++ adaLN-single vectors, six attention layers over [context KV ; block KV]
+(tt_block_attn), and one confidence-unmasking pass over the 131072-entry
+vocabulary (tt_confidence_unmask), with every input already resident in HBM.
+
+Default workload ("ctx8k"): 64 sequences, each with 8192 context tokens per
+layer, block S = 16 with all 16 slots masked, 32 query / 2 KV heads, d = 128,
+6 attention layers, bf16, logits 64 x 16 x 131072 bf16 drawn as N(0, 8.5^2)
+(about 30% of rows reach p >= 0.8 at temperature 1).  --workload ragged64
+draws contexts uniform in [1024, 8192] instead; --workload batch128 uses 128
+sequences with contexts uniform in [2048, 16384].
+
+Prints one JSON line (rank 0): the metric, the dominant kernel's roofline
+(attention: algorithmic bytes per launch / mean launch time from HIP events on
+the launch stream), and the fp64 oracle timed on the host cores on a bounded
+sample, scaled to the same metric.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ctx8k", choices=["ctx8k", "ragged64", "batch128"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=8)
+    return ap.parse_args()
+
+
+def workload(name):
+    import synth
+    if name == "ctx8k":
+        B, lens = 64, [8192] * 64
+    elif name == "ragged64":
+        B = 64
+        lens = synth.uniform_int(B, 1024, 8192, seed=3).tolist()
+    else:
+        B = 128
+        lens = synth.uniform_int(B, 2048, 16384, seed=5).tolist()
+    return dict(name=name, B=B, lens=lens, S=16, Hq=32, Hkv=2, d=128, layers=6, V=131072,
+                logit_std=8.5, gamma=0.8, tau=1.0, seed=1234)
+
+
+def algorithmic_bytes(w, n_masked_rows):
+    """Bytes a step must move at least once: context K+V of every layer, q in,
+    out, block k/v, the adaLN vectors, and the logits of the masked rows."""
+    S, Hq, Hkv, d = w["S"], w["Hq"], w["Hkv"], w["d"]
+    per_layer = 0
+    for L in w["lens"]:
+        per_layer += 2 * L * Hkv * d * 2 + S * Hq * d * 2 * 2 + 2 * S * Hkv * d * 2 + 3 * Hq * d * 4
+    return per_layer, w["layers"] * per_layer + n_masked_rows * w["V"] * 2
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the block-denoising "
+              "step is data-parallel over sequences with no exchange, so N GPUs would each run "
+              "this same single-GPU step on their own share.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_mask_diffusion_tt_amd as tt
+    import synth
+
+    dev = "cuda"
+    w = workload(args.workload)
+    B, S, Hq, Hkv, d, NL, V = w["B"], w["S"], w["Hq"], w["Hkv"], w["d"], w["layers"], w["V"]
+    W = Hq * d
+    bf = torch.bfloat16
+    sd = w["seed"]
+    lens = w["lens"]
+    total = sum(lens)
+    max_len = max(lens)
+    start = torch.tensor(np.concatenate([[0], np.cumsum(lens)[:-1]]), dtype=torch.int64, device=dev)
+    clen = torch.tensor(lens, dtype=torch.int32, device=dev)
+    kc = [synth.normal((total, Hkv, d), 1.0, sd + 10 + l, bf, dev) for l in range(NL)]
+    vc = [synth.normal((total, Hkv, d), 1.0, sd + 20 + l, bf, dev) for l in range(NL)]
+    qb = [synth.normal((B, S, Hq, d), 1.0, sd + 30 + l, bf, dev) for l in range(NL)]
+    kb = [synth.normal((B, S, Hkv, d), 1.0, sd + 40 + l, bf, dev) for l in range(NL)]
+    vb = [synth.normal((B, S, Hkv, d), 1.0, sd + 50 + l, bf, dev) for l in range(NL)]
+    ada_w = synth.normal((256, 3 * W), 0.05, sd + 60, bf, dev)
+    ada_b = synth.normal((3 * W,), 0.1, sd + 61, torch.float32, dev)
+    ada_t = synth.normal((NL, 3, W), 0.1, sd + 62, torch.float32, dev)
+    logits = synth.normal((B, S, V), w["logit_std"], sd + 70, bf, dev)
+    tokens0 = torch.full((B, S), 3, dtype=torch.int32, device=dev)
+    masked0 = torch.ones((B, S), dtype=torch.uint8, device=dev)
+    tokens, masked = tokens0.clone(), masked0.clone()
+    n_masked = torch.empty((B,), dtype=torch.int32, device=dev)
+    t_step = torch.full((B,), 1.0, dtype=torch.float32, device=dev)   # n_masked / S at step 0
+    emb = torch.empty((B, 256), dtype=torch.float32, device=dev)
+    ada = torch.empty((NL, 3, B, W), dtype=torch.float32, device=dev)
+    out = torch.empty((B, S, Hq, d), dtype=bf, device=dev)
+    shape = tt.attn_shape(B, Hq, Hkv, d, S, bf)
+    aws = torch.empty(tt.block_attn_workspace_size(shape, max_len), dtype=torch.uint8, device=dev)
+    uws = torch.empty(tt.unmask_workspace_size(B, S, V), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    attn_events = []
+
+    def step(record):
+        tokens.copy_(tokens0)            # every step starts from a fully masked block
+        masked.copy_(masked0)
+        tt.timestep_embed(B, t_step, emb)
+        tt.adaln_single(B, W, NL, emb, ada_w, ada_b, ada_t, ada)
+        for l in range(NL):
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            tt.block_attn(shape, qb[l], kb[l], vb[l], kc[l], vc[l], start, clen, max_len, out, aws,
+                          ada_shift=ada[l, 0], ada_scale=ada[l, 1], ada_gate=ada[l, 2])
+            if record:
+                e1.record(stream)
+                attn_events.append((e0, e1))
+        tt.confidence_unmask(B, S, V, logits, V, w["gamma"], w["tau"], 3, 0, tokens, masked, uws,
+                             n_masked=n_masked)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step(True)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in attn_events]
+    attn_avg = float(np.mean(attn_ms))
+    committed = int(B * S - n_masked.sum().item())
+
+    per_launch, step_bytes = algorithmic_bytes(w, B * S)
+    qtok_s = B * S / (ms * 1e-3)
+    attn_gbps = per_launch / (attn_avg * 1e-3) / 1e9
+    result = {
+        "metric": "block-denoise query-tokens/s (S=16, ctx 8k, bf16)",
+        "value": round(qtok_s, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w["name"], "batch": B, "ctx_min": min(lens), "ctx_max": max_len,
+                   "block_size": S, "masked_slots": B * S, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": d, "layers": NL, "vocab": V, "gamma": w["gamma"],
+                   "temperature": w["tau"]},
+        "hbm_gbps_step": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "hbm_frac_step": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "committed_per_step": committed,
+        "roofline": {"kernel": "tt_block_attn (attention + merge)", "bound": "hbm",
+                     "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": per_launch, "mean_launch_ms": round(attn_avg, 4)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs, kc, vc, qb, kb, vb, ada,
+                                              logits, start)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, n_seq, kc, vc, qb, kb, vb, ada, logits, start):
+    """The fp64 oracle on the host cores: attention of n_seq sequences over all
+    layers plus their unmasking pass, on D2H copies of the same inputs, scaled
+    linearly (in context tokens for attention, in rows for unmasking) to the
+    whole step."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    f64 = lambda t: t.detach().float().cpu().numpy().astype(np.float64)  # noqa: E731
+    B, S, NL = w["B"], w["S"], w["layers"]
+    seqs = list(range(min(n_seq, B)))
+    st = start.cpu().numpy()
+    t_attn = 0.0
+    for l in range(NL):
+        for b in seqs:
+            L = w["lens"][b]
+            args = (f64(qb[l][b:b + 1]), f64(kb[l][b:b + 1]), f64(vb[l][b:b + 1]),
+                    f64(kc[l][st[b]:st[b] + L]), f64(vc[l][st[b]:st[b] + L]))
+            sh, sc, g = (f64(ada[l, j, b:b + 1]) for j in range(3))
+            t0 = time.perf_counter()
+            oracle.block_attn(*args, [0], [L], shift=sh, scale=sc, gate=g)
+            t_attn += time.perf_counter() - t0
+    lg = f64(logits[seqs[0]:seqs[-1] + 1])
+    t0 = time.perf_counter()
+    oracle.confidence_unmask(lg, np.full((len(seqs), S), 3), np.ones((len(seqs), S)), w["gamma"],
+                             w["tau"], 3, 0)
+    t_unmask = time.perf_counter() - t0
+    sample_tokens = sum(w["lens"][b] + S for b in seqs)
+    all_tokens = sum(L + S for L in w["lens"])
+    t_step = t_attn * all_tokens / sample_tokens + t_unmask * B / len(seqs)
+    return {"value": round(B * S / t_step, 3), "unit": "query-tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"{len(seqs)} of {B} sequences x {NL} layers attention + their unmasking "
+                       f"rows (fp64 NumPy, {t_attn + t_unmask:.1f} s measured), scaled linearly "
+                       "in context tokens and rows to the full step")}
+
+
+if __name__ == "__main__":
+    main()

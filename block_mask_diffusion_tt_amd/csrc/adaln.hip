@@ -1,0 +1,156 @@
+// Timestep conditioning (adaLN-single) and the small bookkeeping kernels of
+// the denoising loop.
+//
+// [dothoosh] two-tower mechanism section: every denoiser layer is modulated
+// by the diffusion timestep through adaLN-single, about 1.5 M parameters.
+// [modelcard] technical features section: scale, shift and gate are injected
+// per timestep into each layer.  The embedding (DiT sinusoid), the shared
+// SiLU -> Linear(256 -> 3*width) and the per-layer table are the reading of
+// "adaLN-single" used throughout (PixArt-alpha's construction).
+#include <math.h>
+
+#include "tt_internal.h"
+
+namespace tt {
+namespace {
+
+constexpr int kEmb = 256;
+
+// emb[b, i] = cos(1000 t f_i), emb[b, 128 + i] = sin(1000 t f_i),
+// f_i = 10000^(-i/128); t from `t` or, when t is NULL, n_masked[b] / S.
+__global__ void timestep_embed_kernel(int B, const float* t, const int32_t* n_masked, int S,
+                                      float* emb) {
+  const int b = blockIdx.x;
+  const int i = threadIdx.x;  // 0..127
+  if (b >= B || i >= kEmb / 2) return;
+  const double tb = t ? static_cast<double>(t[b])
+                      : static_cast<double>(n_masked[b]) / static_cast<double>(S);
+  const double f = exp(-log(10000.0) * static_cast<double>(i) / (kEmb / 2));
+  const double arg = 1000.0 * tb * f;
+  emb[static_cast<int64_t>(b) * kEmb + i] = static_cast<float>(cos(arg));
+  emb[static_cast<int64_t>(b) * kEmb + kEmb / 2 + i] = static_cast<float>(sin(arg));
+}
+
+// One thread per output column n of u = SiLU(emb) @ W (W bf16 [256, N]),
+// for a chunk of kRows sequences; W is read once per chunk with coalesced
+// loads, the SiLU'd embedding rows sit in LDS.  The epilogue adds the bias
+// and writes every layer's copy with its table row.
+constexpr int kRows = 16;
+constexpr int kCols = 256;
+
+__global__ __launch_bounds__(kCols) void adaln_kernel(int B, int width, int n_layers,
+                                                      const float* __restrict__ emb,
+                                                      const uint16_t* __restrict__ w,
+                                                      const float* __restrict__ bias,
+                                                      const float* __restrict__ table,
+                                                      float* __restrict__ ada) {
+  __shared__ float s_e[kRows][kEmb];
+  const int N = 3 * width;
+  const int n = blockIdx.x * kCols + threadIdx.x;
+  const int b0 = blockIdx.y * kRows;
+  const int nb = min(kRows, B - b0);
+  for (int idx = threadIdx.x; idx < kRows * kEmb; idx += kCols) {
+    const int r = idx / kEmb, k = idx % kEmb;
+    float v = 0.f;
+    if (r < nb) {
+      const float e = emb[static_cast<int64_t>(b0 + r) * kEmb + k];
+      v = e / (1.f + expf(-e));
+    }
+    s_e[r][k] = v;
+  }
+  __syncthreads();
+  if (n >= N) return;
+  float acc[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) acc[r] = 0.f;
+  for (int k = 0; k < kEmb; ++k) {
+    const float wk = __uint_as_float(static_cast<uint32_t>(w[static_cast<int64_t>(k) * N + n]) << 16);
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) acc[r] = fmaf(s_e[r][k], wk, acc[r]);
+  }
+  const float bn = bias ? bias[n] : 0.f;
+  const int j = n / width, c = n % width;
+  for (int l = 0; l < n_layers; ++l) {
+    const float tv = table ? table[(static_cast<int64_t>(l) * 3 + j) * width + c] : 0.f;
+    float* dst = ada + ((static_cast<int64_t>(l) * 3 + j) * B) * width + c;
+    for (int r = 0; r < nb; ++r) dst[static_cast<int64_t>(b0 + r) * width] = acc[r] + bn + tv;
+  }
+}
+
+__global__ void active_kernel(int B, const int32_t* n_masked, uint8_t* active, int32_t* total) {
+  int local = 0;
+  for (int b = threadIdx.x; b < B; b += blockDim.x) {
+    const int n = n_masked[b];
+    active[b] = n > 0;
+    local += n;
+  }
+  for (int off = 32; off >= 1; off >>= 1) local += __shfl_xor(local, off);
+  __shared__ int s[16];
+  if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = local;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int t = 0;
+    for (int i = 0; i < static_cast<int>(blockDim.x >> 6); ++i) t += s[i];
+    *total = t;
+  }
+}
+
+__global__ void count_masked_kernel(int B, int S, const uint8_t* masked, int32_t* n_masked) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  int n = 0;
+  for (int s = 0; s < S; ++s) n += masked[static_cast<int64_t>(b) * S + s] != 0;
+  n_masked[b] = n;
+}
+
+__global__ void clear_kernel(uint4* p, size_t n16, uint8_t* tail, size_t ntail) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t k = i; k < n16; k += stride) p[k] = make_uint4(0, 0, 0, 0);
+  if (i < ntail) tail[i] = 0;
+}
+
+}  // namespace
+
+hipError_t launch_timestep_embed(int B, const float* t, const int32_t* n_masked, int S,
+                                 float* emb, hipStream_t st) {
+  hipLaunchKernelGGL(timestep_embed_kernel, dim3(B), dim3(kEmb / 2), 0, st, B, t, n_masked, S, emb);
+  return hipGetLastError();
+}
+
+hipError_t launch_adaln_single(int B, int width, int n_layers, const float* emb, const void* w,
+                               const float* bias, const float* table, float* ada,
+                               hipStream_t st) {
+  const int N = 3 * width;
+  const dim3 grid(static_cast<unsigned>(ceil_div(N, kCols)), static_cast<unsigned>(ceil_div(B, kRows)));
+  hipLaunchKernelGGL(adaln_kernel, grid, dim3(kCols), 0, st, B, width, n_layers, emb,
+                     static_cast<const uint16_t*>(w), bias, table, ada);
+  return hipGetLastError();
+}
+
+hipError_t launch_active_from_masked(int B, const int32_t* n_masked, uint8_t* active,
+                                     int32_t* total, hipStream_t st) {
+  hipLaunchKernelGGL(active_kernel, dim3(1), dim3(1024), 0, st, B, n_masked, active, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_count_masked(int B, int S, const uint8_t* masked, int32_t* n_masked,
+                               hipStream_t st) {
+  hipLaunchKernelGGL(count_masked_kernel, dim3(static_cast<unsigned>(ceil_div(B, 256))), dim3(256),
+                     0, st, B, S, masked, n_masked);
+  return hipGetLastError();
+}
+
+hipError_t launch_clear(void* p, size_t bytes, hipStream_t st) {
+  if (bytes == 0) return hipSuccess;
+  const size_t n16 = bytes / 16, ntail = bytes % 16;
+  uint8_t* tail = static_cast<uint8_t*>(p) + n16 * 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(clear_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
+                     static_cast<uint4*>(p), n16, tail, ntail);
+  return hipGetLastError();
+}
+
+}  // namespace tt

@@ -1,0 +1,593 @@
+// Per-layer block attention of the denoiser over [context KV ; block KV].
+//
+// [dothoosh] two-tower mechanism section: inside a block the denoiser
+// attends bidirectionally, and causally to the earlier clean blocks; layer i
+// of the denoiser talks to layer i of the frozen context tower (whose KV cache
+// covers the prompt and the committed tokens).  [modelcard] technical
+// features section: bidirectional self-attention in the block plus
+// layer-aligned cross-attention to the same layer's context KV; adaLN-single
+// scale/shift/gate per timestep.  One softmax spans all keys of a query.
+//
+// Work decomposition (split-K over the context, flash-decode style):
+//   * the R = S*G query rows that share KV head g (S block slots x G query
+//     heads of the group) form the M dimension of dense tiles: every K/V
+//     tile staged in LDS is used by all of them, so each context byte is
+//     read from HBM once per layer;
+//   * a unit = (sequence b, KV head g, row block rb, context chunk c); chunk 0
+//     also takes the S block keys; units write (max, sum, accumulator)
+//     partials that the merge kernel combines in chunk order (deterministic).
+//
+// bf16 kernel (gfx950 matrix cores, 64-wide waves): 4 waves x 64 rows.
+//   S^T = K Q'^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 channels
+//   straight from the LDS K tile, B = the wave's pre-modulated Q' held in
+//   registers), so each lane ends with 16 scores of one row; the online
+//   softmax needs only one cross-lane exchange (lanes l and l^32 share rows).
+//   O^T += V^T P^T with the same instruction: the scores' accumulator layout
+//   is already the B-operand layout of P^T, and V is written transposed into
+//   LDS so each lane reads 2 x 8 bytes of one channel.  Scores are in log2
+//   units (log2(e)/sqrt(d) folded into Q'), and the running max is only
+//   raised when a tile exceeds it by more than 2^8 (values stay <= 256), so
+//   the accumulators are rarely rescaled.  K/V tiles are double-buffered:
+//   the global loads of tile t+1 are in flight while tile t is multiplied.
+#include <float.h>
+#include <math.h>
+
+#include "tt_internal.h"
+
+namespace tt {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kTK = 64;          // keys per LDS tile
+constexpr int kKPad = 8;         // bf16 padding of an LDS K row
+constexpr int kVPad = 4;         // bf16 padding of an LDS V^T row
+constexpr int kRowsBf16 = 256;   // rows per bf16 workgroup (4 waves x 64)
+constexpr int kRowsF32 = 64;     // rows per fp32 workgroup (1 wave, 1 row per lane)
+constexpr float kRescaleTh = 8.f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct KParams {
+  int B, S, Hq, Hkv, G, R;
+  int rows_per_unit, RB, NC, chunk;
+  const uint16_t* q; const uint16_t* kb; const uint16_t* vb;
+  const uint16_t* kc; const uint16_t* vc;
+  const void* qf; const void* kbf; const void* vbf; const void* kcf; const void* vcf;
+  const int64_t* ctx_start; const int32_t* ctx_len; const uint8_t* active;
+  const float* shift; const float* scale;
+  float qscale;
+  float* part_acc; float* part_ml;
+};
+
+struct MParams {
+  int B, S, Hq, Hkv, G, R, D;
+  int rows_per_unit, RB, NC, chunk;
+  const int32_t* ctx_len; const uint8_t* active;
+  const float* gate; const void* residual; void* out; float* lse;
+  const float* part_acc; const float* part_ml;
+};
+
+__device__ __forceinline__ int units_of(int L, int chunk, int NC) {
+  int n = (L + chunk - 1) / chunk;
+  n = n < 1 ? 1 : n;
+  return n > NC ? NC : n;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// Decode the unit of this workgroup; false when it has nothing to do.
+struct Unit {
+  int b, g, rb, c, nunits;
+  int k_beg, k_end;   // context keys of this unit
+  bool has_blk;
+};
+
+__device__ __forceinline__ bool decode_unit(int u, int Hkv, int RB, int NC, int chunk,
+                                            const int32_t* ctx_len, const uint8_t* active,
+                                            Unit& un) {
+  un.c = u % NC;
+  int t = u / NC;
+  un.rb = t % RB;
+  t /= RB;
+  un.g = t % Hkv;
+  un.b = t / Hkv;
+  if (active && !active[un.b]) return false;
+  const int L = ctx_len[un.b];
+  un.nunits = units_of(L, chunk, NC);
+  if (un.c >= un.nunits) return false;
+  un.k_beg = un.c * chunk;
+  un.k_end = (un.c == un.nunits - 1) ? L : (un.c + 1) * chunk;
+  if (un.k_end < un.k_beg) un.k_end = un.k_beg;  // L == 0
+  un.has_blk = (un.c == 0);
+  return true;
+}
+
+// ------------------------------------------------------------------ bf16
+template <int D>
+struct SmemBf16 {
+  uint16_t k[2][kTK][D + kKPad];
+  uint16_t vt[2][D][kTK + kVPad];
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void attn_bf16_kernel(KParams p) {
+  constexpr int KSTEPS = D / 16;      // MFMA k-steps of QK^T
+  constexpr int DT = D / 32;          // 32-channel tiles of the output
+  constexpr int SEGS = D / 8;         // 16-byte segments per key row
+  constexpr int KVEC = kTK * SEGS / 256;       // K vectors per thread per tile
+  constexpr int VPAIR = (kTK / 2) * SEGS / 256; // V key-pair units per thread
+  __shared__ SmemBf16<D> sm;
+
+  Unit un;
+  if (!decode_unit(blockIdx.x, p.Hkv, p.RB, p.NC, p.chunk, p.ctx_len, p.active, un)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int64_t kstride = static_cast<int64_t>(p.Hkv) * D;  // elements between keys
+
+  // ---- Q' = (q * (1 + scale) + shift) * log2(e)/sqrt(d), rounded to bf16
+  bf16x8 qf[2][KSTEPS];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int row = un.rb * kRowsBf16 + wave * 64 + rt * 32 + l32;
+    const bool valid = row < p.R;
+    const int s = valid ? row / p.G : 0;
+    const int h = un.g * p.G + (valid ? row % p.G : 0);
+    const uint16_t* qrow = p.q + ((static_cast<int64_t>(un.b) * p.S + s) * p.Hq + h) * D;
+    const float* sc = p.scale ? p.scale + (static_cast<int64_t>(un.b) * p.Hq + h) * D : nullptr;
+    const float* sh = p.shift ? p.shift + (static_cast<int64_t>(un.b) * p.Hq + h) * D : nullptr;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const int d0 = kk * 16 + half * 8;
+      float v[8];
+      if (valid) {
+        const uint4 w = *reinterpret_cast<const uint4*>(qrow + d0);
+        v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
+        v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
+        v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xffff0000u);
+        v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xffff0000u);
+        if (sc) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = v[i] * (1.f + sc[d0 + i]);
+        }
+        if (sh) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = v[i] + sh[d0 + i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[rt][kk][i] = static_cast<__bf16>(v[i] * p.qscale);
+    }
+  }
+
+  // ---- tile sources
+  const int n_ctx_tiles = (un.k_end - un.k_beg + kTK - 1) / kTK;
+  const int n_tiles = (un.has_blk ? 1 : 0) + n_ctx_tiles;
+  const int64_t ctx0 = p.ctx_start[un.b];
+  auto tile_src = [&](int t, const uint16_t*& kp, const uint16_t*& vp, int& nvalid) {
+    if (un.has_blk && t == 0) {
+      const int64_t off = (static_cast<int64_t>(un.b) * p.S * p.Hkv + un.g) * D;
+      kp = p.kb + off;
+      vp = p.vb + off;
+      nvalid = p.S;
+    } else {
+      const int i = t - (un.has_blk ? 1 : 0);
+      const int key0 = un.k_beg + i * kTK;
+      const int64_t off = ((ctx0 + key0) * p.Hkv + un.g) * D;
+      kp = p.kc + off;
+      vp = p.vc + off;
+      nvalid = min(kTK, un.k_end - key0);
+    }
+  };
+
+  uint4 kreg[KVEC];
+  uint4 vreg[VPAIR][2];
+  auto gload = [&](int t) {
+    const uint16_t* kp;
+    const uint16_t* vp;
+    int nv;
+    tile_src(t, kp, vp, nv);
+#pragma unroll
+    for (int j = 0; j < KVEC; ++j) {
+      const int v = tid + 256 * j;
+      const int key = v / SEGS, seg = v % SEGS;
+      kreg[j] = key < nv ? *reinterpret_cast<const uint4*>(kp + key * kstride + seg * 8)
+                         : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < VPAIR; ++j) {
+      const int pu = tid + 256 * j;
+      const int seg = pu % SEGS, kp2 = pu / SEGS;
+      const int k0 = 2 * kp2;
+      vreg[j][0] = k0 < nv ? *reinterpret_cast<const uint4*>(vp + k0 * kstride + seg * 8)
+                           : make_uint4(0, 0, 0, 0);
+      vreg[j][1] = k0 + 1 < nv ? *reinterpret_cast<const uint4*>(vp + (k0 + 1) * kstride + seg * 8)
+                               : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < KVEC; ++j) {
+      const int v = tid + 256 * j;
+      const int key = v / SEGS, seg = v % SEGS;
+      *reinterpret_cast<uint4*>(&sm.k[buf][key][seg * 8]) = kreg[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VPAIR; ++j) {
+      const int pu = tid + 256 * j;
+      const int seg = pu % SEGS, kp2 = pu / SEGS;
+      const uint32_t a[4] = {vreg[j][0].x, vreg[j][0].y, vreg[j][0].z, vreg[j][0].w};
+      const uint32_t c[4] = {vreg[j][1].x, vreg[j][1].y, vreg[j][1].z, vreg[j][1].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = (a[i] & 0xffffu) | (c[i] << 16);          // channel 2i
+        const uint32_t hi = (a[i] >> 16) | (c[i] & 0xffff0000u);      // channel 2i+1
+        *reinterpret_cast<uint32_t*>(&sm.vt[buf][seg * 8 + 2 * i][2 * kp2]) = lo;
+        *reinterpret_cast<uint32_t*>(&sm.vt[buf][seg * 8 + 2 * i + 1][2 * kp2]) = hi;
+      }
+    }
+  };
+
+  f32x16 acc[2][DT];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rt][dt][r] = 0.f;
+  float mu[2] = {-INFINITY, -INFINITY};
+  float lsum[2] = {0.f, 0.f};
+  const bool wave_has_rows = un.rb * kRowsBf16 + wave * 64 < p.R;
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) gload(t + 1);
+    int nvalid;
+    {
+      const uint16_t* kp;
+      const uint16_t* vp;
+      tile_src(t, kp, vp, nvalid);
+    }
+    if (wave_has_rows) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        if (kt * 32 >= nvalid) break;
+        f32x16 sacc[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[rt][r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&sm.k[buf][kt * 32 + l32][kk * 16 + half * 8]);
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+            sacc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[rt][kk], sacc[rt], 0, 0, 0);
+        }
+        if (nvalid < kt * 32 + 32) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            if (key >= nvalid) {
+              sacc[0][r] = -INFINITY;
+              sacc[1][r] = -INFINITY;
+            }
+          }
+        }
+        float tmax[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          float m = sacc[rt][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) m = fmaxf(m, sacc[rt][r]);
+          tmax[rt] = fmaxf(m, __shfl_xor(m, 32));
+        }
+        const bool need = (tmax[0] > mu[0] + kRescaleTh) || (tmax[1] > mu[1] + kRescaleTh);
+        if (__any(need)) {
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) {
+            const float mn = fmaxf(mu[rt], tmax[rt]);
+            const float alpha = __builtin_amdgcn_exp2f(mu[rt] - mn);
+            lsum[rt] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) acc[rt][dt][r] *= alpha;
+            mu[rt] = mn;
+          }
+        }
+        bf16x8 pb[2][2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          float ps = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = __builtin_amdgcn_exp2f(sacc[rt][r] - mu[rt]);
+            ps += e;
+            pb[rt][r >> 3][r & 7] = static_cast<__bf16>(e);
+          }
+          lsum[rt] += ps;
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const uint16_t* vrow = &sm.vt[buf][dt * 32 + l32][kt * 32 + 16 * ks + 4 * half];
+            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+            const uint4 w = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+              acc[rt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[rt][ks], acc[rt][dt], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (t + 1 < n_tiles) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- partials: (max, sum) per row and the unnormalised accumulator
+  const int64_t u = blockIdx.x;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const float ltot = lsum[rt] + __shfl_xor(lsum[rt], 32);
+    const int rl = wave * 64 + rt * 32 + l32;
+    if (un.rb * kRowsBf16 + rl >= p.R) continue;
+    if (half == 0) {
+      p.part_ml[(u * kRowsBf16 + rl) * 2 + 0] = mu[rt];
+      p.part_ml[(u * kRowsBf16 + rl) * 2 + 1] = ltot;
+    }
+    float* dst = p.part_acc + (u * kRowsBf16 + rl) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(dst + dt * 32 + 8 * j + 4 * half) =
+            make_float4(acc[rt][dt][4 * j], acc[rt][dt][4 * j + 1], acc[rt][dt][4 * j + 2],
+                        acc[rt][dt][4 * j + 3]);
+  }
+}
+
+// ------------------------------------------------------------------ fp32
+// Full-precision path: one lane per query row, fp32 throughout, exact running
+// max.  Used for fp32 storage (small problems and precision checks).
+template <int D>
+__global__ __launch_bounds__(64) void attn_f32_kernel(KParams p) {
+  constexpr int TKF = 16;
+  __shared__ float qs[kRowsF32][D + 1];
+  __shared__ float ks[TKF][D];
+  __shared__ float vs[TKF][D];
+  Unit un;
+  if (!decode_unit(blockIdx.x, p.Hkv, p.RB, p.NC, p.chunk, p.ctx_len, p.active, un)) return;
+  const int tid = threadIdx.x;
+  const float* q = static_cast<const float*>(p.qf);
+  const float* kb = static_cast<const float*>(p.kbf);
+  const float* vb = static_cast<const float*>(p.vbf);
+  const float* kc = static_cast<const float*>(p.kcf);
+  const float* vc = static_cast<const float*>(p.vcf);
+  const int64_t kstride = static_cast<int64_t>(p.Hkv) * D;
+  const int row = un.rb * kRowsF32 + tid;
+  const bool valid = row < p.R;
+  {
+    const int s = valid ? row / p.G : 0;
+    const int h = un.g * p.G + (valid ? row % p.G : 0);
+    const float* qrow = q + ((static_cast<int64_t>(un.b) * p.S + s) * p.Hq + h) * D;
+    const float* sc = p.scale ? p.scale + (static_cast<int64_t>(un.b) * p.Hq + h) * D : nullptr;
+    const float* sh = p.shift ? p.shift + (static_cast<int64_t>(un.b) * p.Hq + h) * D : nullptr;
+    for (int dd = 0; dd < D; ++dd) {
+      float v = valid ? qrow[dd] : 0.f;
+      if (valid && sc) v = v * (1.f + sc[dd]);
+      if (valid && sh) v = v + sh[dd];
+      qs[tid][dd] = v * p.qscale;
+    }
+  }
+  float acc[D];
+#pragma unroll
+  for (int dd = 0; dd < D; ++dd) acc[dd] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const int64_t ctx0 = p.ctx_start[un.b];
+  const int n_blk_tiles = un.has_blk ? (p.S + TKF - 1) / TKF : 0;
+  const int n_ctx_tiles = (un.k_end - un.k_beg + TKF - 1) / TKF;
+  const int n_tiles = n_blk_tiles + n_ctx_tiles;
+  for (int t = 0; t < n_tiles; ++t) {
+    const float* kp;
+    const float* vp;
+    int nv;
+    if (t < n_blk_tiles) {
+      const int64_t off = ((static_cast<int64_t>(un.b) * p.S + t * TKF) * p.Hkv + un.g) * D;
+      kp = kb + off;
+      vp = vb + off;
+      nv = min(TKF, p.S - t * TKF);
+    } else {
+      const int key0 = un.k_beg + (t - n_blk_tiles) * TKF;
+      const int64_t off = ((ctx0 + key0) * p.Hkv + un.g) * D;
+      kp = kc + off;
+      vp = vc + off;
+      nv = min(TKF, un.k_end - key0);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < TKF * D; idx += 64) {
+      const int key = idx / D, dd = idx % D;
+      ks[key][dd] = key < nv ? kp[key * kstride + dd] : 0.f;
+      vs[key][dd] = key < nv ? vp[key * kstride + dd] : 0.f;
+    }
+    __syncthreads();
+    for (int key = 0; key < nv; ++key) {
+      float s = 0.f;
+#pragma unroll 8
+      for (int dd = 0; dd < D; ++dd) s = fmaf(qs[tid][dd], ks[key][dd], s);
+      const float mn = fmaxf(m, s);
+      const float alpha = exp2f(m - mn);
+      const float pr = exp2f(s - mn);
+      l = l * alpha + pr;
+#pragma unroll
+      for (int dd = 0; dd < D; ++dd) acc[dd] = fmaf(pr, vs[key][dd], acc[dd] * alpha);
+      m = mn;
+    }
+  }
+  if (!valid) return;
+  const int64_t u = blockIdx.x;
+  p.part_ml[(u * kRowsF32 + tid) * 2 + 0] = m;
+  p.part_ml[(u * kRowsF32 + tid) * 2 + 1] = l;
+  float* dst = p.part_acc + (u * kRowsF32 + tid) * D;
+#pragma unroll
+  for (int dd = 0; dd < D; ++dd) dst[dd] = acc[dd];
+}
+
+// ------------------------------------------------------------------ merge
+// o = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c, combined in chunk
+// order; lse = ln2 * (M + log2 sum); out = residual + gate * o.
+template <typename OutT>
+__device__ __forceinline__ void store4(OutT* dst, float a, float b, float c, float d);
+
+template <>
+__device__ __forceinline__ void store4<float>(float* dst, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+}
+
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* dst, float a, float b, float c, float d) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 v = {static_cast<__bf16>(a), static_cast<__bf16>(b), static_cast<__bf16>(c),
+              static_cast<__bf16>(d)};
+  *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, v);
+}
+
+template <typename OutT>
+__device__ __forceinline__ void load4(const OutT* src, float (&v)[4]);
+
+template <>
+__device__ __forceinline__ void load4<float>(const float* src, float (&v)[4]) {
+  const float4 x = *reinterpret_cast<const float4*>(src);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+}
+
+template <>
+__device__ __forceinline__ void load4<uint16_t>(const uint16_t* src, float (&v)[4]) {
+  const uint2 x = *reinterpret_cast<const uint2*>(src);
+  v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xffff0000u);
+  v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xffff0000u);
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(256) void merge_kernel(MParams p) {
+  const int D = p.D;
+  const int quads = D / 4;
+  const int grp = blockIdx.y;  // (b, g, rb)
+  const int rb = grp % p.RB;
+  const int g = (grp / p.RB) % p.Hkv;
+  const int b = grp / (p.RB * p.Hkv);
+  if (p.active && !p.active[b]) return;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int rl = idx / quads, dq = idx % quads;
+  if (rl >= p.rows_per_unit) return;
+  const int row = rb * p.rows_per_unit + rl;
+  if (row >= p.R) return;
+  const int n = units_of(p.ctx_len[b], p.chunk, p.NC);
+  const int64_t u0 = static_cast<int64_t>(grp) * p.NC;
+  float M = -INFINITY;
+  for (int c = 0; c < n; ++c) M = fmaxf(M, p.part_ml[((u0 + c) * p.rows_per_unit + rl) * 2]);
+  float wsum = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  for (int c = 0; c < n; ++c) {
+    const int64_t base = (u0 + c) * p.rows_per_unit + rl;
+    const float w = exp2f(p.part_ml[base * 2] - M);
+    wsum = fmaf(w, p.part_ml[base * 2 + 1], wsum);
+    const float4 a = *reinterpret_cast<const float4*>(p.part_acc + base * D + dq * 4);
+    o0 = fmaf(w, a.x, o0); o1 = fmaf(w, a.y, o1); o2 = fmaf(w, a.z, o2); o3 = fmaf(w, a.w, o3);
+  }
+  const float inv = 1.f / wsum;
+  float o[4] = {o0 * inv, o1 * inv, o2 * inv, o3 * inv};
+  const int s = row / p.G, h = g * p.G + row % p.G;
+  const int64_t orow = (static_cast<int64_t>(b) * p.S + s) * p.Hq + h;
+  if (p.gate) {
+    const float4 gv = *reinterpret_cast<const float4*>(p.gate + (static_cast<int64_t>(b) * p.Hq + h) * D + dq * 4);
+    o[0] *= gv.x; o[1] *= gv.y; o[2] *= gv.z; o[3] *= gv.w;
+  }
+  if (p.residual) {
+    float r[4];
+    load4<OutT>(static_cast<const OutT*>(p.residual) + orow * D + dq * 4, r);
+    o[0] += r[0]; o[1] += r[1]; o[2] += r[2]; o[3] += r[3];
+  }
+  store4<OutT>(static_cast<OutT*>(p.out) + orow * D + dq * 4, o[0], o[1], o[2], o[3]);
+  if (p.lse && dq == 0) p.lse[orow] = 0.6931471805599453f * (M + log2f(wsum));
+}
+
+}  // namespace
+
+AttnPlan attn_plan(int B, int S, int Hq, int Hkv, int d, int dtype, int max_ctx_len) {
+  AttnPlan pl{};
+  const int G = Hq / Hkv;
+  pl.rows = S * G;
+  pl.rows_per_unit = dtype == 0 ? kRowsBf16 : kRowsF32;
+  pl.row_blocks = static_cast<int>(ceil_div(pl.rows, pl.rows_per_unit));
+  const int64_t groups = static_cast<int64_t>(B) * Hkv * pl.row_blocks;
+  const int64_t want = ceil_div(2 * kNumCUs, groups);
+  int64_t chunk = max_ctx_len > 0 ? ceil_div(max_ctx_len, want < 1 ? 1 : want) : kTK;
+  chunk = static_cast<int64_t>(align_up(static_cast<size_t>(chunk), kTK));
+  if (chunk < kTK) chunk = kTK;
+  pl.chunk = static_cast<int>(chunk);
+  int64_t nc = max_ctx_len > 0 ? ceil_div(max_ctx_len, chunk) : 1;
+  pl.n_chunks = static_cast<int>(nc < 1 ? 1 : nc);
+  const int64_t units = groups * pl.n_chunks;
+  pl.part_acc_bytes = align_up(static_cast<size_t>(units) * pl.rows_per_unit * d * sizeof(float), 256);
+  pl.part_ml_bytes = align_up(static_cast<size_t>(units) * pl.rows_per_unit * 2 * sizeof(float), 256);
+  pl.total_bytes = pl.part_acc_bytes + pl.part_ml_bytes;
+  return pl;
+}
+
+hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& pl, void* ws, hipStream_t st) {
+  const int G = a.Hq / a.Hkv;
+  KParams kp{};
+  kp.B = a.B; kp.S = a.S; kp.Hq = a.Hq; kp.Hkv = a.Hkv; kp.G = G; kp.R = pl.rows;
+  kp.rows_per_unit = pl.rows_per_unit; kp.RB = pl.row_blocks; kp.NC = pl.n_chunks;
+  kp.chunk = pl.chunk;
+  kp.q = static_cast<const uint16_t*>(a.q); kp.kb = static_cast<const uint16_t*>(a.kb);
+  kp.vb = static_cast<const uint16_t*>(a.vb); kp.kc = static_cast<const uint16_t*>(a.kc);
+  kp.vc = static_cast<const uint16_t*>(a.vc);
+  kp.qf = a.q; kp.kbf = a.kb; kp.vbf = a.vb; kp.kcf = a.kc; kp.vcf = a.vc;
+  kp.ctx_start = a.ctx_start; kp.ctx_len = a.ctx_len; kp.active = a.active;
+  kp.shift = a.shift; kp.scale = a.scale;
+  kp.qscale = kLog2e / sqrtf(static_cast<float>(a.d));
+  kp.part_acc = static_cast<float*>(ws);
+  kp.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.part_acc_bytes);
+  const int64_t units = static_cast<int64_t>(a.B) * a.Hkv * pl.row_blocks * pl.n_chunks;
+  if (a.dtype == 0) {
+    if (a.d == 128)
+      hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(static_cast<unsigned>(units)), dim3(256), 0, st, kp);
+    else
+      hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(static_cast<unsigned>(units)), dim3(256), 0, st, kp);
+  } else {
+    if (a.d == 128)
+      hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(static_cast<unsigned>(units)), dim3(64), 0, st, kp);
+    else
+      hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(static_cast<unsigned>(units)), dim3(64), 0, st, kp);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  MParams mp{};
+  mp.B = a.B; mp.S = a.S; mp.Hq = a.Hq; mp.Hkv = a.Hkv; mp.G = G; mp.R = pl.rows; mp.D = a.d;
+  mp.rows_per_unit = pl.rows_per_unit; mp.RB = pl.row_blocks; mp.NC = pl.n_chunks;
+  mp.chunk = pl.chunk; mp.ctx_len = a.ctx_len; mp.active = a.active; mp.gate = a.gate;
+  mp.residual = a.residual; mp.out = a.out; mp.lse = a.lse;
+  mp.part_acc = kp.part_acc; mp.part_ml = kp.part_ml;
+  const int per_grp = pl.rows_per_unit * (a.d / 4);
+  const dim3 mg(static_cast<unsigned>(ceil_div(per_grp, 256)),
+                static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * pl.row_blocks));
+  if (a.dtype == 0)
+    hipLaunchKernelGGL(merge_kernel<uint16_t>, mg, dim3(256), 0, st, mp);
+  else
+    hipLaunchKernelGGL(merge_kernel<float>, mg, dim3(256), 0, st, mp);
+  return hipGetLastError();
+}
+
+}  // namespace tt

@@ -1,0 +1,366 @@
+// Host side of the C ABI declared in include/tt.h: argument validation (no
+// HIP call happens before every host-visible argument has been checked),
+// workspace carving, kernel launches and the block denoising loop.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/tt.h"
+#include "tt_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+tt_status fail(tt_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+tt_status ok() {
+  g_err.clear();
+  return TT_OK;
+}
+
+tt_status hip_fail(hipError_t e, const char* what) {
+  return fail(TT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elt_size(int dtype) { return dtype == TT_BF16 ? 2 : 4; }
+
+tt_status check_shape(const tt_attn_shape* s) {
+  if (!s) return fail(TT_ERR_INVALID_ARG, "shape is NULL");
+  if (s->batch < 0) return fail(TT_ERR_INVALID_ARG, "batch %d < 0", s->batch);
+  if (s->n_q_heads < 1 || s->n_kv_heads < 1)
+    return fail(TT_ERR_INVALID_ARG, "head counts must be >= 1 (Hq=%d, Hkv=%d)", s->n_q_heads,
+                s->n_kv_heads);
+  if (s->n_q_heads % s->n_kv_heads != 0)
+    return fail(TT_ERR_INVALID_ARG, "n_q_heads %d is not a multiple of n_kv_heads %d",
+                s->n_q_heads, s->n_kv_heads);
+  if (s->n_q_heads > 4096) return fail(TT_ERR_INVALID_ARG, "n_q_heads %d > 4096", s->n_q_heads);
+  if (s->head_dim < 1) return fail(TT_ERR_INVALID_ARG, "head_dim %d < 1", s->head_dim);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(TT_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", s->head_dim);
+  if (s->block_size < 1 || s->block_size > 64)
+    return fail(TT_ERR_INVALID_ARG, "block_size %d outside [1, 64]", s->block_size);
+  if (s->dtype != TT_BF16 && s->dtype != TT_F32)
+    return fail(TT_ERR_INVALID_ARG, "dtype %d is neither TT_BF16 nor TT_F32", s->dtype);
+  return TT_OK;
+}
+
+tt_status check_unmask_scalars(int32_t batch, int32_t S, int32_t V, int64_t row_stride,
+                               float gamma, float temperature) {
+  if (batch < 0) return fail(TT_ERR_INVALID_ARG, "batch %d < 0", batch);
+  if (S < 1 || S > 64) return fail(TT_ERR_INVALID_ARG, "block_size %d outside [1, 64]", S);
+  if (V < 1) return fail(TT_ERR_INVALID_ARG, "vocab %d < 1", V);
+  if (row_stride < V)
+    return fail(TT_ERR_INVALID_ARG, "row_stride %lld < vocab %d", (long long)row_stride, V);
+  if (isnan(gamma)) return fail(TT_ERR_INVALID_ARG, "gamma is NaN");
+  if (!(temperature >= 1e-30f) || isinf(temperature))
+    return fail(TT_ERR_INVALID_ARG, "temperature %g must be finite and >= 1e-30", temperature);
+  return TT_OK;
+}
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  void* take(size_t bytes) {
+    void* p = base + off;
+    off += tt::align_up(bytes, 256);
+    return p;
+  }
+};
+
+size_t denoise_bytes(const tt_attn_shape* s, int n_layers, int max_ctx_len, int vocab) {
+  const size_t B = s->batch, S = s->block_size, Hq = s->n_q_heads, Hkv = s->n_kv_heads,
+               d = s->head_dim, e = elt_size(s->dtype), W = Hq * d;
+  size_t t = 0;
+  auto add = [&](size_t b) { t += tt::align_up(b, 256); };
+  add(static_cast<size_t>(n_layers) * 3 * B * W * 4);  // ada
+  add(B * TT_TIMESTEP_DIM * 4);                          // emb
+  add(B * S * Hq * d * e);                               // q
+  add(B * S * Hkv * d * e);                              // k
+  add(B * S * Hkv * d * e);                              // v
+  add(B * S * Hq * d * e);                               // out
+  add(B * S * static_cast<size_t>(vocab) * e);           // logits
+  add(B * 4);                                            // n_masked
+  add(B);                                                // active
+  add(4);                                                // total
+  const tt::AttnPlan ap = tt::attn_plan(s->batch, s->block_size, s->n_q_heads, s->n_kv_heads,
+                                        s->head_dim, s->dtype, max_ctx_len);
+  add(ap.total_bytes);
+  const tt::UnmaskPlan up = tt::unmask_plan(s->batch, s->block_size, vocab);
+  add(up.total_bytes);
+  return t;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tt_last_error(void) { return g_err.c_str(); }
+
+int tt_abi_version(void) { return TT_ABI_VERSION; }
+
+size_t tt_block_attn_workspace_size(const tt_attn_shape* shape, int32_t max_ctx_len) {
+  if (check_shape(shape) != TT_OK) return 0;
+  if (max_ctx_len < 0) {
+    fail(TT_ERR_INVALID_ARG, "max_ctx_len %d < 0", max_ctx_len);
+    return 0;
+  }
+  ok();
+  const tt::AttnPlan p = tt::attn_plan(shape->batch, shape->block_size, shape->n_q_heads,
+                                       shape->n_kv_heads, shape->head_dim, shape->dtype,
+                                       max_ctx_len);
+  return p.total_bytes < 256 ? 256 : p.total_bytes;
+}
+
+tt_status tt_block_attn(const tt_attn_shape* shape, const void* q_blk, const void* k_blk,
+                        const void* v_blk, const void* k_ctx, const void* v_ctx,
+                        const int64_t* ctx_start, const int32_t* ctx_len, int32_t max_ctx_len,
+                        const uint8_t* active, const float* ada_shift, const float* ada_scale,
+                        const float* ada_gate, const void* residual, void* out, float* lse,
+                        void* workspace, size_t workspace_bytes, tt_stream stream) {
+  tt_status st = check_shape(shape);
+  if (st != TT_OK) return st;
+  if (max_ctx_len < 0) return fail(TT_ERR_INVALID_ARG, "max_ctx_len %d < 0", max_ctx_len);
+  if (!q_blk || !k_blk || !v_blk || !out)
+    return fail(TT_ERR_INVALID_ARG, "q_blk, k_blk, v_blk and out must be non-NULL");
+  if (!k_ctx || !v_ctx || !ctx_start || !ctx_len)
+    return fail(TT_ERR_INVALID_ARG, "k_ctx, v_ctx, ctx_start and ctx_len must be non-NULL");
+  const void* tensors[] = {q_blk, k_blk, v_blk, k_ctx, v_ctx, out, residual};
+  for (const void* t : tensors)
+    if (t && !aligned(t, 16))
+      return fail(TT_ERR_INVALID_ARG, "q/k/v/context/out/residual buffers must be 16-byte aligned");
+  if (ada_gate && !aligned(ada_gate, 16))
+    return fail(TT_ERR_INVALID_ARG, "ada_gate must be 16-byte aligned");
+  if (!aligned(ctx_start, 8) || !aligned(ctx_len, 4) || (lse && !aligned(lse, 4)) ||
+      (ada_shift && !aligned(ada_shift, 4)) || (ada_scale && !aligned(ada_scale, 4)))
+    return fail(TT_ERR_INVALID_ARG, "misaligned ctx_start/ctx_len/lse/ada buffer");
+  if (shape->batch == 0) return ok();
+  const tt::AttnPlan p = tt::attn_plan(shape->batch, shape->block_size, shape->n_q_heads,
+                                       shape->n_kv_heads, shape->head_dim, shape->dtype,
+                                       max_ctx_len);
+  if (!workspace || workspace_bytes < p.total_bytes)
+    return fail(TT_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
+                p.total_bytes);
+  if (!aligned(workspace, 256))
+    return fail(TT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  tt::AttnArgs a{};
+  a.B = shape->batch; a.S = shape->block_size; a.Hq = shape->n_q_heads;
+  a.Hkv = shape->n_kv_heads; a.d = shape->head_dim; a.dtype = shape->dtype;
+  a.q = q_blk; a.kb = k_blk; a.vb = v_blk; a.kc = k_ctx; a.vc = v_ctx;
+  a.ctx_start = ctx_start; a.ctx_len = ctx_len; a.active = active;
+  a.shift = ada_shift; a.scale = ada_scale; a.gate = ada_gate;
+  a.residual = residual; a.out = out; a.lse = lse;
+  const hipError_t e = tt::launch_block_attn(a, p, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tt_block_attn launch");
+  return ok();
+}
+
+tt_status tt_workspace_clear(void* workspace, size_t bytes, tt_stream stream) {
+  if (bytes == 0) return ok();
+  if (!workspace) return fail(TT_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(workspace, 16)) return fail(TT_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const hipError_t e = tt::launch_clear(workspace, bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tt_workspace_clear launch");
+  return ok();
+}
+
+tt_status tt_timestep_embed(int32_t batch, const float* t, float* emb, tt_stream stream) {
+  if (batch < 0) return fail(TT_ERR_INVALID_ARG, "batch %d < 0", batch);
+  if (!t || !emb) return fail(TT_ERR_INVALID_ARG, "t and emb must be non-NULL");
+  if (batch == 0) return ok();
+  const hipError_t e =
+      tt::launch_timestep_embed(batch, t, nullptr, 1, emb, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tt_timestep_embed launch");
+  return ok();
+}
+
+tt_status tt_adaln_single(int32_t batch, int32_t width, int32_t n_layers, const float* t_emb,
+                          const void* w, const float* bias, const float* table, float* ada,
+                          tt_stream stream) {
+  if (batch < 0) return fail(TT_ERR_INVALID_ARG, "batch %d < 0", batch);
+  if (width < 4 || width % 4 != 0)
+    return fail(TT_ERR_INVALID_ARG, "width %d must be a positive multiple of 4", width);
+  if (n_layers < 1) return fail(TT_ERR_INVALID_ARG, "n_layers %d < 1", n_layers);
+  if (!t_emb || !w || !ada) return fail(TT_ERR_INVALID_ARG, "t_emb, w and ada must be non-NULL");
+  if (!aligned(w, 2) || !aligned(t_emb, 4) || !aligned(ada, 4))
+    return fail(TT_ERR_INVALID_ARG, "misaligned adaLN buffer");
+  if (batch == 0) return ok();
+  const hipError_t e = tt::launch_adaln_single(batch, width, n_layers, t_emb, w, bias, table, ada,
+                                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tt_adaln_single launch");
+  return ok();
+}
+
+size_t tt_unmask_workspace_size(int32_t batch, int32_t block_size, int32_t vocab) {
+  if (check_unmask_scalars(batch, block_size, vocab, vocab, 0.f, 1.f) != TT_OK) return 0;
+  ok();
+  const tt::UnmaskPlan p = tt::unmask_plan(batch, block_size, vocab);
+  return p.total_bytes < 256 ? 256 : p.total_bytes;
+}
+
+tt_status tt_confidence_unmask(int32_t batch, int32_t block_size, int32_t vocab,
+                               const void* logits, int32_t dtype, int64_t row_stride, float gamma,
+                               float temperature, int32_t mask_token_id, int32_t step,
+                               int32_t* tokens, uint8_t* masked, uint8_t* committed_now,
+                               float* conf, int32_t* pred, int8_t* commit_step,
+                               int32_t* n_masked, void* workspace, size_t workspace_bytes,
+                               tt_stream stream) {
+  tt_status st = check_unmask_scalars(batch, block_size, vocab, row_stride, gamma, temperature);
+  if (st != TT_OK) return st;
+  if (dtype != TT_BF16 && dtype != TT_F32)
+    return fail(TT_ERR_INVALID_ARG, "dtype %d is neither TT_BF16 nor TT_F32", dtype);
+  if (!logits || !tokens || !masked)
+    return fail(TT_ERR_INVALID_ARG, "logits, tokens and masked must be non-NULL");
+  if (!aligned(logits, elt_size(dtype)) || !aligned(tokens, 4) || (conf && !aligned(conf, 4)) ||
+      (pred && !aligned(pred, 4)) || (n_masked && !aligned(n_masked, 4)))
+    return fail(TT_ERR_INVALID_ARG, "misaligned unmasking buffer");
+  if (batch == 0) return ok();
+  const tt::UnmaskPlan p = tt::unmask_plan(batch, block_size, vocab);
+  if (!workspace || workspace_bytes < p.total_bytes)
+    return fail(TT_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
+                p.total_bytes);
+  if (!aligned(workspace, 16)) return fail(TT_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  tt::UnmaskArgs a{};
+  a.B = batch; a.S = block_size; a.V = vocab; a.dtype = dtype;
+  a.logits = logits; a.row_stride = row_stride; a.gamma = gamma; a.temperature = temperature;
+  a.mask_id = mask_token_id; a.step = step; a.tokens = tokens; a.masked = masked;
+  a.committed_now = committed_now; a.conf = conf; a.pred = pred; a.commit_step = commit_step;
+  a.n_masked = n_masked;
+  const hipError_t e =
+      tt::launch_confidence_unmask(a, p, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tt_confidence_unmask launch");
+  return ok();
+}
+
+size_t tt_denoise_workspace_size(const tt_attn_shape* shape, int32_t n_layers,
+                                 int32_t max_ctx_len, int32_t vocab) {
+  if (check_shape(shape) != TT_OK) return 0;
+  if (n_layers < 1 || max_ctx_len < 0 || vocab < 1) {
+    fail(TT_ERR_INVALID_ARG, "n_layers %d, max_ctx_len %d, vocab %d", n_layers, max_ctx_len, vocab);
+    return 0;
+  }
+  ok();
+  return denoise_bytes(shape, n_layers, max_ctx_len, vocab);
+}
+
+tt_status tt_denoise_block(const tt_attn_shape* shape, int32_t n_layers, int32_t max_steps,
+                           float gamma, float temperature, int32_t mask_token_id, int32_t vocab,
+                           const void* const* k_ctx_layers, const void* const* v_ctx_layers,
+                           const int64_t* ctx_start, const int32_t* ctx_len, int32_t max_ctx_len,
+                           const void* ada_w, const float* ada_bias, const float* ada_table,
+                           const tt_step_provider* provider, int32_t* tokens, uint8_t* masked,
+                           int8_t* commit_step, int32_t* steps_taken, void* workspace,
+                           size_t workspace_bytes, tt_stream stream) {
+  if (steps_taken) *steps_taken = 0;
+  tt_status st = check_shape(shape);
+  if (st != TT_OK) return st;
+  const int S = shape->block_size;
+  if (n_layers < 1) return fail(TT_ERR_INVALID_ARG, "n_layers %d < 1", n_layers);
+  if (max_steps < 0 || max_steps > S)
+    return fail(TT_ERR_INVALID_ARG, "max_steps %d outside [0, block_size=%d]", max_steps, S);
+  if (max_ctx_len < 0) return fail(TT_ERR_INVALID_ARG, "max_ctx_len %d < 0", max_ctx_len);
+  st = check_unmask_scalars(shape->batch, S, vocab, vocab, gamma, temperature);
+  if (st != TT_OK) return st;
+  if (!k_ctx_layers || !v_ctx_layers)
+    return fail(TT_ERR_INVALID_ARG, "k_ctx_layers and v_ctx_layers must be non-NULL");
+  for (int l = 0; l < n_layers; ++l) {
+    if (!k_ctx_layers[l] || !v_ctx_layers[l])
+      return fail(TT_ERR_INVALID_ARG, "context cache of layer %d is NULL", l);
+    if (!aligned(k_ctx_layers[l], 16) || !aligned(v_ctx_layers[l], 16))
+      return fail(TT_ERR_INVALID_ARG, "context cache of layer %d is not 16-byte aligned", l);
+  }
+  if (!ctx_start || !ctx_len) return fail(TT_ERR_INVALID_ARG, "ctx_start and ctx_len must be non-NULL");
+  if (!provider || !provider->layer_inputs || !provider->logits)
+    return fail(TT_ERR_INVALID_ARG, "provider and both of its callbacks must be non-NULL");
+  if (!tokens || !masked) return fail(TT_ERR_INVALID_ARG, "tokens and masked must be non-NULL");
+  if (ada_w && (shape->n_q_heads * shape->head_dim) % 4 != 0)
+    return fail(TT_ERR_INVALID_ARG, "adaLN width must be a multiple of 4");
+  if (shape->batch == 0 || max_steps == 0) return ok();
+  const size_t need = denoise_bytes(shape, n_layers, max_ctx_len, vocab);
+  if (!workspace || workspace_bytes < need)
+    return fail(TT_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(TT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+  const int B = shape->batch, Hq = shape->n_q_heads, Hkv = shape->n_kv_heads, d = shape->head_dim;
+  const size_t e = elt_size(shape->dtype), W = static_cast<size_t>(Hq) * d;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  Carver cv{static_cast<char*>(workspace)};
+  float* ada = static_cast<float*>(cv.take(static_cast<size_t>(n_layers) * 3 * B * W * 4));
+  float* emb = static_cast<float*>(cv.take(static_cast<size_t>(B) * TT_TIMESTEP_DIM * 4));
+  void* q = cv.take(static_cast<size_t>(B) * S * Hq * d * e);
+  void* kb = cv.take(static_cast<size_t>(B) * S * Hkv * d * e);
+  void* vb = cv.take(static_cast<size_t>(B) * S * Hkv * d * e);
+  void* out = cv.take(static_cast<size_t>(B) * S * Hq * d * e);
+  void* logits = cv.take(static_cast<size_t>(B) * S * vocab * e);
+  int32_t* n_masked = static_cast<int32_t*>(cv.take(static_cast<size_t>(B) * 4));
+  uint8_t* active = static_cast<uint8_t*>(cv.take(B));
+  int32_t* total = static_cast<int32_t*>(cv.take(4));
+  const tt::AttnPlan ap = tt::attn_plan(B, S, Hq, Hkv, d, shape->dtype, max_ctx_len);
+  void* attn_ws = cv.take(ap.total_bytes);
+  const tt::UnmaskPlan up = tt::unmask_plan(B, S, vocab);
+  void* unmask_ws = cv.take(up.total_bytes);
+
+  hipError_t he = tt::launch_count_masked(B, S, masked, n_masked, hs);
+  if (he != hipSuccess) return hip_fail(he, "tt_denoise_block count");
+  for (int k = 0; k < max_steps; ++k) {
+    he = tt::launch_active_from_masked(B, n_masked, active, total, hs);
+    if (he != hipSuccess) return hip_fail(he, "tt_denoise_block active");
+    int32_t host_total = 0;
+    he = hipMemcpyAsync(&host_total, total, sizeof(int32_t), hipMemcpyDeviceToHost, hs);
+    if (he == hipSuccess) he = hipStreamSynchronize(hs);
+    if (he != hipSuccess) return hip_fail(he, "tt_denoise_block masked-count readback");
+    if (host_total == 0) break;
+    if (ada_w) {
+      he = tt::launch_timestep_embed(B, nullptr, n_masked, S, emb, hs);
+      if (he == hipSuccess)
+        he = tt::launch_adaln_single(B, static_cast<int>(W), n_layers, emb, ada_w, ada_bias,
+                                     ada_table, ada, hs);
+      if (he != hipSuccess) return hip_fail(he, "tt_denoise_block adaLN");
+    }
+    for (int l = 0; l < n_layers; ++l) {
+      const int rc = provider->layer_inputs(provider->user, k, l, l == 0 ? nullptr : out, q, kb,
+                                            vb, stream);
+      if (rc != 0)
+        return fail(TT_ERR_CALLBACK, "layer_inputs(step %d, layer %d) returned %d", k, l, rc);
+      tt::AttnArgs a{};
+      a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.dtype = shape->dtype;
+      a.q = q; a.kb = kb; a.vb = vb; a.kc = k_ctx_layers[l]; a.vc = v_ctx_layers[l];
+      a.ctx_start = ctx_start; a.ctx_len = ctx_len; a.active = active;
+      if (ada_w) {
+        a.shift = ada + (static_cast<size_t>(l) * 3 + 0) * B * W;
+        a.scale = ada + (static_cast<size_t>(l) * 3 + 1) * B * W;
+        a.gate = ada + (static_cast<size_t>(l) * 3 + 2) * B * W;
+      }
+      a.residual = nullptr; a.out = out; a.lse = nullptr;
+      he = tt::launch_block_attn(a, ap, attn_ws, hs);
+      if (he != hipSuccess) return hip_fail(he, "tt_denoise_block attention");
+    }
+    const int rc = provider->logits(provider->user, k, out, logits, stream);
+    if (rc != 0) return fail(TT_ERR_CALLBACK, "logits(step %d) returned %d", k, rc);
+    tt::UnmaskArgs ua{};
+    ua.B = B; ua.S = S; ua.V = vocab; ua.dtype = shape->dtype; ua.logits = logits;
+    ua.row_stride = vocab; ua.gamma = gamma; ua.temperature = temperature;
+    ua.mask_id = mask_token_id; ua.step = k; ua.tokens = tokens; ua.masked = masked;
+    ua.commit_step = commit_step; ua.n_masked = n_masked;
+    he = tt::launch_confidence_unmask(ua, up, unmask_ws, hs);
+    if (he != hipSuccess) return hip_fail(he, "tt_denoise_block unmasking");
+    if (steps_taken) *steps_taken = k + 1;
+  }
+  he = hipStreamSynchronize(hs);
+  if (he != hipSuccess) return hip_fail(he, "tt_denoise_block final sync");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Internal declarations shared by the libtt translation units: launch
+// parameter blocks, sizing rules and the kernel launchers.  Nothing here is
+// part of the C ABI (include/tt.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tt {
+
+// The launch-shape rules are fixed for the 256-CU MI355X so that a workspace
+// size computed on any host matches what the launch uses.
+constexpr int kNumCUs = 256;
+
+constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- attention
+// Rows of one (sequence, KV head) group: r = s * G + j  (block slot s, query
+// head h = g * G + j).  Keys of a unit: the block's S keys (chunk 0 only)
+// then context tokens [c * chunk, end).  Partials of unit u = (((b * Hkv + g)
+// * RB + rb) * NC + c) hold, per row of the row block, the running max m
+// (log2 units), the sum l and the unnormalised accumulator acc[d].
+struct AttnPlan {
+  int rows;           // R = S * G
+  int rows_per_unit;  // rows a workgroup owns (row block height)
+  int row_blocks;     // RB
+  int chunk;          // context keys per unit (multiple of 64)
+  int n_chunks;       // NC: unit slots per (b, g, rb)
+  size_t part_acc_bytes;
+  size_t part_ml_bytes;
+  size_t total_bytes;
+};
+
+struct AttnArgs {
+  int B, S, Hq, Hkv, d, dtype;
+  const void* q; const void* kb; const void* vb;
+  const void* kc; const void* vc;
+  const int64_t* ctx_start; const int32_t* ctx_len;
+  const uint8_t* active;
+  const float* shift; const float* scale; const float* gate;
+  const void* residual; void* out; float* lse;
+};
+
+AttnPlan attn_plan(int B, int S, int Hq, int Hkv, int d, int dtype, int max_ctx_len);
+hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, void* ws, hipStream_t st);
+
+// ---------------------------------------------------------------- unmasking
+struct UnmaskPlan {
+  int splits;      // workgroups per row
+  int split_len;   // vocab entries per split (multiple of 8)
+  size_t part_bytes;
+  size_t total_bytes;
+};
+
+struct UnmaskArgs {
+  int B, S, V, dtype;
+  const void* logits; int64_t row_stride;
+  float gamma, temperature;
+  int mask_id, step;
+  int32_t* tokens; uint8_t* masked;
+  uint8_t* committed_now; float* conf; int32_t* pred;
+  int8_t* commit_step; int32_t* n_masked;
+};
+
+UnmaskPlan unmask_plan(int B, int S, int V);
+hipError_t launch_confidence_unmask(const UnmaskArgs& a, const UnmaskPlan& p, void* ws,
+                                    hipStream_t st);
+
+// ---------------------------------------------------------------- adaLN
+hipError_t launch_timestep_embed(int B, const float* t, const int32_t* n_masked, int S,
+                                 float* emb, hipStream_t st);
+hipError_t launch_adaln_single(int B, int width, int n_layers, const float* emb,
+                               const void* w, const float* bias, const float* table,
+                               float* ada, hipStream_t st);
+hipError_t launch_active_from_masked(int B, const int32_t* n_masked, uint8_t* active,
+                                     int32_t* total, hipStream_t st);
+hipError_t launch_count_masked(int B, int S, const uint8_t* masked, int32_t* n_masked,
+                               hipStream_t st);
+hipError_t launch_clear(void* p, size_t bytes, hipStream_t st);
+
+}  // namespace tt

@@ -1,0 +1,266 @@
+/*
+ * tt.h -- C ABI of libtt: the block-denoising step of a two-tower block
+ * mask-diffusion language model, hand-written for AMD MI355X (gfx950).
+ *
+ * Pages cited (title, site):
+ *   [keyframe]  "Diffusion Nemotron: Nvidia's "Two Brain" Diffusion Model"
+ *               (keyframe.defihacklabs.io)
+ *   [news]      "NVIDIA发布Nemotron两塔模型，实现2.42倍文本生成吞吐并保持98.7%质量"
+ *               (889990.xyz)
+ *   [dothoosh]  "فرآیند انتشار در برابر رمزگشایی متوالی در مدل جدید انویدیا"
+ *               (dothoosh.com)
+ *   [modelcard] "Nemotron-Labs-TwoTower-30B-A3B-Base-BF16" digest (aitrends.kr)
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers marked "device" are HIP device (or managed) memory; "host"
+ *     pointers are ordinary CPU memory.  The caller owns every buffer.  The
+ *     library allocates no device memory: scratch space comes from a
+ *     caller-provided workspace sized by the matching *_workspace_size().
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL means the null
+ *     stream), except tt_denoise_block, which waits on the stream once per
+ *     denoising step to read how many slots are still masked.
+ *   - Every host-visible argument is validated before anything is launched.
+ *     An invalid call returns a status, stores a message readable through
+ *     tt_last_error() and launches nothing.  A failing HIP call returns
+ *     TT_ERR_HIP.
+ *   - No global mutable state besides the thread-local error message; calls
+ *     on different streams with different workspaces may run concurrently.
+ *     Two calls in flight must not share one workspace.
+ *   - bf16 is IEEE-754 binary32 truncated to its upper 16 bits (bfloat16).
+ *   - Limits: head_dim in {64, 128}; block_size S in [1, 64]; n_q_heads a
+ *     multiple of n_kv_heads; temperature finite and > 0; gamma finite.
+ */
+#ifndef TT_H
+#define TT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TT_ABI_VERSION 1
+#define TT_TIMESTEP_DIM 256 /* width of the timestep embedding */
+
+typedef enum {
+  TT_OK = 0,
+  TT_ERR_INVALID_ARG = 1, /* a pointer, size or value outside the contract  */
+  TT_ERR_UNSUPPORTED = 2, /* valid but not implemented (e.g. head_dim 96)    */
+  TT_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required     */
+  TT_ERR_HIP = 4,         /* a HIP runtime call failed                       */
+  TT_ERR_CALLBACK = 5     /* a step-provider callback returned non-zero     */
+} tt_status;
+
+typedef enum { TT_BF16 = 0, TT_F32 = 1 } tt_dtype;
+
+typedef void* tt_stream; /* hipStream_t */
+
+/* Message of the last failing call on this thread ("" if none).  Valid until
+ * the next libtt call on the same thread. */
+const char* tt_last_error(void);
+
+/* TT_ABI_VERSION of the loaded library. */
+int tt_abi_version(void);
+
+/* Shape of one attention layer of the denoiser.  batch = B sequences, each
+ * with one block of block_size = S slots; n_q_heads = Hq, n_kv_heads = Hkv,
+ * head_dim = d; dtype (a tt_dtype) is the storage type of q/k/v/residual/out
+ * and of the context cache. */
+typedef struct {
+  int32_t batch;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t dtype;
+} tt_attn_shape;
+
+/* ------------------------------------------------------------------------
+ * tt_block_attn -- one denoiser attention layer over [context KV ; block KV].
+ *
+ * [dothoosh] two-tower mechanism section: inside a block the denoiser
+ * attends bidirectionally, and causally to the earlier clean blocks; layer i
+ * of the denoiser talks to layer i of the frozen context tower, which keeps
+ * the per-layer KV cache of the prompt and committed tokens.  [modelcard]
+ * technical features section: bidirectional self-attention inside the block
+ * plus layer-aligned cross-attention to the same layer's context KV, with
+ * adaLN-single scale/shift/gate per timestep.
+ *
+ * For sequence b, query head h and its KV head g = h / (Hq/Hkv):
+ *   keys   K = [k_ctx[ctx_start[b] .. ctx_start[b]+ctx_len[b]-1, g, :] ;
+ *               k_blk[b, 0..S-1, g, :]]          (V likewise)
+ *   q'     = q_blk[b, s, h, :] * (1 + ada_scale[b, h*d:(h+1)*d])
+ *            + ada_shift[b, h*d:(h+1)*d]
+ *   o      = softmax(q' K^T / sqrt(d)) V           (one softmax over all keys)
+ *   lse    = ln sum_j exp(q' K_j / sqrt(d))
+ *   out    = residual + ada_gate[b, h*d:(h+1)*d] * o
+ * (missing shift/scale: 0; missing gate: 1; missing residual: 0).  All S
+ * slots are computed alike, masked ones included.
+ *
+ * Layouts (row-major, contiguous):
+ *   q_blk, residual, out  device [B, S, Hq, d]   dtype
+ *   k_blk, v_blk          device [B, S, Hkv, d]  dtype
+ *   k_ctx, v_ctx          device [T_ctx, Hkv, d] dtype  (this layer's cache;
+ *                         sequence b owns tokens ctx_start[b] ..
+ *                         ctx_start[b]+ctx_len[b]-1; sequences may share or
+ *                         interleave nothing else is assumed)
+ *   ctx_start             device [B] int64, ctx_len device [B] int32 (>= 0)
+ *   active                device [B] uint8 or NULL (all active); for an
+ *                         inactive sequence nothing is read or written
+ *   ada_shift/scale/gate  device [B, Hq*d] fp32, each may be NULL
+ *   lse                   device [B, S, Hq] fp32 or NULL
+ * max_ctx_len (host) sizes the launch; correctness never depends on it, but
+ * sequences longer than it run with less parallelism.  residual may alias
+ * out.  k_blk/v_blk/q_blk/k_ctx/v_ctx must be 16-byte aligned for bf16.
+ * Precision (bf16): q' and the probabilities are rounded to bf16 for the
+ * matrix cores, sums are fp32, out is rounded to nearest-even.  (fp32: all
+ * fp32.)  Deterministic: identical inputs give identical bits.
+ * Errors: TT_ERR_INVALID_ARG (null required pointer, bad shape, Hq % Hkv,
+ * max_ctx_len < 0), TT_ERR_UNSUPPORTED (head_dim not 64/128),
+ * TT_ERR_WORKSPACE (workspace NULL or smaller than
+ * tt_block_attn_workspace_size(shape, max_ctx_len)), TT_ERR_HIP.
+ * The workspace needs no initialisation; its contents are dead after the
+ * call's kernels finish.
+ * ---------------------------------------------------------------------- */
+size_t tt_block_attn_workspace_size(const tt_attn_shape* shape, int32_t max_ctx_len);
+
+tt_status tt_block_attn(const tt_attn_shape* shape,
+                        const void* q_blk, const void* k_blk, const void* v_blk,
+                        const void* k_ctx, const void* v_ctx,
+                        const int64_t* ctx_start, const int32_t* ctx_len,
+                        int32_t max_ctx_len, const uint8_t* active,
+                        const float* ada_shift, const float* ada_scale,
+                        const float* ada_gate, const void* residual,
+                        void* out, float* lse,
+                        void* workspace, size_t workspace_bytes, tt_stream stream);
+
+/* Zero-fill `bytes` of device memory at `workspace` on `stream` with a
+ * kernel (no memset node, so the call can sit inside captured graphs). */
+tt_status tt_workspace_clear(void* workspace, size_t bytes, tt_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tt_timestep_embed -- the 256-wide sinusoidal embedding of the diffusion
+ * timestep that feeds adaLN-single ([dothoosh] two-tower mechanism section:
+ * every layer is modulated by the diffusion timestep through adaLN-single;
+ * the embedding is not on the pages: DiT's sinusoid is used):
+ *   emb[b, i]       = cos(1000 * t[b] * 10000^(-i/128)),  i < 128
+ *   emb[b, 128 + i] = sin(1000 * t[b] * 10000^(-i/128))
+ * t device [B] fp32, emb device [B, 256] fp32.  Computed in fp64.
+ * ---------------------------------------------------------------------- */
+tt_status tt_timestep_embed(int32_t batch, const float* t, float* emb, tt_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tt_adaln_single -- per-layer (shift, scale, gate) vectors from the timestep
+ * embedding ([dothoosh] two-tower mechanism section: adaLN-single adds about
+ * 1.5 M parameters; [modelcard] technical features section: scale, shift and
+ * gate per timestep for every denoiser layer):
+ *   u[b, :]          = SiLU(t_emb[b, :]) @ w + bias           (fp32 sums)
+ *   ada[l, j, b, c]  = u[b, j*width + c] + table[l, j, c]
+ * with j = 0 shift, 1 scale, 2 gate.
+ *   t_emb device [B, 256] fp32;  w device [256, 3*width] bf16;
+ *   bias device [3*width] fp32 or NULL;  table device [n_layers, 3, width]
+ *   fp32 or NULL;  ada device [n_layers, 3, B, width] fp32.
+ * width must be a multiple of 4.
+ * ---------------------------------------------------------------------- */
+tt_status tt_adaln_single(int32_t batch, int32_t width, int32_t n_layers,
+                          const float* t_emb, const void* w, const float* bias,
+                          const float* table, float* ada, tt_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tt_confidence_unmask -- one unmasking pass over B blocks.
+ *
+ * [keyframe] key point 3: all masked slots of the block are predicted at
+ * once, confident tokens are committed step by step and the undetermined
+ * rest is masked again.  [dothoosh] benchmark paragraph: the confidence
+ * threshold gamma sets how many tokens a step commits.  [news] code example:
+ * confidence_threshold=0.8, mask_token_id=3, temperature=0.1.
+ *
+ * For every slot (b, s) with masked[b, s] != 0 on entry:
+ *   pred = lowest v with logits[b, s, v] = max_v logits[b, s, v]
+ *   p    = 1 / sum_v exp((logits[b, s, v] - max) / temperature)
+ * Commit set of sequence b: C = {s : p >= gamma}; if C is empty and some
+ * slot is masked, C = {the slot of largest p, lowest s on ties}.  For s in
+ * C: tokens = pred, masked = 0, committed_now = 1, commit_step = step.
+ * Other masked slots: tokens = mask_token_id, committed_now = 0.  Slots not
+ * masked on entry are left alone (committed_now 0, conf NaN, pred -1).
+ * n_masked[b] = masked slots left.
+ * Decisions are exact with respect to fp64 arithmetic: p is computed in fp32
+ * and every p within 2^-14 of gamma (or of the best p, when the one-commit
+ * rule applies) is recomputed in fp64 before it decides anything.
+ *   logits   device, element (b, s, v) at ((b*S + s) * row_stride + v),
+ *            dtype TT_BF16 or TT_F32, finite (or -inf with one finite
+ *            value per row)
+ *   tokens   device [B, S] int32 in/out;  masked device [B, S] uint8 in/out
+ *   committed_now, conf (fp32), pred (int32), commit_step (int8): device
+ *            [B, S], each may be NULL; commit_step is only written at
+ *            committed slots
+ *   n_masked device [B] int32 out, may be NULL
+ * Errors: TT_ERR_INVALID_ARG (null logits/tokens/masked, block_size outside
+ * [1, 64], vocab < 1, row_stride < vocab, temperature not > 0, gamma NaN),
+ * TT_ERR_WORKSPACE, TT_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+size_t tt_unmask_workspace_size(int32_t batch, int32_t block_size, int32_t vocab);
+
+tt_status tt_confidence_unmask(int32_t batch, int32_t block_size, int32_t vocab,
+                               const void* logits, int32_t dtype, int64_t row_stride,
+                               float gamma, float temperature, int32_t mask_token_id,
+                               int32_t step, int32_t* tokens, uint8_t* masked,
+                               uint8_t* committed_now, float* conf, int32_t* pred,
+                               int8_t* commit_step, int32_t* n_masked,
+                               void* workspace, size_t workspace_bytes, tt_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tt_denoise_block -- the block denoising loop ([dothoosh] two-tower
+ * mechanism section: a block starts as [MASK] tokens and is refined over T
+ * steps until final; [news] code example: steps_per_block = block_size =
+ * 16).  For step k = 0 .. max_steps-1 while any slot is masked:
+ *   1. t[b] = n_masked[b] / S; emb = tt_timestep_embed(t);
+ *      ada = tt_adaln_single(emb, ada_w, ada_bias, ada_table)  (skipped,
+ *      identity modulation, when ada_w is NULL);
+ *   2. for layer l: provider->layer_inputs(user, k, l, prev_out, q_blk,
+ *      k_blk, v_blk, stream) fills the block's q/k/v, then tt_block_attn
+ *      over layer l's context cache with layer l's (shift, scale, gate), no
+ *      residual, and active[b] = (n_masked[b] > 0), writing `out`;
+ *   3. provider->logits(user, k, out, logits, stream) fills [B, S, vocab]
+ *      logits of the shape's dtype; tt_confidence_unmask(step = k).
+ * Sequences with nothing masked are inactive.  Slots still masked after
+ * max_steps stay masked.  The provider stands for the rest of the denoiser
+ * (the pages' weights are not part of this library); its buffers live in the
+ * workspace and it must enqueue its work on `stream`.
+ *   k_ctx_layers, v_ctx_layers  host arrays of n_layers device pointers
+ *   ctx_start, ctx_len          device [B]
+ *   ada_w [256, 3*Hq*d] bf16, ada_bias [3*Hq*d] fp32, ada_table
+ *   [n_layers, 3, Hq*d] fp32 (device; bias/table may be NULL)
+ *   tokens [B,S] int32, masked [B,S] uint8 device in/out; commit_step
+ *   [B,S] int8 device in/out or NULL; steps_taken host int32 out or NULL.
+ * Errors: as tt_block_attn and tt_confidence_unmask, plus TT_ERR_CALLBACK
+ * when a callback returns non-zero (state is that of the last completed
+ * step), TT_ERR_INVALID_ARG for max_steps outside [0, S] or n_layers < 1.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  void* user;
+  int (*layer_inputs)(void* user, int32_t step, int32_t layer, const void* prev_out,
+                      void* q_blk, void* k_blk, void* v_blk, tt_stream stream);
+  int (*logits)(void* user, int32_t step, const void* last_out, void* logits,
+                tt_stream stream);
+} tt_step_provider;
+
+size_t tt_denoise_workspace_size(const tt_attn_shape* shape, int32_t n_layers,
+                                 int32_t max_ctx_len, int32_t vocab);
+
+tt_status tt_denoise_block(const tt_attn_shape* shape, int32_t n_layers, int32_t max_steps,
+                           float gamma, float temperature, int32_t mask_token_id,
+                           int32_t vocab, const void* const* k_ctx_layers,
+                           const void* const* v_ctx_layers, const int64_t* ctx_start,
+                           const int32_t* ctx_len, int32_t max_ctx_len,
+                           const void* ada_w, const float* ada_bias, const float* ada_table,
+                           const tt_step_provider* provider, int32_t* tokens,
+                           uint8_t* masked, int8_t* commit_step, int32_t* steps_taken,
+                           void* workspace, size_t workspace_bytes, tt_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TT_H */

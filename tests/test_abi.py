@@ -1,0 +1,155 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol the header
+declares, and rejects invalid calls with the documented status before any
+HIP call (these run without a GPU: validation returns before a launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_mask_diffusion_tt_amd as tt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20          # a 256-byte-aligned non-NULL address; never dereferenced
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "tt.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tt_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    names = _header_functions()
+    assert "tt_block_attn" in names and "tt_denoise_block" in names
+    lib = ctypes.CDLL(tt.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(tt.EXPORTED) == names
+
+
+def test_abi_version():
+    assert tt.abi_version() == 1
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def _attn(shape, ws_bytes=1 << 30, **over):
+    args = dict(q=FAKE, kb=FAKE, vb=FAKE, kc=FAKE, vc=FAKE, cs=FAKE, cl=FAKE, maxl=128,
+                active=None, shift=None, scale=None, gate=None, res=None, out=FAKE, lse=None,
+                ws=FAKE, stream=None)
+    args.update(over)
+    return tt.lib().tt_block_attn(ctypes.byref(shape), args["q"], args["kb"], args["vb"],
+                                  args["kc"], args["vc"], args["cs"], args["cl"], args["maxl"],
+                                  args["active"], args["shift"], args["scale"], args["gate"],
+                                  args["res"], args["out"], args["lse"], args["ws"], ws_bytes,
+                                  args["stream"])
+
+
+@pytest.mark.parametrize("shape,status", [
+    ((1, 32, 3, 128, 16, 0), tt.TT_ERR_INVALID_ARG),    # Hq % Hkv
+    ((1, 32, 2, 96, 16, 0), tt.TT_ERR_UNSUPPORTED),     # head_dim 96
+    ((1, 32, 2, 0, 16, 0), tt.TT_ERR_INVALID_ARG),      # head_dim 0
+    ((1, 32, 2, 128, 0, 0), tt.TT_ERR_INVALID_ARG),     # S = 0
+    ((1, 32, 2, 128, 65, 0), tt.TT_ERR_INVALID_ARG),    # S > 64
+    ((1, 32, 2, 128, 16, 7), tt.TT_ERR_INVALID_ARG),    # dtype
+    ((-1, 32, 2, 128, 16, 0), tt.TT_ERR_INVALID_ARG),   # batch < 0
+    ((1, 0, 2, 128, 16, 0), tt.TT_ERR_INVALID_ARG),     # no heads
+])
+def test_block_attn_rejects_bad_shapes(shape, status):
+    s = tt.AttnShape(*shape)
+    assert _attn(s) == status
+    assert tt.last_error() != ""
+
+
+def test_block_attn_rejects_bad_pointers_and_workspace():
+    s = tt.AttnShape(2, 32, 2, 128, 16, 0)
+    assert _attn(s, q=None) == tt.TT_ERR_INVALID_ARG
+    assert _attn(s, cl=None) == tt.TT_ERR_INVALID_ARG
+    assert _attn(s, q=FAKE + 2) == tt.TT_ERR_INVALID_ARG            # misaligned
+    assert _attn(s, gate=FAKE + 4) == tt.TT_ERR_INVALID_ARG          # gate needs 16 B
+    assert _attn(s, maxl=-1) == tt.TT_ERR_INVALID_ARG
+    need = tt.block_attn_workspace_size(s, 128)
+    assert _attn(s, ws_bytes=need - 1) == tt.TT_ERR_WORKSPACE
+    assert _attn(s, ws=None) == tt.TT_ERR_WORKSPACE
+    assert "workspace" in tt.last_error()
+
+
+def test_block_attn_empty_batch_is_ok_without_gpu():
+    s = tt.AttnShape(0, 32, 2, 128, 16, 0)
+    assert _attn(s, ws_bytes=0, ws=None) == tt.TT_OK
+
+
+def test_workspace_sizes_monotone():
+    a = tt.block_attn_workspace_size(tt.attn_shape(8, 32, 2, 128, 16, 0), 1024)
+    b = tt.block_attn_workspace_size(tt.attn_shape(8, 32, 2, 128, 16, 0), 32768)
+    assert 0 < a <= b
+    assert tt.unmask_workspace_size(64, 16, 131072) >= 64 * 16 * 16
+    with pytest.raises(tt.TTError):
+        tt.unmask_workspace_size(1, 0, 10)
+
+
+def _unmask(B=1, S=16, V=1024, logits=FAKE, dtype=0, stride=None, gamma=0.8, tau=1.0,
+            tokens=FAKE, masked=FAKE, ws=FAKE, ws_bytes=1 << 20):
+    return tt.lib().tt_confidence_unmask(B, S, V, logits, dtype, V if stride is None else stride,
+                                         gamma, tau, 3, 0, tokens, masked, None, None, None, None,
+                                         None, ws, ws_bytes, None)
+
+
+def test_unmask_rejects_bad_arguments():
+    assert _unmask(S=0) == tt.TT_ERR_INVALID_ARG
+    assert _unmask(S=65) == tt.TT_ERR_INVALID_ARG
+    assert _unmask(V=0) == tt.TT_ERR_INVALID_ARG
+    assert _unmask(stride=100) == tt.TT_ERR_INVALID_ARG
+    assert _unmask(tau=0.0) == tt.TT_ERR_INVALID_ARG
+    assert _unmask(tau=-1.0) == tt.TT_ERR_INVALID_ARG
+    assert _unmask(tau=float("inf")) == tt.TT_ERR_INVALID_ARG
+    assert _unmask(gamma=float("nan")) == tt.TT_ERR_INVALID_ARG
+    assert _unmask(dtype=5) == tt.TT_ERR_INVALID_ARG
+    assert _unmask(logits=None) == tt.TT_ERR_INVALID_ARG
+    assert _unmask(tokens=None) == tt.TT_ERR_INVALID_ARG
+    assert _unmask(ws_bytes=1) == tt.TT_ERR_WORKSPACE
+    assert _unmask(B=0, ws=None, ws_bytes=0) == tt.TT_OK
+
+
+def test_adaln_and_embed_reject_bad_arguments():
+    L = tt.lib()
+    assert L.tt_timestep_embed(-1, FAKE, FAKE, None) == tt.TT_ERR_INVALID_ARG
+    assert L.tt_timestep_embed(2, None, FAKE, None) == tt.TT_ERR_INVALID_ARG
+    assert L.tt_adaln_single(2, 6, 1, FAKE, FAKE, None, None, FAKE, None) == tt.TT_ERR_INVALID_ARG
+    assert L.tt_adaln_single(2, 8, 0, FAKE, FAKE, None, None, FAKE, None) == tt.TT_ERR_INVALID_ARG
+    assert L.tt_adaln_single(2, 8, 1, None, FAKE, None, None, FAKE, None) == tt.TT_ERR_INVALID_ARG
+    assert L.tt_workspace_clear(None, 16, None) == tt.TT_ERR_INVALID_ARG
+    assert L.tt_workspace_clear(None, 0, None) == tt.TT_OK
+
+
+def test_denoise_rejects_bad_arguments():
+    s = tt.AttnShape(2, 4, 1, 64, 16, 1)
+    L = tt.lib()
+    ptrs = (ctypes.c_void_p * 1)(FAKE)
+    prov = tt.StepProvider()
+
+    def call(shape=s, n_layers=1, max_steps=16, provider=None, k=ptrs, ws_bytes=1 << 30):
+        taken = ctypes.c_int32(-5)
+        st = L.tt_denoise_block(ctypes.byref(shape), n_layers, max_steps, 0.8, 1.0, 3, 64,
+                                k, ptrs, FAKE, FAKE, 8, None, None, None,
+                                provider, FAKE, FAKE, None, ctypes.byref(taken), FAKE,
+                                ws_bytes, None)
+        assert taken.value == 0
+        return st
+    assert call(max_steps=17) == tt.TT_ERR_INVALID_ARG
+    assert call(max_steps=-1) == tt.TT_ERR_INVALID_ARG
+    assert call(n_layers=0) == tt.TT_ERR_INVALID_ARG
+    assert call(provider=None) == tt.TT_ERR_INVALID_ARG
+    assert call(provider=ctypes.byref(prov)) == tt.TT_ERR_INVALID_ARG    # NULL callbacks
+    assert call(k=(ctypes.c_void_p * 1)(None)) == tt.TT_ERR_INVALID_ARG
+    assert tt.denoise_workspace_size(s, 1, 8, 64) > 0
+
+
+def test_binding_raises_with_message():
+    with pytest.raises(tt.TTError) as ei:
+        tt.block_attn_workspace_size(tt.AttnShape(1, 3, 2, 64, 4, 0), 8)
+    assert "multiple" in str(ei.value)

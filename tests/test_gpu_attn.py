@@ -1,0 +1,144 @@
+"""GPU parity of tt_block_attn against the fp64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+from .gpu_cases import (TOL, assert_attn_close, attn_case, np64, oracle_attn, run_attn, say)
+
+pytestmark = pytest.mark.gpu
+
+BF16, F32 = torch.bfloat16, torch.float32
+
+
+def _check(c, what, seqs=None, **kw):
+    say(what, {k: c[k] for k in ("B", "S", "Hq", "Hkv", "d", "dtype")}, "lens", c["lens"][:8])
+    out, lse = run_attn(c, **kw)
+    ro, rl = oracle_attn(c, seqs)
+    sl = slice(None) if seqs is None else list(seqs)
+    gate = None if c["gate"] is None else c["gate"][sl]
+    return assert_attn_close(out[sl], lse[sl], ro, rl, c["dtype"], what, gate=gate)
+
+
+# The tiny fp32 step: batch 1, 4 query heads / 1 KV head, d = 64, 128 context
+# tokens, S = 16, Q/K/V ~ N(0, 1).
+def test_tiny_fp32_step():
+    c = attn_case(1, 16, 4, 1, 64, [128], dtype=F32, seed=1)
+    _check(c, "tiny fp32")
+
+
+@pytest.mark.parametrize("L", [0, 1, 15, 16, 17, 127, 4096])
+@pytest.mark.parametrize("dtype", [BF16, F32])
+def test_context_lengths(L, dtype):
+    c = attn_case(2, 16, 32, 2, 128, [L, max(L - 1, 0)], dtype=dtype, seed=10 + L)
+    _check(c, f"L={L}")
+
+
+@pytest.mark.parametrize("S", [1, 4, 16, 64])
+@pytest.mark.parametrize("heads", [(4, 1), (8, 8), (32, 2)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_shapes_bf16(S, heads, d):
+    Hq, Hkv = heads
+    c = attn_case(3, S, Hq, Hkv, d, [300, 0, 77], dtype=BF16, seed=100 + S + d + Hq,
+                  ada=True, residual=True, reverse_layout=True, gap=5)
+    _check(c, f"S={S} heads={heads} d={d}")
+
+
+@pytest.mark.parametrize("S,heads,d", [(1, (4, 1), 64), (16, (32, 2), 128), (64, (8, 8), 128),
+                                       (4, (32, 2), 64)])
+def test_shapes_fp32(S, heads, d):
+    Hq, Hkv = heads
+    c = attn_case(2, S, Hq, Hkv, d, [130, 33], dtype=F32, seed=200 + S, ada=True, residual=True)
+    _check(c, f"fp32 S={S} heads={heads} d={d}")
+
+
+# peaked attention (q x 4) and short contexts, where the block keys carry a
+# large share of the mass: a wrong block-local part cannot hide here.  No gate
+# and no residual, so the bound is the plain 2e-2 on the attention output.
+@pytest.mark.parametrize("L", [8, 64, 128, 2048])
+def test_peaked_small_context(L):
+    c = attn_case(4, 16, 32, 2, 128, [L, L // 2, 0, L], dtype=BF16, seed=300 + L, qscale=4.0,
+                  ada=True)
+    c["gate"] = None
+    _check(c, f"peaked L={L}")
+    out, _ = run_attn(c)
+    assert float(np.sqrt((np64(out) ** 2).mean())) > 0.2    # outputs are not near zero
+
+
+# the same with gate and residual (error scaled by |gate|, plus the store)
+@pytest.mark.parametrize("L", [8, 128])
+def test_peaked_gated(L):
+    c = attn_case(4, 16, 32, 2, 128, [L, L // 2, 0, L], dtype=BF16, seed=350 + L, qscale=4.0,
+                  ada=True, residual=True)
+    _check(c, f"peaked gated L={L}")
+
+
+def test_inactive_sequences_untouched():
+    c = attn_case(3, 16, 8, 2, 64, [50, 60, 70], dtype=BF16, seed=400, active=[1, 0, 1])
+    out, lse = run_attn(c)
+    ro, rl = oracle_attn(c, [0, 2])
+    assert_attn_close(out[[0, 2]], lse[[0, 2]], ro, rl, BF16, "active rows", gate=None)
+    assert torch.all(out[1] == 7.0) and torch.all(lse[1] == 7.0)
+
+
+def test_residual_aliases_out():
+    c = attn_case(2, 16, 32, 2, 128, [200, 90], dtype=BF16, seed=500, ada=True, residual=True)
+    ro, rl = oracle_attn(c)
+    buf = c["residual"].clone()
+    c["residual"] = buf
+    out, lse = run_attn(c, out=buf)
+    assert out.data_ptr() == buf.data_ptr()
+    assert_attn_close(out, lse, ro, rl, BF16, "aliased residual", gate=c["gate"])
+
+
+# P10: the split of the context into chunks does not change the result beyond
+# rounding; a launch-size hint smaller than the real length stays correct.
+def test_chunking_invariance_and_small_hint():
+    c = attn_case(2, 16, 32, 2, 128, [3000, 1500], dtype=BF16, seed=600, ada=True)
+    a, la = run_attn(c)
+    b, lb = run_attn(c, max_ctx_len=64)
+    ro, rl = oracle_attn(c)
+    assert_attn_close(a, la, ro, rl, BF16, "hint = max len", gate=c["gate"])
+    assert_attn_close(b, lb, ro, rl, BF16, "hint = 64", gate=c["gate"])
+
+
+def test_deterministic():
+    c = attn_case(4, 16, 32, 2, 128, [2048, 999, 1, 4000], dtype=BF16, seed=700, ada=True)
+    a, la = run_attn(c)
+    b, lb = run_attn(c)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_empty_batch():
+    c = attn_case(1, 16, 32, 2, 128, [10], dtype=BF16, seed=800)
+    import block_mask_diffusion_tt_amd as tt
+    shape = tt.attn_shape(0, 32, 2, 128, 16, BF16)
+    tt.block_attn(shape, c["q"], c["kb"], c["vb"], c["kc"], c["vc"], c["ctx_start"],
+                  c["ctx_len"], 0, c["q"], None)
+
+
+# Single sequence, bf16, 32/2 heads, d = 128, 4096 context tokens, S = 16,
+# adaLN vectors present (the second workload of the method's configurations).
+def test_single_sequence_4096():
+    c = attn_case(1, 16, 32, 2, 128, [4096], dtype=BF16, seed=900, ada=True)
+    _check(c, "single seq 4096")
+
+
+# Ragged batch 64, contexts uniform in [1024, 8192] (full size, the launch the
+# benchmark times) -- checked on a sample of sequences.
+def test_ragged_batch64_sampled():
+    import synth
+    lens = synth.uniform_int(64, 1024, 8192, seed=3).tolist()
+    c = attn_case(64, 16, 32, 2, 128, lens, dtype=BF16, seed=1000, ada=True)
+    _check(c, "ragged 64", seqs=[0, 17, 40, 63])
+
+
+def test_headline_batch64_ctx8192_sampled():
+    c = attn_case(64, 16, 32, 2, 128, [8192] * 64, dtype=BF16, seed=1100, ada=True)
+    _check(c, "headline 64x8192", seqs=[0, 31, 63])
+
+
+# Block-size sweep shape: batch 8, context 32768, S in {4, 16, 64} (sampled)
+@pytest.mark.parametrize("S", [4, 16, 64])
+def test_context_32768_sampled(S):
+    c = attn_case(8, S, 32, 2, 128, [32768] * 8, dtype=BF16, seed=1200 + S)
+    _check(c, f"ctx 32768 S={S}", seqs=[0, 7])
