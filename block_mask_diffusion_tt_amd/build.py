@@ -5,6 +5,7 @@ Usage:  python -m block_mask_diffusion_tt_amd.build   (or build() from Python)
 """
 import concurrent.futures
 import os
+import re
 import subprocess
 import sys
 
@@ -22,6 +23,12 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function", "-I", os.path.join(ROOT, "include")] + DEVICE_FLAGS
 
 
+# The attention kernels never produce or consume NaN (masked scores are -inf,
+# every softmax row has a finite score): dropping NaN canonicalization halves
+# the cost of the running max.
+FILE_FLAGS = {"attn.hip": ["-fno-honor-nans"]}
+
+
 def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     noise = "is not a recognized feature for this target"
@@ -29,6 +36,20 @@ def _run(cmd):
     if r.returncode != 0:
         raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
     return out
+
+
+def _check_m0(asm_path):
+    """The attention kernel writes M0 itself (inline asm right before each
+    direct global->LDS copy).  Fail the build if the compiler also uses M0
+    anywhere in that file, since nothing would then preserve it."""
+    lines = open(asm_path).read().splitlines()
+    for i, line in enumerate(lines):
+        if re.search(r"\bm0\b", line.split(";")[0]):
+            ok = (re.match(r"\s*s_mov_b32 m0, s\d+\s*$", line) and i + 2 < len(lines)
+                  and lines[i + 1].strip() == "s_nop 0"
+                  and lines[i + 2].strip().startswith("global_load_lds_dwordx4"))
+            if not ok:
+                raise RuntimeError(f"{asm_path}:{i + 1}: unexpected use of m0: {line.strip()}")
 
 
 def build(verbose=False):
@@ -39,12 +60,16 @@ def build(verbose=False):
         for src in SOURCES:
             obj = os.path.join(BUILD, src + ".o")
             objs.append(obj)
-            cmd = [HIPCC] + CFLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [HIPCC] + CFLAGS + FILE_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
             jobs.append(ex.submit(_run, cmd))
         for j in jobs:
             out = j.result()
             if verbose and out.strip():
                 print(out)
+    asm = os.path.join(BUILD, "attn.s")
+    _run([HIPCC] + CFLAGS + FILE_FLAGS["attn.hip"] +
+         ["--cuda-device-only", "-S", os.path.join(CSRC, "attn.hip"), "-o", asm])
+    _check_m0(asm)
     tmp = LIB + ".tmp"
     out = _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs)
     if verbose and out.strip():

@@ -31,25 +31,42 @@ __global__ void timestep_embed_kernel(int B, const float* t, const int32_t* n_ma
   emb[static_cast<int64_t>(b) * kEmb + kEmb / 2 + i] = static_cast<float>(sin(arg));
 }
 
-// One thread per output column n of u = SiLU(emb) @ W (W bf16 [256, N]),
-// for a chunk of kRows sequences; W is read once per chunk with coalesced
-// loads, the SiLU'd embedding rows sit in LDS.  The epilogue adds the bias
-// and writes every layer's copy with its table row.
-constexpr int kRows = 16;
-constexpr int kCols = 256;
+// u = SiLU(emb) @ W for a tile of kRows sequences x 128 columns per
+// workgroup: 256 threads = 8 k-slices x 32 column quads.  Each thread owns 4
+// adjacent columns for the tile's rows and 32 values of k; its 32 loads of W
+// (8 bytes each) are issued before any arithmetic.  The 8 k-slices are summed
+// in LDS in a fixed order (deterministic), then the epilogue adds the bias and
+// writes every layer's copy with its table row.
+constexpr int kRows = 8;
+constexpr int kCols = 128;
+constexpr int kSlices = 8;
+constexpr int kPerSlice = kEmb / kSlices;
 
-__global__ __launch_bounds__(kCols) void adaln_kernel(int B, int width, int n_layers,
-                                                      const float* __restrict__ emb,
-                                                      const uint16_t* __restrict__ w,
-                                                      const float* __restrict__ bias,
-                                                      const float* __restrict__ table,
-                                                      float* __restrict__ ada) {
+__global__ __launch_bounds__(256) void adaln_kernel(int B, int width, int n_layers,
+                                                    const float* __restrict__ emb,
+                                                    const uint16_t* __restrict__ w,
+                                                    const float* __restrict__ bias,
+                                                    const float* __restrict__ table,
+                                                    float* __restrict__ ada) {
   __shared__ float s_e[kRows][kEmb];
+  __shared__ float s_part[kSlices][kRows][kCols + 4];
   const int N = 3 * width;
-  const int n = blockIdx.x * kCols + threadIdx.x;
+  const int n0 = blockIdx.x * kCols;
   const int b0 = blockIdx.y * kRows;
   const int nb = min(kRows, B - b0);
-  for (int idx = threadIdx.x; idx < kRows * kEmb; idx += kCols) {
+  const int slice = threadIdx.x >> 5, cq = threadIdx.x & 31;
+  const int n = n0 + 4 * cq;
+  uint2 wv[kPerSlice];
+  if (n < N) {   // width is a multiple of 4, so a quad never straddles N
+    const uint16_t* wp = w + static_cast<int64_t>(slice * kPerSlice) * N + n;
+#pragma unroll
+    for (int kk = 0; kk < kPerSlice; ++kk)
+      wv[kk] = *reinterpret_cast<const uint2*>(wp + static_cast<int64_t>(kk) * N);
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < kPerSlice; ++kk) wv[kk] = make_uint2(0, 0);
+  }
+  for (int idx = threadIdx.x; idx < kRows * kEmb; idx += 256) {
     const int r = idx / kEmb, k = idx % kEmb;
     float v = 0.f;
     if (r < nb) {
@@ -59,21 +76,50 @@ __global__ __launch_bounds__(kCols) void adaln_kernel(int B, int width, int n_la
     s_e[r][k] = v;
   }
   __syncthreads();
-  if (n >= N) return;
-  float acc[kRows];
+  float acc[kRows][4];
 #pragma unroll
-  for (int r = 0; r < kRows; ++r) acc[r] = 0.f;
-  for (int k = 0; k < kEmb; ++k) {
-    const float wk = __uint_as_float(static_cast<uint32_t>(w[static_cast<int64_t>(k) * N + n]) << 16);
+  for (int r = 0; r < kRows; ++r)
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) acc[r] = fmaf(s_e[r][k], wk, acc[r]);
+    for (int j = 0; j < 4; ++j) acc[r][j] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < kPerSlice; kk += 4) {
+    float wf[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      wf[q][0] = __uint_as_float(wv[kk + q].x << 16);
+      wf[q][1] = __uint_as_float(wv[kk + q].x & 0xffff0000u);
+      wf[q][2] = __uint_as_float(wv[kk + q].y << 16);
+      wf[q][3] = __uint_as_float(wv[kk + q].y & 0xffff0000u);
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const float4 e = *reinterpret_cast<const float4*>(&s_e[r][slice * kPerSlice + kk]);
+      const float ev[4] = {e.x, e.y, e.z, e.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[r][j] = fmaf(ev[q], wf[q][j], acc[r][j]);
+    }
   }
-  const float bn = bias ? bias[n] : 0.f;
-  const int j = n / width, c = n % width;
-  for (int l = 0; l < n_layers; ++l) {
-    const float tv = table ? table[(static_cast<int64_t>(l) * 3 + j) * width + c] : 0.f;
-    float* dst = ada + ((static_cast<int64_t>(l) * 3 + j) * B) * width + c;
-    for (int r = 0; r < nb; ++r) dst[static_cast<int64_t>(b0 + r) * width] = acc[r] + bn + tv;
+#pragma unroll
+  for (int r = 0; r < kRows; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s_part[slice][r][4 * cq + j] = acc[r][j];
+  __syncthreads();
+  // epilogue: 256 threads over (row, column) pairs of the tile
+  for (int idx = threadIdx.x; idx < kRows * kCols; idx += 256) {
+    const int r = idx / kCols, c = idx % kCols;
+    const int col = n0 + c;
+    if (r >= nb || col >= N) continue;
+    float u = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < kSlices; ++sl) u += s_part[sl][r][c];
+    u += bias ? bias[col] : 0.f;
+    const int j = col / width, cc = col % width;
+    for (int l = 0; l < n_layers; ++l) {
+      const float tv = table ? table[(static_cast<int64_t>(l) * 3 + j) * width + cc] : 0.f;
+      ada[((static_cast<int64_t>(l) * 3 + j) * B + b0 + r) * width + cc] = u + tv;
+    }
   }
 }
 
@@ -123,7 +169,7 @@ hipError_t launch_adaln_single(int B, int width, int n_layers, const float* emb,
                                hipStream_t st) {
   const int N = 3 * width;
   const dim3 grid(static_cast<unsigned>(ceil_div(N, kCols)), static_cast<unsigned>(ceil_div(B, kRows)));
-  hipLaunchKernelGGL(adaln_kernel, grid, dim3(kCols), 0, st, B, width, n_layers, emb,
+  hipLaunchKernelGGL(adaln_kernel, grid, dim3(256), 0, st, B, width, n_layers, emb,
                      static_cast<const uint16_t*>(w), bias, table, ada);
   return hipGetLastError();
 }

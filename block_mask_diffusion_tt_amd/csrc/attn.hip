@@ -32,6 +32,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "tt_internal.h"
 
 namespace tt {
@@ -106,32 +108,90 @@ __device__ __forceinline__ bool decode_unit(int u, int Hkv, int RB, int NC, int 
 }
 
 // ------------------------------------------------------------------ bf16
-template <int D>
-struct SmemBf16 {
-  uint16_t k[2][kTK][D + kKPad];
-  uint16_t vt[2][D][kTK + kVPad];
-};
+#define TT_LDS __attribute__((address_space(3)))
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// 16-byte global -> LDS copy through the direct path: lane i writes LDS bytes
+// [lds + 16 i, lds + 16 i + 16).  Written in asm because the compiler would
+// otherwise wait for every such copy in flight before any LDS read (it cannot
+// tell the pipeline stages apart); the stage waits below are explicit.  The
+// instruction has no register result.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// max / sum of a value over lanes l and l^32 (the two halves of a wave)
+__device__ __forceinline__ float xhalf_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bf16_kernel(KParams p) {
-  constexpr int KSTEPS = D / 16;      // MFMA k-steps of QK^T
-  constexpr int DT = D / 32;          // 32-channel tiles of the output
-  constexpr int SEGS = D / 8;         // 16-byte segments per key row
-  constexpr int KVEC = kTK * SEGS / 256;       // K vectors per thread per tile
-  constexpr int VPAIR = (kTK / 2) * SEGS / 256; // V key-pair units per thread
-  __shared__ SmemBf16<D> sm;
+struct Bf16Cfg {
+  static constexpr int CH = D / 8;                 // 16-byte chunks per key row
+  static constexpr int TILE = 64 * D * 2;          // bytes of one K (or V) tile of 64 keys
+  static constexpr int NST = 4;                    // pipeline stages
+  static constexpr int VREG = NST * TILE;          // V tiles follow the NST K tiles
+  static constexpr int CPT = 64 * CH / 512;        // copies per thread per tile tensor
+  static constexpr int SMEM = 2 * NST * TILE;
+};
+
+// LDS tile layouts (16-byte slots).  K: slot = (key/16)*16*CH + c*16 + key%16
+// (chunk-major inside groups of 16 keys), so the 16 lanes reading one chunk of
+// 16 consecutive keys hit 16 different bank groups and every chunk offset is
+// an immediate.  V: slot = (key/4)*4*CH + c*4 + key%4 (4 keys interleaved per
+// chunk), so the transpose reads of 4 keys x 4 chunks x 2 halves by 32 lanes
+// hit all 64 banks once, and a 64-slot copy is 4 whole key rows.
+template <int D>
+__device__ __forceinline__ int kslot(int key, int c) {
+  return (key >> 4) * 16 * (D / 8) + c * 16 + (key & 15);
+}
+template <int D>
+__device__ __forceinline__ int vslot(int key, int c) {
+  return (key >> 2) * 4 * (D / 8) + c * 4 + (key & 3);
+}
+
+// Scheduling hints: interleave n MFMAs with v VALU ops and r LDS reads each.
+#define TT_SCHED_MFMA(n, v, r)                                     \
+  do {                                                             \
+    _Pragma("unroll") for (int _i = 0; _i < (n); ++_i) {           \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           \
+      __builtin_amdgcn_sched_group_barrier(0x002, (v), 0);         \
+      __builtin_amdgcn_sched_group_barrier(0x100, (r), 0);         \
+    }                                                              \
+  } while (0)
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
+  using C = Bf16Cfg<D>;
+  constexpr int KSTEPS = D / 16;   // MFMA k-steps of QK^T
+  constexpr int DT = D / 32;       // 32-channel tiles of the output
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::SMEM];
 
   Unit un;
   if (!decode_unit(blockIdx.x, p.Hkv, p.RB, p.NC, p.chunk, p.ctx_len, p.active, un)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int half = lane >> 5, l32 = lane & 31;
-  const int64_t kstride = static_cast<int64_t>(p.Hkv) * D;  // elements between keys
+  const int half = lane >> 5, l32 = lane & 31, grp = lane >> 4, li = lane & 15;
+  const int64_t kstride = static_cast<int64_t>(p.Hkv) * D;
+  TT_LDS uint8_t* const lsm = (TT_LDS uint8_t*)(smem);  // address-space cast
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lsm));
 
-  // ---- Q' = (q * (1 + scale) + shift) * log2(e)/sqrt(d), rounded to bf16
-  bf16x8 qf[2][KSTEPS];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int row = un.rb * kRowsBf16 + wave * 64 + rt * 32 + l32;
+  // ---- Q' = (q * (1 + scale) + shift) * log2(e)/sqrt(d), rounded to bf16;
+  // this wave's 32 rows, lane l32 holding row wave*32 + l32
+  bf16x8 qf[KSTEPS];
+  {
+    const int row = un.rb * kRowsBf16 + wave * 32 + l32;
     const bool valid = row < p.R;
     const int s = valid ? row / p.G : 0;
     const int h = un.g * p.G + (valid ? row % p.G : 0);
@@ -142,220 +202,247 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(KParams p) {
     for (int kk = 0; kk < KSTEPS; ++kk) {
       const int d0 = kk * 16 + half * 8;
       float v[8];
-      if (valid) {
-        const uint4 w = *reinterpret_cast<const uint4*>(qrow + d0);
-        v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
-        v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
-        v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xffff0000u);
-        v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xffff0000u);
-        if (sc) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = v[i] * (1.f + sc[d0 + i]);
-        }
-        if (sh) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = v[i] + sh[d0 + i];
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+      const uint4 w = valid ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
+      v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
+      v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
+      v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xffff0000u);
+      v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xffff0000u);
+      if (sc && valid) {
+        const float4 a = *reinterpret_cast<const float4*>(sc + d0);
+        const float4 b = *reinterpret_cast<const float4*>(sc + d0 + 4);
+        v[0] *= 1.f + a.x; v[1] *= 1.f + a.y; v[2] *= 1.f + a.z; v[3] *= 1.f + a.w;
+        v[4] *= 1.f + b.x; v[5] *= 1.f + b.y; v[6] *= 1.f + b.z; v[7] *= 1.f + b.w;
+      }
+      if (sh && valid) {
+        const float4 a = *reinterpret_cast<const float4*>(sh + d0);
+        const float4 b = *reinterpret_cast<const float4*>(sh + d0 + 4);
+        v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+        v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qf[rt][kk][i] = static_cast<__bf16>(v[i] * p.qscale);
+      for (int i = 0; i < 8; ++i) qf[kk][i] = static_cast<__bf16>(v[i] * p.qscale);
     }
   }
 
-  // ---- tile sources
+  // ---- tiles: the block's S keys first (chunk 0), then 64-key context tiles
   const int n_ctx_tiles = (un.k_end - un.k_beg + kTK - 1) / kTK;
   const int n_tiles = (un.has_blk ? 1 : 0) + n_ctx_tiles;
   const int64_t ctx0 = p.ctx_start[un.b];
-  auto tile_src = [&](int t, const uint16_t*& kp, const uint16_t*& vp, int& nvalid) {
+  auto tile_valid = [&](int t) {
+    return (un.has_blk && t == 0) ? p.S
+                                  : min(kTK, un.k_end - (un.k_beg + (t - (un.has_blk ? 1 : 0)) * kTK));
+  };
+  // Copy m of a tile tensor fills slots [64m, 64m+64): for K, 16 keys x 4
+  // chunks (key 16*(m/(CH/4)) + lane%16, chunk 4*(m%(CH/4)) + lane/16); for V,
+  // 64 consecutive slots of the 4-key-interleaved layout (whole key rows).
+  // Keys past the tile's end repeat its last key (finite values whose scores
+  // are masked to -inf).  K tiles of the NST stages come first, then V tiles.
+  auto issue = [&](int t) {
+    const int stage = t % C::NST;
+    const uint16_t* kp;
+    const uint16_t* vp;
+    int nv;
     if (un.has_blk && t == 0) {
       const int64_t off = (static_cast<int64_t>(un.b) * p.S * p.Hkv + un.g) * D;
       kp = p.kb + off;
       vp = p.vb + off;
-      nvalid = p.S;
+      nv = p.S;
     } else {
-      const int i = t - (un.has_blk ? 1 : 0);
-      const int key0 = un.k_beg + i * kTK;
+      const int key0 = un.k_beg + (t - (un.has_blk ? 1 : 0)) * kTK;
       const int64_t off = ((ctx0 + key0) * p.Hkv + un.g) * D;
       kp = p.kc + off;
       vp = p.vc + off;
-      nvalid = min(kTK, un.k_end - key0);
+      nv = min(kTK, un.k_end - key0);
+    }
+#pragma unroll
+    for (int j = 0; j < C::CPT; ++j) {
+      const int m = wave * C::CPT + j;
+      const int kkey = 16 * (m / (C::CH / 4)) + (lane & 15);
+      const int kc = 4 * (m % (C::CH / 4)) + (lane >> 4);
+      dma16(kp + min(kkey, nv - 1) * kstride + kc * 8,
+            __builtin_amdgcn_readfirstlane(lds0 + stage * C::TILE + m * 1024));
+      const int slot0 = 64 * m + lane;
+      const int vkey = 4 * (slot0 / (4 * C::CH)) + (slot0 & 3);
+      const int vc = (slot0 % (4 * C::CH)) >> 2;
+      dma16(vp + min(vkey, nv - 1) * kstride + vc * 8,
+            __builtin_amdgcn_readfirstlane(lds0 + C::VREG + stage * C::TILE + m * 1024));
     }
   };
 
-  uint4 kreg[KVEC];
-  uint4 vreg[VPAIR][2];
-  auto gload = [&](int t) {
-    const uint16_t* kp;
-    const uint16_t* vp;
-    int nv;
-    tile_src(t, kp, vp, nv);
+  // per-lane operand bases (bytes within a stage): K chunk 2kk+half of key
+  // kt*32 + l32 is at kbase + kt*32*CH*16 + kk*2*16*16; the V^T transpose read
+  // of channel tile dt, 16-key step ks, second 4-key group r2 is at vbase +
+  // (kt*8 + ks*4 + r2*2)*4*CH*16 + dt*4*4*16.
+  const int kbase = kslot<D>(l32, half) * 16;
+  const int vlo = 2 * (grp & 1) + ((li & 3) >> 1);
+  const int vbase = C::VREG + vslot<D>(4 * half + (li >> 2), vlo) * 16 + ((li & 1) << 3);
+
+  f32x16 acc[DT];
 #pragma unroll
-    for (int j = 0; j < KVEC; ++j) {
-      const int v = tid + 256 * j;
-      const int key = v / SEGS, seg = v % SEGS;
-      kreg[j] = key < nv ? *reinterpret_cast<const uint4*>(kp + key * kstride + seg * 8)
-                         : make_uint4(0, 0, 0, 0);
-    }
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int j = 0; j < VPAIR; ++j) {
-      const int pu = tid + 256 * j;
-      const int seg = pu % SEGS, kp2 = pu / SEGS;
-      const int k0 = 2 * kp2;
-      vreg[j][0] = k0 < nv ? *reinterpret_cast<const uint4*>(vp + k0 * kstride + seg * 8)
-                           : make_uint4(0, 0, 0, 0);
-      vreg[j][1] = k0 + 1 < nv ? *reinterpret_cast<const uint4*>(vp + (k0 + 1) * kstride + seg * 8)
-                               : make_uint4(0, 0, 0, 0);
-    }
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  float mu = -INFINITY;
+  float lsum = 0.f;
+  const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
+
+  // K operands of half kt of the tile in `stage` (A of S^T = K Q'^T)
+  auto kload = [&](int stage, int kt, bf16x8 (&ko)[KSTEPS]) {
+    TT_LDS const uint8_t* kb = lsm + stage * C::TILE + kt * 32 * C::CH * 16 + kbase;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      ko[kk] = *reinterpret_cast<TT_LDS const bf16x8*>(kb + kk * 2 * 16 * 16);
   };
-  auto sstore = [&](int buf) {
+  // S^T of 32 keys x this wave's 32 rows
+  auto qk = [&](const bf16x8 (&ko)[KSTEPS], f32x16& sc) {
 #pragma unroll
-    for (int j = 0; j < KVEC; ++j) {
-      const int v = tid + 256 * j;
-      const int key = v / SEGS, seg = v % SEGS;
-      *reinterpret_cast<uint4*>(&sm.k[buf][key][seg * 8]) = kreg[j];
-    }
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
-    for (int j = 0; j < VPAIR; ++j) {
-      const int pu = tid + 256 * j;
-      const int seg = pu % SEGS, kp2 = pu / SEGS;
-      const uint32_t a[4] = {vreg[j][0].x, vreg[j][0].y, vreg[j][0].z, vreg[j][0].w};
-      const uint32_t c[4] = {vreg[j][1].x, vreg[j][1].y, vreg[j][1].z, vreg[j][1].w};
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ko[kk], qf[kk], sc, 0, 0, 0);
+  };
+  // V^T operands of half kt (A of O^T += V^T P^T), two transpose reads each
+  auto vload = [&](int stage, int kt, bf16x8 (&vo)[2][DT]) {
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    TT_LDS uint8_t* vb = lsm + stage * C::TILE + kt * 8 * 4 * C::CH * 16 + vbase;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = (a[i] & 0xffffu) | (c[i] << 16);          // channel 2i
-        const uint32_t hi = (a[i] >> 16) | (c[i] & 0xffff0000u);      // channel 2i+1
-        *reinterpret_cast<uint32_t*>(&sm.vt[buf][seg * 8 + 2 * i][2 * kp2]) = lo;
-        *reinterpret_cast<uint32_t*>(&sm.vt[buf][seg * 8 + 2 * i + 1][2 * kp2]) = hi;
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        TT_LDS uint8_t* a = vb + ks * 4 * 4 * C::CH * 16 + dt * 4 * 4 * 16;
+        const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<TT_LDS v4i16*>(a));
+        const v4i16 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<TT_LDS v4i16*>(a + 2 * 4 * C::CH * 16));
+        const v8i16 w8 = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
+        vo[ks][dt] = __builtin_bit_cast(bf16x8, w8);
       }
     }
   };
-
-  f32x16 acc[2][DT];
+  auto pv = [&](const bf16x8 (&vo)[2][DT], const bf16x8 (&pb)[2]) {
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo[ks][dt], pb[ks], acc[dt], 0, 0, 0);
+  };
+  // mask keys at or past nvalid in half kt, return the row max
+  auto rowmax = [&](f32x16& sc, int kt, int nvalid) {
+    if (__builtin_expect(nvalid < kt * 32 + 32, 0)) {
+      // key of accumulator r is kt*32 + 4*half + 8*(r/4) + r%4
+      const int lim = nvalid - kt * 32 - 4 * ((static_cast<int>(threadIdx.x) >> 5) & 1);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[rt][dt][r] = 0.f;
-  float mu[2] = {-INFINITY, -INFINITY};
-  float lsum[2] = {0.f, 0.f};
-  const bool wave_has_rows = un.rb * kRowsBf16 + wave * 64 < p.R;
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) gload(t + 1);
-    int nvalid;
-    {
-      const uint16_t* kp;
-      const uint16_t* vp;
-      tile_src(t, kp, vp, nvalid);
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) >= lim) sc[r] = -INFINITY;
     }
-    if (wave_has_rows) {
+    float m = fmaxf(sc[0], sc[1]);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        if (kt * 32 >= nvalid) break;
-        f32x16 sacc[2];
+    for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(sc[r], sc[r + 1]));
+    return xhalf_max(m);
+  };
+  // raise the running max only when a tile exceeds it by more than 2^8
+  auto rescale = [&](float tmax) {
+    if (__any(tmax > mu + kRescaleTh)) {
+      const float mn = fmaxf(mu, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(mu - mn);
+      lsum *= alpha;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[rt][r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&sm.k[buf][kt * 32 + l32][kk * 16 + half * 8]);
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
-            sacc[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qf[rt][kk], sacc[rt], 0, 0, 0);
-        }
-        if (nvalid < kt * 32 + 32) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            if (key >= nvalid) {
-              sacc[0][r] = -INFINITY;
-              sacc[1][r] = -INFINITY;
-            }
-          }
-        }
-        float tmax[2];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          float m = sacc[rt][0];
-#pragma unroll
-          for (int r = 1; r < 16; ++r) m = fmaxf(m, sacc[rt][r]);
-          tmax[rt] = fmaxf(m, __shfl_xor(m, 32));
-        }
-        const bool need = (tmax[0] > mu[0] + kRescaleTh) || (tmax[1] > mu[1] + kRescaleTh);
-        if (__any(need)) {
-#pragma unroll
-          for (int rt = 0; rt < 2; ++rt) {
-            const float mn = fmaxf(mu[rt], tmax[rt]);
-            const float alpha = __builtin_amdgcn_exp2f(mu[rt] - mn);
-            lsum[rt] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) acc[rt][dt][r] *= alpha;
-            mu[rt] = mn;
-          }
-        }
-        bf16x8 pb[2][2];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          float ps = 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(sacc[rt][r] - mu[rt]);
-            ps += e;
-            pb[rt][r >> 3][r & 7] = static_cast<__bf16>(e);
-          }
-          lsum[rt] += ps;
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const uint16_t* vrow = &sm.vt[buf][dt * 32 + l32][kt * 32 + 16 * ks + 4 * half];
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-            const uint4 w = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-              acc[rt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[rt][ks], acc[rt][dt], 0, 0, 0);
-          }
-        }
-      }
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      mu = mn;
     }
-    if (t + 1 < n_tiles) sstore(buf ^ 1);
+  };
+  // P = 2^(S - mu) rounded to bf16 (the B operand of P^T); sums of the
+  // rounded values (two at a time) so numerator and denominator agree
+  auto softmax = [&](const f32x16& sc, bf16x8 (&pb)[2]) {
+    float ps = lsum;
+    uint32_t pk[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const bf16x2 pr = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[r] - mu)),
+                         static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[r + 1] - mu))};
+      ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
+      pk[r >> 1] = __builtin_bit_cast(uint32_t, pr);
+    }
+    pb[0] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    pb[1] = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
+    lsum = ps;
+  };
+  constexpr int LD = 2 * C::CPT;  // copies per thread per tile
+  // wait until this thread's copies of tile t have landed (`later` tiles
+  // issued after it may still be in flight), then make everyone's visible
+  auto wait_tile = [&](int later) {
+    if (later >= 1) wait_vmem<LD>();
+    else wait_vmem<0>();
     __syncthreads();
-  }
+  };
+
+  // Pipeline (per wave; tile t in stage t % 4, halves h = 0, 1).  Operands
+  // of each phase are read from LDS one phase ahead of their MFMAs.
+  //   S(t,1) = QK       overlapped with  P(t,0) = softmax
+  //   O += PV(t,0)      overlapped with  max of S(t,1)
+  //   [tile t+1 visible; tile t+3 copies issued into the stage of tile t-1]
+  //   S(t+1,0) = QK     overlapped with  P(t,1) = softmax
+  //   O += PV(t,1)      overlapped with  max of S(t+1,0)
+  const int pre = n_tiles < C::NST - 1 ? n_tiles : C::NST - 1;
+  for (int t = 0; t < pre; ++t) issue(t);
+  wait_tile(n_tiles > 2 ? 1 : (n_tiles - 1));   // tile 0 (tiles 1..2 may fly)
+  f32x16 sA, sB;
+  bf16x8 pb[2];
+  bf16x8 ko[KSTEPS];
+  bf16x8 vo[2][DT];
+  kload(0, 0, ko);
+  qk(ko, sA);
+  kload(0, 1, ko);
+  float tmax = rowmax(sA, 0, tile_valid(0));
+  auto tile_step = [&](int t, auto more_c) {
+    constexpr bool MORE = decltype(more_c)::value;
+    const int st = t % C::NST;
+    const int nv = tile_valid(t);
+    vload(st, 0, vo);
+    rescale(tmax);
+    softmax(sA, pb);
+    qk(ko, sB);                 // K(t,1) was loaded in the previous phase
+    pv(vo, pb);
+    TT_SCHED_MFMA(KSTEPS, 10, 0);
+    TT_SCHED_MFMA(2 * DT, 1, 0);
+    tmax = rowmax(sB, 1, nv);
+    if (MORE) {
+      wait_tile(t + 2 < n_tiles ? 1 : 0);          // tile t+1 visible
+      if (t + C::NST - 1 < n_tiles) issue(t + C::NST - 1);
+      kload((t + 1) % C::NST, 0, ko);
+    }
+    vload(st, 1, vo);
+    rescale(tmax);
+    softmax(sB, pb);
+    if (MORE) qk(ko, sA);
+    pv(vo, pb);
+    TT_SCHED_MFMA(KSTEPS, 10, 0);
+    TT_SCHED_MFMA(2 * DT, 1, 0);
+    if (MORE) {
+      kload((t + 1) % C::NST, 1, ko);
+      tmax = rowmax(sA, 0, tile_valid(t + 1));
+    }
+  };
+  for (int t = 0; t + 1 < n_tiles; ++t) tile_step(t, std::true_type{});
+  tile_step(n_tiles - 1, std::false_type{});
 
   // ---- partials: (max, sum) per row and the unnormalised accumulator
   const int64_t u = blockIdx.x;
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const float ltot = lsum[rt] + __shfl_xor(lsum[rt], 32);
-    const int rl = wave * 64 + rt * 32 + l32;
-    if (un.rb * kRowsBf16 + rl >= p.R) continue;
-    if (half == 0) {
-      p.part_ml[(u * kRowsBf16 + rl) * 2 + 0] = mu[rt];
-      p.part_ml[(u * kRowsBf16 + rl) * 2 + 1] = ltot;
-    }
-    float* dst = p.part_acc + (u * kRowsBf16 + rl) * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<float4*>(dst + dt * 32 + 8 * j + 4 * half) =
-            make_float4(acc[rt][dt][4 * j], acc[rt][dt][4 * j + 1], acc[rt][dt][4 * j + 2],
-                        acc[rt][dt][4 * j + 3]);
+  const float ltot = xhalf_sum(lsum);
+  const int rl = wave * 32 + l32;
+  if (un.rb * kRowsBf16 + rl >= p.R) return;
+  if (half == 0) {
+    p.part_ml[(u * kRowsBf16 + rl) * 2 + 0] = mu;
+    p.part_ml[(u * kRowsBf16 + rl) * 2 + 1] = ltot;
   }
+  float* dst = p.part_acc + (u * kRowsBf16 + rl) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(dst + dt * 32 + 8 * j + 4 * half) =
+          make_float4(acc[dt][4 * j], acc[dt][4 * j + 1], acc[dt][4 * j + 2], acc[dt][4 * j + 3]);
 }
 
 // ------------------------------------------------------------------ fp32
@@ -531,7 +618,7 @@ AttnPlan attn_plan(int B, int S, int Hq, int Hkv, int d, int dtype, int max_ctx_
   pl.rows_per_unit = dtype == 0 ? kRowsBf16 : kRowsF32;
   pl.row_blocks = static_cast<int>(ceil_div(pl.rows, pl.rows_per_unit));
   const int64_t groups = static_cast<int64_t>(B) * Hkv * pl.row_blocks;
-  const int64_t want = ceil_div(2 * kNumCUs, groups);
+  const int64_t want = ceil_div(kNumCUs, groups);
   int64_t chunk = max_ctx_len > 0 ? ceil_div(max_ctx_len, want < 1 ? 1 : want) : kTK;
   chunk = static_cast<int64_t>(align_up(static_cast<size_t>(chunk), kTK));
   if (chunk < kTK) chunk = kTK;
@@ -539,6 +626,7 @@ AttnPlan attn_plan(int B, int S, int Hq, int Hkv, int d, int dtype, int max_ctx_
   int64_t nc = max_ctx_len > 0 ? ceil_div(max_ctx_len, chunk) : 1;
   pl.n_chunks = static_cast<int>(nc < 1 ? 1 : nc);
   const int64_t units = groups * pl.n_chunks;
+  pl.groups = groups;
   pl.part_acc_bytes = align_up(static_cast<size_t>(units) * pl.rows_per_unit * d * sizeof(float), 256);
   pl.part_ml_bytes = align_up(static_cast<size_t>(units) * pl.rows_per_unit * 2 * sizeof(float), 256);
   pl.total_bytes = pl.part_acc_bytes + pl.part_ml_bytes;
@@ -563,9 +651,9 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& pl, void* ws, hi
   const int64_t units = static_cast<int64_t>(a.B) * a.Hkv * pl.row_blocks * pl.n_chunks;
   if (a.dtype == 0) {
     if (a.d == 128)
-      hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(static_cast<unsigned>(units)), dim3(256), 0, st, kp);
+      hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(static_cast<unsigned>(units)), dim3(512), 0, st, kp);
     else
-      hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(static_cast<unsigned>(units)), dim3(256), 0, st, kp);
+      hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(static_cast<unsigned>(units)), dim3(512), 0, st, kp);
   } else {
     if (a.d == 128)
       hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(static_cast<unsigned>(units)), dim3(64), 0, st, kp);

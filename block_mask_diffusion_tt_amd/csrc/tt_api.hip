@@ -141,11 +141,12 @@ tt_status tt_block_attn(const tt_attn_shape* shape, const void* q_blk, const voi
   for (const void* t : tensors)
     if (t && !aligned(t, 16))
       return fail(TT_ERR_INVALID_ARG, "q/k/v/context/out/residual buffers must be 16-byte aligned");
-  if (ada_gate && !aligned(ada_gate, 16))
-    return fail(TT_ERR_INVALID_ARG, "ada_gate must be 16-byte aligned");
-  if (!aligned(ctx_start, 8) || !aligned(ctx_len, 4) || (lse && !aligned(lse, 4)) ||
-      (ada_shift && !aligned(ada_shift, 4)) || (ada_scale && !aligned(ada_scale, 4)))
-    return fail(TT_ERR_INVALID_ARG, "misaligned ctx_start/ctx_len/lse/ada buffer");
+  const void* ada[] = {ada_shift, ada_scale, ada_gate};
+  for (const void* t : ada)
+    if (t && !aligned(t, 16))
+      return fail(TT_ERR_INVALID_ARG, "ada_shift/ada_scale/ada_gate must be 16-byte aligned");
+  if (!aligned(ctx_start, 8) || !aligned(ctx_len, 4) || (lse && !aligned(lse, 4)))
+    return fail(TT_ERR_INVALID_ARG, "misaligned ctx_start/ctx_len/lse buffer");
   if (shape->batch == 0) return ok();
   const tt::AttnPlan p = tt::attn_plan(shape->batch, shape->block_size, shape->n_q_heads,
                                        shape->n_kv_heads, shape->head_dim, shape->dtype,
@@ -194,8 +195,8 @@ tt_status tt_adaln_single(int32_t batch, int32_t width, int32_t n_layers, const 
     return fail(TT_ERR_INVALID_ARG, "width %d must be a positive multiple of 4", width);
   if (n_layers < 1) return fail(TT_ERR_INVALID_ARG, "n_layers %d < 1", n_layers);
   if (!t_emb || !w || !ada) return fail(TT_ERR_INVALID_ARG, "t_emb, w and ada must be non-NULL");
-  if (!aligned(w, 2) || !aligned(t_emb, 4) || !aligned(ada, 4))
-    return fail(TT_ERR_INVALID_ARG, "misaligned adaLN buffer");
+  if (!aligned(w, 8) || !aligned(t_emb, 4) || !aligned(ada, 4))
+    return fail(TT_ERR_INVALID_ARG, "misaligned adaLN buffer (w needs 8 bytes)");
   if (batch == 0) return ok();
   const hipError_t e = tt::launch_adaln_single(batch, width, n_layers, t_emb, w, bias, table, ada,
                                                static_cast<hipStream_t>(stream));
@@ -287,6 +288,7 @@ tt_status tt_denoise_block(const tt_attn_shape* shape, int32_t n_layers, int32_t
   if (!tokens || !masked) return fail(TT_ERR_INVALID_ARG, "tokens and masked must be non-NULL");
   if (ada_w && (shape->n_q_heads * shape->head_dim) % 4 != 0)
     return fail(TT_ERR_INVALID_ARG, "adaLN width must be a multiple of 4");
+  if (ada_w && !aligned(ada_w, 8)) return fail(TT_ERR_INVALID_ARG, "ada_w must be 8-byte aligned");
   if (shape->batch == 0 || max_steps == 0) return ok();
   const size_t need = denoise_bytes(shape, n_layers, max_ctx_len, vocab);
   if (!workspace || workspace_bytes < need)

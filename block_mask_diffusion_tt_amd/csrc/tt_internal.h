@@ -23,6 +23,7 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // * RB + rb) * NC + c) hold, per row of the row block, the running max m
 // (log2 units), the sum l and the unnormalised accumulator acc[d].
 struct AttnPlan {
+  int64_t groups;     // B * Hkv * RB
   int rows;           // R = S * G
   int rows_per_unit;  // rows a workgroup owns (row block height)
   int row_blocks;     // RB

@@ -89,26 +89,38 @@ __global__ __launch_bounds__(kThreads) void rowreduce_kernel(
   float m = -FLT_MAX, z = 0.f;
   int a = INT_MAX;
   int scalar_from = beg;
+  // one group of 8 consecutive logits, in increasing index order
+  auto group = [&](const float (&v)[8], int base) {
+    const float m8 = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
+                           fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+    if (m8 > m) {
+      z *= fast_exp2((m - m8) * c);
+      m = m8;
+      int j = 7;
+#pragma unroll
+      for (int k = 6; k >= 0; --k) j = (v[k] == m8) ? k : j;
+      a = base + j;
+    }
+    float e[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) e[k] = fast_exp2((v[k] - m) * c);
+    z += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  };
   if (vec_ok) {
     const int ngroups = (end - beg) >> 3;
-    for (int gi = threadIdx.x; gi < ngroups; gi += kThreads) {
+    int gi = threadIdx.x;
+    // four 16-byte loads in flight per thread, consumed in index order
+    for (; gi + 3 * kThreads < ngroups; gi += 4 * kThreads) {
+      float v[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load8<T>(x, beg + ((gi + u * kThreads) << 3), v[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) group(v[u], beg + ((gi + u * kThreads) << 3));
+    }
+    for (; gi < ngroups; gi += kThreads) {
       float v[8];
-      const int base = beg + (gi << 3);
-      load8<T>(x, base, v);
-      const float m8 = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
-                             fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-      if (m8 > m) {
-        z *= fast_exp2((m - m8) * c);
-        m = m8;
-        int j = 7;
-#pragma unroll
-        for (int k = 6; k >= 0; --k) j = (v[k] == m8) ? k : j;
-        a = base + j;
-      }
-      float e[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) e[k] = fast_exp2((v[k] - m) * c);
-      z += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      load8<T>(x, beg + (gi << 3), v);
+      group(v, beg + (gi << 3));
     }
     scalar_from = beg + (ngroups << 3);
   }

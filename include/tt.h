@@ -112,7 +112,8 @@ typedef struct {
  *   lse                   device [B, S, Hq] fp32 or NULL
  * max_ctx_len (host) sizes the launch; correctness never depends on it, but
  * sequences longer than it run with less parallelism.  residual may alias
- * out.  k_blk/v_blk/q_blk/k_ctx/v_ctx must be 16-byte aligned for bf16.
+ * out.  q_blk/k_blk/v_blk/k_ctx/v_ctx/out/residual and the three ada vectors
+ * must be 16-byte aligned.
  * Precision (bf16): q' and the probabilities are rounded to bf16 for the
  * matrix cores, sums are fp32, out is rounded to nearest-even.  (fp32: all
  * fp32.)  Deterministic: identical inputs give identical bits.
@@ -161,7 +162,7 @@ tt_status tt_timestep_embed(int32_t batch, const float* t, float* emb, tt_stream
  *   t_emb device [B, 256] fp32;  w device [256, 3*width] bf16;
  *   bias device [3*width] fp32 or NULL;  table device [n_layers, 3, width]
  *   fp32 or NULL;  ada device [n_layers, 3, B, width] fp32.
- * width must be a multiple of 4.
+ * width must be a multiple of 4; w must be 8-byte aligned.
  * ---------------------------------------------------------------------- */
 tt_status tt_adaln_single(int32_t batch, int32_t width, int32_t n_layers,
                           const float* t_emb, const void* w, const float* bias,

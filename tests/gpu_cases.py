@@ -64,7 +64,7 @@ def run_attn(c, max_ctx_len=None, out=None, with_lse=True):
     import block_mask_diffusion_tt_amd as tt
     shape = tt.attn_shape(c["B"], c["Hq"], c["Hkv"], c["d"], c["S"], c["dtype"])
     hint = c["max_len"] if max_ctx_len is None else max_ctx_len
-    ws = torch.empty(tt.block_attn_workspace_size(shape, hint), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(tt.block_attn_workspace_size(shape, hint), dtype=torch.uint8, device=DEV)
     if out is None:
         out = torch.full((c["B"], c["S"], c["Hq"], c["d"]), 7.0, dtype=c["dtype"], device=DEV)
     lse = torch.full((c["B"], c["S"], c["Hq"]), 7.0, dtype=torch.float32, device=DEV) if with_lse else None
@@ -75,11 +75,30 @@ def run_attn(c, max_ctx_len=None, out=None, with_lse=True):
     return out, lse
 
 
-def oracle_attn(c, seqs=None):
+def rounded_query(c):
+    """The bf16 path's documented operand rounding of the modulated query:
+    q' = q * (1 + scale) + shift in fp32, times log2(e)/sqrt(d) (fp32), rounded
+    to bf16 (nearest-even), returned in fp64 divided by that same factor -- so
+    the oracle fed with it and no modulation evaluates attention of exactly
+    the query the matrix cores see."""
+    q = c["q"].detach().float().cpu()
+    B, S, Hq, d = q.shape
+    if c["scale"] is not None:
+        q = q * (1.0 + c["scale"].detach().cpu().reshape(B, 1, Hq, d))
+    if c["shift"] is not None:
+        q = q + c["shift"].detach().cpu().reshape(B, 1, Hq, d)
+    f = torch.tensor(1.4426950408889634, dtype=torch.float32) / torch.sqrt(torch.tensor(float(d), dtype=torch.float32))
+    qb = (q * f).to(torch.bfloat16).to(torch.float64)
+    return (qb / f.double()).numpy()
+
+
+def oracle_attn(c, seqs=None, rounded_q=False):
     """Oracle on the D2H bytes; `seqs` restricts to a subset of sequences
-    (sampled checks at full size).  Returns (out, lse) for those sequences."""
+    (sampled checks at full size).  Returns (out, lse) for those sequences.
+    With rounded_q the oracle gets rounded_query(c) and no shift/scale."""
     import oracle
     seqs = list(range(c["B"])) if seqs is None else list(seqs)
+    qr = rounded_query(c) if rounded_q else None
     starts = c["ctx_start"].cpu().numpy()
     lens = c["ctx_len"].cpu().numpy()
     kc_all, vc_all = c["kc"], c["vc"]
@@ -89,10 +108,15 @@ def oracle_attn(c, seqs=None):
         kc = np64(kc_all[st:st + n]) if n else np.zeros((0,) + tuple(kc_all.shape[1:]))
         vc = np64(vc_all[st:st + n]) if n else np.zeros((0,) + tuple(vc_all.shape[1:]))
         sel = lambda t: None if t is None else np64(t[b:b + 1])  # noqa: E731
-        o, l = oracle.block_attn(sel(c["q"]), sel(c["kb"]), sel(c["vb"]), kc, vc,
-                                 np.array([0]), np.array([n]), shift=sel(c["shift"]),
-                                 scale=sel(c["scale"]), gate=sel(c["gate"]),
-                                 residual=sel(c["residual"]))
+        if rounded_q:
+            o, l = oracle.block_attn(qr[b:b + 1], sel(c["kb"]), sel(c["vb"]), kc, vc,
+                                     np.array([0]), np.array([n]), gate=sel(c["gate"]),
+                                     residual=sel(c["residual"]))
+        else:
+            o, l = oracle.block_attn(sel(c["q"]), sel(c["kb"]), sel(c["vb"]), kc, vc,
+                                     np.array([0]), np.array([n]), shift=sel(c["shift"]),
+                                     scale=sel(c["scale"]), gate=sel(c["gate"]),
+                                     residual=sel(c["residual"]))
         outs.append(o[0])
         lses.append(l[0])
     return np.stack(outs), np.stack(lses)

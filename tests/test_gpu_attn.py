@@ -51,25 +51,68 @@ def test_shapes_fp32(S, heads, d):
     _check(c, f"fp32 S={S} heads={heads} d={d}")
 
 
-# peaked attention (q x 4) and short contexts, where the block keys carry a
-# large share of the mass: a wrong block-local part cannot hide here.  No gate
-# and no residual, so the bound is the plain 2e-2 on the attention output.
+# Peaked attention (q x 4) and short contexts, where the block keys carry a
+# large share of the mass: a wrong block-local part cannot hide here.  The
+# bf16 path rounds the modulated query to bf16 for the matrix cores (its
+# documented operand precision); with q x 4 that rounding alone moves scores
+# by up to ~0.03 log2 units, so the max-abs bound is applied against the
+# oracle evaluated on that rounded query, and the exact oracle is held to the
+# relative-Frobenius bound.
+def _check_peaked(c, what):
+    say(what, {k: c[k] for k in ("B", "S", "Hq", "Hkv", "d", "dtype")}, "lens", c["lens"])
+    out, lse = run_attn(c)
+    ro, rl = oracle_attn(c, rounded_q=True)
+    assert_attn_close(out, lse, ro, rl, BF16, what + " (rounded q')", gate=c["gate"])
+    eo, _ = oracle_attn(c)
+    o = np64(out)
+    fro = np.linalg.norm(o - eo) / np.linalg.norm(eo)
+    assert fro <= TOL[BF16]["rel_fro"], f"{what}: rel fro vs exact {fro:.3e}"
+    return out
+
+
 @pytest.mark.parametrize("L", [8, 64, 128, 2048])
 def test_peaked_small_context(L):
     c = attn_case(4, 16, 32, 2, 128, [L, L // 2, 0, L], dtype=BF16, seed=300 + L, qscale=4.0,
                   ada=True)
     c["gate"] = None
-    _check(c, f"peaked L={L}")
-    out, _ = run_attn(c)
+    out = _check_peaked(c, f"peaked L={L}")
     assert float(np.sqrt((np64(out) ** 2).mean())) > 0.2    # outputs are not near zero
 
 
-# the same with gate and residual (error scaled by |gate|, plus the store)
 @pytest.mark.parametrize("L", [8, 128])
 def test_peaked_gated(L):
     c = attn_case(4, 16, 32, 2, 128, [L, L // 2, 0, L], dtype=BF16, seed=350 + L, qscale=4.0,
                   ada=True, residual=True)
-    _check(c, f"peaked gated L={L}")
+    _check_peaked(c, f"peaked gated L={L}")
+
+
+# Moderately peaked (q x 2) against the exact oracle with the plain bound.
+def test_q_x2_exact_bound():
+    c = attn_case(4, 16, 32, 2, 128, [64, 700, 0, 2048], dtype=BF16, seed=390, qscale=2.0,
+                  ada=True)
+    c["gate"] = None
+    _check(c, "q x 2 exact")
+
+
+# One workspace serves calls of different shapes in a row.
+def test_workspace_reuse_across_shapes():
+    import block_mask_diffusion_tt_amd as tt
+    big = attn_case(4, 16, 32, 2, 128, [3000, 100, 2500, 64], dtype=BF16, seed=395, ada=True)
+    small = attn_case(2, 4, 8, 2, 64, [900, 1200], dtype=BF16, seed=396)
+    ref_big, _ = run_attn(big)
+    ref_small, _ = run_attn(small)
+    shapes = [tt.attn_shape(x["B"], x["Hq"], x["Hkv"], x["d"], x["S"], BF16) for x in (big, small)]
+    n = max(tt.block_attn_workspace_size(sh, x["max_len"]) for sh, x in zip(shapes, (big, small)))
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    for x, sh, ref in [(big, shapes[0], ref_big), (small, shapes[1], ref_small),
+                       (big, shapes[0], ref_big), (big, shapes[0], ref_big),
+                       (small, shapes[1], ref_small)]:
+        out = torch.empty_like(ref)
+        tt.block_attn(sh, x["q"], x["kb"], x["vb"], x["kc"], x["vc"], x["ctx_start"], x["ctx_len"],
+                      x["max_len"], out, ws, ada_shift=x["shift"], ada_scale=x["scale"],
+                      ada_gate=x["gate"])
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
 
 
 def test_inactive_sequences_untouched():
