@@ -42,7 +42,82 @@ def parse():
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (its "
                          "hardware byte counters calibrate the attention kernel's)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn the counter_collection.csv files of a FETCH_SIZE and a "
+                         "WRITE_SIZE rocprofv3 run (both with --calib-copy-mb) into "
+                         f"{os.path.relpath(COUNTERS_JSON, ROOT)}")
     return ap.parse_args()
+
+
+COUNTERS_JSON = os.path.join(ROOT, "profiles", "attn_ctx8k_hbm_counters.json")
+ATTN_KERNELS = ("attn_bf16_kernel<128>", "merge_kernel<unsigned short>")
+
+
+def attn_source_hash():
+    """Hash of the attention kernel's sources: the counters describe that code only."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("attn.hip", "tt_internal.h"):
+        with open(os.path.join(ROOT, "block_mask_diffusion_tt_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def summarize_counters(fetch_csv, write_csv):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention call's
+    kernels, scaled by what the same counters read for the calibration copy
+    (the largest copy dispatch, whose size is the --calib-copy-mb argument)."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals, copies = {}, []
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"])
+                name = r["Kernel_Name"]
+                if "copyBuffer" in name:
+                    copies.append(v)
+                for k in ATTN_KERNELS:
+                    if k in name:
+                        vals.setdefault(k, []).append(v)
+        return {k: sum(v) / len(v) for k, v in vals.items()}, max(copies)
+
+    fetch, fcopy = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, wcopy = per_kernel(write_csv, "WRITE_SIZE")
+    copy_kib = 1024 * 1024   # the 1 GiB calibration copy reads and writes this much
+    ff, wf = copy_kib / fcopy, copy_kib / wcopy
+    total = sum(fetch[k] * ff + write[k] * wf for k in ATTN_KERNELS) * 1024
+    out = {"workload": "ctx8k (B=64, L=8192, S=16, 32/2 heads, d=128, bf16)",
+           "source_sha256": attn_source_hash(),
+           "fetch_kib_per_dispatch": {k: round(fetch[k], 2) for k in ATTN_KERNELS},
+           "write_kib_per_dispatch": {k: round(write[k], 2) for k in ATTN_KERNELS},
+           "calibration": {"copy_kib": copy_kib, "fetch_kib_read": fcopy, "write_kib_read": wcopy,
+                           "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+           "hbm_bytes_per_launch": int(round(total)),
+           "commands": [
+               "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o p -- "
+               "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calib-copy-mb 1024",
+               "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o p -- "
+               "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calib-copy-mb 1024"]}
+    with open(COUNTERS_JSON, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out, indent=1))
+
+
+def counted_traffic():
+    """HBM bytes per tt_block_attn launch from the committed counter summary, or
+    None when the attention sources changed since it was taken."""
+    try:
+        with open(COUNTERS_JSON) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != attn_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def workload(name):
@@ -71,6 +146,9 @@ def algorithmic_bytes(w, n_masked_rows):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the block-denoising "
               "step is data-parallel over sequences with no exchange, so N GPUs would each run "
@@ -182,7 +260,7 @@ def main():
         "committed_per_step": committed,
         "roofline": {"kernel": "tt_block_attn (attention + merge)", "bound": "hbm",
                      "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": counted_traffic() if w["name"] == "ctx8k" else None,
                      "bytes_per_launch": per_launch, "mean_launch_ms": round(attn_avg, 4)},
     }
     if not args.no_cpu_baseline:

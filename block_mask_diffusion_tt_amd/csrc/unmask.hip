@@ -19,8 +19,13 @@
 //              row whose p lies within kDelta of gamma -- and, when no row
 //              passes, every row within 2*kDelta of the best p -- so the
 //              commit set is the one fp64 arithmetic gives.  kDelta = 2^-14
-//              bounds the fp32 error of p with a wide margin (the error
-//              analysis is in the design notes: about 260 ulp worst case).
+//              is about ten times the worst-case fp32 error of p at
+//              V = 131072: the longest chain of roundings into Z is about 80
+//              additions (64 group sums per thread at one split, the 3-level
+//              group tree, the 8-level thread/wave tree, the slice merge),
+//              at most 80 * 2^-24 relative, plus the exp2 argument rounding
+//              (|x - m| * c * 2^-24, under 2e-6 for the terms that matter)
+//              and one rounding of 1/Z: about 6e-6 in all.
 #include <float.h>
 #include <limits.h>
 

@@ -13,7 +13,7 @@ Pages followed (tags defined in oracle/__init__.py):
   * [news] "architecture details" section: denoiser layer i cross-attends
     context-tower layer i.
 
-Readings where the pages are silent (all listed in the design doc):
+Readings where the pages are silent:
   * one joint softmax over the concatenation [context keys ; block keys]
     (the block-causal mask of the dense form below);
   * scores scaled by 1/sqrt(d), no bias, no soft-cap;

@@ -14,7 +14,7 @@ Pages followed (tags defined in oracle/__init__.py):
   * [modelcard] "good to know" and "differentiators": confidence unmasking at
     gamma=0.8 commits several tokens per iteration.
 
-Readings where the pages are silent (listed in the design doc):
+Readings where the pages are silent:
   * confidence = the largest softmax probability of the row, computed as
     softmax(l / tau); the prediction is the argmax, lowest token id on ties;
   * commit every masked slot with p >= gamma (inclusive); if none qualifies,
