@@ -17,18 +17,21 @@
 //     also takes the S block keys; units write (max, sum, accumulator)
 //     partials that the merge kernel combines in chunk order (deterministic).
 //
-// bf16 kernel (gfx950 matrix cores, 64-wide waves): 4 waves x 64 rows.
+// bf16 kernel (gfx950 matrix cores, 64-wide waves): 8 waves x 32 rows, one
+// workgroup per CU (two waves per SIMD).
 //   S^T = K Q'^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 channels
 //   straight from the LDS K tile, B = the wave's pre-modulated Q' held in
 //   registers), so each lane ends with 16 scores of one row; the online
 //   softmax needs only one cross-lane exchange (lanes l and l^32 share rows).
 //   O^T += V^T P^T with the same instruction: the scores' accumulator layout
-//   is already the B-operand layout of P^T, and V is written transposed into
-//   LDS so each lane reads 2 x 8 bytes of one channel.  Scores are in log2
-//   units (log2(e)/sqrt(d) folded into Q'), and the running max is only
-//   raised when a tile exceeds it by more than 2^8 (values stay <= 256), so
-//   the accumulators are rarely rescaled.  K/V tiles are double-buffered:
-//   the global loads of tile t+1 are in flight while tile t is multiplied.
+//   is already the B-operand layout of P^T, and the V^T operand comes from
+//   the LDS V tile through the transposing ds_read_b64_tr_b16.  Scores are in
+//   log2 units (log2(e)/sqrt(d) folded into Q') and relative to a per-row
+//   reference mu: the QK^T accumulation starts from -mu, so the exponentials
+//   need no subtraction.  mu is only raised when a half-tile exceeds it by
+//   more than 8 (values of P stay <= 256), so accumulators are rarely
+//   rescaled.  K/V tiles stream HBM -> LDS through the direct copy path in a
+//   4-stage ring: three tiles are in flight while one is multiplied.
 #include <float.h>
 #include <math.h>
 
@@ -45,7 +48,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kTK = 64;          // keys per LDS tile
 constexpr int kKPad = 8;         // bf16 padding of an LDS K row
 constexpr int kVPad = 4;         // bf16 padding of an LDS V^T row
-constexpr int kRowsBf16 = 256;   // rows per bf16 workgroup (4 waves x 64)
+constexpr int kRowsBf16 = 256;   // rows per bf16 workgroup (8 waves x 32)
 constexpr int kRowsF32 = 64;     // rows per fp32 workgroup (1 wave, 1 row per lane)
 constexpr float kRescaleTh = 8.f;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -122,6 +125,13 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
                :: "v"(g), "s"(lds) : "memory");
 }
 
+// The same copy from a wave-uniform base plus a per-lane byte offset (the
+// SGPR-base form: no per-copy address arithmetic).
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(lds) : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
@@ -181,7 +191,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
 
   Unit un;
   if (!decode_unit(blockIdx.x, p.Hkv, p.RB, p.NC, p.chunk, p.ctx_len, p.active, un)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31, grp = lane >> 4, li = lane & 15;
   const int64_t kstride = static_cast<int64_t>(p.Hkv) * D;
   TT_LDS uint8_t* const lsm = (TT_LDS uint8_t*)(smem);  // address-space cast
@@ -232,11 +243,25 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
     return (un.has_blk && t == 0) ? p.S
                                   : min(kTK, un.k_end - (un.k_beg + (t - (un.has_blk ? 1 : 0)) * kTK));
   };
-  // Copy m of a tile tensor fills slots [64m, 64m+64): for K, 16 keys x 4
-  // chunks (key 16*(m/(CH/4)) + lane%16, chunk 4*(m%(CH/4)) + lane/16); for V,
-  // 64 consecutive slots of the 4-key-interleaved layout (whole key rows).
-  // Keys past the tile's end repeat its last key (finite values whose scores
-  // are masked to -inf).  K tiles of the NST stages come first, then V tiles.
+  // Copy m (0 <= m < CH) of a tile tensor fills 16-byte slots [64m, 64m+64):
+  // for K, 16 keys x 4 chunks (key 16*(m/(CH/4)) + lane%16, chunk
+  // 4*(m%(CH/4)) + lane/16); for V, 64 consecutive slots of the
+  // 4-key-interleaved layout (whole key rows).  Wave w issues copies
+  // m = w*CPT .. w*CPT+CPT-1.  Full tiles use precomputed byte offsets from a
+  // wave-uniform tile base; a tile with fewer than 64 keys repeats its last
+  // key (finite values whose scores are masked to -inf).  K tiles of the NST
+  // stages come first, then V tiles.
+  auto kkey_of = [&](int m) { return 16 * (m / (C::CH / 4)) + (lane & 15); };
+  auto kch_of = [&](int m) { return 4 * (m % (C::CH / 4)) + (lane >> 4); };
+  auto vkey_of = [&](int m) { const int s0 = 64 * m + lane; return 4 * (s0 / (4 * C::CH)) + (s0 & 3); };
+  auto vch_of = [&](int m) { const int s0 = 64 * m + lane; return (s0 % (4 * C::CH)) >> 2; };
+  uint32_t koff[C::CPT], voff[C::CPT];
+#pragma unroll
+  for (int j = 0; j < C::CPT; ++j) {
+    const int m = wave * C::CPT + j;
+    koff[j] = static_cast<uint32_t>((kkey_of(m) * kstride + kch_of(m) * 8) * 2);
+    voff[j] = static_cast<uint32_t>((vkey_of(m) * kstride + vch_of(m) * 8) * 2);
+  }
   auto issue = [&](int t) {
     const int stage = t % C::NST;
     const uint16_t* kp;
@@ -254,18 +279,23 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
       vp = p.vc + off;
       nv = min(kTK, un.k_end - key0);
     }
+    const uint32_t kl = __builtin_amdgcn_readfirstlane(lds0 + stage * C::TILE + wave * C::CPT * 1024);
+    const uint32_t vl = __builtin_amdgcn_readfirstlane(lds0 + C::VREG + stage * C::TILE + wave * C::CPT * 1024);
+    if (nv == kTK) {
 #pragma unroll
-    for (int j = 0; j < C::CPT; ++j) {
-      const int m = wave * C::CPT + j;
-      const int kkey = 16 * (m / (C::CH / 4)) + (lane & 15);
-      const int kc = 4 * (m % (C::CH / 4)) + (lane >> 4);
-      dma16(kp + min(kkey, nv - 1) * kstride + kc * 8,
-            __builtin_amdgcn_readfirstlane(lds0 + stage * C::TILE + m * 1024));
-      const int slot0 = 64 * m + lane;
-      const int vkey = 4 * (slot0 / (4 * C::CH)) + (slot0 & 3);
-      const int vc = (slot0 % (4 * C::CH)) >> 2;
-      dma16(vp + min(vkey, nv - 1) * kstride + vc * 8,
-            __builtin_amdgcn_readfirstlane(lds0 + C::VREG + stage * C::TILE + m * 1024));
+      for (int j = 0; j < C::CPT; ++j) {
+        dma16s(kp, koff[j], kl + j * 1024);
+        dma16s(vp, voff[j], vl + j * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::CPT; ++j) {
+        const int m = wave * C::CPT + j;
+        const uint32_t ko = static_cast<uint32_t>((min(kkey_of(m), nv - 1) * kstride + kch_of(m) * 8) * 2);
+        const uint32_t vo = static_cast<uint32_t>((min(vkey_of(m), nv - 1) * kstride + vch_of(m) * 8) * 2);
+        dma16s(kp, ko, kl + j * 1024);
+        dma16s(vp, vo, vl + j * 1024);
+      }
     }
   };
 
@@ -282,8 +312,14 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-  float mu = -INFINITY;
+  // Scores are kept relative to the row's running reference mu: the QK^T
+  // accumulation starts from -mu (negmu, all 16 entries of a lane belong to
+  // one row), so no subtraction is needed before the exponentials.
+  float mu = 0.f;
   float lsum = 0.f;
+  f32x16 negmu;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negmu[r] = 0.f;
   const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
   // K operands of half kt of the tile in `stage` (A of S^T = K Q'^T)
@@ -295,10 +331,9 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
   };
   // S^T of 32 keys x this wave's 32 rows
   auto qk = [&](const bf16x8 (&ko)[KSTEPS], f32x16& sc) {
+    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ko[0], qf[0], negmu, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
+    for (int kk = 1; kk < KSTEPS; ++kk)
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ko[kk], qf[kk], sc, 0, 0, 0);
   };
   // V^T operands of half kt (A of O^T += V^T P^T), two transpose reads each
@@ -339,17 +374,23 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
     for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(sc[r], sc[r + 1]));
     return xhalf_max(m);
   };
-  // raise the running max only when a tile exceeds it by more than 2^8
-  auto rescale = [&](float tmax) {
-    if (__any(tmax > mu + kRescaleTh)) {
-      const float mn = fmaxf(mu, tmax);
-      const float alpha = __builtin_amdgcn_exp2f(mu - mn);
+  // raise the reference only when a half-tile exceeds it by more than 2^8
+  // (tmax and sc are relative to mu); sc is shifted to the new reference
+  auto rescale = [&](float tmax, f32x16& sc) {
+    if (__any(tmax > kRescaleTh)) {
+      const float up = fmaxf(tmax, 0.f);
+      const float alpha = __builtin_amdgcn_exp2f(-up);
       lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-      mu = mn;
+      mu += up;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sc[r] -= up;
+        negmu[r] = -mu;
+      }
     }
   };
   // P = 2^(S - mu) rounded to bf16 (the B operand of P^T); sums of the
@@ -359,8 +400,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
     uint32_t pk[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const bf16x2 pr = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[r] - mu)),
-                         static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[r + 1] - mu))};
+      const bf16x2 pr = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[r])),
+                         static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[r + 1]))};
       ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
       pk[r >> 1] = __builtin_bit_cast(uint32_t, pr);
     }
@@ -395,12 +436,21 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
   qk(ko, sA);
   kload(0, 1, ko);
   float tmax = rowmax(sA, 0, tile_valid(0));
+  // the first half-tile sets the reference to its row maximum (finite: the
+  // first half of a unit's first tile always holds a valid key)
+  mu = tmax;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    sA[r] -= tmax;
+    negmu[r] = -mu;
+  }
+  tmax = 0.f;
   auto tile_step = [&](int t, auto more_c) {
     constexpr bool MORE = decltype(more_c)::value;
     const int st = t % C::NST;
     const int nv = tile_valid(t);
     vload(st, 0, vo);
-    rescale(tmax);
+    rescale(tmax, sA);
     softmax(sA, pb);
     qk(ko, sB);                 // K(t,1) was loaded in the previous phase
     pv(vo, pb);
@@ -413,7 +463,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
       kload((t + 1) % C::NST, 0, ko);
     }
     vload(st, 1, vo);
-    rescale(tmax);
+    rescale(tmax, sB);
     softmax(sB, pb);
     if (MORE) qk(ko, sA);
     pv(vo, pb);
