@@ -29,6 +29,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+ROW_REPS = 10          # calls per row in the per-row timing pass
+METRIC = "block-denoise query-tokens/s + achieved HBM GB/s (S=16, ctx 8k, bf16)"
 
 
 def parse():
@@ -180,9 +182,11 @@ def main():
     ada_b = synth.normal((3 * W,), 0.1, sd + 61, torch.float32, dev)
     ada_t = synth.normal((NL, 3, W), 0.1, sd + 62, torch.float32, dev)
     logits = synth.normal((B, S, V), w["logit_std"], sd + 70, bf, dev)
-    tokens0 = torch.full((B, S), 3, dtype=torch.int32, device=dev)
-    masked0 = torch.ones((B, S), dtype=torch.uint8, device=dev)
-    tokens, masked = tokens0.clone(), masked0.clone()
+    # every step starts from a fully masked block: one fresh state per step,
+    # prepared before timing (the unmasking pass updates it in place)
+    n_states = args.warmup + args.steps + ROW_REPS
+    tokens_all = torch.full((n_states, B, S), 3, dtype=torch.int32, device=dev)
+    masked_all = torch.ones((n_states, B, S), dtype=torch.uint8, device=dev)
     n_masked = torch.empty((B,), dtype=torch.int32, device=dev)
     t_step = torch.full((B,), 1.0, dtype=torch.float32, device=dev)   # n_masked / S at step 0
     emb = torch.empty((B, 256), dtype=torch.float32, device=dev)
@@ -195,9 +199,7 @@ def main():
 
     attn_events = []
 
-    def step(record):
-        tokens.copy_(tokens0)            # every step starts from a fully masked block
-        masked.copy_(masked0)
+    def step(i, record):
         tt.timestep_embed(B, t_step, emb)
         tt.adaln_single(B, W, NL, emb, ada_w, ada_b, ada_t, ada)
         # one event pair brackets the six back-to-back attention calls of the
@@ -212,8 +214,8 @@ def main():
         if record:
             e1.record(stream)
             attn_events.append((e0, e1))
-        tt.confidence_unmask(B, S, V, logits, V, w["gamma"], w["tau"], 3, 0, tokens, masked, uws,
-                             n_masked=n_masked)
+        tt.confidence_unmask(B, S, V, logits, V, w["gamma"], w["tau"], 3, 0, tokens_all[i],
+                             masked_all[i], uws, n_masked=n_masked)
 
     if args.calib_copy_mb:
         src = torch.ones(args.calib_copy_mb << 20, dtype=torch.uint8, device=dev)
@@ -222,26 +224,43 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    for _ in range(args.warmup):
-        step(False)
+    for i in range(args.warmup):
+        step(i, False)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
-    for _ in range(args.steps):
-        step(True)
+    for i in range(args.steps):
+        step(args.warmup + i, True)
     t1.record(stream)
     torch.cuda.synchronize()
+    committed = int(B * S - n_masked.sum().item())
+
+    # Per-row times, after the timed region: each row's calls alone,
+    # ROW_REPS times, bracketed by one event pair.
+    def timed(fn):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for r in range(ROW_REPS):
+            fn(r)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / ROW_REPS * 1e3   # us per call
+    base = args.warmup + args.steps
+    us_ada = timed(lambda r: (tt.timestep_embed(B, t_step, emb),
+                              tt.adaln_single(B, W, NL, emb, ada_w, ada_b, ada_t, ada)))
+    us_unmask = timed(lambda r: tt.confidence_unmask(
+        B, S, V, logits, V, w["gamma"], w["tau"], 3, 0, tokens_all[base + r], masked_all[base + r],
+        uws, n_masked=n_masked))
     ms = t0.elapsed_time(t1) / args.steps
     attn_ms = [a.elapsed_time(b) / NL for a, b in attn_events]
     attn_avg = float(np.mean(attn_ms))
-    committed = int(B * S - n_masked.sum().item())
-
     per_launch, step_bytes = algorithmic_bytes(w, B * S)
     qtok_s = B * S / (ms * 1e-3)
     attn_gbps = per_launch / (attn_avg * 1e-3) / 1e9
     result = {
-        "metric": "block-denoise query-tokens/s (S=16, ctx 8k, bf16)",
+        "metric": METRIC,
         "value": round(qtok_s, 1),
         "unit": "query-tokens/s",
         "n_gpus": 1,
@@ -264,6 +283,21 @@ def main():
                      "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": counted_traffic() if w["name"] == "ctx8k" else None,
                      "bytes_per_launch": per_launch, "mean_launch_ms": round(attn_avg, 4)},
+    }
+    # algorithmic bytes of the other rows: adaLN reads W, bias and the table
+    # and writes every layer's vectors; unmasking reads the masked rows'
+    # logits once (the state arrays are a few KB)
+    ada_bytes = 256 * 3 * W * 2 + 3 * W * 4 + NL * 3 * W * 4 + NL * 3 * B * W * 4 + 2 * B * 256 * 4
+    unmask_bytes = B * S * V * 2
+
+    def row(us, nbytes, what):
+        gbps = nbytes / (us * 1e-6) / 1e9
+        return {"calls": what, "us_per_call": round(us, 2), "bytes": nbytes,
+                "gbps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
+    result["rows"] = {
+        "a1_timestep_adaln": row(us_ada, ada_bytes, "tt_timestep_embed + tt_adaln_single"),
+        "a2_a5_block_attn": row(attn_avg * 1e3, per_launch, "tt_block_attn (timed region)"),
+        "a6_a7_unmask": row(us_unmask, unmask_bytes, "tt_confidence_unmask, all rows masked"),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs, kc, vc, qb, kb, vb, ada,

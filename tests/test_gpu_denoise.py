@@ -129,3 +129,15 @@ def test_callback_error_reports_status():
                          torch.full((1,), 8, dtype=torch.int32, device=DEV), 8, prov, tok, msk, ws)
     assert ei.value.status == tt.TT_ERR_CALLBACK and "boom" in str(ei.value)
     assert int(msk.sum()) == S       # state of the last completed step (none)
+
+
+# Block-size sweep of the full loop (the ctx-32768 sweep's S and gamma grid at
+# a size the oracle replays in seconds): every step's commits, the final ids
+# and masks, commit steps and step count must equal the oracle's.
+@pytest.mark.parametrize("S", [4, 16, 64])
+@pytest.mark.parametrize("gamma", [0.6, 0.8, 0.95])
+def test_block_size_gamma_sweep(S, gamma):
+    lens = [1500, 263] if S < 64 else [700, 129]
+    taken, r = _run(2, S, 32, 2, 128, 2048, 1, lens, S, torch.bfloat16, 7.0, gamma, 1.0,
+                    ada=True, seed=100 + S + int(100 * gamma))
+    assert r["masked"].sum() == 0 and taken <= S
