@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ctx8k", choices=["ctx8k", "ragged64", "batch128"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=8)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=24)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (its "
                          "hardware byte counters calibrate the attention kernel's)")

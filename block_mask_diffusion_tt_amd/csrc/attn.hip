@@ -320,7 +320,6 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
   f32x16 negmu;
 #pragma unroll
   for (int r = 0; r < 16; ++r) negmu[r] = 0.f;
-  const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
   // K operands of half kt of the tile in `stage` (A of S^T = K Q'^T)
   auto kload = [&](int stage, int kt, bf16x8 (&ko)[KSTEPS]) {
@@ -393,21 +392,28 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
       }
     }
   };
-  // P = 2^(S - mu) rounded to bf16 (the B operand of P^T); sums of the
-  // rounded values (two at a time) so numerator and denominator agree
+  // P = 2^S (scores relative to mu) rounded to bf16, the B operand of P^T.
+  // The row sum adds the fp32 values in two chains of plain adds: the
+  // dot-product instruction would serialize with the matrix products.
   auto softmax = [&](const f32x16& sc, bf16x8 (&pb)[2]) {
-    float ps = lsum;
+    float e[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(sc[r]);
     uint32_t pk[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const bf16x2 pr = {static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[r])),
-                         static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[r + 1]))};
-      ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
+      const bf16x2 pr = {static_cast<__bf16>(e[r]), static_cast<__bf16>(e[r + 1])};
       pk[r >> 1] = __builtin_bit_cast(uint32_t, pr);
     }
+    float s0 = e[0], s1 = e[1];
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) {
+      s0 += e[r];
+      s1 += e[r + 1];
+    }
+    lsum += s0 + s1;
     pb[0] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
     pb[1] = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
-    lsum = ps;
   };
   constexpr int LD = 2 * C::CPT;  // copies per thread per tile
   // wait until this thread's copies of tile t have landed (`later` tiles
