@@ -126,9 +126,10 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
 }
 
 // The same copy from a wave-uniform base plus a per-lane byte offset (the
-// SGPR-base form: no per-copy address arithmetic).
+// SGPR-base form: no per-copy address arithmetic), marked non-temporal: the
+// context K/V is read once per layer, so the caches need not keep it.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :: "v"(off), "s"(base), "s"(lds) : "memory");
 }
 
@@ -359,7 +360,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
       for (int dt = 0; dt < DT; ++dt)
         acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo[ks][dt], pb[ks], acc[dt], 0, 0, 0);
   };
-  // mask keys at or past nvalid in half kt, return the row max
+  // mask keys at or past nvalid in half kt, return the maximum of this
+  // lane's 16 scores (lanes l and l^32 hold the two halves of a row)
   auto rowmax = [&](f32x16& sc, int kt, int nvalid) {
     if (__builtin_expect(nvalid < kt * 32 + 32, 0)) {
       // key of accumulator r is kt*32 + 4*half + 8*(r/4) + r%4
@@ -371,13 +373,15 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
     float m = fmaxf(sc[0], sc[1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(sc[r], sc[r + 1]));
-    return xhalf_max(m);
+    return m;
   };
   // raise the reference only when a half-tile exceeds it by more than 2^8
-  // (tmax and sc are relative to mu); sc is shifted to the new reference
-  auto rescale = [&](float tmax, f32x16& sc) {
-    if (__any(tmax > kRescaleTh)) {
-      const float up = fmaxf(tmax, 0.f);
+  // (scores are relative to mu): the lane maxima decide, and only then are
+  // the two halves of each row combined, so both lanes of a row move mu
+  // together; sc is shifted to the new reference
+  auto rescale = [&](float lmax, f32x16& sc) {
+    if (__any(lmax > kRescaleTh)) {
+      const float up = fmaxf(xhalf_max(lmax), 0.f);
       const float alpha = __builtin_amdgcn_exp2f(-up);
       lsum *= alpha;
 #pragma unroll
@@ -441,7 +445,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
   kload(0, 0, ko);
   qk(ko, sA);
   kload(0, 1, ko);
-  float tmax = rowmax(sA, 0, tile_valid(0));
+  float tmax = xhalf_max(rowmax(sA, 0, tile_valid(0)));
   // the first half-tile sets the reference to its row maximum (finite: the
   // first half of a unit's first tile always holds a valid key)
   mu = tmax;
