@@ -106,19 +106,31 @@ __global__ __launch_bounds__(256) void adaln_kernel(int B, int width, int n_laye
 #pragma unroll
     for (int j = 0; j < 4; ++j) s_part[slice][r][4 * cq + j] = acc[r][j];
   __syncthreads();
-  // epilogue: 256 threads over (row, column) pairs of the tile
-  for (int idx = threadIdx.x; idx < kRows * kCols; idx += 256) {
-    const int r = idx / kCols, c = idx % kCols;
-    const int col = n0 + c;
-    if (r >= nb || col >= N) continue;
-    float u = 0.f;
+  // epilogue: one 4-column quad of one row per thread (8 rows x 32 quads);
+  // width is a multiple of 4, so a quad never straddles shift/scale/gate
+  {
+    const int r = threadIdx.x >> 5, q = threadIdx.x & 31;
+    const int col = n0 + 4 * q;
+    if (r < nb && col < N) {
+      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int sl = 0; sl < kSlices; ++sl) u += s_part[sl][r][c];
-    u += bias ? bias[col] : 0.f;
-    const int j = col / width, cc = col % width;
-    for (int l = 0; l < n_layers; ++l) {
-      const float tv = table ? table[(static_cast<int64_t>(l) * 3 + j) * width + cc] : 0.f;
-      ada[((static_cast<int64_t>(l) * 3 + j) * B + b0 + r) * width + cc] = u + tv;
+      for (int sl = 0; sl < kSlices; ++sl) {
+        const float4 v = *reinterpret_cast<const float4*>(&s_part[sl][r][4 * q]);
+        u.x += v.x; u.y += v.y; u.z += v.z; u.w += v.w;
+      }
+      if (bias) {
+        const float4 bv = *reinterpret_cast<const float4*>(bias + col);
+        u.x += bv.x; u.y += bv.y; u.z += bv.z; u.w += bv.w;
+      }
+      const int j = col / width, cc = col % width;
+      for (int l = 0; l < n_layers; ++l) {
+        float4 o = u;
+        if (table) {
+          const float4 tv = *reinterpret_cast<const float4*>(table + (static_cast<int64_t>(l) * 3 + j) * width + cc);
+          o.x += tv.x; o.y += tv.y; o.z += tv.z; o.w += tv.w;
+        }
+        *reinterpret_cast<float4*>(ada + ((static_cast<int64_t>(l) * 3 + j) * B + b0 + r) * width + cc) = o;
+      }
     }
   }
 }

@@ -626,17 +626,20 @@ __device__ __forceinline__ void load4<uint16_t>(const uint16_t* src, float (&v)[
   v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xffff0000u);
 }
 
-template <typename OutT>
+// One workgroup per 64 rows of a (sequence, KV head, row block) group: four
+// threads per row, each owning D/4 channels, read every chunk's partial of
+// their row (16-byte loads) before the arithmetic.
+template <typename OutT, int D>
 __global__ __launch_bounds__(256) void merge_kernel(MParams p) {
-  const int D = p.D;
-  const int quads = D / 4;
+  constexpr int CPT = D / 4;   // channels per thread
+  constexpr int Q = CPT / 4;   // 16-byte loads per thread per chunk
   const int grp = blockIdx.y;  // (b, g, rb)
   const int rb = grp % p.RB;
   const int g = (grp / p.RB) % p.Hkv;
   const int b = grp / (p.RB * p.Hkv);
   if (p.active && !p.active[b]) return;
-  const int idx = blockIdx.x * 256 + threadIdx.x;
-  const int rl = idx / quads, dq = idx % quads;
+  const int rl = blockIdx.x * 64 + (threadIdx.x >> 2);
+  const int c0 = (threadIdx.x & 3) * CPT;
   if (rl >= p.rows_per_unit) return;
   const int row = rb * p.rows_per_unit + rl;
   if (row >= p.R) return;
@@ -644,29 +647,47 @@ __global__ __launch_bounds__(256) void merge_kernel(MParams p) {
   const int64_t u0 = static_cast<int64_t>(grp) * p.NC;
   float M = -INFINITY;
   for (int c = 0; c < n; ++c) M = fmaxf(M, p.part_ml[((u0 + c) * p.rows_per_unit + rl) * 2]);
-  float wsum = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  float L = 0.f;
+  float o[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) o[i] = 0.f;
   for (int c = 0; c < n; ++c) {
     const int64_t base = (u0 + c) * p.rows_per_unit + rl;
     const float w = exp2f(p.part_ml[base * 2] - M);
-    wsum = fmaf(w, p.part_ml[base * 2 + 1], wsum);
-    const float4 a = *reinterpret_cast<const float4*>(p.part_acc + base * D + dq * 4);
-    o0 = fmaf(w, a.x, o0); o1 = fmaf(w, a.y, o1); o2 = fmaf(w, a.z, o2); o3 = fmaf(w, a.w, o3);
+    L = fmaf(w, p.part_ml[base * 2 + 1], L);
+    const float4* src = reinterpret_cast<const float4*>(p.part_acc + base * D + c0);
+    float4 a[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) a[q] = src[q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      o[4 * q + 0] = fmaf(w, a[q].x, o[4 * q + 0]);
+      o[4 * q + 1] = fmaf(w, a[q].y, o[4 * q + 1]);
+      o[4 * q + 2] = fmaf(w, a[q].z, o[4 * q + 2]);
+      o[4 * q + 3] = fmaf(w, a[q].w, o[4 * q + 3]);
+    }
   }
-  const float inv = 1.f / wsum;
-  float o[4] = {o0 * inv, o1 * inv, o2 * inv, o3 * inv};
+  const float inv = 1.f / L;
   const int s = row / p.G, h = g * p.G + row % p.G;
   const int64_t orow = (static_cast<int64_t>(b) * p.S + s) * p.Hq + h;
-  if (p.gate) {
-    const float4 gv = *reinterpret_cast<const float4*>(p.gate + (static_cast<int64_t>(b) * p.Hq + h) * D + dq * 4);
-    o[0] *= gv.x; o[1] *= gv.y; o[2] *= gv.z; o[3] *= gv.w;
+  const float* gp = p.gate ? p.gate + (static_cast<int64_t>(b) * p.Hq + h) * D + c0 : nullptr;
+  const OutT* rp = p.residual ? static_cast<const OutT*>(p.residual) + orow * D + c0 : nullptr;
+  OutT* op = static_cast<OutT*>(p.out) + orow * D + c0;
+#pragma unroll
+  for (int q = 0; q < Q; ++q) {
+    float v[4] = {o[4 * q] * inv, o[4 * q + 1] * inv, o[4 * q + 2] * inv, o[4 * q + 3] * inv};
+    if (gp) {
+      const float4 gv = *reinterpret_cast<const float4*>(gp + 4 * q);
+      v[0] *= gv.x; v[1] *= gv.y; v[2] *= gv.z; v[3] *= gv.w;
+    }
+    if (rp) {
+      float r[4];
+      load4<OutT>(rp + 4 * q, r);
+      v[0] += r[0]; v[1] += r[1]; v[2] += r[2]; v[3] += r[3];
+    }
+    store4<OutT>(op + 4 * q, v[0], v[1], v[2], v[3]);
   }
-  if (p.residual) {
-    float r[4];
-    load4<OutT>(static_cast<const OutT*>(p.residual) + orow * D + dq * 4, r);
-    o[0] += r[0]; o[1] += r[1]; o[2] += r[2]; o[3] += r[3];
-  }
-  store4<OutT>(static_cast<OutT*>(p.out) + orow * D + dq * 4, o[0], o[1], o[2], o[3]);
-  if (p.lse && dq == 0) p.lse[orow] = 0.6931471805599453f * (M + log2f(wsum));
+  if (p.lse && c0 == 0) p.lse[orow] = 0.6931471805599453f * (M + log2f(L));
 }
 
 }  // namespace
@@ -728,13 +749,15 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& pl, void* ws, hi
   mp.chunk = pl.chunk; mp.ctx_len = a.ctx_len; mp.active = a.active; mp.gate = a.gate;
   mp.residual = a.residual; mp.out = a.out; mp.lse = a.lse;
   mp.part_acc = kp.part_acc; mp.part_ml = kp.part_ml;
-  const int per_grp = pl.rows_per_unit * (a.d / 4);
-  const dim3 mg(static_cast<unsigned>(ceil_div(per_grp, 256)),
+  const dim3 mg(static_cast<unsigned>(ceil_div(pl.rows_per_unit, 64)),
                 static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * pl.row_blocks));
-  if (a.dtype == 0)
-    hipLaunchKernelGGL(merge_kernel<uint16_t>, mg, dim3(256), 0, st, mp);
-  else
-    hipLaunchKernelGGL(merge_kernel<float>, mg, dim3(256), 0, st, mp);
+  if (a.dtype == 0) {
+    if (a.d == 128) hipLaunchKernelGGL((merge_kernel<uint16_t, 128>), mg, dim3(256), 0, st, mp);
+    else hipLaunchKernelGGL((merge_kernel<uint16_t, 64>), mg, dim3(256), 0, st, mp);
+  } else {
+    if (a.d == 128) hipLaunchKernelGGL((merge_kernel<float, 128>), mg, dim3(256), 0, st, mp);
+    else hipLaunchKernelGGL((merge_kernel<float, 64>), mg, dim3(256), 0, st, mp);
+  }
   return hipGetLastError();
 }
 

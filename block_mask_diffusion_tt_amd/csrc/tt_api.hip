@@ -195,8 +195,10 @@ tt_status tt_adaln_single(int32_t batch, int32_t width, int32_t n_layers, const 
     return fail(TT_ERR_INVALID_ARG, "width %d must be a positive multiple of 4", width);
   if (n_layers < 1) return fail(TT_ERR_INVALID_ARG, "n_layers %d < 1", n_layers);
   if (!t_emb || !w || !ada) return fail(TT_ERR_INVALID_ARG, "t_emb, w and ada must be non-NULL");
-  if (!aligned(w, 8) || !aligned(t_emb, 4) || !aligned(ada, 4))
-    return fail(TT_ERR_INVALID_ARG, "misaligned adaLN buffer (w needs 8 bytes)");
+  if (!aligned(w, 8) || !aligned(t_emb, 4) || !aligned(ada, 16) || !aligned(bias, 16) ||
+      !aligned(table, 16))
+    return fail(TT_ERR_INVALID_ARG,
+                "misaligned adaLN buffer (w needs 8 bytes; ada, bias and table 16)");
   if (batch == 0) return ok();
   const hipError_t e = tt::launch_adaln_single(batch, width, n_layers, t_emb, w, bias, table, ada,
                                                static_cast<hipStream_t>(stream));
@@ -289,6 +291,8 @@ tt_status tt_denoise_block(const tt_attn_shape* shape, int32_t n_layers, int32_t
   if (ada_w && (shape->n_q_heads * shape->head_dim) % 4 != 0)
     return fail(TT_ERR_INVALID_ARG, "adaLN width must be a multiple of 4");
   if (ada_w && !aligned(ada_w, 8)) return fail(TT_ERR_INVALID_ARG, "ada_w must be 8-byte aligned");
+  if (ada_w && (!aligned(ada_bias, 16) || !aligned(ada_table, 16)))
+    return fail(TT_ERR_INVALID_ARG, "ada_bias and ada_table must be 16-byte aligned");
   if (shape->batch == 0 || max_steps == 0) return ok();
   const size_t need = denoise_bytes(shape, n_layers, max_ctx_len, vocab);
   if (!workspace || workspace_bytes < need)

@@ -162,7 +162,8 @@ tt_status tt_timestep_embed(int32_t batch, const float* t, float* emb, tt_stream
  *   t_emb device [B, 256] fp32;  w device [256, 3*width] bf16;
  *   bias device [3*width] fp32 or NULL;  table device [n_layers, 3, width]
  *   fp32 or NULL;  ada device [n_layers, 3, B, width] fp32.
- * width must be a multiple of 4; w must be 8-byte aligned.
+ * width must be a multiple of 4; w must be 8-byte aligned; ada, bias and
+ * table must be 16-byte aligned.
  * ---------------------------------------------------------------------- */
 tt_status tt_adaln_single(int32_t batch, int32_t width, int32_t n_layers,
                           const float* t_emb, const void* w, const float* bias,
@@ -232,7 +233,8 @@ tt_status tt_confidence_unmask(int32_t batch, int32_t block_size, int32_t vocab,
  *   k_ctx_layers, v_ctx_layers  host arrays of n_layers device pointers
  *   ctx_start, ctx_len          device [B]
  *   ada_w [256, 3*Hq*d] bf16, ada_bias [3*Hq*d] fp32, ada_table
- *   [n_layers, 3, Hq*d] fp32 (device; bias/table may be NULL)
+ *   [n_layers, 3, Hq*d] fp32 (device; bias/table may be NULL; w 8-byte,
+ *   bias and table 16-byte aligned)
  *   tokens [B,S] int32, masked [B,S] uint8 device in/out; commit_step
  *   [B,S] int8 device in/out or NULL; steps_taken host int32 out or NULL.
  * Errors: as tt_block_attn and tt_confidence_unmask, plus TT_ERR_CALLBACK
