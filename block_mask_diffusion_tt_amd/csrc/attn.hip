@@ -173,15 +173,6 @@ __device__ __forceinline__ int vslot(int key, int c) {
   return (key >> 2) * 4 * (D / 8) + c * 4 + (key & 3);
 }
 
-// Scheduling hints: interleave n MFMAs with v VALU ops and r LDS reads each.
-#define TT_SCHED_MFMA(n, v, r)                                     \
-  do {                                                             \
-    _Pragma("unroll") for (int _i = 0; _i < (n); ++_i) {           \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           \
-      __builtin_amdgcn_sched_group_barrier(0x002, (v), 0);         \
-      __builtin_amdgcn_sched_group_barrier(0x100, (r), 0);         \
-    }                                                              \
-  } while (0)
 
 template <int D>
 __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
@@ -464,8 +455,6 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
     softmax(sA, pb);
     qk(ko, sB);                 // K(t,1) was loaded in the previous phase
     pv(vo, pb);
-    TT_SCHED_MFMA(KSTEPS, 10, 0);
-    TT_SCHED_MFMA(2 * DT, 1, 0);
     tmax = rowmax(sB, 1, nv);
     if (MORE) {
       wait_tile(t + 2 < n_tiles ? 1 : 0);          // tile t+1 visible
@@ -477,8 +466,6 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
     softmax(sB, pb);
     if (MORE) qk(ko, sA);
     pv(vo, pb);
-    TT_SCHED_MFMA(KSTEPS, 10, 0);
-    TT_SCHED_MFMA(2 * DT, 1, 0);
     if (MORE) {
       kload((t + 1) % C::NST, 1, ko);
       tmax = rowmax(sA, 0, tile_valid(t + 1));
