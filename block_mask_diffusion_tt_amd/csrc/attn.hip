@@ -613,20 +613,26 @@ __device__ __forceinline__ void load4<uint16_t>(const uint16_t* src, float (&v)[
   v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xffff0000u);
 }
 
-// One workgroup per 64 rows of a (sequence, KV head, row block) group: four
-// threads per row, each owning D/4 channels, read every chunk's partial of
-// their row (16-byte loads) before the arithmetic.
+// Each thread owns kMergeQuads 4-channel quads of one row (16-byte loads);
+// a workgroup covers 256 / (D / (4 kMergeQuads)) rows of one (sequence, KV
+// head, row block) group.  Two quads per thread measured fastest (1, 2, 4
+// and 8 tried at the headline shape: 10.1, 8.6, 10.1, 13.0 us).
+constexpr int kMergeQuads = 2;
+template <int D>
+constexpr int merge_rows_per_wg() { return 256 / (D / (4 * kMergeQuads)); }
+
 template <typename OutT, int D>
 __global__ __launch_bounds__(256) void merge_kernel(MParams p) {
-  constexpr int CPT = D / 4;   // channels per thread
-  constexpr int Q = CPT / 4;   // 16-byte loads per thread per chunk
+  constexpr int CPT = 4 * kMergeQuads;   // channels per thread
+  constexpr int Q = kMergeQuads;         // 16-byte loads per thread per chunk
+  constexpr int TPR = D / CPT;           // threads per row
   const int grp = blockIdx.y;  // (b, g, rb)
   const int rb = grp % p.RB;
   const int g = (grp / p.RB) % p.Hkv;
   const int b = grp / (p.RB * p.Hkv);
   if (p.active && !p.active[b]) return;
-  const int rl = blockIdx.x * 64 + (threadIdx.x >> 2);
-  const int c0 = (threadIdx.x & 3) * CPT;
+  const int rl = blockIdx.x * merge_rows_per_wg<D>() + threadIdx.x / TPR;
+  const int c0 = (threadIdx.x % TPR) * CPT;
   if (rl >= p.rows_per_unit) return;
   const int row = rb * p.rows_per_unit + rl;
   if (row >= p.R) return;
@@ -736,7 +742,8 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& pl, void* ws, hi
   mp.chunk = pl.chunk; mp.ctx_len = a.ctx_len; mp.active = a.active; mp.gate = a.gate;
   mp.residual = a.residual; mp.out = a.out; mp.lse = a.lse;
   mp.part_acc = kp.part_acc; mp.part_ml = kp.part_ml;
-  const dim3 mg(static_cast<unsigned>(ceil_div(pl.rows_per_unit, 64)),
+  const dim3 mg(static_cast<unsigned>(ceil_div(pl.rows_per_unit, a.d == 128 ? merge_rows_per_wg<128>()
+                                                                         : merge_rows_per_wg<64>())),
                 static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * pl.row_blocks));
   if (a.dtype == 0) {
     if (a.d == 128) hipLaunchKernelGGL((merge_kernel<uint16_t, 128>), mg, dim3(256), 0, st, mp);
