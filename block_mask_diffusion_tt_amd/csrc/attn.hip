@@ -148,6 +148,29 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// e[r0..r0+7] rounded to bf16 (round to nearest even), packed in order
+__device__ __forceinline__ bf16x8 pack_bf16(const float (&e)[16], int r0) {
+  uint32_t pk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 pr = {static_cast<__bf16>(e[r0 + 2 * i]), static_cast<__bf16>(e[r0 + 2 * i + 1])};
+    pk[i] = __builtin_bit_cast(uint32_t, pr);
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
+}
+
+// Instruction interleaving requests for the machine scheduler: groups of
+// `n` instructions of one class, in the order requested (class masks of
+// the scheduler: 0x8 matrix products, 0x402 vector ALU incl. transcendental,
+// 0x100 LDS reads).
+constexpr int kSchedMfma = 0x8, kSchedValu = 0x402, kSchedLdsRead = 0x100;
+#define TT_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+
+// Keeps a value's computation before this point: an empty asm that reads and
+// "writes" the register, so the compiler cannot sink the arithmetic that
+// produces it into a later basic block.
+#define TT_PIN(x) asm volatile("" : "+v"(x))
+
 template <int D>
 struct Bf16Cfg {
   static constexpr int CH = D / 8;                 // 16-byte chunks per key row
@@ -327,29 +350,25 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
     for (int kk = 1; kk < KSTEPS; ++kk)
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ko[kk], qf[kk], sc, 0, 0, 0);
   };
-  // V^T operands of half kt (A of O^T += V^T P^T), two transpose reads each
-  auto vload = [&](int stage, int kt, bf16x8 (&vo)[2][DT]) {
+  // V^T operands of k-step ks (keys 16ks..16ks+15) of half kt (A of
+  // O^T += V^T P^T), two transpose reads each
+  auto vload = [&](int stage, int kt, int ks, bf16x8 (&vo)[2][DT]) {
     typedef short v8i16 __attribute__((ext_vector_type(8)));
-    TT_LDS uint8_t* vb = lsm + stage * C::TILE + kt * 8 * 4 * C::CH * 16 + vbase;
+    TT_LDS uint8_t* vb = lsm + stage * C::TILE + kt * 8 * 4 * C::CH * 16 + vbase + ks * 4 * 4 * C::CH * 16;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        TT_LDS uint8_t* a = vb + ks * 4 * 4 * C::CH * 16 + dt * 4 * 4 * 16;
-        const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<TT_LDS v4i16*>(a));
-        const v4i16 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<TT_LDS v4i16*>(a + 2 * 4 * C::CH * 16));
-        const v8i16 w8 = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
-        vo[ks][dt] = __builtin_bit_cast(bf16x8, w8);
-      }
+    for (int dt = 0; dt < DT; ++dt) {
+      TT_LDS uint8_t* a = vb + dt * 4 * 4 * 16;
+      const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<TT_LDS v4i16*>(a));
+      const v4i16 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<TT_LDS v4i16*>(a + 2 * 4 * C::CH * 16));
+      const v8i16 w8 = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
+      vo[ks][dt] = __builtin_bit_cast(bf16x8, w8);
     }
   };
-  auto pv = [&](const bf16x8 (&vo)[2][DT], const bf16x8 (&pb)[2]) {
+  auto pv = [&](const bf16x8 (&vo)[2][DT], const bf16x8 (&pb)[2], int ks) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo[ks][dt], pb[ks], acc[dt], 0, 0, 0);
+    for (int dt = 0; dt < DT; ++dt)
+      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo[ks][dt], pb[ks], acc[dt], 0, 0, 0);
   };
   // mask keys at or past nvalid in half kt, return the maximum of this
   // lane's 16 scores (lanes l and l^32 hold the two halves of a row)
@@ -361,6 +380,12 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
       for (int r = 0; r < 16; ++r)
         if (8 * (r >> 2) + (r & 3) >= lim) sc[r] = -INFINITY;
     }
+    float m = fmaxf(sc[0], sc[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(sc[r], sc[r + 1]));
+    return m;
+  };
+  auto rowmax_full = [&](const f32x16& sc) {
     float m = fmaxf(sc[0], sc[1]);
 #pragma unroll
     for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(sc[r], sc[r + 1]));
@@ -387,19 +412,24 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
       }
     }
   };
-  // P = 2^S (scores relative to mu) rounded to bf16, the B operand of P^T.
-  // The row sum adds the fp32 values in two chains of plain adds: the
-  // dot-product instruction would serialize with the matrix products.
-  auto softmax = [&](const f32x16& sc, bf16x8 (&pb)[2]) {
-    float e[16];
+  // P = 2^S (scores relative to mu) rounded to bf16, the B operand of P^T,
+  // in two parts: exponentials 0..kExpA-1 and the k-step-0 operand pb[0]
+  // (overlapped with the QK^T products), then the rest and pb[1]
+  // (overlapped with the first PV^T products).  The row sum adds the fp32
+  // values in two chains of plain adds: the dot-product instruction would
+  // serialize with the matrix products.
+  constexpr int kExpA = 10;
+  auto softmax_a = [&](const f32x16& sc, float (&e)[16], bf16x8 (&pb)[2]) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(sc[r]);
-    uint32_t pk[8];
+    for (int r = 0; r < kExpA; ++r) e[r] = __builtin_amdgcn_exp2f(sc[r]);
+    pb[0] = pack_bf16(e, 0);
+  };
+  auto softmax_b = [&](const f32x16& sc, float (&e)[16], bf16x8 (&pb)[2]) {
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const bf16x2 pr = {static_cast<__bf16>(e[r]), static_cast<__bf16>(e[r + 1])};
-      pk[r >> 1] = __builtin_bit_cast(uint32_t, pr);
-    }
+    for (int r = kExpA; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(sc[r]);
+    pb[1] = pack_bf16(e, 8);
+  };
+  auto row_sum = [&](const float (&e)[16]) {
     float s0 = e[0], s1 = e[1];
 #pragma unroll
     for (int r = 2; r < 16; r += 2) {
@@ -407,8 +437,6 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
       s1 += e[r + 1];
     }
     lsum += s0 + s1;
-    pb[0] = __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-    pb[1] = __builtin_bit_cast(bf16x8, make_uint4(pk[4], pk[5], pk[6], pk[7]));
   };
   constexpr int LD = 2 * C::CPT;  // copies per thread per tile
   // wait until this thread's copies of tile t have landed (`later` tiles
@@ -419,13 +447,21 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
     __syncthreads();
   };
 
-  // Pipeline (per wave; tile t in stage t % 4, halves h = 0, 1).  Operands
-  // of each phase are read from LDS one phase ahead of their MFMAs.
-  //   S(t,1) = QK       overlapped with  P(t,0) = softmax
-  //   O += PV(t,0)      overlapped with  max of S(t,1)
-  //   [tile t+1 visible; tile t+3 copies issued into the stage of tile t-1]
-  //   S(t+1,0) = QK     overlapped with  P(t,1) = softmax
-  //   O += PV(t,1)      overlapped with  max of S(t+1,0)
+  // Pipeline (per wave; tile t in stage t % 4, halves h = 0, 1).  Each
+  // half-tile runs three phases, each a run of matrix products with the
+  // vector work that does not feed them interleaved:
+  //   1. S(next) = QK (8 products)    with exponentials 0..9 of P(h), pb[0]
+  //   2. O += PV(h) k-step 0 (4)      with exponentials 10..15, pb[1]; the
+  //                                   K operands of the next QK are read
+  //   3. O += PV(h) k-step 1 (4)      with the row sum of P(h) and the row
+  //                                   maximum of S(next); the V^T operands of
+  //                                   the next half's k-step 0 are read
+  // where S(next) is S(t,1) in half 0 and S(t+1,0) in half 1.  At the start
+  // of tile t the workgroup waits until tile t+1 is visible and issues the
+  // copies of tile t+3 into the stage of tile t-1, so every LDS operand read
+  // has a full phase or more before its products.  Only the first tile (the
+  // block's S keys) and the last context tile can hold fewer than 64 keys;
+  // the steps that touch them mask scores, the others do not.
   const int pre = n_tiles < C::NST - 1 ? n_tiles : C::NST - 1;
   for (int t = 0; t < pre; ++t) issue(t);
   wait_tile(n_tiles > 2 ? 1 : (n_tiles - 1));   // tile 0 (tiles 1..2 may fly)
@@ -436,6 +472,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
   kload(0, 0, ko);
   qk(ko, sA);
   kload(0, 1, ko);
+  vload(0, 0, 0, vo);
   float tmax = xhalf_max(rowmax(sA, 0, tile_valid(0)));
   // the first half-tile sets the reference to its row maximum (finite: the
   // first half of a unit's first tile always holds a valid key)
@@ -446,33 +483,85 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
     negmu[r] = -mu;
   }
   tmax = 0.f;
-  auto tile_step = [&](int t, auto more_c) {
-    constexpr bool MORE = decltype(more_c)::value;
+  // interleaving of the three phases (one product, then vector or LDS work)
+  auto sched_phase1 = [&]() {
+#pragma unroll
+    for (int i = 0; i < KSTEPS - 1; ++i) {
+      TT_SCHED_GROUP(kSchedMfma, 1);
+      TT_SCHED_GROUP(kSchedValu, 2);
+    }
+    TT_SCHED_GROUP(kSchedMfma, 1);
+  };
+  auto sched_phase2 = [&](bool kreads) {
+#pragma unroll
+    for (int i = 0; i < DT; ++i) {
+      TT_SCHED_GROUP(kSchedMfma, 1);
+      TT_SCHED_GROUP(kSchedValu, 3);
+      if (kreads) TT_SCHED_GROUP(kSchedLdsRead, KSTEPS / DT);
+    }
+  };
+  auto sched_phase3 = [&]() {
+#pragma unroll
+    for (int i = 0; i < DT; ++i) {
+      TT_SCHED_GROUP(kSchedMfma, 1);
+      TT_SCHED_GROUP(kSchedValu, 6);
+    }
+  };
+  auto tile_step = [&](int t, auto more_c, auto mask_c) {
+    constexpr bool MORE = decltype(more_c)::value;   // a tile t+1 follows
+    constexpr bool MASK = decltype(mask_c)::value;   // tile t or t+1 may be partial
     const int st = t % C::NST;
-    const int nv = tile_valid(t);
-    vload(st, 0, vo);
-    rescale(tmax, sA);
-    softmax(sA, pb);
-    qk(ko, sB);                 // K(t,1) was loaded in the previous phase
-    pv(vo, pb);
-    tmax = rowmax(sB, 1, nv);
+    const int st1 = (t + 1) % C::NST;
     if (MORE) {
       wait_tile(t + 2 < n_tiles ? 1 : 0);          // tile t+1 visible
       if (t + C::NST - 1 < n_tiles) issue(t + C::NST - 1);
-      kload((t + 1) % C::NST, 0, ko);
     }
-    vload(st, 1, vo);
+    float e[16];
+    // ---- half 0: P(t,0) from sA; S(t,1) into sB
+    vload(st, 0, 1, vo);
+    rescale(tmax, sA);
+    softmax_a(sA, e, pb);
+    qk(ko, sB);                                    // K(t,1)
+    sched_phase1();
+    softmax_b(sA, e, pb);
+    pv(vo, pb, 0);
+    if (MORE) kload(st1, 0, ko);                   // K(t+1,0)
+    sched_phase2(MORE);
+    pv(vo, pb, 1);
+    vload(st, 1, 0, vo);
+    row_sum(e);
+    tmax = MASK ? rowmax(sB, 1, tile_valid(t)) : rowmax_full(sB);
+    sched_phase3();
+    TT_PIN(tmax);
+    TT_PIN(lsum);
+    // ---- half 1: P(t,1) from sB; S(t+1,0) into sA
+    vload(st, 1, 1, vo);
     rescale(tmax, sB);
-    softmax(sB, pb);
-    if (MORE) qk(ko, sA);
-    pv(vo, pb);
+    softmax_a(sB, e, pb);
     if (MORE) {
-      kload((t + 1) % C::NST, 1, ko);
-      tmax = rowmax(sA, 0, tile_valid(t + 1));
+      qk(ko, sA);                                  // K(t+1,0)
+      sched_phase1();
     }
+    softmax_b(sB, e, pb);
+    pv(vo, pb, 0);
+    if (MORE) kload(st1, 1, ko);                   // K(t+1,1)
+    sched_phase2(MORE);
+    pv(vo, pb, 1);
+    if (MORE) {
+      vload(st1, 0, 0, vo);                        // V(t+1,0), k-step 0
+      row_sum(e);
+      tmax = MASK ? rowmax(sA, 0, tile_valid(t + 1)) : rowmax_full(sA);
+      sched_phase3();
+      TT_PIN(tmax);
+    } else {
+      row_sum(e);
+    }
+    TT_PIN(lsum);
   };
-  for (int t = 0; t + 1 < n_tiles; ++t) tile_step(t, std::true_type{});
-  tile_step(n_tiles - 1, std::false_type{});
+  if (n_tiles >= 2) tile_step(0, std::true_type{}, std::true_type{});
+  for (int t = 1; t + 2 < n_tiles; ++t) tile_step(t, std::true_type{}, std::false_type{});
+  if (n_tiles >= 3) tile_step(n_tiles - 2, std::true_type{}, std::true_type{});
+  tile_step(n_tiles - 1, std::false_type{}, std::true_type{});
 
   // ---- partials: (max, sum) per row and the unnormalised accumulator
   const int64_t u = blockIdx.x;
