@@ -204,8 +204,13 @@ def main():
     stream = torch.cuda.current_stream()
 
     attn_events = []
+    step_events = []   # one event at the start of every timed step
 
     def step(i, record):
+        if record:
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(stream)
+            step_events.append(ev)
         tt.timestep_embed(B, t_step, emb)
         tt.adaln_single(B, W, NL, emb, ada_w, ada_b, ada_t, ada)
         # one event pair brackets the six back-to-back attention calls of the
@@ -261,8 +266,13 @@ def main():
         uws, n_masked=n_masked))
     loop = denoise_loop(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, clen)
     ms = t0.elapsed_time(t1) / args.steps
+    bounds = step_events + [t1]
+    step_ms = [a.elapsed_time(b) for a, b in zip(bounds[:-1], bounds[1:])]
     attn_ms = [a.elapsed_time(b) / NL for a, b in attn_events]
     attn_avg = float(np.mean(attn_ms))
+
+    def pct(x):
+        return [round(float(v), 4) for v in np.percentile(np.asarray(x), [10, 50, 90])]
     per_launch, step_bytes = algorithmic_bytes(w, B * S)
     qtok_s = B * S / (ms * 1e-3)
     attn_gbps = per_launch / (attn_avg * 1e-3) / 1e9
@@ -274,6 +284,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms_p10_p50_p90": pct(step_ms),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -289,7 +300,8 @@ def main():
         "roofline": {"kernel": "tt_block_attn (attention + merge)", "bound": "hbm",
                      "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": counted_traffic() if w["name"] == "ctx8k" else None,
-                     "bytes_per_launch": per_launch, "mean_launch_ms": round(attn_avg, 4)},
+                     "bytes_per_launch": per_launch, "mean_launch_ms": round(attn_avg, 4),
+                     "launch_ms_p10_p50_p90": pct(attn_ms)},
     }
     # algorithmic bytes of the other rows: adaLN reads W, bias and the table
     # and writes every layer's vectors; unmasking reads the masked rows'

@@ -175,6 +175,17 @@ def test_ragged_batch64_sampled():
     _check(c, "ragged 64", seqs=[0, 17, 40, 63])
 
 
+# Throughput shape: batch 128, contexts uniform in [2048, 16384] (full size,
+# about 1.2 M context tokens) -- sampled, including the shortest and longest
+# sequences of the draw.
+def test_throughput_batch128_sampled():
+    import synth
+    lens = synth.uniform_int(128, 2048, 16384, seed=5).tolist()
+    picks = sorted({0, 127, int(np.argmin(lens)), int(np.argmax(lens))})
+    c = attn_case(128, 16, 32, 2, 128, lens, dtype=BF16, seed=1300, ada=True)
+    _check(c, "throughput 128", seqs=picks)
+
+
 def test_headline_batch64_ctx8192_sampled():
     c = attn_case(64, 16, 32, 2, 128, [8192] * 64, dtype=BF16, seed=1100, ada=True)
     _check(c, "headline 64x8192", seqs=[0, 31, 63])
