@@ -36,8 +36,11 @@ METRIC = "block-denoise query-tokens/s + achieved HBM GB/s (S=16, ctx 8k, bf16)"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # defaults: the GPU leaves its idle clocks over the first ~30 steps (about
+    # 35 ms of work), so 40 warm-up steps put the 100 timed ones at the
+    # sustained rate
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="ctx8k", choices=["ctx8k", "ragged64", "batch128"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=24)
