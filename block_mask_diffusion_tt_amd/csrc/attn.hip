@@ -62,7 +62,7 @@ struct KParams {
   const int64_t* ctx_start; const int32_t* ctx_len; const uint8_t* active;
   const float* shift; const float* scale;
   float qscale;
-  float* part_acc; float* part_ml;
+  void* part_acc; float* part_ml;   // part_acc: fp16 (bf16 kernel) or fp32 (fp32 kernel)
 };
 
 struct MParams {
@@ -70,7 +70,7 @@ struct MParams {
   int rows_per_unit, RB, NC, chunk;
   const int32_t* ctx_len; const uint8_t* active;
   const float* gate; const void* residual; void* out; float* lse;
-  const float* part_acc; const float* part_ml;
+  const void* part_acc; const float* part_ml;
 };
 
 __device__ __forceinline__ int units_of(int L, int chunk, int NC) {
@@ -568,17 +568,33 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
   const float ltot = xhalf_sum(lsum);
   const int rl = wave * 32 + l32;
   if (un.rb * kRowsBf16 + rl >= p.R) return;
-  if (half == 0) {
-    p.part_ml[(u * kRowsBf16 + rl) * 2 + 0] = mu;
-    p.part_ml[(u * kRowsBf16 + rl) * 2 + 1] = ltot;
-  }
-  float* dst = p.part_acc + (u * kRowsBf16 + rl) * D;
+  // o = acc / l in fp16, scaled by 2^-k so the row's largest |o| lands in
+  // [2^14, 2^15): full fp16 precision (2^-11 relative) whatever the scale of
+  // V, no overflow; (m, l, k) in fp32.  k stays in [-100, 127] so that 2^-k
+  // / l and the merge's weight 2^k w l are finite, normal fp32 numbers.
+  const float inv = 1.f / ltot;
+  float amax = 0.f;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<float4*>(dst + dt * 32 + 8 * j + 4 * half) =
-          make_float4(acc[dt][4 * j], acc[dt][4 * j + 1], acc[dt][4 * j + 2], acc[dt][4 * j + 3]);
+    for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(acc[dt][r]));
+  int ex;
+  frexpf(xhalf_max(amax) * inv, &ex);
+  const int k = min(max(ex - 15, -100), 127);
+  const float sc = ldexpf(inv, -k);
+  if (half == 0)
+    *reinterpret_cast<float4*>(p.part_ml + (u * kRowsBf16 + rl) * 4) =
+        make_float4(mu, ltot, static_cast<float>(k), 0.f);
+  uint16_t* dst = static_cast<uint16_t*>(p.part_acc) + (u * kRowsBf16 + rl) * D;
+  typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const half4 h = {static_cast<_Float16>(acc[dt][4 * j] * sc), static_cast<_Float16>(acc[dt][4 * j + 1] * sc),
+                       static_cast<_Float16>(acc[dt][4 * j + 2] * sc), static_cast<_Float16>(acc[dt][4 * j + 3] * sc)};
+      *reinterpret_cast<uint2*>(dst + dt * 32 + 8 * j + 4 * half) = __builtin_bit_cast(uint2, h);
+    }
 }
 
 // ------------------------------------------------------------------ fp32
@@ -660,11 +676,11 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(KParams p) {
   }
   if (!valid) return;
   const int64_t u = blockIdx.x;
-  p.part_ml[(u * kRowsF32 + tid) * 2 + 0] = m;
-  p.part_ml[(u * kRowsF32 + tid) * 2 + 1] = l;
-  float* dst = p.part_acc + (u * kRowsF32 + tid) * D;
+  *reinterpret_cast<float4*>(p.part_ml + (u * kRowsF32 + tid) * 4) = make_float4(m, l, 0.f, 0.f);
+  float* dst = static_cast<float*>(p.part_acc) + (u * kRowsF32 + tid) * D;
+  const float inv = 1.f / l;
 #pragma unroll
-  for (int dd = 0; dd < D; ++dd) dst[dd] = acc[dd];
+  for (int dd = 0; dd < D; ++dd) dst[dd] = acc[dd] * inv;
 }
 
 // ------------------------------------------------------------------ merge
@@ -702,6 +718,27 @@ __device__ __forceinline__ void load4<uint16_t>(const uint16_t* src, float (&v)[
   v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xffff0000u);
 }
 
+// N consecutive partial values from element offset `off`: fp16 partials
+// (bf16 output) or fp32 partials (fp32 output), in 16-byte loads.
+template <typename OutT, int N>
+__device__ __forceinline__ void load_part(const void* part, int64_t off, float (&a)[N]);
+
+template <>
+__device__ __forceinline__ void load_part<float, 8>(const void* part, int64_t off, float (&a)[8]) {
+  const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(part) + off);
+  const float4 x = src[0], y = src[1];
+  a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w;
+  a[4] = y.x; a[5] = y.y; a[6] = y.z; a[7] = y.w;
+}
+
+template <>
+__device__ __forceinline__ void load_part<uint16_t, 8>(const void* part, int64_t off, float (&a)[8]) {
+  typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+  const half8 h = __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(part) + off));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = static_cast<float>(h[i]);
+}
+
 // Each thread owns kMergeQuads 4-channel quads of one row (16-byte loads);
 // a workgroup covers 256 / (D / (4 kMergeQuads)) rows of one (sequence, KV
 // head, row block) group.  Two quads per thread measured fastest (1, 2, 4
@@ -727,27 +764,24 @@ __global__ __launch_bounds__(256) void merge_kernel(MParams p) {
   if (row >= p.R) return;
   const int n = units_of(p.ctx_len[b], p.chunk, p.NC);
   const int64_t u0 = static_cast<int64_t>(grp) * p.NC;
+  // chunk c contributes w_c l_c o_c with w_c = 2^(m_c - M); its stored
+  // partial is o_c 2^-k_c (fp16 for bf16 output, fp32 for fp32 output)
   float M = -INFINITY;
-  for (int c = 0; c < n; ++c) M = fmaxf(M, p.part_ml[((u0 + c) * p.rows_per_unit + rl) * 2]);
+  for (int c = 0; c < n; ++c) M = fmaxf(M, p.part_ml[((u0 + c) * p.rows_per_unit + rl) * 4]);
   float L = 0.f;
   float o[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) o[i] = 0.f;
   for (int c = 0; c < n; ++c) {
     const int64_t base = (u0 + c) * p.rows_per_unit + rl;
-    const float w = exp2f(p.part_ml[base * 2] - M);
-    L = fmaf(w, p.part_ml[base * 2 + 1], L);
-    const float4* src = reinterpret_cast<const float4*>(p.part_acc + base * D + c0);
-    float4 a[Q];
+    const float4 ml = *reinterpret_cast<const float4*>(p.part_ml + base * 4);
+    const float wl = exp2f(ml.x - M) * ml.y;
+    L += wl;
+    const float coef = ldexpf(wl, static_cast<int>(ml.z));
+    float a[CPT];
+    load_part<OutT, CPT>(p.part_acc, base * D + c0, a);
 #pragma unroll
-    for (int q = 0; q < Q; ++q) a[q] = src[q];
-#pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      o[4 * q + 0] = fmaf(w, a[q].x, o[4 * q + 0]);
-      o[4 * q + 1] = fmaf(w, a[q].y, o[4 * q + 1]);
-      o[4 * q + 2] = fmaf(w, a[q].z, o[4 * q + 2]);
-      o[4 * q + 3] = fmaf(w, a[q].w, o[4 * q + 3]);
-    }
+    for (int i = 0; i < CPT; ++i) o[i] = fmaf(coef, a[i], o[i]);
   }
   const float inv = 1.f / L;
   const int s = row / p.G, h = g * p.G + row % p.G;
@@ -790,8 +824,9 @@ AttnPlan attn_plan(int B, int S, int Hq, int Hkv, int d, int dtype, int max_ctx_
   pl.n_chunks = static_cast<int>(nc < 1 ? 1 : nc);
   const int64_t units = groups * pl.n_chunks;
   pl.groups = groups;
-  pl.part_acc_bytes = align_up(static_cast<size_t>(units) * pl.rows_per_unit * d * sizeof(float), 256);
-  pl.part_ml_bytes = align_up(static_cast<size_t>(units) * pl.rows_per_unit * 2 * sizeof(float), 256);
+  const size_t part_elt = dtype == 0 ? 2 : 4;   // fp16 partials for bf16, fp32 for fp32
+  pl.part_acc_bytes = align_up(static_cast<size_t>(units) * pl.rows_per_unit * d * part_elt, 256);
+  pl.part_ml_bytes = align_up(static_cast<size_t>(units) * pl.rows_per_unit * 4 * sizeof(float), 256);
   pl.total_bytes = pl.part_acc_bytes + pl.part_ml_bytes;
   return pl;
 }
@@ -809,7 +844,7 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& pl, void* ws, hi
   kp.ctx_start = a.ctx_start; kp.ctx_len = a.ctx_len; kp.active = a.active;
   kp.shift = a.shift; kp.scale = a.scale;
   kp.qscale = kLog2e / sqrtf(static_cast<float>(a.d));
-  kp.part_acc = static_cast<float*>(ws);
+  kp.part_acc = ws;
   kp.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.part_acc_bytes);
   const int64_t units = static_cast<int64_t>(a.B) * a.Hkv * pl.row_blocks * pl.n_chunks;
   if (a.dtype == 0) {

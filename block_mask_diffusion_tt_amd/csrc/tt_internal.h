@@ -20,8 +20,10 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // Rows of one (sequence, KV head) group: r = s * G + j  (block slot s, query
 // head h = g * G + j).  Keys of a unit: the block's S keys (chunk 0 only)
 // then context tokens [c * chunk, end).  Partials of unit u = (((b * Hkv + g)
-// * RB + rb) * NC + c) hold, per row of the row block, the running max m
-// (log2 units), the sum l and the unnormalised accumulator acc[d].
+// * RB + rb) * NC + c) hold, per row of the row block, (m, l, k, 0) in fp32
+// -- the running max m (log2 units), the sum l and a scale exponent k --
+// and the normalised output o = acc / l times 2^-k: d fp16 values for bf16
+// storage (k keeps |o 2^-k| below 2^15), d fp32 values with k = 0 for fp32.
 struct AttnPlan {
   int64_t groups;     // B * Hkv * RB
   int rows;           // R = S * G

@@ -175,6 +175,26 @@ def test_ragged_batch64_sampled():
     _check(c, "ragged 64", seqs=[0, 17, 40, 63])
 
 
+# Value magnitudes far from 1: the bf16 path stores each unit's normalised
+# output in fp16 with a power-of-two row scale, which must neither overflow
+# (|V| beyond the fp16 range) nor lose relative precision (|V| far below it).
+# Scaling V by a power of two is exact in bf16; the relative Frobenius check
+# is the meaningful one for the tiny case.
+# The output (no residual) is linear in V, so both sides are divided by the
+# scale and held to the unit-scale bound.
+@pytest.mark.parametrize("vscale", [2.0 ** 17, 2.0 ** -20])
+def test_value_magnitudes(vscale):
+    c = attn_case(3, 16, 32, 2, 128, [5000, 700, 0], dtype=BF16, seed=1400, ada=True)
+    for key in ("vb", "vc"):
+        c[key].mul_(vscale)
+    what = f"|V| scaled by {vscale:g}"
+    say(what)
+    out, lse = run_attn(c)
+    ro, rl = oracle_attn(c)
+    assert np.isfinite(np64(out)).all(), what
+    assert_attn_close(np64(out) / vscale, lse, ro / vscale, rl, BF16, what, gate=c["gate"])
+
+
 # Throughput shape: batch 128, contexts uniform in [2048, 16384] (full size,
 # about 1.2 M context tokens) -- sampled, including the shortest and longest
 # sequences of the draw.
