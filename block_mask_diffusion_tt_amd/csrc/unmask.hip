@@ -17,8 +17,9 @@
 //   decide     grid B, 256 threads.  Combines the slices of each row in
 //              slice order, p = 1/Z in fp32, then recomputes in fp64 every
 //              row whose p lies within kDelta of gamma -- and, when no row
-//              passes, every row within 2*kDelta of the best p -- so the
-//              commit set is the one fp64 arithmetic gives.  kDelta = 2^-14
+//              passes and a second row lies within 2*kDelta of the best p,
+//              every row in that band -- so the commit set is the one fp64
+//              arithmetic gives.  kDelta = 2^-14
 //              is about ten times the worst-case fp32 error of p at
 //              V = 131072: the longest chain of roundings into Z is about 80
 //              additions (64 group sums per thread at one split, the 3-level
@@ -165,7 +166,22 @@ template <typename T>
 __device__ double recheck_row(const T* x, int V, float m, double tau, double* red) {
   double acc = 0.0;
   const double md = static_cast<double>(m);
-  for (int i = threadIdx.x; i < V; i += kThreads)
+  // scalar head up to 16-byte alignment, then 8 logits per thread per
+  // iteration (one or two 16-byte loads, eight independent exponentials),
+  // then a scalar tail
+  const int head = min(V, static_cast<int>(((16 - reinterpret_cast<uintptr_t>(x) % 16) % 16) / sizeof(T)));
+  if (static_cast<int>(threadIdx.x) < head)
+    acc += exp((static_cast<double>(load1(x, threadIdx.x)) - md) / tau);
+  const int nvec = (V - head) / 8;
+  for (int j = threadIdx.x; j < nvec; j += kThreads) {
+    float v[8];
+    load8<T>(x, head + 8 * static_cast<int64_t>(j), v);
+    double e[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) e[k] = exp((static_cast<double>(v[k]) - md) / tau);
+    acc += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  }
+  for (int i = head + 8 * nvec + threadIdx.x; i < V; i += kThreads)
     acc += exp((static_cast<double>(load1(x, i)) - md) / tau);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
@@ -232,10 +248,14 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
   }
   __syncthreads();
   if (s_choice == -2) {
-    // every row within 2*kDelta of the best fp32/fp64 p is settled in fp64
+    // every row within 2*kDelta of the best fp32/fp64 p is settled in fp64 --
+    // unless the best is the only such row: every p is within kDelta/10 of
+    // its fp64 value, so the fp64 argmax is then that same row
     const double best = red[0];
     __syncthreads();
-    for (int s = 0; s < S; ++s) {
+    int near = 0;
+    for (int s = 0; s < S; ++s) near += s_msk[s] && s_p[s] >= best - 2.0 * kDelta;
+    for (int s = 0; s < S && near > 1; ++s) {
       if (s_msk[s] && !s_checked[s] && s_p[s] >= best - 2.0 * kDelta) {
         const double p64 = recheck_row<T>(logits + (row0 + s) * row_stride, V, s_m[s], tau, red);
         if (tid == 0) { s_p[s] = p64; s_checked[s] = 1; }
