@@ -27,8 +27,10 @@ __global__ void timestep_embed_kernel(int B, const float* t, const int32_t* n_ma
                       : static_cast<double>(n_masked[b]) / static_cast<double>(S);
   const double f = exp(-log(10000.0) * static_cast<double>(i) / (kEmb / 2));
   const double arg = 1000.0 * tb * f;
-  emb[static_cast<int64_t>(b) * kEmb + i] = static_cast<float>(cos(arg));
-  emb[static_cast<int64_t>(b) * kEmb + kEmb / 2 + i] = static_cast<float>(sin(arg));
+  double sn, cs;
+  sincos(arg, &sn, &cs);
+  emb[static_cast<int64_t>(b) * kEmb + i] = static_cast<float>(cs);
+  emb[static_cast<int64_t>(b) * kEmb + kEmb / 2 + i] = static_cast<float>(sn);
 }
 
 // u = SiLU(emb) @ W for a tile of kRows sequences x 128 columns per
@@ -37,7 +39,8 @@ __global__ void timestep_embed_kernel(int B, const float* t, const int32_t* n_ma
 // (8 bytes each) are issued before any arithmetic.  The 8 k-slices are summed
 // in LDS in a fixed order (deterministic), then the epilogue adds the bias and
 // writes every layer's copy with its table row.
-constexpr int kRows = 8;
+constexpr int kRows = 8;   // 16 rows halve the W re-reads but their LDS allows one
+                           // workgroup per CU: twice as slow, measured
 constexpr int kCols = 128;
 constexpr int kSlices = 8;
 constexpr int kPerSlice = kEmb / kSlices;
@@ -106,10 +109,11 @@ __global__ __launch_bounds__(256) void adaln_kernel(int B, int width, int n_laye
 #pragma unroll
     for (int j = 0; j < 4; ++j) s_part[slice][r][4 * cq + j] = acc[r][j];
   __syncthreads();
-  // epilogue: one 4-column quad of one row per thread (8 rows x 32 quads);
-  // width is a multiple of 4, so a quad never straddles shift/scale/gate
-  {
-    const int r = threadIdx.x >> 5, q = threadIdx.x & 31;
+  // epilogue: one 4-column quad of one row per thread and pass (8 rows x 32
+  // quads per pass); width is a multiple of 4, so a quad never straddles
+  // shift/scale/gate
+  for (int r = threadIdx.x >> 5; r < kRows; r += 256 / 32) {
+    const int q = threadIdx.x & 31;
     const int col = n0 + 4 * q;
     if (r < nb && col < N) {
       float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
