@@ -31,6 +31,13 @@ What is pinned, and how (tests/test_oracle_*.py):
                     one-commit rule with lowest-position ties, lowest-id argmax
                     ties, monotonicity in gamma, loop invariants, scalar-loop
                     brute force.
+  context tower  -- empty context reduces to torch's fp64 causal
+                    scaled-dot-product attention; equals the dense block-causal
+                    form with one block per new token; row s equals a one-token
+                    decode step over [context ; block tokens < s]; the last row
+                    equals the denoiser's bidirectional last row; rows ignore
+                    later block keys; scalar-loop brute force; cache append and
+                    length rule on hand-built regions (room, no room, inactive).
   adaLN-single   -- SiLU(0)=0, sinusoid special values, scalar-loop brute
                     force of the affine map.  The PLACEMENT of scale/shift/gate
                     and the timestep definition are readings the pages do not
@@ -43,6 +50,11 @@ from .attention import (  # noqa: F401
     modulate_q,
     block_attn,
     dense_block_causal_attn,
+)
+from .context import (  # noqa: F401
+    ctx_block_attn,
+    kv_append,
+    ctx_advance,
 )
 from .unmask import (  # noqa: F401
     row_confidence,

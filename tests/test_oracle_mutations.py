@@ -8,9 +8,11 @@ import pytest
 
 import oracle
 import oracle.attention as attention_src
+import oracle.context as context_src
 import oracle.unmask as unmask_src
 
 from . import test_oracle_attention as TA
+from . import test_oracle_context as TC
 from . import test_oracle_unmask as TU
 
 ATTN_PINS = [TA.test_p1_empty_context_is_library_attention,
@@ -43,6 +45,26 @@ ATTN_MUTANTS = [
     ("u[None, :, :, :] + table[:, :, None, :]", "u[None, :, :, :] + 0 * table[:, :, None, :]"),
     ("u.reshape(e.shape[0], 3, width).transpose(1, 0, 2)",
      "u.reshape(e.shape[0], width, 3).transpose(2, 0, 1)"),     # interleaved chunks
+]
+
+CONTEXT_PINS = [TC.test_c1_empty_context_is_library_causal_attention,
+                TC.test_c2_dense_mask_with_one_block_per_token,
+                TC.test_c3_row_equals_single_token_decode,
+                TC.test_c4_last_row_bidirectional_first_row_value,
+                TC.test_c5_causality_and_context_permutation, TC.test_c6_brute_force_tiny,
+                TC.test_k1_append_regions_and_length_rule, TC.test_k2_grown_context_feeds_next_block]
+
+CONTEXT_MUTANTS = [
+    ("kb[b, :s + 1, g, :]], axis=0)", "kb[b, :, g, :]], axis=0)"),     # no causal mask
+    ("kb[b, :s + 1, g, :]], axis=0)", "kb[b, :s + 2, g, :]], axis=0)"),  # off by one
+    ("vb[b, :s + 1, g, :]], axis=0)", "vb[b, :s + 1, g, :]][::-1], axis=0)"),  # misaligned V
+    ("keys = np.concatenate([kc[st:st + n, g, :], ", "keys = np.concatenate([kc[st:st + n, 0, :], "),
+    ("/ np.sqrt(d)            # [n + s + 1]", "           # [n + s + 1]"),  # dropped 1/sqrt(d)
+    ("o = o + _f64(residual)[b, s, h, :]", "o = o"),                      # dropped residual
+    ("kc[st + n:st + n + S] = kb[b]", "kc[st + n - 1:st + n - 1 + S] = kb[b]"),  # overwrites context
+    ("if n + S > int(ctx_end[b]) - st:", "if n + S > int(ctx_end[b]):"),  # room test ignores start
+    ("if n[b] + block_size <= int(ctx_end[b]) - int(ctx_start[b]):",
+     "if n[b] < int(ctx_end[b]) - int(ctx_start[b]):"),                  # length rule without S
 ]
 
 UNMASK_MUTANTS = [
@@ -81,6 +103,14 @@ def test_attention_mutant_is_caught(monkeypatch, old, new):
                  "dense_block_causal_attn"):
         monkeypatch.setattr(oracle, name, getattr(mod, name))
     assert _caught(ATTN_PINS)
+
+
+@pytest.mark.parametrize("old,new", CONTEXT_MUTANTS)
+def test_context_mutant_is_caught(monkeypatch, old, new):
+    mod = _mutant(context_src, old, new)
+    for name in ("ctx_block_attn", "kv_append", "ctx_advance"):
+        monkeypatch.setattr(oracle, name, getattr(mod, name))
+    assert _caught(CONTEXT_PINS)
 
 
 @pytest.mark.parametrize("old,new", UNMASK_MUTANTS)
