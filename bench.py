@@ -178,9 +178,14 @@ def main():
     bf = torch.bfloat16
     sd = w["seed"]
     lens = w["lens"]
-    total = sum(lens)
     max_len = max(lens)
-    start = torch.tensor(np.concatenate([[0], np.cumsum(lens)[:-1]]), dtype=torch.int64, device=dev)
+    # each sequence's cache region holds its context plus room for one block,
+    # which the context-tower row appends into (the denoiser reads the first
+    # ctx_len rows only)
+    region = [L + S for L in lens]
+    total = sum(region)
+    start = torch.tensor(np.concatenate([[0], np.cumsum(region)[:-1]]), dtype=torch.int64, device=dev)
+    ctx_end = start + torch.tensor(region, dtype=torch.int64, device=dev)
     clen = torch.tensor(lens, dtype=torch.int32, device=dev)
     kc = [synth.normal((total, Hkv, d), 1.0, sd + 10 + l, bf, dev) for l in range(NL)]
     vc = [synth.normal((total, Hkv, d), 1.0, sd + 20 + l, bf, dev) for l in range(NL)]
@@ -193,7 +198,7 @@ def main():
     logits = synth.normal((B, S, V), w["logit_std"], sd + 70, bf, dev)
     # every step starts from a fully masked block: one fresh state per step,
     # prepared before timing (the unmasking pass updates it in place)
-    n_states = args.warmup + args.steps + ROW_REPS
+    n_states = args.warmup + args.steps + ROW_REPS + 1
     tokens_all = torch.full((n_states, B, S), 3, dtype=torch.int32, device=dev)
     masked_all = torch.ones((n_states, B, S), dtype=torch.uint8, device=dev)
     n_masked = torch.empty((B,), dtype=torch.int32, device=dev)
@@ -250,9 +255,11 @@ def main():
     torch.cuda.synchronize()
     committed = int(B * S - n_masked.sum().item())
 
-    # Per-row times, after the timed region: each row's calls alone,
-    # ROW_REPS times, bracketed by one event pair.
+    # Per-row times, after the timed region: each row's calls alone, one
+    # untimed call (first launches of a kernel load its code), then ROW_REPS
+    # calls bracketed by one event pair.
     def timed(fn):
+        fn(-1)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -265,8 +272,20 @@ def main():
     us_ada = timed(lambda r: (tt.timestep_embed(B, t_step, emb),
                               tt.adaln_single(B, W, NL, emb, ada_w, ada_b, ada_t, ada)))
     us_unmask = timed(lambda r: tt.confidence_unmask(
-        B, S, V, logits, V, w["gamma"], w["tau"], 3, 0, tokens_all[base + r], masked_all[base + r],
+        B, S, V, logits, V, w["gamma"], w["tau"], 3, 0, tokens_all[base + 1 + r], masked_all[base + 1 + r],
         uws, n_masked=n_masked))
+    # context-tower row: the six layers' causal attention over [context ;
+    # committed block] with the append of the block's K/V into the room after
+    # each context (ctx_len is left alone, so every repetition is the same
+    # work), then the length update on a copy of the lengths
+    us_ctx = timed(lambda r: [tt.ctx_block_attn(shape, qb[l], kb[l], vb[l], kc[l], vc[l], start,
+                                                clen, max_len, out, aws, ctx_end=ctx_end)
+                              for l in range(NL)]) / NL
+    clen2 = clen.clone()
+    appended = torch.empty((B,), dtype=torch.uint8, device=dev)
+    us_adv = timed(lambda r: (clen2.copy_(clen), tt.ctx_advance(B, S, start, ctx_end, clen2,
+                                                                appended=appended)))
+    assert int(appended.sum().item()) == B and clen2.tolist() == [L + S for L in lens]
     loop = denoise_loop(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, clen)
     ms = t0.elapsed_time(t1) / args.steps
     bounds = step_events + [t1]
@@ -311,6 +330,9 @@ def main():
     # logits once (the state arrays are a few KB)
     ada_bytes = 256 * 3 * W * 2 + 3 * W * 4 + NL * 3 * W * 4 + NL * 3 * B * W * 4 + 2 * B * 256 * 4
     unmask_bytes = B * S * V * 2
+    # context-tower call: context K+V, q in, out, block k/v read, and the
+    # block k/v written into the cache
+    ctx_bytes = sum(2 * L * Hkv * d * 2 + S * Hq * d * 2 * 2 + 2 * 2 * S * Hkv * d * 2 for L in lens)
 
     def row(us, nbytes, what):
         gbps = nbytes / (us * 1e-6) / 1e9
@@ -321,6 +343,10 @@ def main():
         "a1_timestep_adaln": row(us_ada, ada_bytes, "tt_timestep_embed + tt_adaln_single"),
         "a2_a5_block_attn": row(attn_avg * 1e3, per_launch, "tt_block_attn (timed region)"),
         "a6_a7_unmask": row(us_unmask, unmask_bytes, "tt_confidence_unmask, all rows masked"),
+        "f1_ctx_commit_attn": row(us_ctx, ctx_bytes,
+                                  "tt_ctx_block_attn with the cache append, per layer"),
+        "f1_ctx_advance": {"calls": "tt_ctx_advance + a 4*B-byte length reset copy",
+                           "us_per_call": round(us_adv, 2)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs, kc, vc, qb, kb, vb, ada,

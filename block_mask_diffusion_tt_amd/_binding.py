@@ -27,7 +27,7 @@ _STATUS_NAMES = {0: "TT_OK", 1: "TT_ERR_INVALID_ARG", 2: "TT_ERR_UNSUPPORTED",
 EXPORTED = ["tt_last_error", "tt_abi_version", "tt_block_attn_workspace_size", "tt_block_attn",
             "tt_workspace_clear", "tt_timestep_embed", "tt_adaln_single",
             "tt_unmask_workspace_size", "tt_confidence_unmask", "tt_denoise_workspace_size",
-            "tt_denoise_block"]
+            "tt_denoise_block", "tt_ctx_block_attn", "tt_ctx_advance"]
 
 
 class TTError(RuntimeError):
@@ -66,6 +66,9 @@ def _load():
         "tt_block_attn_workspace_size": (sz, [shp, i32]),
         "tt_block_attn": (ctypes.c_int, [shp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                          vp, vp, vp, vp, sz, vp]),
+        "tt_ctx_block_attn": (ctypes.c_int, [shp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
+                                             vp, vp, vp, sz, vp]),
+        "tt_ctx_advance": (ctypes.c_int, [i32, i32, vp, vp, vp, vp, vp, vp]),
         "tt_workspace_clear": (ctypes.c_int, [vp, sz, vp]),
         "tt_timestep_embed": (ctypes.c_int, [i32, vp, vp, vp]),
         "tt_adaln_single": (ctypes.c_int, [i32, i32, i32, vp, vp, vp, vp, vp, vp]),
@@ -148,6 +151,22 @@ def block_attn(shape, q_blk, k_blk, v_blk, k_ctx, v_ctx, ctx_start, ctx_len, max
                               int(max_ctx_len), _ptr(active), _ptr(ada_shift), _ptr(ada_scale),
                               _ptr(ada_gate), _ptr(residual), _ptr(out), _ptr(lse),
                               _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def ctx_block_attn(shape, q_blk, k_blk, v_blk, k_ctx, v_ctx, ctx_start, ctx_len, max_ctx_len,
+                   out, workspace, ctx_end=None, active=None, residual=None, lse=None,
+                   stream=None):
+    _check(_lib.tt_ctx_block_attn(ctypes.byref(shape), _ptr(q_blk), _ptr(k_blk), _ptr(v_blk),
+                                  _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_start), _ptr(ctx_len),
+                                  _ptr(ctx_end), int(max_ctx_len), _ptr(active), _ptr(residual),
+                                  _ptr(out), _ptr(lse), _ptr(workspace), _nbytes(workspace),
+                                  _stream(stream)))
+
+
+def ctx_advance(batch, block_size, ctx_start, ctx_end, ctx_len, active=None, appended=None,
+                stream=None):
+    _check(_lib.tt_ctx_advance(int(batch), int(block_size), _ptr(ctx_start), _ptr(ctx_end),
+                               _ptr(ctx_len), _ptr(active), _ptr(appended), _stream(stream)))
 
 
 def workspace_clear(workspace, nbytes=None, stream=None):

@@ -63,6 +63,9 @@ struct KParams {
   const float* shift; const float* scale;
   float qscale;
   void* part_acc; float* part_ml;   // part_acc: fp16 (bf16 kernel) or fp32 (fp32 kernel)
+  int causal;                       // block slot s sees block keys 0..s only
+  const int64_t* ctx_end;           // non-NULL: append the block's K/V to the cache
+  void* kc_out; void* vc_out;
 };
 
 struct MParams {
@@ -108,6 +111,35 @@ __device__ __forceinline__ bool decode_unit(int u, int Hkv, int RB, int NC, int 
   if (un.k_end < un.k_beg) un.k_end = un.k_beg;  // L == 0
   un.has_blk = (un.c == 0);
   return true;
+}
+
+// The context tower's cache append, done by the unit that owns the block
+// keys of (b, g): block rows s < S of KV head g are copied to cache rows
+// ctx_start[b] + ctx_len[b] + s when the sequence's reserved region
+// [ctx_start[b], ctx_end[b]) has room for them.  No unit reads those rows
+// (every unit of b reads context rows below ctx_len[b]), so the copies need
+// no ordering with the attention.  16-byte pieces, all threads of the
+// workgroup.
+__device__ __forceinline__ void append_block_kv(const KParams& p, const Unit& un, int D, int esize) {
+  if (!p.ctx_end || !un.has_blk || un.rb != 0) return;
+  const int64_t st = p.ctx_start[un.b];
+  const int64_t L = p.ctx_len[un.b];
+  if (L + p.S > p.ctx_end[un.b] - st) return;
+  const int per_row = D * esize / 16;
+  const int n = p.S * per_row;
+  const int64_t row_bytes = static_cast<int64_t>(p.Hkv) * D * esize;
+  const char* kb = static_cast<const char*>(p.kbf) + (static_cast<int64_t>(un.b) * p.S * p.Hkv + un.g) * D * esize;
+  const char* vb = static_cast<const char*>(p.vbf) + (static_cast<int64_t>(un.b) * p.S * p.Hkv + un.g) * D * esize;
+  char* kd = static_cast<char*>(p.kc_out) + ((st + L) * p.Hkv + un.g) * D * esize;
+  char* vd = static_cast<char*>(p.vc_out) + ((st + L) * p.Hkv + un.g) * D * esize;
+  for (int i = threadIdx.x; i < 2 * n; i += blockDim.x) {
+    const int j = i < n ? i : i - n;
+    const int64_t off = (j / per_row) * row_bytes + (j % per_row) * 16;
+    if (i < n)
+      *reinterpret_cast<uint4*>(kd + off) = *reinterpret_cast<const uint4*>(kb + off);
+    else
+      *reinterpret_cast<uint4*>(vd + off) = *reinterpret_cast<const uint4*>(vb + off);
+  }
 }
 
 // ------------------------------------------------------------------ bf16
@@ -211,6 +243,14 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
   const int half = lane >> 5, l32 = lane & 31, grp = lane >> 4, li = lane & 15;
   const int64_t kstride = static_cast<int64_t>(p.Hkv) * D;
   TT_LDS uint8_t* const lsm = (TT_LDS uint8_t*)(smem);  // address-space cast
+  append_block_kv(p, un, D, 2);
+  // block keys visible to this lane's row: all S, or slots 0..s when causal
+  // (rows past R take all S, so every row has a finite maximum)
+  int blk_valid = p.S;
+  if (p.causal) {
+    const int row = un.rb * kRowsBf16 + wave * 32 + l32;
+    blk_valid = row < p.R ? row / p.G + 1 : p.S;
+  }
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lsm));
 
   // ---- Q' = (q * (1 + scale) + shift) * log2(e)/sqrt(d), rounded to bf16;
@@ -255,7 +295,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
   const int n_tiles = (un.has_blk ? 1 : 0) + n_ctx_tiles;
   const int64_t ctx0 = p.ctx_start[un.b];
   auto tile_valid = [&](int t) {
-    return (un.has_blk && t == 0) ? p.S
+    return (un.has_blk && t == 0) ? blk_valid
                                   : min(kTK, un.k_end - (un.k_beg + (t - (un.has_blk ? 1 : 0)) * kTK));
   };
   // Copy m (0 <= m < CH) of a tile tensor fills 16-byte slots [64m, 64m+64):
@@ -617,6 +657,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(KParams p) {
   const int64_t kstride = static_cast<int64_t>(p.Hkv) * D;
   const int row = un.rb * kRowsF32 + tid;
   const bool valid = row < p.R;
+  append_block_kv(p, un, D, 4);
+  // block keys visible to this row: all S, or slots 0..s when causal
+  const int blk_valid = (p.causal && valid) ? row / p.G + 1 : p.S;
   {
     const int s = valid ? row / p.G : 0;
     const int h = un.g * p.G + (valid ? row % p.G : 0);
@@ -661,7 +704,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(KParams p) {
       vs[key][dd] = key < nv ? vp[key * kstride + dd] : 0.f;
     }
     __syncthreads();
-    for (int key = 0; key < nv; ++key) {
+    const int nk = t < n_blk_tiles ? min(nv, blk_valid - t * TKF) : nv;
+    for (int key = 0; key < nk; ++key) {
       float s = 0.f;
 #pragma unroll 8
       for (int dd = 0; dd < D; ++dd) s = fmaf(qs[tid][dd], ks[key][dd], s);
@@ -846,6 +890,8 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& pl, void* ws, hi
   kp.qscale = kLog2e / sqrtf(static_cast<float>(a.d));
   kp.part_acc = ws;
   kp.part_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + pl.part_acc_bytes);
+  kp.causal = a.causal;
+  kp.ctx_end = a.ctx_end; kp.kc_out = a.kc_out; kp.vc_out = a.vc_out;
   const int64_t units = static_cast<int64_t>(a.B) * a.Hkv * pl.row_blocks * pl.n_chunks;
   if (a.dtype == 0) {
     if (a.d == 128)

@@ -124,38 +124,47 @@ size_t tt_block_attn_workspace_size(const tt_attn_shape* shape, int32_t max_ctx_
   return p.total_bytes < 256 ? 256 : p.total_bytes;
 }
 
-tt_status tt_block_attn(const tt_attn_shape* shape, const void* q_blk, const void* k_blk,
-                        const void* v_blk, const void* k_ctx, const void* v_ctx,
-                        const int64_t* ctx_start, const int32_t* ctx_len, int32_t max_ctx_len,
-                        const uint8_t* active, const float* ada_shift, const float* ada_scale,
-                        const float* ada_gate, const void* residual, void* out, float* lse,
-                        void* workspace, size_t workspace_bytes, tt_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch shared by the denoiser's and the context tower's
+// attention calls.
+tt_status block_attn_common(const char* fn, const tt_attn_shape* shape, const void* q_blk,
+                            const void* k_blk, const void* v_blk, const void* k_ctx,
+                            const void* v_ctx, const int64_t* ctx_start, const int32_t* ctx_len,
+                            const int64_t* ctx_end, int32_t max_ctx_len, const uint8_t* active,
+                            const float* ada_shift, const float* ada_scale, const float* ada_gate,
+                            const void* residual, void* out, float* lse, int causal,
+                            void* workspace, size_t workspace_bytes, tt_stream stream) {
   tt_status st = check_shape(shape);
   if (st != TT_OK) return st;
-  if (max_ctx_len < 0) return fail(TT_ERR_INVALID_ARG, "max_ctx_len %d < 0", max_ctx_len);
+  if (max_ctx_len < 0) return fail(TT_ERR_INVALID_ARG, "%s: max_ctx_len %d < 0", fn, max_ctx_len);
   if (!q_blk || !k_blk || !v_blk || !out)
-    return fail(TT_ERR_INVALID_ARG, "q_blk, k_blk, v_blk and out must be non-NULL");
+    return fail(TT_ERR_INVALID_ARG, "%s: q_blk, k_blk, v_blk and out must be non-NULL", fn);
   if (!k_ctx || !v_ctx || !ctx_start || !ctx_len)
-    return fail(TT_ERR_INVALID_ARG, "k_ctx, v_ctx, ctx_start and ctx_len must be non-NULL");
+    return fail(TT_ERR_INVALID_ARG, "%s: k_ctx, v_ctx, ctx_start and ctx_len must be non-NULL", fn);
   const void* tensors[] = {q_blk, k_blk, v_blk, k_ctx, v_ctx, out, residual};
   for (const void* t : tensors)
     if (t && !aligned(t, 16))
-      return fail(TT_ERR_INVALID_ARG, "q/k/v/context/out/residual buffers must be 16-byte aligned");
+      return fail(TT_ERR_INVALID_ARG,
+                  "%s: q/k/v/context/out/residual buffers must be 16-byte aligned", fn);
   const void* ada[] = {ada_shift, ada_scale, ada_gate};
   for (const void* t : ada)
     if (t && !aligned(t, 16))
-      return fail(TT_ERR_INVALID_ARG, "ada_shift/ada_scale/ada_gate must be 16-byte aligned");
-  if (!aligned(ctx_start, 8) || !aligned(ctx_len, 4) || (lse && !aligned(lse, 4)))
-    return fail(TT_ERR_INVALID_ARG, "misaligned ctx_start/ctx_len/lse buffer");
+      return fail(TT_ERR_INVALID_ARG, "%s: ada_shift/ada_scale/ada_gate must be 16-byte aligned", fn);
+  if (!aligned(ctx_start, 8) || !aligned(ctx_len, 4) || (lse && !aligned(lse, 4)) ||
+      (ctx_end && !aligned(ctx_end, 8)))
+    return fail(TT_ERR_INVALID_ARG, "%s: misaligned ctx_start/ctx_end/ctx_len/lse buffer", fn);
   if (shape->batch == 0) return ok();
   const tt::AttnPlan p = tt::attn_plan(shape->batch, shape->block_size, shape->n_q_heads,
                                        shape->n_kv_heads, shape->head_dim, shape->dtype,
                                        max_ctx_len);
   if (!workspace || workspace_bytes < p.total_bytes)
-    return fail(TT_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
+    return fail(TT_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes,
                 p.total_bytes);
   if (!aligned(workspace, 256))
-    return fail(TT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    return fail(TT_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
   tt::AttnArgs a{};
   a.B = shape->batch; a.S = shape->block_size; a.Hq = shape->n_q_heads;
   a.Hkv = shape->n_kv_heads; a.d = shape->head_dim; a.dtype = shape->dtype;
@@ -163,8 +172,55 @@ tt_status tt_block_attn(const tt_attn_shape* shape, const void* q_blk, const voi
   a.ctx_start = ctx_start; a.ctx_len = ctx_len; a.active = active;
   a.shift = ada_shift; a.scale = ada_scale; a.gate = ada_gate;
   a.residual = residual; a.out = out; a.lse = lse;
+  a.causal = causal;
+  a.ctx_end = ctx_end;
+  a.kc_out = const_cast<void*>(k_ctx);
+  a.vc_out = const_cast<void*>(v_ctx);
   const hipError_t e = tt::launch_block_attn(a, p, workspace, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "tt_block_attn launch");
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+tt_status tt_block_attn(const tt_attn_shape* shape, const void* q_blk, const void* k_blk,
+                        const void* v_blk, const void* k_ctx, const void* v_ctx,
+                        const int64_t* ctx_start, const int32_t* ctx_len, int32_t max_ctx_len,
+                        const uint8_t* active, const float* ada_shift, const float* ada_scale,
+                        const float* ada_gate, const void* residual, void* out, float* lse,
+                        void* workspace, size_t workspace_bytes, tt_stream stream) {
+  return block_attn_common("tt_block_attn", shape, q_blk, k_blk, v_blk, k_ctx, v_ctx, ctx_start,
+                           ctx_len, nullptr, max_ctx_len, active, ada_shift, ada_scale, ada_gate,
+                           residual, out, lse, 0, workspace, workspace_bytes, stream);
+}
+
+tt_status tt_ctx_block_attn(const tt_attn_shape* shape, const void* q_blk, const void* k_blk,
+                            const void* v_blk, void* k_ctx, void* v_ctx,
+                            const int64_t* ctx_start, const int32_t* ctx_len,
+                            const int64_t* ctx_end, int32_t max_ctx_len, const uint8_t* active,
+                            const void* residual, void* out, float* lse, void* workspace,
+                            size_t workspace_bytes, tt_stream stream) {
+  return block_attn_common("tt_ctx_block_attn", shape, q_blk, k_blk, v_blk, k_ctx, v_ctx,
+                           ctx_start, ctx_len, ctx_end, max_ctx_len, active, nullptr, nullptr,
+                           nullptr, residual, out, lse, 1, workspace, workspace_bytes, stream);
+}
+
+tt_status tt_ctx_advance(int32_t batch, int32_t block_size, const int64_t* ctx_start,
+                         const int64_t* ctx_end, int32_t* ctx_len, const uint8_t* active,
+                         uint8_t* appended, tt_stream stream) {
+  if (batch < 0) return fail(TT_ERR_INVALID_ARG, "tt_ctx_advance: batch %d < 0", batch);
+  if (block_size < 1 || block_size > 64)
+    return fail(TT_ERR_INVALID_ARG, "tt_ctx_advance: block_size %d outside [1, 64]", block_size);
+  if (!ctx_start || !ctx_end || !ctx_len)
+    return fail(TT_ERR_INVALID_ARG, "tt_ctx_advance: ctx_start, ctx_end and ctx_len must be non-NULL");
+  if (!aligned(ctx_start, 8) || !aligned(ctx_end, 8) || !aligned(ctx_len, 4))
+    return fail(TT_ERR_INVALID_ARG, "tt_ctx_advance: misaligned ctx_start/ctx_end/ctx_len");
+  if (batch == 0) return ok();
+  const hipError_t e = tt::launch_ctx_advance(batch, block_size, ctx_start, ctx_end, ctx_len,
+                                              active, appended, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "tt_ctx_advance launch");
   return ok();
 }
 

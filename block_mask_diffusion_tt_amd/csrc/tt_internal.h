@@ -44,6 +44,11 @@ struct AttnArgs {
   const uint8_t* active;
   const float* shift; const float* scale; const float* gate;
   const void* residual; void* out; float* lse;
+  // Context-tower form: causal inside the block (slot s sees block keys
+  // 0..s), and, when ctx_end is set, the block's K/V written into the cache
+  // rows right after each sequence's context (kc_out/vc_out alias kc/vc).
+  int causal;
+  const int64_t* ctx_end; void* kc_out; void* vc_out;
 };
 
 AttnPlan attn_plan(int B, int S, int Hq, int Hkv, int d, int dtype, int max_ctx_len);
@@ -82,5 +87,8 @@ hipError_t launch_active_from_masked(int B, const int32_t* n_masked, uint8_t* ac
 hipError_t launch_count_masked(int B, int S, const uint8_t* masked, int32_t* n_masked,
                                hipStream_t st);
 hipError_t launch_clear(void* p, size_t bytes, hipStream_t st);
+hipError_t launch_ctx_advance(int B, int S, const int64_t* ctx_start, const int64_t* ctx_end,
+                              int32_t* ctx_len, const uint8_t* active, uint8_t* appended,
+                              hipStream_t st);
 
 }  // namespace tt

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define TT_ABI_VERSION 1
+#define TT_ABI_VERSION 2
 #define TT_TIMESTEP_DIM 256 /* width of the timestep embedding */
 
 typedef enum {
@@ -135,6 +135,63 @@ tt_status tt_block_attn(const tt_attn_shape* shape,
                         const float* ada_gate, const void* residual,
                         void* out, float* lse,
                         void* workspace, size_t workspace_bytes, tt_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tt_ctx_block_attn -- one attention layer of the frozen context tower over
+ * a block that has just been committed, with the append of that block's K/V
+ * to the layer's cache.
+ *
+ * [dothoosh] two-tower mechanism section: the context tower runs causally
+ * over the prompt and the committed tokens and produces every layer's KV
+ * cache, which the denoiser reads layer by layer.  [news] architecture
+ * details section: the autoregressive context tower is the part that
+ * generates the KV cache.  (Reading: once a block is final, the context tower
+ * consumes its S tokens like an autoregressive prefill chunk.)
+ *
+ * For sequence b, query head h, KV head g = h / (Hq/Hkv) and block token s:
+ *   keys   K_s = [k_ctx[ctx_start[b] .. ctx_start[b]+ctx_len[b]-1, g, :] ;
+ *                 k_blk[b, 0..s, g, :]]          (V likewise: causal in the block)
+ *   o      = softmax(q_blk[b, s, h, :] K_s^T / sqrt(d)) V_s
+ *   lse    = ln sum_j exp(q_blk[b, s, h, :] K_s,j / sqrt(d))
+ *   out    = residual + o                     (no adaLN: denoiser only)
+ * Append: when ctx_end is non-NULL, every active sequence b with
+ * ctx_len[b] + S <= ctx_end[b] - ctx_start[b] also gets
+ *   k_ctx[ctx_start[b] + ctx_len[b] + s, g, :] = k_blk[b, s, g, :]  (s < S, all g)
+ * (v likewise).  ctx_len is NOT changed (call tt_ctx_advance once after the
+ * last layer); a sequence without room is not written, and its attention is
+ * still computed.  Sequences' reserved regions [ctx_start[b], ctx_end[b])
+ * must not overlap.  NULL ctx_end: attention only, the cache is read-only.
+ *
+ * Layouts, alignment, precision, determinism and errors are those of
+ * tt_block_attn (ada vectors absent); ctx_end is device [B] int64.  The
+ * workspace is sized by tt_block_attn_workspace_size(shape, max_ctx_len).
+ * ---------------------------------------------------------------------- */
+tt_status tt_ctx_block_attn(const tt_attn_shape* shape,
+                            const void* q_blk, const void* k_blk, const void* v_blk,
+                            void* k_ctx, void* v_ctx,
+                            const int64_t* ctx_start, const int32_t* ctx_len,
+                            const int64_t* ctx_end, int32_t max_ctx_len,
+                            const uint8_t* active, const void* residual,
+                            void* out, float* lse,
+                            void* workspace, size_t workspace_bytes, tt_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tt_ctx_advance -- grow every context that took the block: for each active
+ * sequence b (active NULL = all) with ctx_len[b] + block_size <=
+ * ctx_end[b] - ctx_start[b]: ctx_len[b] += block_size and appended[b] = 1;
+ * otherwise ctx_len[b] is unchanged and appended[b] = 0.  The room test is
+ * the one tt_ctx_block_attn's append uses, so after the layers' append calls
+ * and this call the caches and lengths agree ([dothoosh] two-tower mechanism
+ * section: the context tower's cache covers the prompt and every committed
+ * token).
+ *   ctx_start, ctx_end device [B] int64; ctx_len device [B] int32 in/out;
+ *   active device [B] uint8 or NULL; appended device [B] uint8 out or NULL.
+ * Errors: TT_ERR_INVALID_ARG (batch < 0, block_size outside [1, 64], NULL
+ * or misaligned ctx_start/ctx_end/ctx_len), TT_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+tt_status tt_ctx_advance(int32_t batch, int32_t block_size, const int64_t* ctx_start,
+                         const int64_t* ctx_end, int32_t* ctx_len, const uint8_t* active,
+                         uint8_t* appended, tt_stream stream);
 
 /* Zero-fill `bytes` of device memory at `workspace` on `stream` with a
  * kernel (no memset node, so the call can sit inside captured graphs). */

@@ -30,7 +30,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version():
-    assert tt.abi_version() == 1
+    assert tt.abi_version() == 2
 
 
 def _status(fn, *args):
@@ -153,3 +153,37 @@ def test_binding_raises_with_message():
     with pytest.raises(tt.TTError) as ei:
         tt.block_attn_workspace_size(tt.AttnShape(1, 3, 2, 64, 4, 0), 8)
     assert "multiple" in str(ei.value)
+
+
+def _ctx_attn(shape, ws_bytes=1 << 30, **over):
+    args = dict(q=FAKE, kb=FAKE, vb=FAKE, kc=FAKE, vc=FAKE, cs=FAKE, cl=FAKE, ce=FAKE, maxl=128,
+                active=None, res=None, out=FAKE, lse=None, ws=FAKE, stream=None)
+    args.update(over)
+    return tt.lib().tt_ctx_block_attn(ctypes.byref(shape), args["q"], args["kb"], args["vb"],
+                                      args["kc"], args["vc"], args["cs"], args["cl"], args["ce"],
+                                      args["maxl"], args["active"], args["res"], args["out"],
+                                      args["lse"], args["ws"], ws_bytes, args["stream"])
+
+
+def test_ctx_block_attn_rejects_bad_arguments():
+    s = tt.AttnShape(2, 32, 2, 128, 16, 0)
+    assert _ctx_attn(tt.AttnShape(1, 32, 3, 128, 16, 0)) == tt.TT_ERR_INVALID_ARG
+    assert _ctx_attn(tt.AttnShape(1, 32, 2, 96, 16, 0)) == tt.TT_ERR_UNSUPPORTED
+    assert _ctx_attn(s, kc=None) == tt.TT_ERR_INVALID_ARG
+    assert _ctx_attn(s, ce=FAKE + 4) == tt.TT_ERR_INVALID_ARG         # ctx_end needs 8 B
+    assert _ctx_attn(s, vc=FAKE + 8) == tt.TT_ERR_INVALID_ARG         # cache needs 16 B
+    assert _ctx_attn(s, maxl=-3) == tt.TT_ERR_INVALID_ARG
+    need = tt.block_attn_workspace_size(s, 128)
+    assert _ctx_attn(s, ws_bytes=need - 1) == tt.TT_ERR_WORKSPACE
+    assert "tt_ctx_block_attn" in tt.last_error()
+    assert _ctx_attn(tt.AttnShape(0, 32, 2, 128, 16, 0), ws=None, ws_bytes=0) == tt.TT_OK
+
+
+def test_ctx_advance_rejects_bad_arguments():
+    L = tt.lib()
+    assert L.tt_ctx_advance(-1, 16, FAKE, FAKE, FAKE, None, None, None) == tt.TT_ERR_INVALID_ARG
+    assert L.tt_ctx_advance(2, 0, FAKE, FAKE, FAKE, None, None, None) == tt.TT_ERR_INVALID_ARG
+    assert L.tt_ctx_advance(2, 65, FAKE, FAKE, FAKE, None, None, None) == tt.TT_ERR_INVALID_ARG
+    assert L.tt_ctx_advance(2, 16, FAKE, None, FAKE, None, None, None) == tt.TT_ERR_INVALID_ARG
+    assert L.tt_ctx_advance(2, 16, FAKE, FAKE, FAKE + 2, None, None, None) == tt.TT_ERR_INVALID_ARG
+    assert L.tt_ctx_advance(0, 16, FAKE, FAKE, FAKE, None, None, None) == tt.TT_OK
