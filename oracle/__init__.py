@@ -38,6 +38,14 @@ What is pinned, and how (tests/test_oracle_*.py):
                     equals the denoiser's bidirectional last row; rows ignore
                     later block keys; scalar-loop brute force; cache append and
                     length rule on hand-built regions (room, no room, inactive).
+  sampling       -- Philox4x32-10 known-answer vectors; the uniform map's
+                    range and fp32 exactness; Gumbel mean and variance; token
+                    frequencies matching softmax(l / tau); closed forms of the
+                    reported confidence; commit rule under sampling.
+  generation     -- EOS stop and cache-room stop on hand-built logits; caches
+                    holding the provider's K/V of every generated block in
+                    order; the next block's attention equal to attention over
+                    the explicit concatenation; every generated slot final.
   adaLN-single   -- SiLU(0)=0, sinusoid special values, scalar-loop brute
                     force of the affine map.  The PLACEMENT of scale/shift/gate
                     and the timestep definition are readings the pages do not
@@ -61,3 +69,10 @@ from .unmask import (  # noqa: F401
     confidence_unmask,
     denoise_block,
 )
+from .sampling import (  # noqa: F401
+    philox4x32_10,
+    uniform_words,
+    gumbel_noise,
+    row_sample,
+)
+from .generate import generate  # noqa: F401

@@ -31,6 +31,7 @@ import math
 import numpy as np
 
 from .attention import adaln_single, block_attn, timestep_embedding
+from .sampling import row_sample
 
 # Decisions whose fp64 margin is nonzero but below this are reported as
 # ambiguous: two correct fp64 evaluations could take them either way.  Exact
@@ -52,7 +53,8 @@ def row_confidence(row, temperature):
 
 
 def confidence_unmask(logits, tokens, masked, gamma, temperature,
-                      mask_token_id, step, commit_step=None):
+                      mask_token_id, step, commit_step=None, sample=None,
+                      commit_all=False):
     """One unmasking pass over a batch of blocks.
 
     logits [B,S,V], tokens [B,S] int, masked [B,S] bool/uint8 (slots still
@@ -63,6 +65,12 @@ def confidence_unmask(logits, tokens, masked, gamma, temperature,
     masked, C = {the slot of largest p, lowest s on ties}.  Slots in C take
     token pred_s, leave the mask and record commit_step = step; the other
     masked slots get mask_token_id.
+
+    sample = (seed, block): temperature sampling instead of the argmax --
+    (pred_s, p_s) from sampling.row_sample with row id b*S + s (the
+    perturbed-score margins below AMBIGUOUS_MARGIN * (1 + |max|) are counted
+    as ambiguous too).  commit_all: every masked slot is committed (the last
+    step a block is allowed).
 
     Returns a dict of new arrays: tokens, masked (uint8), committed_now
     (uint8), conf (float64, NaN where not masked on entry), pred (int64, -1
@@ -83,8 +91,14 @@ def confidence_unmask(logits, tokens, masked, gamma, temperature,
     for b in range(B):
         slots = [s for s in range(S) if msk[b, s]]
         for s in slots:
-            pred[b, s], conf[b, s] = row_confidence(lg[b, s], temperature)
-        chosen = [s for s in slots if conf[b, s] >= g]
+            if sample is None:
+                pred[b, s], conf[b, s] = row_confidence(lg[b, s], temperature)
+            else:
+                pred[b, s], conf[b, s], margin = row_sample(lg[b, s], temperature, sample[0],
+                                                            b * S + s, step, sample[1])
+                scale = 1.0 + abs(float(np.max(lg[b, s])))
+                ambiguous += int(0.0 < margin < AMBIGUOUS_MARGIN * scale)
+        chosen = [s for s in slots if conf[b, s] >= g or commit_all]
         ambiguous += sum(1 for s in slots if 0.0 < abs(conf[b, s] - g) < AMBIGUOUS_MARGIN)
         if not chosen and slots:
             best = max(conf[b, s] for s in slots)
@@ -109,7 +123,8 @@ def confidence_unmask(logits, tokens, masked, gamma, temperature,
 def denoise_block(layer_inputs, step_logits, k_ctx_layers, v_ctx_layers,
                   ctx_start, ctx_len, tokens, masked, gamma, temperature,
                   mask_token_id, max_steps=None, ada_w=None, ada_bias=None,
-                  ada_table=None, commit_step=None):
+                  ada_table=None, commit_step=None, sample=None,
+                  finish_block=False):
     """The block denoising loop, replaying the bytes a step provider gave.
 
     [dothoosh] "two-tower mechanism": a block of [MASK] tokens is refined over
@@ -122,7 +137,9 @@ def denoise_block(layer_inputs, step_logits, k_ctx_layers, v_ctx_layers,
          layer l, residual None, active = n_masked > 0);
       3. logits = step_logits(k); confidence_unmask(...).
     Sequences with nothing masked are inactive (no attention rows, no
-    unmasking).  Slots still masked after max_steps stay masked.
+    unmasking).  Slots still masked after max_steps stay masked -- unless
+    finish_block, when the last allowed step commits every masked slot.
+    sample = (seed, block) selects temperature sampling (confidence_unmask).
 
     Returns dict(tokens, masked, commit_step, steps_taken, n_masked_trace
     [steps+1, B], outputs [step][layer] (out, lse), ambiguous).
@@ -159,7 +176,8 @@ def denoise_block(layer_inputs, step_logits, k_ctx_layers, v_ctx_layers,
                                         active=active))
         outputs.append(per_layer)
         r = confidence_unmask(step_logits(k), tok, msk, gamma, temperature,
-                              mask_token_id, k, cstep)
+                              mask_token_id, k, cstep, sample=sample,
+                              commit_all=finish_block and k == steps - 1)
         tok, msk, cstep = r["tokens"], r["masked"], r["commit_step"]
         ambiguous += r["ambiguous"]
         n_trace.append(r["n_masked"])

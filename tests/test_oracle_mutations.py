@@ -9,10 +9,14 @@ import pytest
 import oracle
 import oracle.attention as attention_src
 import oracle.context as context_src
+import oracle.generate as generate_src
+import oracle.sampling as sampling_src
 import oracle.unmask as unmask_src
 
 from . import test_oracle_attention as TA
 from . import test_oracle_context as TC
+from . import test_oracle_generate as TG
+from . import test_oracle_sampling as TS
 from . import test_oracle_unmask as TU
 
 ATTN_PINS = [TA.test_p1_empty_context_is_library_attention,
@@ -67,8 +71,41 @@ CONTEXT_MUTANTS = [
      "if n[b] < int(ctx_end[b]) - int(ctx_start[b]):"),                  # length rule without S
 ]
 
+SAMPLING_PINS = [TS.test_s1_philox_known_answers, TS.test_s2_uniform_map, TS.test_s3_gumbel_moments,
+                 TS.test_s4_sampling_follows_softmax, TS.test_s5_confidence_closed_forms,
+                 TS.test_s6_counter_fields, TS.test_s7_sampled_unmask_commit_rule]
+
+SAMPLING_MUTANTS = [
+    ("_M0, _M1 = np.uint64(0xD2511F53), np.uint64(0xCD9E8D57)",
+     "_M0, _M1 = np.uint64(0xCD9E8D57), np.uint64(0xD2511F53)"),        # swapped multipliers
+    ("        if r:\n            k0 = (k0 + _W0) & _MASK32", "        if False:\n            k0 = (k0 + _W0) & _MASK32"),
+    ("c0, c1, c2, c3 = hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0", "c0, c1, c2, c3 = hi0 ^ c1 ^ k0, lo1, hi1 ^ c3 ^ k1, lo0"),
+    ("for r in range(10):", "for r in range(7):"),                      # too few rounds
+    ("(2.0 * (w >> np.uint64(9)).astype(np.float64) + 1.0) / 16777216.0",
+     "(w >> np.uint64(8)).astype(np.float64) / 16777216.0"),            # u may be 0
+    ("return -np.log(-np.log(u))", "return -np.log(u)"),                # exponential, not Gumbel
+    ("key = x + tau * g", "key = x + g"),                               # noise not scaled by tau
+    ("return pred, math.exp((x[pred] - m) / tau) / z, margin", "return pred, 1.0 / z, margin"),  # greedy p
+    ("pred = int(np.flatnonzero(key == best)[0])", "pred = int(np.argmax(x))"),  # no sampling
+]
+
+GENERATE_PINS = [TG.test_g1_eos_stop, TG.test_g2_cache_contents,
+                 TG.test_g3_next_block_sees_committed_block, TG.test_g4_last_step_commits_the_rest,
+                 TG.test_g5_room_stop, TG.test_g6_sampling_small_temperature_is_argmax]
+
+GENERATE_MUTANTS = [
+    ("if eos_token_id is not None and np.any(tok[b] == eos_token_id):", "if False:"),  # no EOS stop
+    ("            elif not appended[b]:", "            elif False:"),                   # no room stop
+    ("max_steps=steps,\n", "max_steps=S,\n"),                                     # steps ignored
+    ("finish_block=True)", "finish_block=False)"),                                 # blocks left unfinished
+    ("sample=None if seed is None else (seed, blk)", "sample=None if seed is None else (seed, 0)"),
+    ("lens, appended = ctx_advance(S, ctx_start, ctx_end, lens, act_u8)",
+     "_, appended = ctx_advance(S, ctx_start, ctx_end, lens, act_u8)"),              # lengths never grow
+    ("            kc[layer], vc[layer], _ = kv_append(", "            _, _, _ = kv_append("),  # no append
+]
+
 UNMASK_MUTANTS = [
-    ("conf[b, s] >= g]", "conf[b, s] > g]"),                    # exclusive threshold
+    ("conf[b, s] >= g or", "conf[b, s] > g or"),                # exclusive threshold
     ("np.flatnonzero(x == m)[0]", "np.flatnonzero(x == m)[-1]"),  # highest id on ties
     ("/ float(temperature)", ""),                               # ignored temperature
     ("top = min(s for s", "top = max(s for s"),                 # highest slot on ties
@@ -111,6 +148,24 @@ def test_context_mutant_is_caught(monkeypatch, old, new):
     for name in ("ctx_block_attn", "kv_append", "ctx_advance"):
         monkeypatch.setattr(oracle, name, getattr(mod, name))
     assert _caught(CONTEXT_PINS)
+
+
+@pytest.mark.parametrize("old,new", SAMPLING_MUTANTS)
+def test_sampling_mutant_is_caught(monkeypatch, old, new):
+    mod = _mutant(sampling_src, old, new)
+    for name in ("philox4x32_10", "uniform_words", "gumbel_noise", "row_sample"):
+        monkeypatch.setattr(sampling_src, name, getattr(mod, name))
+        monkeypatch.setattr(oracle, name, getattr(mod, name))
+    import oracle.unmask as um
+    monkeypatch.setattr(um, "row_sample", mod.row_sample)
+    assert _caught(SAMPLING_PINS)
+
+
+@pytest.mark.parametrize("old,new", GENERATE_MUTANTS)
+def test_generate_mutant_is_caught(monkeypatch, old, new):
+    mod = _mutant(generate_src, old, new)
+    monkeypatch.setattr(oracle, "generate", mod.generate)
+    assert _caught(GENERATE_PINS)
 
 
 @pytest.mark.parametrize("old,new", UNMASK_MUTANTS)
