@@ -27,7 +27,7 @@ _STATUS_NAMES = {0: "TT_OK", 1: "TT_ERR_INVALID_ARG", 2: "TT_ERR_UNSUPPORTED",
 EXPORTED = ["tt_last_error", "tt_abi_version", "tt_block_attn_workspace_size", "tt_block_attn",
             "tt_workspace_clear", "tt_timestep_embed", "tt_adaln_single",
             "tt_unmask_workspace_size", "tt_confidence_unmask", "tt_denoise_workspace_size",
-            "tt_denoise_block", "tt_ctx_block_attn", "tt_ctx_advance"]
+            "tt_denoise_block", "tt_ctx_block_attn", "tt_ctx_advance", "tt_sample_unmask"]
 
 
 class TTError(RuntimeError):
@@ -75,6 +75,9 @@ def _load():
         "tt_unmask_workspace_size": (sz, [i32, i32, i32]),
         "tt_confidence_unmask": (ctypes.c_int, [i32, i32, i32, vp, i32, i64, f32, f32, i32, i32,
                                                 vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "tt_sample_unmask": (ctypes.c_int, [i32, i32, i32, vp, i32, i64, f32, f32, ctypes.c_uint64,
+                                            i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                            vp]),
         "tt_denoise_workspace_size": (sz, [shp, i32, i32, i32]),
         "tt_denoise_block": (ctypes.c_int, [shp, i32, i32, f32, f32, i32, i32, vp, vp, vp, vp,
                                             i32, vp, vp, vp, ctypes.POINTER(StepProvider), vp,
@@ -201,6 +204,18 @@ def confidence_unmask(batch, block_size, vocab, logits, row_stride, gamma, tempe
                                      _ptr(committed_now), _ptr(conf), _ptr(pred),
                                      _ptr(commit_step), _ptr(n_masked), _ptr(workspace),
                                      _nbytes(workspace), _stream(stream)))
+
+
+def sample_unmask(batch, block_size, vocab, logits, row_stride, gamma, temperature, seed,
+                  block_index, mask_token_id, step, tokens, masked, workspace, committed_now=None,
+                  conf=None, pred=None, commit_step=None, n_masked=None, dtype=None, stream=None):
+    code = dtype_code(logits.dtype) if dtype is None else dtype
+    _check(_lib.tt_sample_unmask(int(batch), int(block_size), int(vocab), _ptr(logits), code,
+                                 int(row_stride), float(gamma), float(temperature), int(seed),
+                                 int(block_index), int(mask_token_id), int(step), _ptr(tokens),
+                                 _ptr(masked), _ptr(committed_now), _ptr(conf), _ptr(pred),
+                                 _ptr(commit_step), _ptr(n_masked), _ptr(workspace),
+                                 _nbytes(workspace), _stream(stream)))
 
 
 def denoise_workspace_size(shape, n_layers, max_ctx_len, vocab):

@@ -269,6 +269,53 @@ size_t tt_unmask_workspace_size(int32_t batch, int32_t block_size, int32_t vocab
   return p.total_bytes < 256 ? 256 : p.total_bytes;
 }
 
+}  // extern "C"
+
+namespace {
+
+tt_status unmask_common(const char* fn, int32_t batch, int32_t block_size, int32_t vocab,
+                        const void* logits, int32_t dtype, int64_t row_stride, float gamma,
+                        float temperature, int sample, uint64_t seed, int32_t block_index,
+                        int32_t mask_token_id, int32_t step, int32_t* tokens, uint8_t* masked,
+                        uint8_t* committed_now, float* conf, int32_t* pred, int8_t* commit_step,
+                        int32_t* n_masked, void* workspace, size_t workspace_bytes,
+                        tt_stream stream) {
+  tt_status st = check_unmask_scalars(batch, block_size, vocab, row_stride, gamma, temperature);
+  if (st != TT_OK) return st;
+  if (dtype != TT_BF16 && dtype != TT_F32)
+    return fail(TT_ERR_INVALID_ARG, "%s: dtype %d is neither TT_BF16 nor TT_F32", fn, dtype);
+  if (!logits || !tokens || !masked)
+    return fail(TT_ERR_INVALID_ARG, "%s: logits, tokens and masked must be non-NULL", fn);
+  if (sample && (step < 0 || block_index < 0))
+    return fail(TT_ERR_INVALID_ARG, "%s: step %d and block_index %d must be >= 0", fn, step,
+                block_index);
+  if (!aligned(logits, elt_size(dtype)) || !aligned(tokens, 4) || (conf && !aligned(conf, 4)) ||
+      (pred && !aligned(pred, 4)) || (n_masked && !aligned(n_masked, 4)))
+    return fail(TT_ERR_INVALID_ARG, "%s: misaligned unmasking buffer", fn);
+  if (batch == 0) return ok();
+  const tt::UnmaskPlan p = tt::unmask_plan(batch, block_size, vocab);
+  if (!workspace || workspace_bytes < p.total_bytes)
+    return fail(TT_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes,
+                p.total_bytes);
+  if (!aligned(workspace, 16))
+    return fail(TT_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+  tt::UnmaskArgs a{};
+  a.B = batch; a.S = block_size; a.V = vocab; a.dtype = dtype;
+  a.logits = logits; a.row_stride = row_stride; a.gamma = gamma; a.temperature = temperature;
+  a.mask_id = mask_token_id; a.step = step; a.tokens = tokens; a.masked = masked;
+  a.committed_now = committed_now; a.conf = conf; a.pred = pred; a.commit_step = commit_step;
+  a.n_masked = n_masked;
+  a.sample = sample; a.seed = seed; a.block_index = block_index;
+  const hipError_t e =
+      tt::launch_confidence_unmask(a, p, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
 tt_status tt_confidence_unmask(int32_t batch, int32_t block_size, int32_t vocab,
                                const void* logits, int32_t dtype, int64_t row_stride, float gamma,
                                float temperature, int32_t mask_token_id, int32_t step,
@@ -276,31 +323,23 @@ tt_status tt_confidence_unmask(int32_t batch, int32_t block_size, int32_t vocab,
                                float* conf, int32_t* pred, int8_t* commit_step,
                                int32_t* n_masked, void* workspace, size_t workspace_bytes,
                                tt_stream stream) {
-  tt_status st = check_unmask_scalars(batch, block_size, vocab, row_stride, gamma, temperature);
-  if (st != TT_OK) return st;
-  if (dtype != TT_BF16 && dtype != TT_F32)
-    return fail(TT_ERR_INVALID_ARG, "dtype %d is neither TT_BF16 nor TT_F32", dtype);
-  if (!logits || !tokens || !masked)
-    return fail(TT_ERR_INVALID_ARG, "logits, tokens and masked must be non-NULL");
-  if (!aligned(logits, elt_size(dtype)) || !aligned(tokens, 4) || (conf && !aligned(conf, 4)) ||
-      (pred && !aligned(pred, 4)) || (n_masked && !aligned(n_masked, 4)))
-    return fail(TT_ERR_INVALID_ARG, "misaligned unmasking buffer");
-  if (batch == 0) return ok();
-  const tt::UnmaskPlan p = tt::unmask_plan(batch, block_size, vocab);
-  if (!workspace || workspace_bytes < p.total_bytes)
-    return fail(TT_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
-                p.total_bytes);
-  if (!aligned(workspace, 16)) return fail(TT_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  tt::UnmaskArgs a{};
-  a.B = batch; a.S = block_size; a.V = vocab; a.dtype = dtype;
-  a.logits = logits; a.row_stride = row_stride; a.gamma = gamma; a.temperature = temperature;
-  a.mask_id = mask_token_id; a.step = step; a.tokens = tokens; a.masked = masked;
-  a.committed_now = committed_now; a.conf = conf; a.pred = pred; a.commit_step = commit_step;
-  a.n_masked = n_masked;
-  const hipError_t e =
-      tt::launch_confidence_unmask(a, p, workspace, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "tt_confidence_unmask launch");
-  return ok();
+  return unmask_common("tt_confidence_unmask", batch, block_size, vocab, logits, dtype, row_stride,
+                       gamma, temperature, 0, 0, 0, mask_token_id, step, tokens, masked,
+                       committed_now, conf, pred, commit_step, n_masked, workspace,
+                       workspace_bytes, stream);
+}
+
+tt_status tt_sample_unmask(int32_t batch, int32_t block_size, int32_t vocab, const void* logits,
+                           int32_t dtype, int64_t row_stride, float gamma, float temperature,
+                           uint64_t seed, int32_t block_index, int32_t mask_token_id,
+                           int32_t step, int32_t* tokens, uint8_t* masked,
+                           uint8_t* committed_now, float* conf, int32_t* pred,
+                           int8_t* commit_step, int32_t* n_masked, void* workspace,
+                           size_t workspace_bytes, tt_stream stream) {
+  return unmask_common("tt_sample_unmask", batch, block_size, vocab, logits, dtype, row_stride,
+                       gamma, temperature, 1, seed, block_index, mask_token_id, step, tokens,
+                       masked, committed_now, conf, pred, commit_step, n_masked, workspace,
+                       workspace_bytes, stream);
 }
 
 size_t tt_denoise_workspace_size(const tt_attn_shape* shape, int32_t n_layers,

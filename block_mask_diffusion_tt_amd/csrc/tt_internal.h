@@ -56,10 +56,12 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& p, void* ws, hip
 
 // ---------------------------------------------------------------- unmasking
 struct UnmaskPlan {
-  int splits;      // workgroups per row
+  int splits;      // workgroups per row (argmax pass)
   int split_len;   // vocab entries per split (multiple of 8)
+  int s_splits;    // workgroups per row (sampling pass: fixed slices)
   size_t part_bytes;
-  size_t total_bytes;
+  size_t s_part_bytes;
+  size_t total_bytes;  // enough for either pass
 };
 
 struct UnmaskArgs {
@@ -70,6 +72,8 @@ struct UnmaskArgs {
   int32_t* tokens; uint8_t* masked;
   uint8_t* committed_now; float* conf; int32_t* pred;
   int8_t* commit_step; int32_t* n_masked;
+  // temperature sampling (Gumbel-max over Philox4x32-10 noise) when set
+  int sample; uint64_t seed; int block_index;
 };
 
 UnmaskPlan unmask_plan(int B, int S, int V);

@@ -27,6 +27,19 @@
 //              at most 80 * 2^-24 relative, plus the exp2 argument rounding
 //              (|x - m| * c * 2^-24, under 2e-6 for the terms that matter)
 //              and one rounding of 1/Z: about 6e-6 in all.
+//
+// Temperature sampling (the same decision rule, a different prediction):
+//   rowsample  grid (V / 8192 slices, B*S), 256 threads.  Each thread holds
+//              32 logits of its slice in registers, so the slice maximum is
+//              known before anything else: Z of the slice relative to it, and
+//              the Gumbel-max candidates -- the only tokens that can win,
+//              those within tau * (Gumbel range) of the slice maximum.  Only
+//              candidates draw their Philox4x32-10 noise (a few per slice),
+//              so the pass stays one read of the row.
+//   decide     the same kernel as above with the slices' (max, Z, best
+//              perturbed score, second best, token, logit); rows whose best
+//              two perturbed scores lie within kDelta * (1 + |max| + 20 tau)
+//              get their candidates rescored in fp64 first.
 #include <float.h>
 #include <limits.h>
 
@@ -159,6 +172,221 @@ __global__ __launch_bounds__(kThreads) void rowreduce_kernel(
   }
 }
 
+// ------------------------------------------------------------- sampling
+// Philox4x32-10 (J. K. Salmon, M. A. Moraes, R. O. Dror, D. E. Shaw,
+// "Parallel random numbers: as easy as 1, 2, 3", SC 2011): ten rounds of two
+// 32x32->64-bit products; the key advances by the Weyl constants between
+// rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+  }
+  return c;
+}
+
+// Noise stream of one slot: key = seed (low word first), counter =
+// (token / 4, b * S + s, step, block), word token % 4.
+struct NoiseKey {
+  uint32_t k0, k1, row, step, block;
+};
+
+__device__ __forceinline__ uint32_t noise_word(const NoiseKey& nk, int v) {
+  const uint4 w = philox4x32_10(make_uint4(static_cast<uint32_t>(v) >> 2, nk.row, nk.step, nk.block),
+                                nk.k0, nk.k1);
+  const int j = v & 3;
+  return j == 0 ? w.x : (j == 1 ? w.y : (j == 2 ? w.z : w.w));
+}
+
+// Standard Gumbel draw from one word: u = (2 (w >> 9) + 1) 2^-24 (23 bits,
+// strictly inside (0, 1), exact in fp32 and fp64), G = -ln(-ln u).  G lies in
+// [-2.8117, 16.6356]; kGumbelLo/Hi bound that range with room to spare.
+__device__ __forceinline__ float gumbel32(uint32_t w) {
+  const float u = static_cast<float>(2u * (w >> 9) + 1u) * 5.9604644775390625e-08f;
+  return -logf(-logf(u));
+}
+__device__ __forceinline__ double gumbel64(uint32_t w) {
+  const double u = static_cast<double>(2u * (w >> 9) + 1u) * 5.9604644775390625e-08;
+  return -log(-log(u));
+}
+constexpr float kGumbelSpread = 20.f;   // >= (kGumbelHi = 17) - (kGumbelLo = -3)
+
+// Tokens whose logit is below m - cand_margin(m, tau) cannot reach within
+// the decision band of the best perturbed score l + tau G of their slice
+// (their score is at most l + 17 tau, the slice maximum's at least m - 3 tau):
+// only the others draw noise.  The 2^-12 term keeps every token within
+// kDelta * (1 + |m| + 20 tau) of the best score a candidate.
+__device__ __forceinline__ float cand_margin(float m, float tau) {
+  return kGumbelSpread * tau + 2.44140625e-04f * (1.f + fabsf(m));
+}
+
+struct SamplePart {
+  float m;      // slice maximum
+  float z;      // sum of exp2((x - m) * c) over the slice
+  float key;    // best perturbed score l + tau G among the slice's candidates
+  float key2;   // second best (-inf if none)
+  int idx;      // token of `key` (INT_MAX if no candidate)
+  float lx;     // its logit
+  int pad0, pad1;
+};
+
+// (key, key2, idx, lx) <- the better of itself and (ok, ok2, oi, ol): higher
+// score, lower token on equal scores; the second best follows.
+__device__ __forceinline__ void merge_best(float& key, float& key2, int& idx, float& lx, float ok,
+                                           float ok2, int oi, float ol) {
+  if (ok > key || (ok == key && oi < idx)) {
+    key2 = fmaxf(key, ok2);
+    key = ok;
+    idx = oi;
+    lx = ol;
+  } else {
+    key2 = fmaxf(key2, ok);
+  }
+}
+
+constexpr int kSampleSlice = 8192;                 // tokens per workgroup
+constexpr int kSamplePerThread = kSampleSlice / kThreads;  // 32: 4 groups of 8
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rowsample_kernel(
+    const T* __restrict__ logits, int64_t row_stride, int V, const uint8_t* __restrict__ masked,
+    float c, float tau, NoiseKey nk, int splits, int vec_ok, SamplePart* __restrict__ part) {
+  const int row = blockIdx.y;
+  if (!masked[row]) return;
+  const int split = blockIdx.x;
+  const int beg = split * kSampleSlice;
+  const T* x = logits + static_cast<int64_t>(row) * row_stride;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // v[8u + k] is token beg + 8 (tid + 256 u) + k
+  float v[kSamplePerThread];
+  if (vec_ok && beg + kSampleSlice <= V) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float g[8];
+      load8<T>(x, beg + 8 * (tid + kThreads * u), g);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[8 * u + k] = g[k];
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int t = beg + 8 * (tid + kThreads * u) + k;
+        v[8 * u + k] = t < V ? load1(x, t) : -INFINITY;
+      }
+  }
+  __shared__ float s_red[kThreads / 64];
+  __shared__ SamplePart s_best[kThreads / 64];
+  // slice maximum (exact), then the slice's Z relative to it
+  float m = -FLT_MAX;
+#pragma unroll
+  for (int i = 0; i < kSamplePerThread; ++i) m = fmaxf(m, v[i]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) s_red[wave] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  float z = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float e[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) e[k] = fast_exp2((v[8 * u + k] - m) * c);
+    z += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  }
+  // candidates draw their noise
+  const float thr = m - cand_margin(m, tau);
+  float key = -INFINITY, key2 = -INFINITY, lx = 0.f;
+  int idx = INT_MAX;
+  NoiseKey rk = nk;
+  rk.row = static_cast<uint32_t>(row);
+#pragma unroll
+  for (int i = 0; i < kSamplePerThread; ++i) {
+    if (v[i] >= thr && v[i] != -INFINITY) {
+      const int t = beg + 8 * (tid + kThreads * (i >> 3)) + (i & 7);
+      const float sc = v[i] + tau * gumbel32(noise_word(rk, t));
+      merge_best(key, key2, idx, lx, sc, -INFINITY, t, v[i]);
+    }
+  }
+  // fixed-shape trees: Z and the best pair over the wave, then the four waves
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    z += __shfl_xor(z, off);
+    const float ok = __shfl_xor(key, off), ok2 = __shfl_xor(key2, off), ol = __shfl_xor(lx, off);
+    const int oi = __shfl_xor(idx, off);
+    merge_best(key, key2, idx, lx, ok, ok2, oi, ol);
+  }
+  __syncthreads();
+  if (lane == 0) {
+    s_red[wave] = z;
+    s_best[wave] = SamplePart{m, z, key, key2, idx, lx, 0, 0};
+  }
+  __syncthreads();
+  if (tid == 0) {
+    SamplePart r = s_best[0];
+    r.z = (s_red[0] + s_red[1]) + (s_red[2] + s_red[3]);
+    for (int w = 1; w < kThreads / 64; ++w)
+      merge_best(r.key, r.key2, r.idx, r.lx, s_best[w].key, s_best[w].key2, s_best[w].idx,
+                 s_best[w].lx);
+    part[static_cast<int64_t>(row) * splits + split] = r;
+  }
+}
+
+// fp64 rescoring of one row's candidates (those within cand_margin of the
+// row maximum m): the token of the largest l + tau G in fp64, lowest token on
+// equal scores.  All threads take part; every thread returns the result.
+template <typename T>
+__device__ void rescore_row64(const T* x, int V, float m, float tau, double tau64, const NoiseKey& nk,
+                              double* red_k, int* red_i, int& out_idx, float& out_l) {
+  const float thr = m - cand_margin(m, tau);
+  double best = -INFINITY;
+  int bi = INT_MAX;
+  for (int t = threadIdx.x; t < V; t += kThreads) {
+    const float l = load1(x, t);
+    if (l >= thr && l != -INFINITY) {
+      const double sc = static_cast<double>(l) + tau64 * gumbel64(noise_word(nk, t));
+      if (sc > best || (sc == best && t < bi)) {
+        best = sc;
+        bi = t;
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const double ob = __shfl_xor(best, off);
+    const int oi = __shfl_xor(bi, off);
+    if (ob > best || (ob == best && oi < bi)) {
+      best = ob;
+      bi = oi;
+    }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) {
+    red_k[wave] = best;
+    red_i[wave] = bi;
+  }
+  __syncthreads();
+  best = red_k[0];
+  bi = red_i[0];
+  for (int w = 1; w < kThreads / 64; ++w)
+    if (red_k[w] > best || (red_k[w] == best && red_i[w] < bi)) {
+      best = red_k[w];
+      bi = red_i[w];
+    }
+  __syncthreads();
+  if (bi == INT_MAX) bi = 0;   // no finite logit: outside the contract
+  out_idx = bi;
+  out_l = load1(x, bi);
+}
+
 // fp64 probability of the argmax of one row: 1 / sum_v exp((x_v - m) / tau),
 // reduced in a fixed order (thread-strided sums, then a fixed tree) so equal
 // rows give equal bits.
@@ -194,18 +422,22 @@ __device__ double recheck_row(const T* x, int V, float m, double tau, double* re
   return 1.0 / tot;
 }
 
-template <typename T>
+template <typename T, bool SAMPLE>
 __global__ __launch_bounds__(kThreads) void decide_kernel(
     const T* __restrict__ logits, int64_t row_stride, int S, int V,
-    const RowPart* __restrict__ part, int splits, float c, float gamma, double tau,
-    int mask_id, int step, int32_t* tokens, uint8_t* masked, uint8_t* committed_now,
+    const void* __restrict__ parts, int splits, float c, float gamma, float tau, double tau64,
+    NoiseKey nk, int mask_id, int step, int32_t* tokens, uint8_t* masked, uint8_t* committed_now,
     float* conf, int32_t* pred, int8_t* commit_step, int32_t* n_masked) {
   __shared__ float s_m[64];
+  __shared__ float s_lx[64];      // logit of the prediction (= s_m for the argmax)
+  __shared__ float s_z[64];       // fp32 Z relative to s_m (sampling)
   __shared__ int s_pred[64];
   __shared__ double s_p[64];      // fp32 p widened, or the fp64 recheck
   __shared__ int s_checked[64];
   __shared__ int s_msk[64];
+  __shared__ int s_rescore[64];
   __shared__ double red[kThreads / 64];
+  __shared__ int red_i[kThreads / 64];
   __shared__ int s_choice;        // -1: threshold set; else the single slot
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -214,21 +446,62 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
     const int msk = masked[row0 + tid] != 0;
     s_msk[tid] = msk;
     s_checked[tid] = 0;
-    if (msk) {
-      const RowPart* p = part + (row0 + tid) * splits;
+    s_rescore[tid] = 0;
+    if (msk && !SAMPLE) {
+      const RowPart* p = static_cast<const RowPart*>(parts) + (row0 + tid) * splits;
       float m = p[0].m, z = p[0].z;
       int a = p[0].arg;
       for (int k = 1; k < splits; ++k) merge(m, z, a, p[k].m, p[k].z, p[k].arg, c);
       s_m[tid] = m;
+      s_lx[tid] = m;
       s_pred[tid] = a;
       s_p[tid] = static_cast<double>(1.0f / z);
+    } else if (msk) {
+      // slices in order: row maximum, Z relative to it, best perturbed score
+      const SamplePart* p = static_cast<const SamplePart*>(parts) + (row0 + tid) * splits;
+      float m = p[0].m;
+      for (int k = 1; k < splits; ++k) m = fmaxf(m, p[k].m);
+      float z = 0.f, key = p[0].key, key2 = p[0].key2, lx = p[0].lx;
+      int idx = p[0].idx;
+      for (int k = 0; k < splits; ++k) {
+        z += p[k].z * fast_exp2((p[k].m - m) * c);
+        if (k) merge_best(key, key2, idx, lx, p[k].key, p[k].key2, p[k].idx, p[k].lx);
+      }
+      s_m[tid] = m;
+      s_z[tid] = z;
+      s_lx[tid] = lx;
+      s_pred[tid] = idx;
+      s_p[tid] = static_cast<double>(fast_exp2((lx - m) * c) / z);
+      // the fp32 scores of the two best can be off by far less than this band
+      s_rescore[tid] = (key - key2) <= kDelta * (1.f + fabsf(m) + kGumbelSpread * tau);
+    }
+  }
+  __syncthreads();
+  if (SAMPLE) {
+    // near-ties of the perturbed scores: rescore the row's candidates in fp64
+    for (int s = 0; s < S; ++s) {
+      if (s_msk[s] && s_rescore[s]) {
+        NoiseKey k = nk;
+        k.row = static_cast<uint32_t>(row0 + s);
+        int idx;
+        float lx;
+        rescore_row64<T>(logits + (row0 + s) * row_stride, V, s_m[s], tau, tau64, k, red, red_i,
+                         idx, lx);
+        if (tid == 0) {
+          s_pred[s] = idx;
+          s_lx[s] = lx;
+          s_p[s] = static_cast<double>(fast_exp2((lx - s_m[s]) * c) / s_z[s]);
+        }
+        __syncthreads();
+      }
     }
   }
   __syncthreads();
   // rows whose fp32 p is within kDelta of gamma: decide them in fp64
   for (int s = 0; s < S; ++s) {
     if (s_msk[s] && fabs(s_p[s] - static_cast<double>(gamma)) <= kDelta) {
-      const double p64 = recheck_row<T>(logits + (row0 + s) * row_stride, V, s_m[s], tau, red);
+      const double p64 = exp((static_cast<double>(s_lx[s]) - s_m[s]) / tau64) *
+                         recheck_row<T>(logits + (row0 + s) * row_stride, V, s_m[s], tau64, red);
       if (tid == 0) { s_p[s] = p64; s_checked[s] = 1; }
       __syncthreads();
     }
@@ -257,7 +530,8 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
     for (int s = 0; s < S; ++s) near += s_msk[s] && s_p[s] >= best - 2.0 * kDelta;
     for (int s = 0; s < S && near > 1; ++s) {
       if (s_msk[s] && !s_checked[s] && s_p[s] >= best - 2.0 * kDelta) {
-        const double p64 = recheck_row<T>(logits + (row0 + s) * row_stride, V, s_m[s], tau, red);
+        const double p64 = exp((static_cast<double>(s_lx[s]) - s_m[s]) / tau64) *
+                           recheck_row<T>(logits + (row0 + s) * row_stride, V, s_m[s], tau64, red);
         if (tid == 0) { s_p[s] = p64; s_checked[s] = 1; }
         __syncthreads();
       }
@@ -306,33 +580,52 @@ UnmaskPlan unmask_plan(int B, int S, int V) {
   if (len < 2048) len = 2048;
   p.split_len = static_cast<int>(len);
   p.splits = static_cast<int>(ceil_div(V, len));
+  p.s_splits = static_cast<int>(ceil_div(V, kSampleSlice));
   p.part_bytes = align_up(static_cast<size_t>(rows) * p.splits * sizeof(RowPart), 256);
-  p.total_bytes = p.part_bytes;
+  p.s_part_bytes = align_up(static_cast<size_t>(rows) * p.s_splits * sizeof(SamplePart), 256);
+  p.total_bytes = p.part_bytes > p.s_part_bytes ? p.part_bytes : p.s_part_bytes;
   return p;
 }
 
+namespace {
+
+template <typename T>
+void launch_unmask_t(const UnmaskArgs& a, const UnmaskPlan& p, void* ws, int vec, hipStream_t st) {
+  const T* x = static_cast<const T*>(a.logits);
+  const float c = static_cast<float>(1.4426950408889634 / static_cast<double>(a.temperature));
+  const double tau64 = static_cast<double>(a.temperature);
+  NoiseKey nk{static_cast<uint32_t>(a.seed & 0xffffffffu), static_cast<uint32_t>(a.seed >> 32), 0u,
+              static_cast<uint32_t>(a.step), static_cast<uint32_t>(a.block_index)};
+  const dim3 blk(kThreads);
+  if (!a.sample) {
+    RowPart* part = static_cast<RowPart*>(ws);
+    hipLaunchKernelGGL(rowreduce_kernel<T>, dim3(p.splits, a.B * a.S), blk, 0, st, x, a.row_stride,
+                       a.V, a.masked, c, p.split_len, p.splits, vec, part);
+    hipLaunchKernelGGL((decide_kernel<T, false>), dim3(a.B), blk, 0, st, x, a.row_stride, a.S, a.V,
+                       static_cast<const void*>(part), p.splits, c, a.gamma, a.temperature, tau64,
+                       nk, a.mask_id, a.step, a.tokens, a.masked, a.committed_now, a.conf, a.pred,
+                       a.commit_step, a.n_masked);
+  } else {
+    SamplePart* part = static_cast<SamplePart*>(ws);
+    hipLaunchKernelGGL(rowsample_kernel<T>, dim3(p.s_splits, a.B * a.S), blk, 0, st, x,
+                       a.row_stride, a.V, a.masked, c, a.temperature, nk, p.s_splits, vec, part);
+    hipLaunchKernelGGL((decide_kernel<T, true>), dim3(a.B), blk, 0, st, x, a.row_stride, a.S, a.V,
+                       static_cast<const void*>(part), p.s_splits, c, a.gamma, a.temperature,
+                       tau64, nk, a.mask_id, a.step, a.tokens, a.masked, a.committed_now, a.conf,
+                       a.pred, a.commit_step, a.n_masked);
+  }
+}
+
+}  // namespace
+
 hipError_t launch_confidence_unmask(const UnmaskArgs& a, const UnmaskPlan& p, void* ws,
                                     hipStream_t st) {
-  RowPart* part = static_cast<RowPart*>(ws);
-  const float c = static_cast<float>(1.4426950408889634 / static_cast<double>(a.temperature));
-  const double tau = static_cast<double>(a.temperature);
-  const dim3 g1(p.splits, a.B * a.S), blk(kThreads);
   if (a.dtype == 0) {
-    const auto* x = static_cast<const uint16_t*>(a.logits);
-    const int vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (a.row_stride % 8 == 0);
-    hipLaunchKernelGGL(rowreduce_kernel<uint16_t>, g1, blk, 0, st, x, a.row_stride, a.V, a.masked,
-                       c, p.split_len, p.splits, vec, part);
-    hipLaunchKernelGGL(decide_kernel<uint16_t>, dim3(a.B), blk, 0, st, x, a.row_stride, a.S, a.V,
-                       part, p.splits, c, a.gamma, tau, a.mask_id, a.step, a.tokens, a.masked,
-                       a.committed_now, a.conf, a.pred, a.commit_step, a.n_masked);
+    const int vec = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) && (a.row_stride % 8 == 0);
+    launch_unmask_t<uint16_t>(a, p, ws, vec, st);
   } else {
-    const auto* x = static_cast<const float*>(a.logits);
-    const int vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (a.row_stride % 4 == 0);
-    hipLaunchKernelGGL(rowreduce_kernel<float>, g1, blk, 0, st, x, a.row_stride, a.V, a.masked, c,
-                       p.split_len, p.splits, vec, part);
-    hipLaunchKernelGGL(decide_kernel<float>, dim3(a.B), blk, 0, st, x, a.row_stride, a.S, a.V,
-                       part, p.splits, c, a.gamma, tau, a.mask_id, a.step, a.tokens, a.masked,
-                       a.committed_now, a.conf, a.pred, a.commit_step, a.n_masked);
+    const int vec = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) && (a.row_stride % 4 == 0);
+    launch_unmask_t<float>(a, p, ws, vec, st);
   }
   return hipGetLastError();
 }

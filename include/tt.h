@@ -270,6 +270,46 @@ tt_status tt_confidence_unmask(int32_t batch, int32_t block_size, int32_t vocab,
                                void* workspace, size_t workspace_bytes, tt_stream stream);
 
 /* ------------------------------------------------------------------------
+ * tt_sample_unmask -- tt_confidence_unmask with temperature sampling.
+ *
+ * [news] training and inference section, code example: the generation call
+ * takes a temperature (0.1) next to the confidence threshold (0.8).
+ * [keyframe] key point 3: all masked slots are predicted at once and the
+ * confident ones are committed.  (Reading: the prediction of a masked slot
+ * is drawn from softmax(l / temperature); its confidence is the probability
+ * of the drawn token under that distribution.)
+ *
+ * For every slot (b, s) with masked[b, s] != 0 on entry:
+ *   G_v  = -ln(-ln u_v),  u_v = (2 * (w_v >> 9) + 1) / 2^24,  where w_v is
+ *          word v % 4 of Philox4x32-10 (Salmon et al., SC 2011) with
+ *          key = (seed & 0xffffffff, seed >> 32) and
+ *          counter = (v / 4, b * S + s, step, block_index)
+ *   pred = lowest v maximising logits[b, s, v] + temperature * G_v
+ *          (the Gumbel-max draw from softmax(logits / temperature))
+ *   p    = exp((logits[b, s, pred] - max) / temperature)
+ *          / sum_v exp((logits[b, s, v] - max) / temperature)
+ * and then the commit rule of tt_confidence_unmask, unchanged (gamma <= 0
+ * commits every masked slot).  Decisions are exact with respect to fp64:
+ * rows whose two best perturbed scores lie within 2^-14 (1 + |max| +
+ * 20 temperature) are rescored in fp64, and p is rechecked in fp64 near
+ * gamma as in tt_confidence_unmask.
+ * Arguments, layouts and errors are those of tt_confidence_unmask, plus
+ * TT_ERR_INVALID_ARG for step < 0 or block_index < 0.  The workspace is
+ * sized by tt_unmask_workspace_size (the same size serves both calls).
+ * Cost: one read of every masked row; only the tokens within
+ * 20 * temperature of their slice's maximum draw noise, so large
+ * temperatures over flat logits cost more arithmetic.
+ * ---------------------------------------------------------------------- */
+tt_status tt_sample_unmask(int32_t batch, int32_t block_size, int32_t vocab,
+                           const void* logits, int32_t dtype, int64_t row_stride,
+                           float gamma, float temperature, uint64_t seed,
+                           int32_t block_index, int32_t mask_token_id, int32_t step,
+                           int32_t* tokens, uint8_t* masked, uint8_t* committed_now,
+                           float* conf, int32_t* pred, int8_t* commit_step,
+                           int32_t* n_masked, void* workspace, size_t workspace_bytes,
+                           tt_stream stream);
+
+/* ------------------------------------------------------------------------
  * tt_denoise_block -- the block denoising loop ([dothoosh] two-tower
  * mechanism section: a block starts as [MASK] tokens and is refined over T
  * steps until final; [news] code example: steps_per_block = block_size =

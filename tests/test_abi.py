@@ -187,3 +187,20 @@ def test_ctx_advance_rejects_bad_arguments():
     assert L.tt_ctx_advance(2, 16, FAKE, None, FAKE, None, None, None) == tt.TT_ERR_INVALID_ARG
     assert L.tt_ctx_advance(2, 16, FAKE, FAKE, FAKE + 2, None, None, None) == tt.TT_ERR_INVALID_ARG
     assert L.tt_ctx_advance(0, 16, FAKE, FAKE, FAKE, None, None, None) == tt.TT_OK
+
+
+def test_sample_unmask_rejects_bad_arguments():
+    L = tt.lib()
+
+    def call(B=1, S=16, V=1024, logits=FAKE, tau=0.1, gamma=0.8, block=0, step=0, ws_bytes=1 << 20):
+        return L.tt_sample_unmask(B, S, V, logits, 0, V, gamma, tau, 7, block, 3, step, FAKE, FAKE,
+                                  None, None, None, None, None, FAKE, ws_bytes, None)
+    assert call(S=0) == tt.TT_ERR_INVALID_ARG
+    assert call(tau=0.0) == tt.TT_ERR_INVALID_ARG
+    assert call(gamma=float("nan")) == tt.TT_ERR_INVALID_ARG
+    assert call(block=-1) == tt.TT_ERR_INVALID_ARG
+    assert call(step=-2) == tt.TT_ERR_INVALID_ARG
+    assert call(logits=None) == tt.TT_ERR_INVALID_ARG
+    assert call(ws_bytes=1) == tt.TT_ERR_WORKSPACE
+    assert "tt_sample_unmask" in tt.last_error()
+    assert call(B=0) == tt.TT_OK

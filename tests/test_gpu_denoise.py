@@ -73,7 +73,8 @@ def _run(B, S, Hq, Hkv, d, V, n_layers, lens, n_masked, dtype, logit_std, gamma,
     r = oracle.denoise_block(
         lambda k, l: tuple(np64(t) for t in prov.qkv[(k, l)]), lambda k: np64(prov.lg[k]),
         [np64(t) for t in kc], [np64(t) for t in vc], start.cpu().numpy(), clen.cpu().numpy(),
-        tokens.numpy(), masked.numpy(), gamma, tau, 3, max_steps=max_steps,
+        tokens.numpy(), masked.numpy(), float(np.float32(gamma)), float(np.float32(tau)), 3,
+        max_steps=max_steps,
         ada_w=None if ada_w is None else np64(ada_w),
         ada_bias=None if ada_b is None else np64(ada_b),
         ada_table=None if ada_t is None else np64(ada_t))

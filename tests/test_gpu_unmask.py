@@ -46,7 +46,9 @@ def check(logits, tokens, masked, gamma, tau, step=0, what="", row_stride=None, 
     V = logits.shape[-1] if V is None else V
     seqs = list(range(B)) if seqs is None else list(seqs)
     lg = np64(logits.reshape(B, S, -1)[seqs, :, :V])
-    r = oracle.confidence_unmask(lg, tokens.numpy()[seqs], masked.numpy()[seqs], gamma, tau, 3,
+    # the oracle gets gamma and tau as the library receives them (fp32)
+    r = oracle.confidence_unmask(lg, tokens.numpy()[seqs], masked.numpy()[seqs],
+                                 float(np.float32(gamma)), float(np.float32(tau)), 3,
                                  step, commit_step=np.full((len(seqs), S), -1))
     assert r["ambiguous"] == 0
     for key in ("tokens", "masked", "committed_now", "pred", "n_masked"):
