@@ -27,7 +27,8 @@ _STATUS_NAMES = {0: "TT_OK", 1: "TT_ERR_INVALID_ARG", 2: "TT_ERR_UNSUPPORTED",
 EXPORTED = ["tt_last_error", "tt_abi_version", "tt_block_attn_workspace_size", "tt_block_attn",
             "tt_workspace_clear", "tt_timestep_embed", "tt_adaln_single",
             "tt_unmask_workspace_size", "tt_confidence_unmask", "tt_denoise_workspace_size",
-            "tt_denoise_block", "tt_ctx_block_attn", "tt_ctx_advance", "tt_sample_unmask"]
+            "tt_denoise_block", "tt_ctx_block_attn", "tt_ctx_advance", "tt_sample_unmask",
+            "tt_generate_workspace_size", "tt_generate"]
 
 
 class TTError(RuntimeError):
@@ -51,6 +52,21 @@ _LOGITS = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes
 
 class StepProvider(ctypes.Structure):
     _fields_ = [("user", ctypes.c_void_p), ("layer_inputs", _LAYER_INPUTS), ("logits", _LOGITS)]
+
+
+_G_LAYER_INPUTS = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p)
+_G_LOGITS = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p)
+_G_CTX_INPUTS = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p)
+
+
+class GenProvider(ctypes.Structure):
+    _fields_ = [("user", ctypes.c_void_p), ("layer_inputs", _G_LAYER_INPUTS),
+                ("logits", _G_LOGITS), ("ctx_inputs", _G_CTX_INPUTS)]
 
 
 def _load():
@@ -79,6 +95,11 @@ def _load():
                                             i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                             vp]),
         "tt_denoise_workspace_size": (sz, [shp, i32, i32, i32]),
+        "tt_generate_workspace_size": (sz, [shp, i32, i32, i32, i32]),
+        "tt_generate": (ctypes.c_int, [shp, i32, i32, i32, f32, f32, i32, ctypes.c_uint64, i32,
+                                       i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                       ctypes.POINTER(GenProvider), vp, vp, vp,
+                                       ctypes.POINTER(i32), vp, sz, vp]),
         "tt_denoise_block": (ctypes.c_int, [shp, i32, i32, f32, f32, i32, i32, vp, vp, vp, vp,
                                             i32, vp, vp, vp, ctypes.POINTER(StepProvider), vp,
                                             vp, vp, ctypes.POINTER(i32), vp, sz, vp]),
@@ -288,6 +309,92 @@ def denoise_block(shape, n_layers, max_steps, gamma, temperature, mask_token_id,
                                    ctypes.byref(cb), _ptr(tokens), _ptr(masked),
                                    _ptr(commit_step), ctypes.byref(taken), _ptr(workspace),
                                    _nbytes(workspace), _stream(stream))
+    if status != TT_OK:
+        msg = last_error()
+        if errors:
+            msg += f" ({errors[0]!r})"
+        raise TTError(status, msg)
+    return taken.value
+
+
+def generate_workspace_size(shape, n_layers, n_blocks, max_ctx_len, vocab):
+    n = _lib.tt_generate_workspace_size(ctypes.byref(shape), int(n_layers), int(n_blocks),
+                                        int(max_ctx_len), int(vocab))
+    if n == 0:
+        raise TTError(TT_ERR_INVALID_ARG, last_error())
+    return n
+
+
+def generate(shape, n_layers, n_blocks, steps_per_block, gamma, temperature, mask_token_id,
+             eos_token_id, vocab, k_ctx_layers, v_ctx_layers, ctx_start, ctx_end, ctx_len,
+             max_ctx_len, provider, out_tokens, n_generated, workspace, stop_reason=None,
+             seed=None, ada_w=None, ada_bias=None, ada_table=None, stream=None):
+    """Runs tt_generate (seed None: argmax predictions; else temperature
+    sampling with that seed).  `provider` has three methods, called from
+    inside the loop with tensor views of the library's workspace buffers:
+        provider.layer_inputs(block, step, layer, prev_out, q_blk, k_blk, v_blk)
+        provider.logits(block, step, last_out, logits)
+        provider.ctx_inputs(block, layer, tokens, prev_out, q_blk, k_blk, v_blk)
+    each filling its output tensors in place on the current stream (prev_out
+    is None for layer 0; tokens is the committed block [B, S] int32).
+    Returns the number of blocks taken."""
+    B, S, Hq, Hkv, d = shape.batch, shape.block_size, shape.n_q_heads, shape.n_kv_heads, shape.head_dim
+    tdtype = torch.bfloat16 if shape.dtype == TT_BF16 else torch.float32
+    ws_u8 = workspace.view(torch.uint8) if workspace.dtype != torch.uint8 else workspace
+    base = workspace.data_ptr()
+
+    def view(ptr, shape_, dt=tdtype):
+        if not ptr:
+            return None
+        n = 1
+        for x in shape_:
+            n *= x
+        off = ptr - base
+        esz = torch.empty((), dtype=dt).element_size()
+        return ws_u8[off:off + n * esz].view(dt).view(*shape_)
+
+    errors = []
+
+    def _wrap(fn):
+        def inner(*a):
+            try:
+                fn(*a)
+                return 0
+            except Exception as e:  # reported through TT_ERR_CALLBACK
+                errors.append(e)
+                return 1
+        return inner
+
+    @_wrap
+    def _layer_inputs(user, blk, step, layer, prev, q, kb, vb, st):
+        provider.layer_inputs(int(blk), int(step), int(layer), view(prev, (B, S, Hq, d)),
+                              view(q, (B, S, Hq, d)), view(kb, (B, S, Hkv, d)),
+                              view(vb, (B, S, Hkv, d)))
+
+    @_wrap
+    def _logits(user, blk, step, last, lg, st):
+        provider.logits(int(blk), int(step), view(last, (B, S, Hq, d)), view(lg, (B, S, vocab)))
+
+    @_wrap
+    def _ctx_inputs(user, blk, layer, toks, prev, q, kb, vb, st):
+        provider.ctx_inputs(int(blk), int(layer), view(toks, (B, S), torch.int32),
+                            view(prev, (B, S, Hq, d)), view(q, (B, S, Hq, d)),
+                            view(kb, (B, S, Hkv, d)), view(vb, (B, S, Hkv, d)))
+
+    cb = GenProvider(None, _G_LAYER_INPUTS(_layer_inputs), _G_LOGITS(_logits),
+                     _G_CTX_INPUTS(_ctx_inputs))
+    kptrs = (ctypes.c_void_p * n_layers)(*[_ptr(t) for t in k_ctx_layers])
+    vptrs = (ctypes.c_void_p * n_layers)(*[_ptr(t) for t in v_ctx_layers])
+    taken = ctypes.c_int32(0)
+    status = _lib.tt_generate(ctypes.byref(shape), int(n_layers), int(n_blocks),
+                              int(steps_per_block), float(gamma), float(temperature),
+                              0 if seed is None else 1, 0 if seed is None else int(seed),
+                              int(mask_token_id), int(eos_token_id), int(vocab), kptrs, vptrs,
+                              _ptr(ctx_start), _ptr(ctx_end), _ptr(ctx_len), int(max_ctx_len),
+                              _ptr(ada_w), _ptr(ada_bias), _ptr(ada_table), ctypes.byref(cb),
+                              _ptr(out_tokens), _ptr(n_generated), _ptr(stop_reason),
+                              ctypes.byref(taken), _ptr(workspace), _nbytes(workspace),
+                              _stream(stream))
     if status != TT_OK:
         msg = last_error()
         if errors:

@@ -353,6 +353,156 @@ size_t tt_denoise_workspace_size(const tt_attn_shape* shape, int32_t n_layers,
   return denoise_bytes(shape, n_layers, max_ctx_len, vocab);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The workspace buffers of the denoising loop, carved in denoise_bytes order.
+struct DenoiseBufs {
+  float* ada; float* emb;
+  void* q; void* kb; void* vb; void* out; void* logits;
+  int32_t* n_masked; uint8_t* active; int32_t* total;
+  void* attn_ws; void* unmask_ws;
+  tt::AttnPlan ap; tt::UnmaskPlan up;
+};
+
+DenoiseBufs carve_denoise(Carver& cv, const tt_attn_shape* shape, int n_layers, int max_ctx_len,
+                          int vocab) {
+  const size_t B = shape->batch, S = shape->block_size, Hq = shape->n_q_heads,
+               Hkv = shape->n_kv_heads, d = shape->head_dim, e = elt_size(shape->dtype),
+               W = Hq * d;
+  DenoiseBufs z{};
+  z.ada = static_cast<float*>(cv.take(static_cast<size_t>(n_layers) * 3 * B * W * 4));
+  z.emb = static_cast<float*>(cv.take(B * TT_TIMESTEP_DIM * 4));
+  z.q = cv.take(B * S * Hq * d * e);
+  z.kb = cv.take(B * S * Hkv * d * e);
+  z.vb = cv.take(B * S * Hkv * d * e);
+  z.out = cv.take(B * S * Hq * d * e);
+  z.logits = cv.take(B * S * static_cast<size_t>(vocab) * e);
+  z.n_masked = static_cast<int32_t*>(cv.take(B * 4));
+  z.active = static_cast<uint8_t*>(cv.take(B));
+  z.total = static_cast<int32_t*>(cv.take(4));
+  z.ap = tt::attn_plan(shape->batch, shape->block_size, shape->n_q_heads, shape->n_kv_heads,
+                       shape->head_dim, shape->dtype, max_ctx_len);
+  z.attn_ws = cv.take(z.ap.total_bytes);
+  z.up = tt::unmask_plan(shape->batch, shape->block_size, vocab);
+  z.unmask_ws = cv.take(z.up.total_bytes);
+  return z;
+}
+
+struct LoopOpts {
+  int n_layers, max_steps, vocab, mask_id;
+  float gamma, temperature;
+  int sample; uint64_t seed; int block;
+  int finish_block;   // the last allowed step commits every masked slot
+};
+
+// The block denoising loop (tt_denoise_block, and each block of tt_generate):
+// per step, the active set and the masked count (one wait on the stream),
+// adaLN vectors, the layers' attention and the unmasking pass.  The
+// callables fill the provider's buffers: layer_inputs(step, layer, prev_out)
+// and logits(step) return the callback's status.
+template <typename LayerFn, typename LogitsFn>
+tt_status denoise_loop(const char* fn, const tt_attn_shape* shape, const LoopOpts& o,
+                       const void* const* k_ctx_layers, const void* const* v_ctx_layers,
+                       const int64_t* ctx_start, const int32_t* ctx_len, const void* ada_w,
+                       const float* ada_bias, const float* ada_table, LayerFn&& layer_inputs,
+                       LogitsFn&& logits_fn, int32_t* tokens, uint8_t* masked,
+                       int8_t* commit_step, int32_t* steps_taken, const DenoiseBufs& z,
+                       tt_stream stream) {
+  const int B = shape->batch, S = shape->block_size, Hq = shape->n_q_heads,
+            Hkv = shape->n_kv_heads, d = shape->head_dim;
+  const size_t W = static_cast<size_t>(Hq) * d;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t he = tt::launch_count_masked(B, S, masked, z.n_masked, hs);
+  if (he != hipSuccess) return hip_fail(he, fn);
+  for (int k = 0; k < o.max_steps; ++k) {
+    he = tt::launch_active_from_masked(B, z.n_masked, z.active, z.total, hs);
+    if (he != hipSuccess) return hip_fail(he, fn);
+    int32_t host_total = 0;
+    he = hipMemcpyAsync(&host_total, z.total, sizeof(int32_t), hipMemcpyDeviceToHost, hs);
+    if (he == hipSuccess) he = hipStreamSynchronize(hs);
+    if (he != hipSuccess) return hip_fail(he, fn);
+    if (host_total == 0) break;
+    if (ada_w) {
+      he = tt::launch_timestep_embed(B, nullptr, z.n_masked, S, z.emb, hs);
+      if (he == hipSuccess)
+        he = tt::launch_adaln_single(B, static_cast<int>(W), o.n_layers, z.emb, ada_w, ada_bias,
+                                     ada_table, z.ada, hs);
+      if (he != hipSuccess) return hip_fail(he, fn);
+    }
+    for (int l = 0; l < o.n_layers; ++l) {
+      const int rc = layer_inputs(k, l, l == 0 ? nullptr : z.out);
+      if (rc != 0)
+        return fail(TT_ERR_CALLBACK, "%s: layer_inputs(step %d, layer %d) returned %d", fn, k, l, rc);
+      tt::AttnArgs a{};
+      a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.dtype = shape->dtype;
+      a.q = z.q; a.kb = z.kb; a.vb = z.vb; a.kc = k_ctx_layers[l]; a.vc = v_ctx_layers[l];
+      a.ctx_start = ctx_start; a.ctx_len = ctx_len; a.active = z.active;
+      if (ada_w) {
+        a.shift = z.ada + (static_cast<size_t>(l) * 3 + 0) * B * W;
+        a.scale = z.ada + (static_cast<size_t>(l) * 3 + 1) * B * W;
+        a.gate = z.ada + (static_cast<size_t>(l) * 3 + 2) * B * W;
+      }
+      a.residual = nullptr; a.out = z.out; a.lse = nullptr;
+      he = tt::launch_block_attn(a, z.ap, z.attn_ws, hs);
+      if (he != hipSuccess) return hip_fail(he, fn);
+    }
+    const int rc = logits_fn(k);
+    if (rc != 0) return fail(TT_ERR_CALLBACK, "%s: logits(step %d) returned %d", fn, k, rc);
+    tt::UnmaskArgs ua{};
+    ua.B = B; ua.S = S; ua.V = o.vocab; ua.dtype = shape->dtype; ua.logits = z.logits;
+    ua.row_stride = o.vocab;
+    ua.gamma = (o.finish_block && k == o.max_steps - 1) ? -INFINITY : o.gamma;
+    ua.temperature = o.temperature;
+    ua.mask_id = o.mask_id; ua.step = k; ua.tokens = tokens; ua.masked = masked;
+    ua.commit_step = commit_step; ua.n_masked = z.n_masked;
+    ua.sample = o.sample; ua.seed = o.seed; ua.block_index = o.block;
+    he = tt::launch_confidence_unmask(ua, z.up, z.unmask_ws, hs);
+    if (he != hipSuccess) return hip_fail(he, fn);
+    if (steps_taken) *steps_taken = k + 1;
+  }
+  return TT_OK;
+}
+
+tt_status check_layers(const char* fn, int n_layers, const void* const* k_layers,
+                       const void* const* v_layers) {
+  if (!k_layers || !v_layers)
+    return fail(TT_ERR_INVALID_ARG, "%s: k_ctx_layers and v_ctx_layers must be non-NULL", fn);
+  for (int l = 0; l < n_layers; ++l) {
+    if (!k_layers[l] || !v_layers[l])
+      return fail(TT_ERR_INVALID_ARG, "%s: context cache of layer %d is NULL", fn, l);
+    if (!aligned(k_layers[l], 16) || !aligned(v_layers[l], 16))
+      return fail(TT_ERR_INVALID_ARG, "%s: context cache of layer %d is not 16-byte aligned", fn, l);
+  }
+  return TT_OK;
+}
+
+tt_status check_ada(const char* fn, const tt_attn_shape* shape, const void* ada_w,
+                    const float* ada_bias, const float* ada_table) {
+  if (ada_w && (shape->n_q_heads * shape->head_dim) % 4 != 0)
+    return fail(TT_ERR_INVALID_ARG, "%s: adaLN width must be a multiple of 4", fn);
+  if (ada_w && !aligned(ada_w, 8)) return fail(TT_ERR_INVALID_ARG, "%s: ada_w must be 8-byte aligned", fn);
+  if (ada_w && (!aligned(ada_bias, 16) || !aligned(ada_table, 16)))
+    return fail(TT_ERR_INVALID_ARG, "%s: ada_bias and ada_table must be 16-byte aligned", fn);
+  return TT_OK;
+}
+
+size_t generate_bytes(const tt_attn_shape* s, int n_layers, int n_blocks, int max_ctx_len,
+                      int vocab) {
+  const size_t B = s->batch, S = s->block_size;
+  size_t t = denoise_bytes(s, n_layers, max_ctx_len + n_blocks * s->block_size, vocab);
+  t += tt::align_up(B * S * 4, 256);   // tokens of the block
+  t += tt::align_up(B * S, 256);       // masked
+  t += tt::align_up(B, 256);           // unfinished
+  t += tt::align_up(B, 256);           // appended
+  return t;
+}
+
+}  // namespace
+
+extern "C" {
+
 tt_status tt_denoise_block(const tt_attn_shape* shape, int32_t n_layers, int32_t max_steps,
                            float gamma, float temperature, int32_t mask_token_id, int32_t vocab,
                            const void* const* k_ctx_layers, const void* const* v_ctx_layers,
@@ -361,106 +511,168 @@ tt_status tt_denoise_block(const tt_attn_shape* shape, int32_t n_layers, int32_t
                            const tt_step_provider* provider, int32_t* tokens, uint8_t* masked,
                            int8_t* commit_step, int32_t* steps_taken, void* workspace,
                            size_t workspace_bytes, tt_stream stream) {
+  const char* fn = "tt_denoise_block";
   if (steps_taken) *steps_taken = 0;
   tt_status st = check_shape(shape);
   if (st != TT_OK) return st;
   const int S = shape->block_size;
-  if (n_layers < 1) return fail(TT_ERR_INVALID_ARG, "n_layers %d < 1", n_layers);
+  if (n_layers < 1) return fail(TT_ERR_INVALID_ARG, "%s: n_layers %d < 1", fn, n_layers);
   if (max_steps < 0 || max_steps > S)
-    return fail(TT_ERR_INVALID_ARG, "max_steps %d outside [0, block_size=%d]", max_steps, S);
-  if (max_ctx_len < 0) return fail(TT_ERR_INVALID_ARG, "max_ctx_len %d < 0", max_ctx_len);
+    return fail(TT_ERR_INVALID_ARG, "%s: max_steps %d outside [0, block_size=%d]", fn, max_steps, S);
+  if (max_ctx_len < 0) return fail(TT_ERR_INVALID_ARG, "%s: max_ctx_len %d < 0", fn, max_ctx_len);
   st = check_unmask_scalars(shape->batch, S, vocab, vocab, gamma, temperature);
   if (st != TT_OK) return st;
-  if (!k_ctx_layers || !v_ctx_layers)
-    return fail(TT_ERR_INVALID_ARG, "k_ctx_layers and v_ctx_layers must be non-NULL");
-  for (int l = 0; l < n_layers; ++l) {
-    if (!k_ctx_layers[l] || !v_ctx_layers[l])
-      return fail(TT_ERR_INVALID_ARG, "context cache of layer %d is NULL", l);
-    if (!aligned(k_ctx_layers[l], 16) || !aligned(v_ctx_layers[l], 16))
-      return fail(TT_ERR_INVALID_ARG, "context cache of layer %d is not 16-byte aligned", l);
-  }
-  if (!ctx_start || !ctx_len) return fail(TT_ERR_INVALID_ARG, "ctx_start and ctx_len must be non-NULL");
+  st = check_layers(fn, n_layers, k_ctx_layers, v_ctx_layers);
+  if (st != TT_OK) return st;
+  if (!ctx_start || !ctx_len) return fail(TT_ERR_INVALID_ARG, "%s: ctx_start and ctx_len must be non-NULL", fn);
   if (!provider || !provider->layer_inputs || !provider->logits)
-    return fail(TT_ERR_INVALID_ARG, "provider and both of its callbacks must be non-NULL");
-  if (!tokens || !masked) return fail(TT_ERR_INVALID_ARG, "tokens and masked must be non-NULL");
-  if (ada_w && (shape->n_q_heads * shape->head_dim) % 4 != 0)
-    return fail(TT_ERR_INVALID_ARG, "adaLN width must be a multiple of 4");
-  if (ada_w && !aligned(ada_w, 8)) return fail(TT_ERR_INVALID_ARG, "ada_w must be 8-byte aligned");
-  if (ada_w && (!aligned(ada_bias, 16) || !aligned(ada_table, 16)))
-    return fail(TT_ERR_INVALID_ARG, "ada_bias and ada_table must be 16-byte aligned");
+    return fail(TT_ERR_INVALID_ARG, "%s: provider and both of its callbacks must be non-NULL", fn);
+  if (!tokens || !masked) return fail(TT_ERR_INVALID_ARG, "%s: tokens and masked must be non-NULL", fn);
+  st = check_ada(fn, shape, ada_w, ada_bias, ada_table);
+  if (st != TT_OK) return st;
   if (shape->batch == 0 || max_steps == 0) return ok();
   const size_t need = denoise_bytes(shape, n_layers, max_ctx_len, vocab);
   if (!workspace || workspace_bytes < need)
-    return fail(TT_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
-  if (!aligned(workspace, 256)) return fail(TT_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    return fail(TT_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(TT_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
 
-  const int B = shape->batch, Hq = shape->n_q_heads, Hkv = shape->n_kv_heads, d = shape->head_dim;
-  const size_t e = elt_size(shape->dtype), W = static_cast<size_t>(Hq) * d;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
   Carver cv{static_cast<char*>(workspace)};
-  float* ada = static_cast<float*>(cv.take(static_cast<size_t>(n_layers) * 3 * B * W * 4));
-  float* emb = static_cast<float*>(cv.take(static_cast<size_t>(B) * TT_TIMESTEP_DIM * 4));
-  void* q = cv.take(static_cast<size_t>(B) * S * Hq * d * e);
-  void* kb = cv.take(static_cast<size_t>(B) * S * Hkv * d * e);
-  void* vb = cv.take(static_cast<size_t>(B) * S * Hkv * d * e);
-  void* out = cv.take(static_cast<size_t>(B) * S * Hq * d * e);
-  void* logits = cv.take(static_cast<size_t>(B) * S * vocab * e);
-  int32_t* n_masked = static_cast<int32_t*>(cv.take(static_cast<size_t>(B) * 4));
-  uint8_t* active = static_cast<uint8_t*>(cv.take(B));
-  int32_t* total = static_cast<int32_t*>(cv.take(4));
-  const tt::AttnPlan ap = tt::attn_plan(B, S, Hq, Hkv, d, shape->dtype, max_ctx_len);
-  void* attn_ws = cv.take(ap.total_bytes);
-  const tt::UnmaskPlan up = tt::unmask_plan(B, S, vocab);
-  void* unmask_ws = cv.take(up.total_bytes);
+  const DenoiseBufs z = carve_denoise(cv, shape, n_layers, max_ctx_len, vocab);
+  LoopOpts o{};
+  o.n_layers = n_layers; o.max_steps = max_steps; o.vocab = vocab; o.mask_id = mask_token_id;
+  o.gamma = gamma; o.temperature = temperature;
+  auto layer_inputs = [&](int k, int l, const void* prev) {
+    return provider->layer_inputs(provider->user, k, l, prev, z.q, z.kb, z.vb, stream);
+  };
+  auto logits_fn = [&](int k) { return provider->logits(provider->user, k, z.out, z.logits, stream); };
+  st = denoise_loop(fn, shape, o, k_ctx_layers, v_ctx_layers, ctx_start, ctx_len, ada_w, ada_bias,
+                    ada_table, layer_inputs, logits_fn, tokens, masked, commit_step, steps_taken, z,
+                    stream);
+  if (st != TT_OK) return st;
+  const hipError_t he = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "tt_denoise_block final sync");
+  return ok();
+}
 
-  hipError_t he = tt::launch_count_masked(B, S, masked, n_masked, hs);
-  if (he != hipSuccess) return hip_fail(he, "tt_denoise_block count");
-  for (int k = 0; k < max_steps; ++k) {
-    he = tt::launch_active_from_masked(B, n_masked, active, total, hs);
-    if (he != hipSuccess) return hip_fail(he, "tt_denoise_block active");
-    int32_t host_total = 0;
-    he = hipMemcpyAsync(&host_total, total, sizeof(int32_t), hipMemcpyDeviceToHost, hs);
+size_t tt_generate_workspace_size(const tt_attn_shape* shape, int32_t n_layers, int32_t n_blocks,
+                                  int32_t max_ctx_len, int32_t vocab) {
+  if (check_shape(shape) != TT_OK) return 0;
+  if (n_layers < 1 || n_blocks < 0 || max_ctx_len < 0 || vocab < 1) {
+    fail(TT_ERR_INVALID_ARG, "n_layers %d, n_blocks %d, max_ctx_len %d, vocab %d", n_layers,
+         n_blocks, max_ctx_len, vocab);
+    return 0;
+  }
+  ok();
+  return generate_bytes(shape, n_layers, n_blocks, max_ctx_len, vocab);
+}
+
+tt_status tt_generate(const tt_attn_shape* shape, int32_t n_layers, int32_t n_blocks,
+                      int32_t steps_per_block, float gamma, float temperature, int32_t sample,
+                      uint64_t seed, int32_t mask_token_id, int32_t eos_token_id, int32_t vocab,
+                      void* const* k_ctx_layers, void* const* v_ctx_layers,
+                      const int64_t* ctx_start, const int64_t* ctx_end, int32_t* ctx_len,
+                      int32_t max_ctx_len, const void* ada_w, const float* ada_bias,
+                      const float* ada_table, const tt_gen_provider* provider,
+                      int32_t* out_tokens, int32_t* n_generated, int8_t* stop_reason,
+                      int32_t* blocks_taken, void* workspace, size_t workspace_bytes,
+                      tt_stream stream) {
+  const char* fn = "tt_generate";
+  if (blocks_taken) *blocks_taken = 0;
+  tt_status st = check_shape(shape);
+  if (st != TT_OK) return st;
+  const int B = shape->batch, S = shape->block_size;
+  if (n_layers < 1) return fail(TT_ERR_INVALID_ARG, "%s: n_layers %d < 1", fn, n_layers);
+  if (n_blocks < 0) return fail(TT_ERR_INVALID_ARG, "%s: n_blocks %d < 0", fn, n_blocks);
+  if (steps_per_block < 1 || steps_per_block > S)
+    return fail(TT_ERR_INVALID_ARG, "%s: steps_per_block %d outside [1, block_size=%d]", fn,
+                steps_per_block, S);
+  if (max_ctx_len < 0) return fail(TT_ERR_INVALID_ARG, "%s: max_ctx_len %d < 0", fn, max_ctx_len);
+  if (static_cast<int64_t>(max_ctx_len) + static_cast<int64_t>(n_blocks) * S > INT32_MAX)
+    return fail(TT_ERR_INVALID_ARG, "%s: max_ctx_len + n_blocks * S overflows int32", fn);
+  st = check_unmask_scalars(B, S, vocab, vocab, gamma, temperature);
+  if (st != TT_OK) return st;
+  st = check_layers(fn, n_layers, const_cast<const void* const*>(k_ctx_layers),
+                    const_cast<const void* const*>(v_ctx_layers));
+  if (st != TT_OK) return st;
+  if (!ctx_start || !ctx_end || !ctx_len)
+    return fail(TT_ERR_INVALID_ARG, "%s: ctx_start, ctx_end and ctx_len must be non-NULL", fn);
+  if (!aligned(ctx_start, 8) || !aligned(ctx_end, 8) || !aligned(ctx_len, 4))
+    return fail(TT_ERR_INVALID_ARG, "%s: misaligned ctx_start/ctx_end/ctx_len", fn);
+  if (!provider || !provider->layer_inputs || !provider->logits || !provider->ctx_inputs)
+    return fail(TT_ERR_INVALID_ARG, "%s: provider and its three callbacks must be non-NULL", fn);
+  if (!out_tokens || !n_generated)
+    return fail(TT_ERR_INVALID_ARG, "%s: out_tokens and n_generated must be non-NULL", fn);
+  if (!aligned(out_tokens, 4) || !aligned(n_generated, 4))
+    return fail(TT_ERR_INVALID_ARG, "%s: misaligned out_tokens/n_generated", fn);
+  st = check_ada(fn, shape, ada_w, ada_bias, ada_table);
+  if (st != TT_OK) return st;
+  if (B == 0) return ok();
+  const size_t need = generate_bytes(shape, n_layers, n_blocks, max_ctx_len, vocab);
+  if (!workspace || workspace_bytes < need)
+    return fail(TT_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(TT_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int hint = max_ctx_len + n_blocks * S;
+  Carver cv{static_cast<char*>(workspace)};
+  const DenoiseBufs z = carve_denoise(cv, shape, n_layers, hint, vocab);
+  int32_t* tokens = static_cast<int32_t*>(cv.take(static_cast<size_t>(B) * S * 4));
+  uint8_t* masked = static_cast<uint8_t*>(cv.take(static_cast<size_t>(B) * S));
+  uint8_t* unfinished = static_cast<uint8_t*>(cv.take(B));
+  uint8_t* appended = static_cast<uint8_t*>(cv.take(B));
+  hipError_t he = tt::launch_gen_init(B, unfinished, n_generated, stop_reason, hs);
+  if (he != hipSuccess) return hip_fail(he, fn);
+  LoopOpts o{};
+  o.n_layers = n_layers; o.max_steps = steps_per_block; o.vocab = vocab;
+  o.mask_id = mask_token_id; o.gamma = gamma; o.temperature = temperature;
+  o.sample = sample != 0; o.seed = seed; o.finish_block = 1;
+  for (int blk = 0; blk < n_blocks; ++blk) {
+    // a fully masked block for every unfinished sequence; stop when none is left
+    he = tt::launch_gen_block_init(B, S, mask_token_id, unfinished, tokens, masked, z.total, hs);
+    int32_t host_left = 0;
+    if (he == hipSuccess)
+      he = hipMemcpyAsync(&host_left, z.total, sizeof(int32_t), hipMemcpyDeviceToHost, hs);
     if (he == hipSuccess) he = hipStreamSynchronize(hs);
-    if (he != hipSuccess) return hip_fail(he, "tt_denoise_block masked-count readback");
-    if (host_total == 0) break;
-    if (ada_w) {
-      he = tt::launch_timestep_embed(B, nullptr, n_masked, S, emb, hs);
-      if (he == hipSuccess)
-        he = tt::launch_adaln_single(B, static_cast<int>(W), n_layers, emb, ada_w, ada_bias,
-                                     ada_table, ada, hs);
-      if (he != hipSuccess) return hip_fail(he, "tt_denoise_block adaLN");
-    }
+    if (he != hipSuccess) return hip_fail(he, fn);
+    if (host_left == 0) break;
+    o.block = blk;
+    auto layer_inputs = [&](int k, int l, const void* prev) {
+      return provider->layer_inputs(provider->user, blk, k, l, prev, z.q, z.kb, z.vb, stream);
+    };
+    auto logits_fn = [&](int k) {
+      return provider->logits(provider->user, blk, k, z.out, z.logits, stream);
+    };
+    st = denoise_loop(fn, shape, o, const_cast<const void* const*>(k_ctx_layers),
+                      const_cast<const void* const*>(v_ctx_layers), ctx_start, ctx_len, ada_w,
+                      ada_bias, ada_table, layer_inputs, logits_fn, tokens, masked, nullptr,
+                      nullptr, z, stream);
+    if (st != TT_OK) return st;
+    // the context tower takes the block: every layer's causal attention with
+    // the append of the block's K/V, then the lengths grow
     for (int l = 0; l < n_layers; ++l) {
-      const int rc = provider->layer_inputs(provider->user, k, l, l == 0 ? nullptr : out, q, kb,
-                                            vb, stream);
+      const int rc = provider->ctx_inputs(provider->user, blk, l, tokens, l == 0 ? nullptr : z.out,
+                                          z.q, z.kb, z.vb, stream);
       if (rc != 0)
-        return fail(TT_ERR_CALLBACK, "layer_inputs(step %d, layer %d) returned %d", k, l, rc);
+        return fail(TT_ERR_CALLBACK, "%s: ctx_inputs(block %d, layer %d) returned %d", fn, blk, l, rc);
       tt::AttnArgs a{};
-      a.B = B; a.S = S; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.dtype = shape->dtype;
-      a.q = q; a.kb = kb; a.vb = vb; a.kc = k_ctx_layers[l]; a.vc = v_ctx_layers[l];
-      a.ctx_start = ctx_start; a.ctx_len = ctx_len; a.active = active;
-      if (ada_w) {
-        a.shift = ada + (static_cast<size_t>(l) * 3 + 0) * B * W;
-        a.scale = ada + (static_cast<size_t>(l) * 3 + 1) * B * W;
-        a.gate = ada + (static_cast<size_t>(l) * 3 + 2) * B * W;
-      }
-      a.residual = nullptr; a.out = out; a.lse = nullptr;
-      he = tt::launch_block_attn(a, ap, attn_ws, hs);
-      if (he != hipSuccess) return hip_fail(he, "tt_denoise_block attention");
+      a.B = B; a.S = S; a.Hq = shape->n_q_heads; a.Hkv = shape->n_kv_heads; a.d = shape->head_dim;
+      a.dtype = shape->dtype;
+      a.q = z.q; a.kb = z.kb; a.vb = z.vb; a.kc = k_ctx_layers[l]; a.vc = v_ctx_layers[l];
+      a.ctx_start = ctx_start; a.ctx_len = ctx_len; a.active = unfinished;
+      a.out = z.out;
+      a.causal = 1; a.ctx_end = ctx_end; a.kc_out = k_ctx_layers[l]; a.vc_out = v_ctx_layers[l];
+      he = tt::launch_block_attn(a, z.ap, z.attn_ws, hs);
+      if (he != hipSuccess) return hip_fail(he, fn);
     }
-    const int rc = provider->logits(provider->user, k, out, logits, stream);
-    if (rc != 0) return fail(TT_ERR_CALLBACK, "logits(step %d) returned %d", k, rc);
-    tt::UnmaskArgs ua{};
-    ua.B = B; ua.S = S; ua.V = vocab; ua.dtype = shape->dtype; ua.logits = logits;
-    ua.row_stride = vocab; ua.gamma = gamma; ua.temperature = temperature;
-    ua.mask_id = mask_token_id; ua.step = k; ua.tokens = tokens; ua.masked = masked;
-    ua.commit_step = commit_step; ua.n_masked = n_masked;
-    he = tt::launch_confidence_unmask(ua, up, unmask_ws, hs);
-    if (he != hipSuccess) return hip_fail(he, "tt_denoise_block unmasking");
-    if (steps_taken) *steps_taken = k + 1;
+    he = tt::launch_ctx_advance(B, S, ctx_start, ctx_end, ctx_len, unfinished, appended, hs);
+    if (he == hipSuccess)
+      he = tt::launch_gen_block_commit(B, S, blk, n_blocks, eos_token_id, tokens, appended,
+                                       unfinished, out_tokens, n_generated, stop_reason, hs);
+    if (he != hipSuccess) return hip_fail(he, fn);
+    if (blocks_taken) *blocks_taken = blk + 1;
   }
   he = hipStreamSynchronize(hs);
-  if (he != hipSuccess) return hip_fail(he, "tt_denoise_block final sync");
+  if (he != hipSuccess) return hip_fail(he, "tt_generate final sync");
   return ok();
 }
 

@@ -91,6 +91,16 @@ hipError_t launch_active_from_masked(int B, const int32_t* n_masked, uint8_t* ac
 hipError_t launch_count_masked(int B, int S, const uint8_t* masked, int32_t* n_masked,
                                hipStream_t st);
 hipError_t launch_clear(void* p, size_t bytes, hipStream_t st);
+// Generation bookkeeping (csrc/context.hip).
+hipError_t launch_gen_init(int B, uint8_t* unfinished, int32_t* n_generated, int8_t* stop,
+                           hipStream_t st);
+hipError_t launch_gen_block_init(int B, int S, int mask_id, const uint8_t* unfinished,
+                                 int32_t* tokens, uint8_t* masked, int32_t* n_unfinished,
+                                 hipStream_t st);
+hipError_t launch_gen_block_commit(int B, int S, int block, int n_blocks, int eos_id,
+                                   const int32_t* tokens, const uint8_t* appended,
+                                   uint8_t* unfinished, int32_t* out_tokens,
+                                   int32_t* n_generated, int8_t* stop, hipStream_t st);
 hipError_t launch_ctx_advance(int B, int S, const int64_t* ctx_start, const int64_t* ctx_end,
                               int32_t* ctx_len, const uint8_t* active, uint8_t* appended,
                               hipStream_t st);

@@ -359,6 +359,76 @@ tt_status tt_denoise_block(const tt_attn_shape* shape, int32_t n_layers, int32_t
                            uint8_t* masked, int8_t* commit_step, int32_t* steps_taken,
                            void* workspace, size_t workspace_bytes, tt_stream stream);
 
+/* ------------------------------------------------------------------------
+ * tt_generate -- multi-block generation: denoise a block, let the context
+ * tower take it, go on to the next block, stop at EOS.
+ *
+ * [news] training and inference section, code example: the generation call
+ * takes max_new_tokens=128, block_size=16, steps_per_block=16,
+ * mask_token_id=3, temperature=0.1, confidence_threshold=0.8 and
+ * eos_token_id.  [dothoosh] two-tower mechanism section: generation goes
+ * block by block, each block starting as [MASK] tokens refined over T steps
+ * until final; the context tower runs causally over the prompt and the
+ * committed tokens and keeps every layer's KV cache.
+ *
+ * For block k = 0 .. n_blocks-1 while some sequence is unfinished:
+ *   1. every unfinished sequence gets a fully masked block; the loop of
+ *      tt_denoise_block runs up to steps_per_block steps (callbacks
+ *      layer_inputs(k, step, layer, ...) and logits(k, step, ...)), with
+ *      tt_sample_unmask (block_index k) when `sample` is non-zero, else the
+ *      argmax of tt_confidence_unmask; the last allowed step commits every
+ *      slot still masked, so every generated block is final;
+ *   2. the context tower takes the block: for each layer,
+ *      ctx_inputs(k, layer, tokens, prev_out, q, k_blk, v_blk) fills its
+ *      q/k/v and tt_ctx_block_attn runs with the append; then
+ *      tt_ctx_advance grows the contexts;
+ *   3. out_tokens[b, k*S .. k*S+S-1] = the block's tokens and
+ *      n_generated[b] += S; a sequence stops after a block that holds
+ *      eos_token_id (stop_reason 1) or whose append found no room
+ *      (stop_reason 2); otherwise stop_reason stays 0.
+ * The denoiser's attention reads the caches as they grow, with no adaLN when
+ * ada_w is NULL.  Positions of out_tokens past n_generated[b] are not
+ * written.  The callbacks enqueue on `stream`; their buffers live in the
+ * workspace; `tokens` is device [B, S] int32.
+ *   k_ctx_layers, v_ctx_layers  host arrays of n_layers device caches
+ *   ctx_start, ctx_end          device [B] int64 (reserved regions, disjoint)
+ *   ctx_len                     device [B] int32 in/out
+ *   max_ctx_len                 host: the longest initial context
+ *   out_tokens  device [B, n_blocks*S] int32; n_generated device [B] int32;
+ *   stop_reason device [B] int8 or NULL; blocks_taken host int32 or NULL.
+ * eos_token_id < 0: no EOS stop.  Waits on the stream once per step and once
+ * per block.
+ * Errors: as tt_denoise_block and tt_ctx_block_attn, plus
+ * TT_ERR_INVALID_ARG for steps_per_block outside [1, S], n_blocks < 0, a
+ * NULL callback, NULL out_tokens/n_generated/ctx_end; TT_ERR_CALLBACK when a
+ * callback returns non-zero (the state is that of the last completed call).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  void* user;
+  int (*layer_inputs)(void* user, int32_t block, int32_t step, int32_t layer,
+                      const void* prev_out, void* q_blk, void* k_blk, void* v_blk,
+                      tt_stream stream);
+  int (*logits)(void* user, int32_t block, int32_t step, const void* last_out, void* logits,
+                tt_stream stream);
+  int (*ctx_inputs)(void* user, int32_t block, int32_t layer, const int32_t* tokens,
+                    const void* prev_out, void* q_blk, void* k_blk, void* v_blk,
+                    tt_stream stream);
+} tt_gen_provider;
+
+size_t tt_generate_workspace_size(const tt_attn_shape* shape, int32_t n_layers, int32_t n_blocks,
+                                  int32_t max_ctx_len, int32_t vocab);
+
+tt_status tt_generate(const tt_attn_shape* shape, int32_t n_layers, int32_t n_blocks,
+                      int32_t steps_per_block, float gamma, float temperature, int32_t sample,
+                      uint64_t seed, int32_t mask_token_id, int32_t eos_token_id, int32_t vocab,
+                      void* const* k_ctx_layers, void* const* v_ctx_layers,
+                      const int64_t* ctx_start, const int64_t* ctx_end, int32_t* ctx_len,
+                      int32_t max_ctx_len, const void* ada_w, const float* ada_bias,
+                      const float* ada_table, const tt_gen_provider* provider,
+                      int32_t* out_tokens, int32_t* n_generated, int8_t* stop_reason,
+                      int32_t* blocks_taken, void* workspace, size_t workspace_bytes,
+                      tt_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

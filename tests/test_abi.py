@@ -204,3 +204,30 @@ def test_sample_unmask_rejects_bad_arguments():
     assert call(ws_bytes=1) == tt.TT_ERR_WORKSPACE
     assert "tt_sample_unmask" in tt.last_error()
     assert call(B=0) == tt.TT_OK
+
+
+def test_generate_rejects_bad_arguments():
+    s = tt.AttnShape(2, 4, 1, 64, 16, 0)
+    L = tt.lib()
+    ptrs = (ctypes.c_void_p * 1)(FAKE)
+    prov = tt.GenProvider()
+
+    def call(shape=s, n_layers=1, n_blocks=2, steps=16, provider=None, k=ptrs, ce=FAKE,
+             out=FAKE, ws_bytes=1 << 30):
+        taken = ctypes.c_int32(-5)
+        st = L.tt_generate(ctypes.byref(shape), n_layers, n_blocks, steps, 0.8, 0.1, 1, 5, 3, 2,
+                           64, k, ptrs, FAKE, ce, FAKE, 8, None, None, None, provider, out,
+                           FAKE, None, ctypes.byref(taken), FAKE, ws_bytes, None)
+        assert taken.value == 0
+        return st
+    assert call(steps=0) == tt.TT_ERR_INVALID_ARG
+    assert call(steps=17) == tt.TT_ERR_INVALID_ARG
+    assert call(n_blocks=-1) == tt.TT_ERR_INVALID_ARG
+    assert call(n_layers=0) == tt.TT_ERR_INVALID_ARG
+    assert call(provider=None) == tt.TT_ERR_INVALID_ARG
+    assert call(provider=ctypes.byref(prov)) == tt.TT_ERR_INVALID_ARG    # NULL callbacks
+    assert call(ce=None) == tt.TT_ERR_INVALID_ARG
+    assert call(out=None) == tt.TT_ERR_INVALID_ARG
+    assert call(k=(ctypes.c_void_p * 1)(None)) == tt.TT_ERR_INVALID_ARG
+    assert "tt_generate" in tt.last_error()
+    assert tt.generate_workspace_size(s, 1, 2, 8, 64) > tt.denoise_workspace_size(s, 1, 8, 64)
