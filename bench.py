@@ -30,6 +30,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 ROW_REPS = 10          # calls per row in the per-row timing pass
+GEN_BLOCKS = 8         # generation row: max_new_tokens = 128 at S = 16
+ROW_WARM_CALLS = 250   # attention calls (~40 ms) before each row's timing
 METRIC = "block-denoise query-tokens/s + achieved HBM GB/s (S=16, ctx 8k, bf16)"
 
 
@@ -179,10 +181,10 @@ def main():
     sd = w["seed"]
     lens = w["lens"]
     max_len = max(lens)
-    # each sequence's cache region holds its context plus room for one block,
-    # which the context-tower row appends into (the denoiser reads the first
-    # ctx_len rows only)
-    region = [L + S for L in lens]
+    # each sequence's cache region holds its context plus room for the
+    # generation row's blocks, which the context-tower rows append into (the
+    # denoiser step reads the first ctx_len rows only)
+    region = [L + GEN_BLOCKS * S for L in lens]
     total = sum(region)
     start = torch.tensor(np.concatenate([[0], np.cumsum(region)[:-1]]), dtype=torch.int64, device=dev)
     ctx_end = start + torch.tensor(region, dtype=torch.int64, device=dev)
@@ -255,11 +257,16 @@ def main():
     torch.cuda.synchronize()
     committed = int(B * S - n_masked.sum().item())
 
-    # Per-row times, after the timed region: each row's calls alone, one
-    # untimed call (first launches of a kernel load its code), then ROW_REPS
-    # calls bracketed by one event pair.
+    # Per-row times, after the timed region: each row's calls alone, after
+    # ROW_WARM_CALLS back-to-back attention calls (the clocks drop while the
+    # host works between rows and take tens of ms of GPU work to come back)
+    # and one untimed call of the row (first launches load the kernel's
+    # code); then ROW_REPS calls bracketed by one event pair.
     def timed(fn):
+        for i in range(ROW_WARM_CALLS):
+            tt.block_attn(shape, qb[0], kb[0], vb[0], kc[0], vc[0], start, clen, max_len, out, aws)
         fn(-1)
+        torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -271,6 +278,12 @@ def main():
     base = args.warmup + args.steps
     us_ada = timed(lambda r: (tt.timestep_embed(B, t_step, emb),
                               tt.adaln_single(B, W, NL, emb, ada_w, ada_b, ada_t, ada)))
+    us_sample = timed(lambda r: tt.sample_unmask(
+        B, S, V, logits, V, w["gamma"], 0.1, 2024, 0, 3, 0, tokens_all[base + 1 + r],
+        masked_all[base + 1 + r], uws, n_masked=n_masked))
+    # fresh states again for the argmax row
+    tokens_all[base:].fill_(3)
+    masked_all[base:].fill_(1)
     us_unmask = timed(lambda r: tt.confidence_unmask(
         B, S, V, logits, V, w["gamma"], w["tau"], 3, 0, tokens_all[base + 1 + r], masked_all[base + 1 + r],
         uws, n_masked=n_masked))
@@ -287,6 +300,7 @@ def main():
                                                                 appended=appended)))
     assert int(appended.sum().item()) == B and clen2.tolist() == [L + S for L in lens]
     loop = denoise_loop(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, clen)
+    gen = generate_row(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, ctx_end, clen)
     ms = t0.elapsed_time(t1) / args.steps
     bounds = step_events + [t1]
     step_ms = [a.elapsed_time(b) for a, b in zip(bounds[:-1], bounds[1:])]
@@ -343,6 +357,9 @@ def main():
         "a1_timestep_adaln": row(us_ada, ada_bytes, "tt_timestep_embed + tt_adaln_single"),
         "a2_a5_block_attn": row(attn_avg * 1e3, per_launch, "tt_block_attn (timed region)"),
         "a6_a7_unmask": row(us_unmask, unmask_bytes, "tt_confidence_unmask, all rows masked"),
+        "f2_sample_unmask": row(us_sample, unmask_bytes,
+                                "tt_sample_unmask at temperature 0.1, all rows masked"),
+        "f2_generate": gen,
         "f1_ctx_commit_attn": row(us_ctx, ctx_bytes,
                                   "tt_ctx_block_attn with the cache append, per layer"),
         "f1_ctx_advance": {"calls": "tt_ctx_advance + a 4*B-byte length reset copy",
@@ -396,6 +413,60 @@ def denoise_loop(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, 
     return {"calls": "tt_denoise_block, all slots masked, up to S steps", "steps": steps,
             "masked_left": left, "ms_per_loop": round(sec * 1e3, 3),
             "ms_per_step": round(sec * 1e3 / max(steps, 1), 4)}
+
+
+def generate_row(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, ctx_end, clen):
+    """One tt_generate call: GEN_BLOCKS blocks of S slots for every sequence,
+    temperature sampling at 0.1 (the pages' generation settings), adaLN on,
+    the context tower taking every block.  The provider copies the step-0
+    q/k/v and logits of block 0 into the library's buffers and leaves them in
+    place afterwards (so after each block's first step the one-commit rule
+    drives progress); its context-tower inputs are the block's q/k/v again.
+    Timed once after one untimed call, on a copy of the context lengths."""
+    import torch
+    B, S, NL, V = w["B"], w["S"], w["layers"], w["V"]
+    bf = torch.bfloat16
+    shape = tt.attn_shape(B, w["Hq"], w["Hkv"], w["d"], S, bf)
+
+    class Provider:
+        def __init__(self):
+            self.steps = 0
+
+        def layer_inputs(self, blk, step, layer, prev_out, q, k, v):
+            if blk == 0 and step == 0:
+                q.copy_(qb[layer])
+                k.copy_(kb[layer])
+                v.copy_(vb[layer])
+
+        def logits(self, blk, step, last_out, lg):
+            self.steps += 1
+            if blk == 0 and step == 0:
+                lg.copy_(logits)
+
+        def ctx_inputs(self, blk, layer, tokens, prev_out, q, k, v):
+            pass
+
+    ws = torch.empty(tt.generate_workspace_size(shape, NL, GEN_BLOCKS, max(w["lens"]), V),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((B, GEN_BLOCKS * S), dtype=torch.int32, device="cuda")
+    n_gen = torch.empty((B,), dtype=torch.int32, device="cuda")
+
+    def run():
+        lens = clen.clone()
+        prov = Provider()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        blocks = tt.generate(shape, NL, GEN_BLOCKS, S, w["gamma"], 0.1, 3, -1, V, kc, vc, start,
+                             ctx_end, lens, max(w["lens"]), prov, out, n_gen, ws, seed=2024,
+                             ada_w=ada_w, ada_bias=ada_b, ada_table=ada_t)
+        torch.cuda.synchronize()
+        return blocks, prov.steps, time.perf_counter() - t0, int(n_gen.sum().item())
+    run()
+    blocks, steps, sec, tokens = run()
+    return {"calls": f"tt_generate, {GEN_BLOCKS} blocks of {S} slots, sampled at temperature 0.1",
+            "blocks": blocks, "denoise_steps": steps, "generated_tokens": tokens,
+            "ms_per_call": round(sec * 1e3, 2), "ms_per_step": round(sec * 1e3 / max(steps, 1), 4),
+            "generated_tokens_per_s": round(tokens / sec, 1)}
 
 
 def cpu_baseline(w, n_seq, kc, vc, qb, kb, vb, ada, logits, start):

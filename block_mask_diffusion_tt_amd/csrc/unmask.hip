@@ -29,17 +29,18 @@
 //              and one rounding of 1/Z: about 6e-6 in all.
 //
 // Temperature sampling (the same decision rule, a different prediction):
-//   rowsample  grid (V / 8192 slices, B*S), 256 threads.  Each thread holds
-//              32 logits of its slice in registers, so the slice maximum is
-//              known before anything else: Z of the slice relative to it, and
-//              the Gumbel-max candidates -- the only tokens that can win,
-//              those within tau * (Gumbel range) of the slice maximum.  Only
-//              candidates draw their Philox4x32-10 noise (a few per slice),
-//              so the pass stays one read of the row.
+//   rowsample  grid (splits, B*S) as rowreduce, 256 threads.  Each
+//              workgroup streams its slice in passes of 8192 tokens (32 per
+//              thread, held in registers, the next pass's loads in flight):
+//              the pass maximum first (one barrier), so Z and the Gumbel-max
+//              candidates -- the only tokens that can win, those within
+//              tau * (Gumbel range) of the running maximum -- are known
+//              against it.  Only candidates draw their Philox4x32-10 noise
+//              (a few per row), so the pass stays one read of the row.
 //   decide     the same kernel as above with the slices' (max, Z, best
 //              perturbed score, second best, token, logit); rows whose best
-//              two perturbed scores lie within kDelta * (1 + |max| + 20 tau)
-//              get their candidates rescored in fp64 first.
+//              two perturbed scores lie within kKeyBand * (1 + |max| +
+//              20 tau) get their candidates rescored in fp64 first.
 #include <float.h>
 #include <limits.h>
 
@@ -50,6 +51,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr float kDelta = 6.103515625e-05f;  // 2^-14
+// Band of the perturbed scores l + tau G within which the sampled token is
+// settled in fp64: kKeyBand (1 + |max| + 20 tau).  An fp32 score is off by at
+// most about 2^-23 (|l| + 17 tau) + 2^-20 tau (two rounded logarithms, one
+// product, one sum), 60 times less than the band.
+constexpr float kKeyBand = 7.62939453125e-06f;  // 2^-17
 
 struct RowPart {
   float m;   // max of the slice
@@ -221,7 +227,7 @@ constexpr float kGumbelSpread = 20.f;   // >= (kGumbelHi = 17) - (kGumbelLo = -3
 // the decision band of the best perturbed score l + tau G of their slice
 // (their score is at most l + 17 tau, the slice maximum's at least m - 3 tau):
 // only the others draw noise.  The 2^-12 term keeps every token within
-// kDelta * (1 + |m| + 20 tau) of the best score a candidate.
+// kKeyBand * (1 + |m| + 20 tau) of the best score a candidate.
 __device__ __forceinline__ float cand_margin(float m, float tau) {
   return kGumbelSpread * tau + 2.44140625e-04f * (1.f + fabsf(m));
 }
@@ -250,70 +256,143 @@ __device__ __forceinline__ void merge_best(float& key, float& key2, int& idx, fl
   }
 }
 
-constexpr int kSampleSlice = 8192;                 // tokens per workgroup
-constexpr int kSamplePerThread = kSampleSlice / kThreads;  // 32: 4 groups of 8
+constexpr int kChunk = 8192;                   // tokens per workgroup pass
+constexpr int kPerThread = kChunk / kThreads;  // 32: 4 groups of 8 consecutive tokens
 
+// One pass's 32 logits per thread, kept as loaded: group u holds tokens
+// base + 8 (tid + 256 u) .. + 7.  Tokens at or past `end` read as -inf.
+template <typename T>
+struct Chunk;
+
+template <>
+struct Chunk<uint16_t> {
+  uint4 r[4];
+  __device__ __forceinline__ void load(const uint16_t* x, int base, int end, int vec_ok) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int g = base + 8 * (static_cast<int>(threadIdx.x) + kThreads * u);
+      if (vec_ok && g + 8 <= end) {
+        r[u] = *reinterpret_cast<const uint4*>(x + g);
+      } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t lo = g + 2 * k < end ? x[g + 2 * k] : 0xff80u;
+          const uint32_t hi = g + 2 * k + 1 < end ? x[g + 2 * k + 1] : 0xff80u;
+          w[k] = lo | (hi << 16);
+        }
+        r[u] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  }
+  __device__ __forceinline__ float get(int i) const {
+    const uint4 q = r[i >> 3];
+    const int k = i & 7;
+    const uint32_t w = (k >> 1) == 0 ? q.x : ((k >> 1) == 1 ? q.y : ((k >> 1) == 2 ? q.z : q.w));
+    return (k & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+  }
+};
+
+template <>
+struct Chunk<float> {
+  float4 r[8];
+  __device__ __forceinline__ void load(const float* x, int base, int end, int vec_ok) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int g = base + 8 * (static_cast<int>(threadIdx.x) + kThreads * u);
+      if (vec_ok && g + 8 <= end) {
+        r[2 * u] = *reinterpret_cast<const float4*>(x + g);
+        r[2 * u + 1] = *reinterpret_cast<const float4*>(x + g + 4);
+      } else {
+        float w[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) w[k] = g + k < end ? x[g + k] : -INFINITY;
+        r[2 * u] = make_float4(w[0], w[1], w[2], w[3]);
+        r[2 * u + 1] = make_float4(w[4], w[5], w[6], w[7]);
+      }
+    }
+  }
+  __device__ __forceinline__ float get(int i) const {
+    const float4 q = r[i >> 2];
+    const int k = i & 3;
+    return k == 0 ? q.x : (k == 1 ? q.y : (k == 2 ? q.z : q.w));
+  }
+};
+
+// Streams one slice [split*split_len, +split_len) of one masked row in passes
+// of 8192 tokens, the next pass's loads in flight while the current one is
+// processed.  Per pass: the workgroup maximum (one barrier), the running
+// reference M = max so far (Z rescaled when it grows), Z += exp2((x - M) c),
+// and the Gumbel-max candidates x >= M - cand_margin(M): the token holding
+// M was itself a candidate when it arrived, and it outscores every token
+// left out, so the best perturbed score of the slice is among the candidates.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void rowsample_kernel(
     const T* __restrict__ logits, int64_t row_stride, int V, const uint8_t* __restrict__ masked,
-    float c, float tau, NoiseKey nk, int splits, int vec_ok, SamplePart* __restrict__ part) {
+    float c, float tau, NoiseKey nk, int split_len, int splits, int vec_ok,
+    SamplePart* __restrict__ part) {
   const int row = blockIdx.y;
   if (!masked[row]) return;
   const int split = blockIdx.x;
-  const int beg = split * kSampleSlice;
+  const int beg = split * split_len;
+  const int end = min(V, beg + split_len);
   const T* x = logits + static_cast<int64_t>(row) * row_stride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // v[8u + k] is token beg + 8 (tid + 256 u) + k
-  float v[kSamplePerThread];
-  if (vec_ok && beg + kSampleSlice <= V) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float g[8];
-      load8<T>(x, beg + 8 * (tid + kThreads * u), g);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[8 * u + k] = g[k];
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int t = beg + 8 * (tid + kThreads * u) + k;
-        v[8 * u + k] = t < V ? load1(x, t) : -INFINITY;
-      }
-  }
-  __shared__ float s_red[kThreads / 64];
-  __shared__ SamplePart s_best[kThreads / 64];
-  // slice maximum (exact), then the slice's Z relative to it
-  float m = -FLT_MAX;
-#pragma unroll
-  for (int i = 0; i < kSamplePerThread; ++i) m = fmaxf(m, v[i]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if (lane == 0) s_red[wave] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  float z = 0.f;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    float e[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) e[k] = fast_exp2((v[8 * u + k] - m) * c);
-    z += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-  }
-  // candidates draw their noise
-  const float thr = m - cand_margin(m, tau);
-  float key = -INFINITY, key2 = -INFINITY, lx = 0.f;
-  int idx = INT_MAX;
   NoiseKey rk = nk;
   rk.row = static_cast<uint32_t>(row);
+  __shared__ float s_cmax[2][kThreads / 64];
+  __shared__ float s_red[kThreads / 64];
+  __shared__ SamplePart s_best[kThreads / 64];
+  float M = -FLT_MAX, z = 0.f;
+  float key = -INFINITY, key2 = -INFINITY, lx = 0.f;
+  int idx = INT_MAX;
+  const int npass = (end - beg + kChunk - 1) / kChunk;
+  Chunk<T> cur, nxt;
+  cur.load(x, beg, end, vec_ok);
+  for (int k = 0; k < npass; ++k) {
+    const int cb = beg + k * kChunk;
+    if (k + 1 < npass) nxt.load(x, cb + kChunk, end, vec_ok);
+    float tm = -FLT_MAX;
 #pragma unroll
-  for (int i = 0; i < kSamplePerThread; ++i) {
-    if (v[i] >= thr && v[i] != -INFINITY) {
-      const int t = beg + 8 * (tid + kThreads * (i >> 3)) + (i & 7);
-      const float sc = v[i] + tau * gumbel32(noise_word(rk, t));
-      merge_best(key, key2, idx, lx, sc, -INFINITY, t, v[i]);
+    for (int i = 0; i < kPerThread; ++i) tm = fmaxf(tm, cur.get(i));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tm = fmaxf(tm, __shfl_xor(tm, off));
+    // two slots, alternating: a slot is rewritten only after the next
+    // barrier, which every thread passes after reading it
+    if (lane == 0) s_cmax[k & 1][wave] = tm;
+    __syncthreads();
+    const float C = fmaxf(fmaxf(s_cmax[k & 1][0], s_cmax[k & 1][1]),
+                          fmaxf(s_cmax[k & 1][2], s_cmax[k & 1][3]));
+    if (C > M) {   // workgroup-uniform
+      z *= fast_exp2((M - C) * c);
+      M = C;
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = fast_exp2((cur.get(8 * u + j) - M) * c);
+      z += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    }
+    // a bit per candidate, then one loop body for all of them (the logit is
+    // read again -- from the cache, it was just loaded -- rather than
+    // indexed out of the registers)
+    const float thr = M - cand_margin(M, tau);
+    uint32_t cand = 0;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const float v = cur.get(i);
+      cand |= (v >= thr && v != -INFINITY) ? (1u << i) : 0u;
+    }
+    while (cand) {
+      const int i = __builtin_ctz(cand);
+      cand &= cand - 1;
+      const int t = cb + 8 * (tid + kThreads * (i >> 3)) + (i & 7);
+      const float l = load1(x, t);
+      const float sc = l + tau * gumbel32(noise_word(rk, t));
+      merge_best(key, key2, idx, lx, sc, -INFINITY, t, l);
+    }
+    cur = nxt;
   }
   // fixed-shape trees: Z and the best pair over the wave, then the four waves
 #pragma unroll
@@ -323,10 +402,9 @@ __global__ __launch_bounds__(kThreads) void rowsample_kernel(
     const int oi = __shfl_xor(idx, off);
     merge_best(key, key2, idx, lx, ok, ok2, oi, ol);
   }
-  __syncthreads();
   if (lane == 0) {
     s_red[wave] = z;
-    s_best[wave] = SamplePart{m, z, key, key2, idx, lx, 0, 0};
+    s_best[wave] = SamplePart{M, z, key, key2, idx, lx, 0, 0};
   }
   __syncthreads();
   if (tid == 0) {
@@ -348,8 +426,7 @@ __device__ void rescore_row64(const T* x, int V, float m, float tau, double tau6
   const float thr = m - cand_margin(m, tau);
   double best = -INFINITY;
   int bi = INT_MAX;
-  for (int t = threadIdx.x; t < V; t += kThreads) {
-    const float l = load1(x, t);
+  auto visit = [&](float l, int t) {
     if (l >= thr && l != -INFINITY) {
       const double sc = static_cast<double>(l) + tau64 * gumbel64(noise_word(nk, t));
       if (sc > best || (sc == best && t < bi)) {
@@ -357,7 +434,32 @@ __device__ void rescore_row64(const T* x, int V, float m, float tau, double tau6
         bi = t;
       }
     }
+  };
+  // scalar head up to 16-byte alignment, then groups of 8 logits (four
+  // 16-byte loads in flight per thread: the scan is a full read of the row),
+  // then a scalar tail
+  const int head = min(V, static_cast<int>(((16 - reinterpret_cast<uintptr_t>(x) % 16) % 16) / sizeof(T)));
+  if (static_cast<int>(threadIdx.x) < head) visit(load1(x, threadIdx.x), threadIdx.x);
+  const int nvec = (V - head) / 8;
+  int j = threadIdx.x;
+  for (; j + 3 * kThreads < nvec; j += 4 * kThreads) {
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8<T>(x, head + 8 * static_cast<int64_t>(j + u * kThreads), v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float g = fmaxf(fmaxf(fmaxf(v[u][0], v[u][1]), fmaxf(v[u][2], v[u][3])),
+                      fmaxf(fmaxf(v[u][4], v[u][5]), fmaxf(v[u][6], v[u][7])));
+      if (g >= thr)
+        for (int k = 0; k < 8; ++k) visit(v[u][k], head + 8 * (j + u * kThreads) + k);
+    }
   }
+  for (; j < nvec; j += kThreads) {
+    float v[8];
+    load8<T>(x, head + 8 * static_cast<int64_t>(j), v);
+    for (int k = 0; k < 8; ++k) visit(v[k], head + 8 * j + k);
+  }
+  for (int t = head + 8 * nvec + threadIdx.x; t < V; t += kThreads) visit(load1(x, t), t);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const double ob = __shfl_xor(best, off);
@@ -473,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
       s_pred[tid] = idx;
       s_p[tid] = static_cast<double>(fast_exp2((lx - m) * c) / z);
       // the fp32 scores of the two best can be off by far less than this band
-      s_rescore[tid] = (key - key2) <= kDelta * (1.f + fabsf(m) + kGumbelSpread * tau);
+      s_rescore[tid] = (key - key2) <= kKeyBand * (1.f + fabsf(m) + kGumbelSpread * tau);
     }
   }
   __syncthreads();
@@ -580,7 +682,7 @@ UnmaskPlan unmask_plan(int B, int S, int V) {
   if (len < 2048) len = 2048;
   p.split_len = static_cast<int>(len);
   p.splits = static_cast<int>(ceil_div(V, len));
-  p.s_splits = static_cast<int>(ceil_div(V, kSampleSlice));
+  p.s_splits = p.splits;   // the sampling pass streams the same slices
   p.part_bytes = align_up(static_cast<size_t>(rows) * p.splits * sizeof(RowPart), 256);
   p.s_part_bytes = align_up(static_cast<size_t>(rows) * p.s_splits * sizeof(SamplePart), 256);
   p.total_bytes = p.part_bytes > p.s_part_bytes ? p.part_bytes : p.s_part_bytes;
@@ -608,7 +710,8 @@ void launch_unmask_t(const UnmaskArgs& a, const UnmaskPlan& p, void* ws, int vec
   } else {
     SamplePart* part = static_cast<SamplePart*>(ws);
     hipLaunchKernelGGL(rowsample_kernel<T>, dim3(p.s_splits, a.B * a.S), blk, 0, st, x,
-                       a.row_stride, a.V, a.masked, c, a.temperature, nk, p.s_splits, vec, part);
+                       a.row_stride, a.V, a.masked, c, a.temperature, nk, p.split_len, p.s_splits,
+                       vec, part);
     hipLaunchKernelGGL((decide_kernel<T, true>), dim3(a.B), blk, 0, st, x, a.row_stride, a.S, a.V,
                        static_cast<const void*>(part), p.s_splits, c, a.gamma, a.temperature,
                        tau64, nk, a.mask_id, a.step, a.tokens, a.masked, a.committed_now, a.conf,

@@ -290,7 +290,7 @@ tt_status tt_confidence_unmask(int32_t batch, int32_t block_size, int32_t vocab,
  *          / sum_v exp((logits[b, s, v] - max) / temperature)
  * and then the commit rule of tt_confidence_unmask, unchanged (gamma <= 0
  * commits every masked slot).  Decisions are exact with respect to fp64:
- * rows whose two best perturbed scores lie within 2^-14 (1 + |max| +
+ * rows whose two best perturbed scores lie within 2^-17 (1 + |max| +
  * 20 temperature) are rescored in fp64, and p is rechecked in fp64 near
  * gamma as in tt_confidence_unmask.
  * Arguments, layouts and errors are those of tt_confidence_unmask, plus
