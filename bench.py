@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="ctx8k", choices=["ctx8k", "ragged64", "batch128"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the per-row timings after the timed region (counter runs)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=24)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (its "
@@ -111,9 +113,9 @@ def summarize_counters(fetch_csv, write_csv):
            "hbm_bytes_per_launch": int(round(total)),
            "commands": [
                "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmc_fetch -o p -- "
-               "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calib-copy-mb 1024",
+               "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-rows --calib-copy-mb 1024",
                "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmc_write -o p -- "
-               "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --calib-copy-mb 1024"]}
+               "python -u bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-rows --calib-copy-mb 1024"]}
     with open(COUNTERS_JSON, "w") as fh:
         json.dump(out, fh, indent=1)
         fh.write("\n")
@@ -275,32 +277,35 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) / ROW_REPS * 1e3   # us per call
-    base = args.warmup + args.steps
-    us_ada = timed(lambda r: (tt.timestep_embed(B, t_step, emb),
-                              tt.adaln_single(B, W, NL, emb, ada_w, ada_b, ada_t, ada)))
-    us_sample = timed(lambda r: tt.sample_unmask(
-        B, S, V, logits, V, w["gamma"], 0.1, 2024, 0, 3, 0, tokens_all[base + 1 + r],
-        masked_all[base + 1 + r], uws, n_masked=n_masked))
-    # fresh states again for the argmax row
-    tokens_all[base:].fill_(3)
-    masked_all[base:].fill_(1)
-    us_unmask = timed(lambda r: tt.confidence_unmask(
-        B, S, V, logits, V, w["gamma"], w["tau"], 3, 0, tokens_all[base + 1 + r], masked_all[base + 1 + r],
-        uws, n_masked=n_masked))
-    # context-tower row: the six layers' causal attention over [context ;
-    # committed block] with the append of the block's K/V into the room after
-    # each context (ctx_len is left alone, so every repetition is the same
-    # work), then the length update on a copy of the lengths
-    us_ctx = timed(lambda r: [tt.ctx_block_attn(shape, qb[l], kb[l], vb[l], kc[l], vc[l], start,
-                                                clen, max_len, out, aws, ctx_end=ctx_end)
-                              for l in range(NL)]) / NL
-    clen2 = clen.clone()
-    appended = torch.empty((B,), dtype=torch.uint8, device=dev)
-    us_adv = timed(lambda r: (clen2.copy_(clen), tt.ctx_advance(B, S, start, ctx_end, clen2,
-                                                                appended=appended)))
-    assert int(appended.sum().item()) == B and clen2.tolist() == [L + S for L in lens]
-    loop = denoise_loop(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, clen)
-    gen = generate_row(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, ctx_end, clen)
+    def collect_rows():
+        base = args.warmup + args.steps
+        us_ada = timed(lambda r: (tt.timestep_embed(B, t_step, emb),
+                                  tt.adaln_single(B, W, NL, emb, ada_w, ada_b, ada_t, ada)))
+        us_sample = timed(lambda r: tt.sample_unmask(
+            B, S, V, logits, V, w["gamma"], 0.1, 2024, 0, 3, 0, tokens_all[base + 1 + r],
+            masked_all[base + 1 + r], uws, n_masked=n_masked))
+        # fresh states again for the argmax row
+        tokens_all[base:].fill_(3)
+        masked_all[base:].fill_(1)
+        us_unmask = timed(lambda r: tt.confidence_unmask(
+            B, S, V, logits, V, w["gamma"], w["tau"], 3, 0, tokens_all[base + 1 + r], masked_all[base + 1 + r],
+            uws, n_masked=n_masked))
+        # context-tower row: the six layers' causal attention over [context ;
+        # committed block] with the append of the block's K/V into the room after
+        # each context (ctx_len is left alone, so every repetition is the same
+        # work), then the length update on a copy of the lengths
+        us_ctx = timed(lambda r: [tt.ctx_block_attn(shape, qb[l], kb[l], vb[l], kc[l], vc[l], start,
+                                                    clen, max_len, out, aws, ctx_end=ctx_end)
+                                  for l in range(NL)]) / NL
+        clen2 = clen.clone()
+        appended = torch.empty((B,), dtype=torch.uint8, device=dev)
+        us_adv = timed(lambda r: (clen2.copy_(clen), tt.ctx_advance(B, S, start, ctx_end, clen2,
+                                                                    appended=appended)))
+        assert int(appended.sum().item()) == B and clen2.tolist() == [L + S for L in lens]
+        loop = denoise_loop(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, clen)
+        gen = generate_row(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, ctx_end, clen)
+        return us_ada, us_sample, us_unmask, us_ctx, us_adv, loop, gen
+    rows_data = None if args.no_rows else collect_rows()
     ms = t0.elapsed_time(t1) / args.steps
     bounds = step_events + [t1]
     step_ms = [a.elapsed_time(b) for a, b in zip(bounds[:-1], bounds[1:])]
@@ -352,19 +357,21 @@ def main():
         gbps = nbytes / (us * 1e-6) / 1e9
         return {"calls": what, "us_per_call": round(us, 2), "bytes": nbytes,
                 "gbps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
-    result["rows"] = {
-        "a8_denoise_loop": loop,
-        "a1_timestep_adaln": row(us_ada, ada_bytes, "tt_timestep_embed + tt_adaln_single"),
-        "a2_a5_block_attn": row(attn_avg * 1e3, per_launch, "tt_block_attn (timed region)"),
-        "a6_a7_unmask": row(us_unmask, unmask_bytes, "tt_confidence_unmask, all rows masked"),
-        "f2_sample_unmask": row(us_sample, unmask_bytes,
-                                "tt_sample_unmask at temperature 0.1, all rows masked"),
-        "f2_generate": gen,
-        "f1_ctx_commit_attn": row(us_ctx, ctx_bytes,
-                                  "tt_ctx_block_attn with the cache append, per layer"),
-        "f1_ctx_advance": {"calls": "tt_ctx_advance + a 4*B-byte length reset copy",
-                           "us_per_call": round(us_adv, 2)},
-    }
+    if rows_data is not None:
+        us_ada, us_sample, us_unmask, us_ctx, us_adv, loop, gen = rows_data
+        result["rows"] = {
+            "a8_denoise_loop": loop,
+            "a1_timestep_adaln": row(us_ada, ada_bytes, "tt_timestep_embed + tt_adaln_single"),
+            "a2_a5_block_attn": row(attn_avg * 1e3, per_launch, "tt_block_attn (timed region)"),
+            "a6_a7_unmask": row(us_unmask, unmask_bytes, "tt_confidence_unmask, all rows masked"),
+            "f2_sample_unmask": row(us_sample, unmask_bytes,
+                                    "tt_sample_unmask at temperature 0.1, all rows masked"),
+            "f2_generate": gen,
+            "f1_ctx_commit_attn": row(us_ctx, ctx_bytes,
+                                      "tt_ctx_block_attn with the cache append, per layer"),
+            "f1_ctx_advance": {"calls": "tt_ctx_advance + a 4*B-byte length reset copy",
+                               "us_per_call": round(us_adv, 2)},
+        }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs, kc, vc, qb, kb, vb, ada,
                                               logits, start)
