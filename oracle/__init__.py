@@ -46,6 +46,11 @@ What is pinned, and how (tests/test_oracle_*.py):
                     holding the provider's K/V of every generated block in
                     order; the next block's attention equal to attention over
                     the explicit concatenation; every generated slot final.
+  Mamba-2 seed   -- the recurrence equals the state-space duality's quadratic
+                    form; context-then-seeded-block equals one scan of the
+                    concatenation from zero states; the convolution against
+                    numpy.convolve; closed forms (instant decay, zero step);
+                    causality inside the block; brute force.
   adaLN-single   -- SiLU(0)=0, sinusoid special values, scalar-loop brute
                     force of the affine map.  The PLACEMENT of scale/shift/gate
                     and the timestep definition are readings the pages do not
@@ -76,3 +81,8 @@ from .sampling import (  # noqa: F401
     row_sample,
 )
 from .generate import generate  # noqa: F401
+from .mamba import (  # noqa: F401
+    causal_conv,
+    mamba_block_scan,
+    mamba_dual_form,
+)

@@ -10,12 +10,14 @@ import oracle
 import oracle.attention as attention_src
 import oracle.context as context_src
 import oracle.generate as generate_src
+import oracle.mamba as mamba_src
 import oracle.sampling as sampling_src
 import oracle.unmask as unmask_src
 
 from . import test_oracle_attention as TA
 from . import test_oracle_context as TC
 from . import test_oracle_generate as TG
+from . import test_oracle_mamba as TM
 from . import test_oracle_sampling as TS
 from . import test_oracle_unmask as TU
 
@@ -104,6 +106,28 @@ GENERATE_MUTANTS = [
     ("            kc[layer], vc[layer], _ = kv_append(", "            _, _, _ = kv_append("),  # no append
 ]
 
+MAMBA_PINS = [TM.test_m1_scan_equals_dual_form, TM.test_m2_seeded_block_equals_scan_of_concatenation,
+              TM.test_m3_conv_against_numpy, TM.test_m4_closed_forms, TM.test_m5_brute_force_tiny,
+              TM.test_m6_causal_in_block]
+
+MAMBA_MUTANTS = [
+    ("g = h // (H // G)\n            st = _f64(ssm_state[b, h]).copy()",
+     "g = h % G\n            st = _f64(ssm_state[b, h]).copy()"),             # wrong group map
+    ("y[b, s, h] = st @ Cm[s, g] + _f64(D)[h] * x[s, h]", "y[b, s, h] = st @ Cm[s, g]"),  # no skip
+    ("dt = softplus(_f64(dt_raw[b]) + _f64(dt_bias)[None, :])          # [S, H]",
+     "dt = softplus(_f64(dt_raw[b]))          # [S, H]"),                      # dt bias dropped
+    ("out[s] = (u[s:s + W] * w.T).sum(axis=0) + b", "out[s] = (u[s:s + W][::-1] * w.T).sum(axis=0) + b"),
+    ("st = np.exp(dt[s, h] * A[h]) * st + dt[s, h] * np.outer(x[s, h], Bm[s, g])",
+     "st = np.exp(A[h]) * st + dt[s, h] * np.outer(x[s, h], Bm[s, g])"),      # decay without dt
+    ("st = np.exp(dt[s, h] * A[h]) * st + dt[s, h] * np.outer(x[s, h], Bm[s, g])",
+     "st = np.exp(dt[s, h] * A[h]) * st + np.outer(x[s, h], Bm[s, g])"),      # input without dt
+    ("st = _f64(ssm_state[b, h]).copy()", "st = 0.0 * _f64(ssm_state[b, h])"),  # seed ignored
+    ("u = np.concatenate([cs.T, xbc], axis=0)", "u = np.concatenate([0 * cs.T, xbc], axis=0)"),  # conv seed ignored
+    ("return silu(out), u[S:].T.copy()", "return out, u[S:].T.copy()"),      # SiLU dropped
+    ("A = -np.exp(_f64(A_log))\n    y = np.empty((Bn, S, H, P))\n    new_conv",
+     "A = np.exp(_f64(A_log))\n    y = np.empty((Bn, S, H, P))\n    new_conv"),  # growing state
+]
+
 UNMASK_MUTANTS = [
     ("conf[b, s] >= g or", "conf[b, s] > g or"),                # exclusive threshold
     ("np.flatnonzero(x == m)[0]", "np.flatnonzero(x == m)[-1]"),  # highest id on ties
@@ -166,6 +190,14 @@ def test_generate_mutant_is_caught(monkeypatch, old, new):
     mod = _mutant(generate_src, old, new)
     monkeypatch.setattr(oracle, "generate", mod.generate)
     assert _caught(GENERATE_PINS)
+
+
+@pytest.mark.parametrize("old,new", MAMBA_MUTANTS)
+def test_mamba_mutant_is_caught(monkeypatch, old, new):
+    mod = _mutant(mamba_src, old, new)
+    for name in ("softplus", "silu", "causal_conv", "mamba_block_scan"):
+        monkeypatch.setattr(mamba_src, name, getattr(mod, name))
+    assert _caught(MAMBA_PINS)
 
 
 @pytest.mark.parametrize("old,new", UNMASK_MUTANTS)
