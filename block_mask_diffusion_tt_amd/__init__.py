@@ -7,7 +7,8 @@ from ._binding import *  # noqa: F401,F403
 from ._binding import (AttnShape, StepProvider, TTError, abi_version, adaln_single,  # noqa: F401
                        attn_shape, block_attn, block_attn_workspace_size, confidence_unmask,
                        ctx_advance, ctx_block_attn, sample_unmask, generate,
-                       generate_workspace_size, GenProvider,
+                       generate_workspace_size, GenProvider, mamba_shape, mamba_block_scan,
+                       MambaShape,
                        denoise_block, denoise_workspace_size, dtype_code, last_error, lib,
                        timestep_embed, unmask_workspace_size, workspace_clear, EXPORTED,
                        LIB_PATH, TT_BF16, TT_F32)

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtt.so")
-SOURCES = ["attn.hip", "unmask.hip", "adaln.hip", "context.hip", "tt_api.hip"]
+SOURCES = ["attn.hip", "unmask.hip", "adaln.hip", "context.hip", "mamba.hip", "tt_api.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are disabled for every device pass.

@@ -207,6 +207,65 @@ tt_status tt_ctx_block_attn(const tt_attn_shape* shape, const void* q_blk, const
                            nullptr, residual, out, lse, 1, workspace, workspace_bytes, stream);
 }
 
+tt_status tt_mamba_block_scan(const tt_mamba_shape* shape, const void* xbc, const float* dt_raw,
+                              const void* conv_state, const float* ssm_state,
+                              const float* conv_w, const float* conv_b, const float* A_log,
+                              const float* dt_bias, const float* D, const uint8_t* active,
+                              void* y, void* conv_state_out, float* ssm_state_out,
+                              tt_stream stream) {
+  const char* fn = "tt_mamba_block_scan";
+  if (!shape) return fail(TT_ERR_INVALID_ARG, "%s: shape is NULL", fn);
+  const tt_mamba_shape& m = *shape;
+  if (m.batch < 0 || m.n_heads < 1 || m.n_groups < 1 || m.head_dim < 1 || m.d_state < 1)
+    return fail(TT_ERR_INVALID_ARG, "%s: bad sizes (B=%d H=%d G=%d P=%d N=%d)", fn, m.batch,
+                m.n_heads, m.n_groups, m.head_dim, m.d_state);
+  if (m.n_heads % m.n_groups != 0)
+    return fail(TT_ERR_INVALID_ARG, "%s: n_groups %d does not divide n_heads %d", fn, m.n_groups,
+                m.n_heads);
+  if (m.conv_width < 2 || m.conv_width > 8)
+    return fail(TT_ERR_INVALID_ARG, "%s: conv_width %d outside [2, 8]", fn, m.conv_width);
+  if (m.block_size < 1 || m.block_size > 64)
+    return fail(TT_ERR_INVALID_ARG, "%s: block_size %d outside [1, 64]", fn, m.block_size);
+  if (m.dtype != TT_BF16 && m.dtype != TT_F32)
+    return fail(TT_ERR_INVALID_ARG, "%s: dtype %d is neither TT_BF16 nor TT_F32", fn, m.dtype);
+  if (!tt::mamba_supported(m.head_dim, m.d_state))
+    return fail(TT_ERR_UNSUPPORTED, "%s: head_dim %d / d_state %d not supported (32 or 64 / 64 or 128)",
+                fn, m.head_dim, m.d_state);
+  if (static_cast<int64_t>(m.n_heads) * m.head_dim + 2LL * m.n_groups * m.d_state > INT32_MAX / 64)
+    return fail(TT_ERR_INVALID_ARG, "%s: too many channels", fn);
+  if (!xbc || !dt_raw || !conv_state || !ssm_state || !conv_w || !A_log || !y)
+    return fail(TT_ERR_INVALID_ARG, "%s: xbc, dt_raw, conv_state, ssm_state, conv_w, A_log and y must be non-NULL", fn);
+  if (!aligned(ssm_state, 16) || (ssm_state_out && !aligned(ssm_state_out, 16)))
+    return fail(TT_ERR_INVALID_ARG, "%s: ssm_state buffers must be 16-byte aligned", fn);
+  const size_t e = elt_size(m.dtype);
+  const void* ptrs[] = {xbc, conv_state, y, conv_state_out};
+  for (const void* t : ptrs)
+    if (t && !aligned(t, e)) return fail(TT_ERR_INVALID_ARG, "%s: misaligned xbc/conv_state/y buffer", fn);
+  const void* fptrs[] = {dt_raw, conv_w, conv_b, A_log, dt_bias, D};
+  for (const void* t : fptrs)
+    if (t && !aligned(t, 4)) return fail(TT_ERR_INVALID_ARG, "%s: misaligned fp32 parameter", fn);
+  if (conv_state_out) {
+    const size_t C = static_cast<size_t>(m.n_heads) * m.head_dim + 2 * static_cast<size_t>(m.n_groups) * m.d_state;
+    const size_t bytes = static_cast<size_t>(m.batch) * C * (m.conv_width - 1) * e;
+    const char* a0 = static_cast<const char*>(conv_state);
+    const char* b0 = static_cast<const char*>(conv_state_out);
+    if (a0 < b0 + bytes && b0 < a0 + bytes)
+      return fail(TT_ERR_INVALID_ARG, "%s: conv_state_out overlaps conv_state", fn);
+  }
+  if (tt::mamba_lds_bytes(m.block_size, m.head_dim, m.d_state) > 160 * 1024)
+    return fail(TT_ERR_UNSUPPORTED, "%s: block too long for the LDS staging", fn);
+  if (m.batch == 0) return ok();
+  tt::MambaArgs a{};
+  a.B = m.batch; a.S = m.block_size; a.H = m.n_heads; a.P = m.head_dim; a.N = m.d_state;
+  a.G = m.n_groups; a.W = m.conv_width; a.dtype = m.dtype;
+  a.xbc = xbc; a.dt_raw = dt_raw; a.conv_state = conv_state; a.ssm_state = ssm_state;
+  a.conv_w = conv_w; a.conv_b = conv_b; a.A_log = A_log; a.dt_bias = dt_bias; a.D = D;
+  a.active = active; a.y = y; a.conv_state_out = conv_state_out; a.ssm_state_out = ssm_state_out;
+  const hipError_t he = tt::launch_mamba_scan(a, static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, fn);
+  return ok();
+}
+
 tt_status tt_ctx_advance(int32_t batch, int32_t block_size, const int64_t* ctx_start,
                          const int64_t* ctx_end, int32_t* ctx_len, const uint8_t* active,
                          uint8_t* appended, tt_stream stream) {

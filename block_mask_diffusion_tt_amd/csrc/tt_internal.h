@@ -80,6 +80,22 @@ UnmaskPlan unmask_plan(int B, int S, int V);
 hipError_t launch_confidence_unmask(const UnmaskArgs& a, const UnmaskPlan& p, void* ws,
                                     hipStream_t st);
 
+// ---------------------------------------------------------------- Mamba-2
+// One layer's mixer over a block, seeded with the context's states
+// (csrc/mamba.hip).  Channels of xbc: x (H*P), then B (G*N), then C (G*N).
+struct MambaArgs {
+  int B, S, H, P, N, G, W, dtype;
+  const void* xbc; const float* dt_raw;
+  const void* conv_state; const float* ssm_state;
+  const float* conv_w; const float* conv_b; const float* A_log; const float* dt_bias;
+  const float* D; const uint8_t* active;
+  void* y; void* conv_state_out; float* ssm_state_out;
+};
+
+bool mamba_supported(int P, int N);
+size_t mamba_lds_bytes(int S, int P, int N);
+hipError_t launch_mamba_scan(const MambaArgs& a, hipStream_t st);
+
 // ---------------------------------------------------------------- adaLN
 hipError_t launch_timestep_embed(int B, const float* t, const int32_t* n_masked, int S,
                                  float* emb, hipStream_t st);

@@ -429,6 +429,60 @@ tt_status tt_generate(const tt_attn_shape* shape, int32_t n_layers, int32_t n_bl
                       int32_t* blocks_taken, void* workspace, size_t workspace_bytes,
                       tt_stream stream);
 
+/* ------------------------------------------------------------------------
+ * tt_mamba_block_scan -- one Mamba-2 layer's sequence mixer over a block of
+ * S slots, seeded with the context tower's conv and SSM boundary states.
+ *
+ * [dothoosh] two-tower mechanism section: the context tower produces every
+ * layer's KV cache and final Mamba-2 states; the denoiser's Mamba-2 layers
+ * take their initial state directly from the context tower's Mamba state.
+ * [modelcard] notes: the seeding injects the context tower's conv/SSM
+ * boundary states as the initial states of the denoiser's Mamba layers,
+ * causally (no future leakage).  The mixer is the published Mamba-2 one
+ * (T. Dao, A. Gu, "Transformers are SSMs", ICML 2024); the pages give no
+ * layer sizes.
+ *
+ * For sequence b, with u = [conv_state[b] ; xbc[b]] along the slots:
+ *   v[s, c]  = SiLU(sum_{j<W} conv_w[c, j] u[s + j, c] + conv_b[c])
+ *   x, B, C  = channels [0, H*P), [H*P, H*P+G*N), [H*P+G*N, C) of v
+ *   dt[s, h] = softplus(dt_raw[b, s, h] + dt_bias[h]),  A[h] = -exp(A_log[h])
+ *   Hs       = exp(dt A[h]) H{s-1} + dt x[s, h] B[s, g]^T   (H0 = ssm_state[b, h])
+ *   y[b, s, h*P + p] = sum_n Hs[p, n] C[s, g, n] + D[h] x[s, h, p]
+ * with g = h / (H/G).  The denoiser reads the seed (NULL outputs); the
+ * context tower taking a committed block passes ssm_state_out (may alias
+ * ssm_state: the final H) and conv_state_out (must not overlap conv_state:
+ * the last W-1 rows of u).
+ *   shape: batch B, n_heads H, head_dim P in {32, 64}, d_state N in
+ *          {64, 128}, n_groups G (divides H), conv_width W in [2, 8],
+ *          block_size S in [1, 64], dtype of xbc / conv states / y.
+ *   xbc [B, S, C] and y [B, S, H*P] (dtype), C = H*P + 2*G*N;
+ *   dt_raw [B, S, H] fp32; conv_state [B, C, W-1] (dtype);
+ *   ssm_state [B, H, P, N] fp32 (16-byte aligned);
+ *   conv_w [C, W], conv_b [C] or NULL, A_log [H], dt_bias [H] or NULL,
+ *   D [H] or NULL: fp32;  active [B] uint8 or NULL (inactive: untouched).
+ * All device pointers.  fp32 arithmetic throughout; y rounded to nearest
+ * even for bf16.  Errors: TT_ERR_INVALID_ARG (NULL required pointer, bad
+ * sizes, G not dividing H, misaligned state), TT_ERR_UNSUPPORTED (P or N
+ * outside the sets above), TT_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch;
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t d_state;
+  int32_t n_groups;
+  int32_t conv_width;
+  int32_t block_size;
+  int32_t dtype;
+} tt_mamba_shape;
+
+tt_status tt_mamba_block_scan(const tt_mamba_shape* shape, const void* xbc, const float* dt_raw,
+                              const void* conv_state, const float* ssm_state,
+                              const float* conv_w, const float* conv_b, const float* A_log,
+                              const float* dt_bias, const float* D, const uint8_t* active,
+                              void* y, void* conv_state_out, float* ssm_state_out,
+                              tt_stream stream);
+
 #ifdef __cplusplus
 }
 #endif
