@@ -304,7 +304,13 @@ def main():
         assert int(appended.sum().item()) == B and clen2.tolist() == [L + S for L in lens]
         loop = denoise_loop(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, clen)
         gen = generate_row(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, ctx_end, clen)
-        return us_ada, us_sample, us_unmask, us_ctx, us_adv, loop, gen
+        # Mamba-2 seeded block scan (one layer): the denoiser's form (reads the
+        # seed) and the context tower's (also writes the final states)
+        mb = mamba_inputs(tt, B, S)
+        us_mamba = timed(lambda r: tt.mamba_block_scan(*mb["args"], **mb["kw"]))
+        us_mamba_ctx = timed(lambda r: tt.mamba_block_scan(
+            *mb["args"], **mb["kw"], conv_state_out=mb["cso"], ssm_state_out=mb["sso"]))
+        return us_ada, us_sample, us_unmask, us_ctx, us_adv, loop, gen, us_mamba, us_mamba_ctx, mb
     rows_data = None if args.no_rows else collect_rows()
     ms = t0.elapsed_time(t1) / args.steps
     bounds = step_events + [t1]
@@ -358,7 +364,7 @@ def main():
         return {"calls": what, "us_per_call": round(us, 2), "bytes": nbytes,
                 "gbps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
     if rows_data is not None:
-        us_ada, us_sample, us_unmask, us_ctx, us_adv, loop, gen = rows_data
+        us_ada, us_sample, us_unmask, us_ctx, us_adv, loop, gen, us_mamba, us_mamba_ctx, mb = rows_data
         result["rows"] = {
             "a8_denoise_loop": loop,
             "a1_timestep_adaln": row(us_ada, ada_bytes, "tt_timestep_embed + tt_adaln_single"),
@@ -371,6 +377,11 @@ def main():
                                       "tt_ctx_block_attn with the cache append, per layer"),
             "f1_ctx_advance": {"calls": "tt_ctx_advance + a 4*B-byte length reset copy",
                                "us_per_call": round(us_adv, 2)},
+            "f4_mamba_scan": dict(row(us_mamba, mb["bytes"], "tt_mamba_block_scan, seed read "
+                                      "(denoiser), one layer"), shape=mb["desc"]),
+            "f4_mamba_scan_ctx": row(us_mamba_ctx, mb["bytes_ctx"],
+                                     "tt_mamba_block_scan with the final states written "
+                                     "(context tower), one layer"),
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs, kc, vc, qb, kb, vb, ada,
@@ -420,6 +431,43 @@ def denoise_loop(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, 
     return {"calls": "tt_denoise_block, all slots masked, up to S steps", "steps": steps,
             "masked_left": left, "ms_per_loop": round(sec * 1e3, 3),
             "ms_per_step": round(sec * 1e3 / max(steps, 1), 4)}
+
+
+MAMBA = dict(H=64, P=64, N=128, G=8, W=4)   # assumed layer sizes (the pages give none)
+
+
+def mamba_inputs(tt, B, S):
+    """Seeded synthetic inputs of one Mamba-2 layer's block scan at the bench's
+    batch and block: 64 heads of 64 channels, d_state 128, 8 groups, conv
+    width 4 (bf16 activations and conv state, fp32 SSM state and parameters)."""
+    import torch
+
+    import synth
+    H, P, N, G, W = (MAMBA[k] for k in ("H", "P", "N", "G", "W"))
+    C = H * P + 2 * G * N
+    dev, bf, f32 = "cuda", torch.bfloat16, torch.float32
+    xbc = synth.normal((B, S, C), 1.0, 801, bf, dev)
+    dt_raw = synth.normal((B, S, H), 1.0, 802, f32, dev) - 1.0
+    cs = synth.normal((B, C, W - 1), 1.0, 803, bf, dev)
+    ss = synth.normal((B, H, P, N), 1.0, 804, f32, dev)
+    conv_w = synth.normal((C, W), 0.5, 805, f32, dev)
+    conv_b = synth.normal((C,), 0.1, 806, f32, dev)
+    A_log = torch.log(torch.linspace(1.0, 16.0, H, device=dev))
+    dt_bias = synth.normal((H,), 0.3, 807, f32, dev)
+    D = synth.normal((H,), 1.0, 808, f32, dev)
+    y = torch.empty((B, S, H * P), dtype=bf, device=dev)
+    shape = tt.mamba_shape(B, H, P, N, G, W, S, bf)
+    state = B * H * P * N * 4
+    conv_state = B * C * (W - 1) * 2
+    rest = B * S * C * 2 + B * S * H * 4 + B * S * H * P * 2 + C * W * 4 + C * 4 + 3 * H * 4
+    ws = torch.empty(tt.mamba_workspace_size(shape), dtype=torch.uint8, device=dev)
+    return {"args": (shape, xbc, dt_raw, cs, ss, conv_w, A_log, y, ws),
+            "kw": dict(conv_b=conv_b, dt_bias=dt_bias, D=D),
+            # the context tower's form writes its states to second buffers
+            "cso": torch.empty_like(cs), "sso": torch.empty_like(ss),
+            "bytes": state + conv_state + rest,
+            "bytes_ctx": 2 * state + 2 * conv_state + rest,
+            "desc": {"batch": B, "block": S, **MAMBA, "dtype": "bf16 (fp32 state)"}}
 
 
 def generate_row(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, ctx_end, clen):

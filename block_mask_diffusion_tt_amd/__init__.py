@@ -8,6 +8,7 @@ from ._binding import (AttnShape, StepProvider, TTError, abi_version, adaln_sing
                        attn_shape, block_attn, block_attn_workspace_size, confidence_unmask,
                        ctx_advance, ctx_block_attn, sample_unmask, generate,
                        generate_workspace_size, GenProvider, mamba_shape, mamba_block_scan,
+                       mamba_workspace_size,
                        MambaShape,
                        denoise_block, denoise_workspace_size, dtype_code, last_error, lib,
                        timestep_embed, unmask_workspace_size, workspace_clear, EXPORTED,

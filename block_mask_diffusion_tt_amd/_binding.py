@@ -28,7 +28,8 @@ EXPORTED = ["tt_last_error", "tt_abi_version", "tt_block_attn_workspace_size", "
             "tt_workspace_clear", "tt_timestep_embed", "tt_adaln_single",
             "tt_unmask_workspace_size", "tt_confidence_unmask", "tt_denoise_workspace_size",
             "tt_denoise_block", "tt_ctx_block_attn", "tt_ctx_advance", "tt_sample_unmask",
-            "tt_generate_workspace_size", "tt_generate", "tt_mamba_block_scan"]
+            "tt_generate_workspace_size", "tt_generate", "tt_mamba_workspace_size",
+            "tt_mamba_block_scan"]
 
 
 class TTError(RuntimeError):
@@ -103,8 +104,9 @@ def _load():
                                             vp]),
         "tt_denoise_workspace_size": (sz, [shp, i32, i32, i32]),
         "tt_generate_workspace_size": (sz, [shp, i32, i32, i32, i32]),
+        "tt_mamba_workspace_size": (sz, [ctypes.POINTER(MambaShape)]),
         "tt_mamba_block_scan": (ctypes.c_int, [ctypes.POINTER(MambaShape), vp, vp, vp, vp, vp, vp,
-                                               vp, vp, vp, vp, vp, vp, vp, vp]),
+                                               vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "tt_generate": (ctypes.c_int, [shp, i32, i32, i32, f32, f32, i32, ctypes.c_uint64, i32,
                                        i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                        ctypes.POINTER(GenProvider), vp, vp, vp,
@@ -417,10 +419,18 @@ def mamba_shape(batch, n_heads, head_dim, d_state, n_groups, conv_width, block_s
     return MambaShape(batch, n_heads, head_dim, d_state, n_groups, conv_width, block_size, code)
 
 
-def mamba_block_scan(shape, xbc, dt_raw, conv_state, ssm_state, conv_w, A_log, y, conv_b=None,
-                     dt_bias=None, D=None, active=None, conv_state_out=None, ssm_state_out=None,
-                     stream=None):
+def mamba_workspace_size(shape):
+    n = _lib.tt_mamba_workspace_size(ctypes.byref(shape))
+    if n == 0:
+        raise TTError(TT_ERR_INVALID_ARG, last_error())
+    return n
+
+
+def mamba_block_scan(shape, xbc, dt_raw, conv_state, ssm_state, conv_w, A_log, y, workspace,
+                     conv_b=None, dt_bias=None, D=None, active=None, conv_state_out=None,
+                     ssm_state_out=None, stream=None):
     _check(_lib.tt_mamba_block_scan(ctypes.byref(shape), _ptr(xbc), _ptr(dt_raw), _ptr(conv_state),
                                     _ptr(ssm_state), _ptr(conv_w), _ptr(conv_b), _ptr(A_log),
                                     _ptr(dt_bias), _ptr(D), _ptr(active), _ptr(y),
-                                    _ptr(conv_state_out), _ptr(ssm_state_out), _stream(stream)))
+                                    _ptr(conv_state_out), _ptr(ssm_state_out), _ptr(workspace),
+                                    _nbytes(workspace), _stream(stream)))

@@ -11,24 +11,33 @@
 // scalar-decay selective scan H_s = exp(dt_s A) H_{s-1} + dt_s x_s B_s^T,
 // y_s = H_s C_s + D x_s, dt_s = softplus(dt_raw_s + dt_bias).
 //
-// One workgroup per (sequence b, head h), 256 threads, HBM-bound on the
-// fp32 SSM state (P x N floats per head: 32 KB at P = 64, N = 128):
-//   1. conv: thread c walks channel c of the head's x channels and its
-//      group's B and C channels down the S slots with a sliding window that
-//      starts from the conv state (every input read once), writing SiLU
-//      outputs to LDS as [S][P + 2N] fp32; S threads write dt_s and the
-//      decay a_s to LDS;
-//   2. scan: thread (p, q) holds H[p][q*NPT .. q*NPT+NPT) in registers
-//      (NPT = N / (256 / P)), loaded with 16-byte loads; per slot it updates
-//      them with a_s and dt_s x_s[p] B_s and forms its partial of H_s C_s;
-//      the 256/P threads of a row reduce by shuffles; y goes through LDS and
-//      leaves as coalesced rows;
-//   3. optionally (the context tower taking a committed block) the final
-//      state is written back (in place allowed: every thread reads its part
-//      before anyone writes) and the conv state becomes the block's last
-//      W-1 inputs (to a separate buffer: the B/C channels are read by every
-//      head of the group).
+// One workgroup per (sequence b, head h), 256 threads.  The block is short
+// (S <= 64), so the scan is evaluated in its state-space-duality form (Dao &
+// Gu): with cum_s = sum_{k<=s} dt_k A,
+//   y_s = exp(cum_s) H0 C_s + sum_{j<=s} dt_j exp(cum_s - cum_j) (C_s . B_j) x_j
+//         + D x_s
+// which needs one multiply-add per state entry and slot (H0 C_s) instead of
+// the recurrence's three, and no state update unless the final state is
+// asked for.  Two kernels:
+//   mamba_group_kernel, one workgroup per (sequence, group): the conv + SiLU
+//     outputs of the group's B and C channels, [S][2N] fp32, and
+//     G[s][j] = C_s . B_j, into the workspace -- shared by the group's heads;
+//   mamba_scan_kernel, one workgroup of P/16 waves per (sequence, head): the
+//     fp32 seed H0 (most of the HBM traffic) is loaded straight into the
+//     registers of the fp32 matrix-core operand layout, the head's x
+//     channels go through the conv into LDS, the group's B/C outputs are
+//     copied in (C scaled by the decay exp(cum_s)), and
+//     M[s][j] = dt_j exp(cum_s - cum_j) G[s][j]; each wave then forms a
+//     16-row x 16-slot output tile as H0 C'^T + X^T M^T with
+//     v_mfma_f32_16x16x4f32 and adds D x_s.  Optionally (the context tower
+//     taking a committed block) the final state exp(cum_S) H0 +
+//     sum_j dt_j exp(cum_S - cum_j) x_j B_j^T is written back (in place
+//     allowed: every thread has read its part) and the conv state becomes
+//     the block's last W-1 inputs (to a separate buffer: the B/C channels are
+//     read by every head of the group).
 #include <math.h>
+
+#include <type_traits>
 
 #include "tt_internal.h"
 
@@ -36,7 +45,6 @@ namespace tt {
 namespace {
 
 constexpr int kMThreads = 256;
-constexpr int kMaxConvW = 8;
 
 __device__ __forceinline__ float ld_elt(const uint16_t* p, int64_t i) {
   return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
@@ -50,118 +58,256 @@ __device__ __forceinline__ void st_elt(float* p, int64_t i, float v) { p[i] = v;
 __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
 __device__ __forceinline__ float softplus(float v) { return v > 20.f ? v : log1pf(expf(v)); }
 
-template <typename T, int P, int N>
-__global__ __launch_bounds__(kMThreads) void mamba_scan_kernel(MambaArgs a) {
-  constexpr int TPR = kMThreads / P;     // threads per state row
-  constexpr int NPT = N / TPR;           // state entries per thread
-  static_assert(NPT % 4 == 0, "16-byte state loads");
+// The pre-convolution inputs of `nch` channels for window rows
+// t = -(KW-1) .. S-1 (the conv state, then the block), as fp32 into LDS at
+// dst[(t + KW-1) * stride + cc]; channel cc is global channel chan(cc).  Every
+// thread issues kU loads before it stores any (one latency round per kU).
+template <typename T, int KW, int NT, int nch, typename ChanFn>
+__device__ __forceinline__ void load_window(const T* xbc, const T* cst, int C, int S,
+                                            ChanFn chan, float* dst, int stride) {
+  constexpr int kU = 8;
+  const int total = (S + KW - 1) * nch;
+  for (int base = 0; base < total; base += kU * NT) {
+    float v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + u * NT + threadIdx.x;
+      v[u] = 0.f;
+      if (i < total) {
+        const int r = i / nch, cc = i % nch, c = chan(cc);
+        const int t = r - (KW - 1);
+        v[u] = t < 0 ? ld_elt(cst, static_cast<int64_t>(c) * (KW - 1) + r)
+                     : ld_elt(xbc, static_cast<int64_t>(t) * C + c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = base + u * NT + threadIdx.x;
+      if (i < total) dst[(i / nch) * stride + i % nch] = v[u];
+    }
+  }
+}
+
+// Conv + SiLU of `nch` channels over the S slots from a loaded window:
+// out[s * ostride + cc] = SiLU(b[c] + sum_j w[c][j] win[(s + j) * stride + cc]).
+// nch divides the thread count NT, so each thread keeps one channel and its
+// taps.
+template <int KW, int NT, int nch, typename ChanFn>
+__device__ __forceinline__ void conv_window(const float* win, int stride, int S,
+                                            ChanFn chan, const float* conv_w, const float* conv_b,
+                                            float* out, int ostride) {
+  static_assert(NT % nch == 0, "one channel per thread");
+  const int cc = threadIdx.x % nch;
+  const int c = chan(cc);
+  float w[KW];
+#pragma unroll
+  for (int j = 0; j < KW; ++j) w[j] = conv_w[static_cast<int64_t>(c) * KW + j];
+  const float bias = conv_b ? conv_b[c] : 0.f;
+  for (int si = threadIdx.x / nch; si < S; si += NT / nch) {
+    float acc = bias;
+#pragma unroll
+    for (int j = 0; j < KW; ++j) acc = fmaf(w[j], win[(si + j) * stride + cc], acc);
+    out[si * ostride + cc] = silu(acc);
+  }
+}
+
+// Per (sequence, group): the conv outputs of the group's B and C channels,
+// [S][2N] fp32, and G[s][j] = C_s . B_j for j <= s (0 above), [S][S] -- the
+// parts every head of the group shares.
+template <typename T, int N, int KW>
+__global__ __launch_bounds__(kMThreads) void mamba_group_kernel(MambaArgs a, float* ws_bc, float* ws_g) {
+  const int b = blockIdx.x / a.G;
+  const int g = blockIdx.x % a.G;
+  if (a.active && !a.active[b]) return;
+  const int S = a.S, H = a.H, G = a.G, P = a.P;
+  const int C = H * P + 2 * G * N;
+  constexpr int BCP = 2 * N + 4;         // LDS row stride (rows start 4 banks apart)
+  extern __shared__ float lds[];
+  float* win = lds;                      // [S + KW-1][BCP]
+  float* out = lds + (S + KW - 1) * BCP; // [S][BCP]
+  const T* xbc = static_cast<const T*>(a.xbc) + static_cast<int64_t>(b) * S * C;
+  const T* cst = static_cast<const T*>(a.conv_state) + static_cast<int64_t>(b) * C * (KW - 1);
+  auto chan = [&](int cc) { return H * P + (cc < N ? g * N + cc : G * N + g * N + (cc - N)); };
+  load_window<T, KW, kMThreads, 2 * N>(xbc, cst, C, S, chan, win, BCP);
+  __syncthreads();
+  conv_window<KW, kMThreads, 2 * N>(win, BCP, S, chan, a.conv_w, a.conv_b, out, BCP);
+  __syncthreads();
+  float* bc = ws_bc + (static_cast<int64_t>(b) * G + g) * S * 2 * N;
+  for (int i = threadIdx.x; i < S * 2 * N / 4; i += kMThreads) {
+    const int si = (4 * i) / (2 * N), cc = (4 * i) % (2 * N);
+    *reinterpret_cast<float4*>(bc + 4 * i) = *reinterpret_cast<const float4*>(out + si * BCP + cc);
+  }
+  float* gm = ws_g + (static_cast<int64_t>(b) * G + g) * S * S;
+  // (si, j) pairs, 16 j per pass over a row (no division by the runtime S)
+  for (int si = threadIdx.x >> 4; si < S; si += kMThreads >> 4)
+  for (int j = threadIdx.x & 15; j < S; j += 16) {
+    const int k = si * S + j;
+    float d = 0.f;
+    if (j <= si) {
+      const float* cs = out + si * BCP + N;
+      const float* bs = out + j * BCP;
+#pragma unroll 4
+      for (int n = 0; n < N; n += 4) {
+        const float4 x4 = *reinterpret_cast<const float4*>(cs + n);
+        const float4 y4 = *reinterpret_cast<const float4*>(bs + n);
+        d = fmaf(x4.x, y4.x, fmaf(x4.y, y4.y, fmaf(x4.z, y4.z, fmaf(x4.w, y4.w, d))));
+      }
+    }
+    gm[k] = d;
+  }
+}
+
+// Per (sequence, head): P/16 waves; wave w owns state rows 16w..16w+15, lane
+// l row p = 16w + l%16 and entries n in [kg*KS, kg*KS + KS), kg = l/16,
+// KS = N/4.  The outputs of 16 slots at a time are one 16 x 16 fp32 matrix
+// tile per wave, accumulated by v_mfma_f32_16x16x4f32 in two parts:
+//   H0 (exp(cum_s) C_s)  -- K = N, taken in the order n = kg*KS + t at step
+//                            t, so each lane's A operand is its own state
+//                            entry t and its B operand C'[s][kg*KS + t];
+//   X^T M^T              -- K = the slots j (4 per step), the in-block sum
+//                            sum_j M[s][j] x_j[p] (M is 0 for j > s).
+// Lane l then holds y at slot s0 + l%16 for rows 16w + 4 kg + r, r < 4.
+template <typename T, int P, int N, int KW>
+__global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const float* ws_bc,
+                                                          const float* ws_g) {
+  constexpr int NT = 4 * P;              // P/16 waves of 64
+  constexpr int KS = N / 4;              // state entries per lane
+  constexpr int SC = 16;                 // slots per output tile
+  static_assert(KS % 4 == 0, "16-byte state loads");
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
   const int b = blockIdx.x / a.H;
   const int h = blockIdx.x % a.H;
   if (a.active && !a.active[b]) return;
-  const int tid = threadIdx.x;
-  const int S = a.S, W = a.W, H = a.H, G = a.G;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = a.S, H = a.H, G = a.G;
+  const int Sp = (S + SC - 1) / SC * SC; // slots rounded up to whole tiles (zero padded)
+  constexpr int W = KW;
   const int g = h / (H / G);
   const int C = H * P + 2 * G * N;
-  const int CH = P + 2 * N;              // this head's channels: x, then B, C of its group
+  constexpr int XP = P + 4;              // LDS row strides (rows start 4 banks apart)
+  constexpr int BP = N + 4;
   extern __shared__ float lds[];
-  float* conv_out = lds;                 // [S][CH]
-  float* s_dt = lds + S * CH;            // [S]
-  float* s_a = s_dt + S;                 // [S]
-  float* s_y = s_a + S;                  // [S][P]
+  float* s_win = lds;                    // [S + W-1][XP]  x inputs
+  float* s_x = s_win + (S + W - 1) * XP; // [Sp][XP]       conv outputs of the head's x
+  float* s_b = s_x + Sp * XP;            // [S][BP]        the group's B
+  float* s_c = s_b + S * BP;             // [Sp][BP]       exp(cum_s) C_s
+  float* s_dt = s_c + Sp * BP;           // [S]  dt_s
+  float* s_cum = s_dt + S;               // [S]  sum_{k<=s} dt_k A  (log of the decay)
+  float* s_dec = s_cum + S;              // [S]  exp(cum_s)
+  float* s_m = s_dec + S;                // [Sp][Sp]  dt_j exp(cum_s - cum_j) G[s][j]
   const T* xbc = static_cast<const T*>(a.xbc) + static_cast<int64_t>(b) * S * C;
   const T* cst = static_cast<const T*>(a.conv_state) + static_cast<int64_t>(b) * C * (W - 1);
 
-  // ---- state loads first (the HBM-heavy part), then the convolution
-  const int p = tid / TPR, q = tid % TPR;
-  const int64_t sbase = ((static_cast<int64_t>(b) * H + h) * P + p) * N + q * NPT;
-  float st[NPT];
+  // ---- every global load of the workgroup first: the seed's state (most
+  // of the HBM traffic), the group's B/C outputs, the x window, dt
+  const int pl = lane & 15, kg = lane >> 4;
+  const int p = wave * 16 + pl;
+  const int64_t sbase = ((static_cast<int64_t>(b) * H + h) * P + p) * N + kg * KS;
+  float st[KS];
 #pragma unroll
-  for (int j = 0; j < NPT; j += 4) {
+  for (int j = 0; j < KS; j += 4) {
     const float4 v = *reinterpret_cast<const float4*>(a.ssm_state + sbase + j);
     st[j] = v.x; st[j + 1] = v.y; st[j + 2] = v.z; st[j + 3] = v.w;
   }
-  for (int cl = tid; cl < CH; cl += kMThreads) {
-    const int c = cl < P ? h * P + cl
-                         : (cl < P + N ? H * P + g * N + (cl - P) : H * P + G * N + g * N + (cl - P - N));
-    // the W-1 previous inputs and the taps, in registers (fixed-size arrays
-    // with predicated entries: W <= kMaxConvW)
-    float win[kMaxConvW - 1], w[kMaxConvW];
+  const float* bc = ws_bc + (static_cast<int64_t>(b) * G + g) * S * 2 * N;
+  for (int i = tid; i < S * 2 * N / 4; i += NT) {
+    const int si = (4 * i) / (2 * N), cc = (4 * i) % (2 * N);
+    float* dst = cc < N ? s_b + si * BP + cc : s_c + si * BP + (cc - N);
+    *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(bc + 4 * i);
+  }
+  auto chan = [&](int cc) { return h * P + cc; };
+  load_window<T, KW, NT, P>(xbc, cst, C, S, chan, s_win, XP);
+  const float A = -expf(a.A_log[h]);
+  if (tid < S) {
+    s_dt[tid] = softplus(a.dt_raw[(static_cast<int64_t>(b) * S + tid) * H + h] +
+                         (a.dt_bias ? a.dt_bias[h] : 0.f));
+  }
+  __syncthreads();
+  conv_window<KW, NT, P>(s_win, XP, S, chan, a.conv_w, a.conv_b, s_x, XP);
+  for (int i = tid; i < (Sp - S) * XP; i += NT) s_x[S * XP + i] = 0.f;
+  if (tid == 0) {                        // prefix sum of the log decays (S <= 64)
+    float cum = 0.f;
+    for (int i = 0; i < S; ++i) {
+      cum = fmaf(s_dt[i], A, cum);
+      s_cum[i] = cum;
+      s_dec[i] = expf(cum);
+    }
+  }
+  __syncthreads();
+  // C rows scaled by the decay from the seed, zero rows past S; M
+  for (int i = tid; i < Sp * (N / 4); i += NT) {
+    const int si = i / (N / 4), n = 4 * (i % (N / 4));
+    float4* cp = reinterpret_cast<float4*>(s_c + si * BP + n);
+    if (si < S) {
+      const float dec = s_dec[si];
+      const float4 v = *cp;
+      *cp = make_float4(v.x * dec, v.y * dec, v.z * dec, v.w * dec);
+    } else {
+      *cp = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  const float* gm = ws_g + (static_cast<int64_t>(b) * G + g) * S * S;
+  for (int si = tid >> 4; si < Sp; si += NT >> 4)
+    for (int j = tid & 15; j < Sp; j += 16)
+      s_m[si * Sp + j] =
+          (j <= si && si < S) ? s_dt[j] * expf(s_cum[si] - s_cum[j]) * gm[si * S + j] : 0.f;
+  __syncthreads();
+
+  // ---- outputs, one 16-slot tile at a time
+  const float Dh = a.D ? a.D[h] : 0.f;
+  T* y = static_cast<T*>(a.y) + (static_cast<int64_t>(b) * S) * (H * P) + h * P + wave * 16 + 4 * kg;
+  for (int s0 = 0; s0 < Sp; s0 += SC) {
+    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+    const float* crow = s_c + (s0 + pl) * BP + kg * KS;
 #pragma unroll
-    for (int j = 0; j < kMaxConvW - 1; ++j)
-      win[j] = j < W - 1 ? ld_elt(cst, static_cast<int64_t>(c) * (W - 1) + j) : 0.f;
+    for (int t = 0; t < KS; t += 4) {
+      const float4 cv = *reinterpret_cast<const float4*>(crow + t);
+      d = __builtin_amdgcn_mfma_f32_16x16x4f32(st[t], cv.x, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x4f32(st[t + 1], cv.y, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x4f32(st[t + 2], cv.z, d, 0, 0, 0);
+      d = __builtin_amdgcn_mfma_f32_16x16x4f32(st[t + 3], cv.w, d, 0, 0, 0);
+    }
+    const float* mrow = s_m + (s0 + pl) * Sp;
+    for (int j0 = 0; j0 < s0 + SC; j0 += 4)
+      d = __builtin_amdgcn_mfma_f32_16x16x4f32(s_x[(j0 + kg) * XP + p], mrow[j0 + kg], d, 0, 0, 0);
+    const int si = s0 + pl;
+    if (si < S) {
+      const float* xr = s_x + si * XP + wave * 16 + 4 * kg;
 #pragma unroll
-    for (int j = 0; j < kMaxConvW; ++j) w[j] = j < W ? a.conv_w[static_cast<int64_t>(c) * W + j] : 0.f;
-    const float bias = a.conv_b ? a.conv_b[c] : 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float cur = ld_elt(xbc, static_cast<int64_t>(s) * C + c);
-      float acc = bias;
+      for (int r = 0; r < 4; ++r) st_elt(y, static_cast<int64_t>(si) * (H * P) + r, d[r] + Dh * xr[r]);
+    }
+  }
+
+  // ---- the context tower's final state: H_S = exp(cum_S) H0 +
+  // sum_j dt_j exp(cum_S - cum_j) x_j B_j^T (in place allowed: every thread
+  // has read its part), and the conv state = the last W-1 inputs
+  if (a.ssm_state_out) {
+    const float last = s_cum[S - 1];
+    const float d0 = expf(last);
 #pragma unroll
-      for (int j = 0; j < kMaxConvW - 1; ++j)
-        if (j < W - 1) acc = fmaf(w[j], win[j], acc);
+    for (int n = 0; n < KS; ++n) st[n] *= d0;
+    for (int j = 0; j < S; ++j) {
+      const float coef = s_dt[j] * expf(last - s_cum[j]) * s_x[j * XP + p];
+      const float* bs = s_b + j * BP + kg * KS;
 #pragma unroll
-      for (int j = 0; j < kMaxConvW; ++j)
-        if (j == W - 1) acc = fmaf(w[j], cur, acc);
-      conv_out[s * CH + cl] = silu(acc);
-#pragma unroll
-      for (int j = 0; j < kMaxConvW - 1; ++j) {
-        const float nxt = j + 1 < kMaxConvW - 1 ? win[j + 1] : 0.f;
-        if (j < W - 2) win[j] = nxt;
-        else if (j == W - 2) win[j] = cur;
+      for (int n = 0; n < KS; n += 4) {
+        const float4 bv = *reinterpret_cast<const float4*>(bs + n);
+        st[n] = fmaf(coef, bv.x, st[n]);
+        st[n + 1] = fmaf(coef, bv.y, st[n + 1]);
+        st[n + 2] = fmaf(coef, bv.z, st[n + 2]);
+        st[n + 3] = fmaf(coef, bv.w, st[n + 3]);
       }
     }
-  }
-  if (tid < S) {
-    const float A = -expf(a.A_log[h]);
-    const float dt = softplus(a.dt_raw[(static_cast<int64_t>(b) * S + tid) * H + h] +
-                              (a.dt_bias ? a.dt_bias[h] : 0.f));
-    s_dt[tid] = dt;
-    s_a[tid] = expf(dt * A);
-  }
-  __syncthreads();
-
-  // ---- the scan
-  const float Dh = a.D ? a.D[h] : 0.f;
-  const float* Bs = conv_out + P + q * NPT;
-  const float* Cs = conv_out + P + N + q * NPT;
-  for (int s = 0; s < S; ++s) {
-    const float as = s_a[s];
-    const float x = conv_out[s * CH + p];
-    const float dx = s_dt[s] * x;
-    float acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < NPT; j += 4) {
-      const float4 bv = *reinterpret_cast<const float4*>(Bs + s * CH + j);
-      const float4 cv = *reinterpret_cast<const float4*>(Cs + s * CH + j);
-      st[j] = fmaf(as, st[j], dx * bv.x);
-      st[j + 1] = fmaf(as, st[j + 1], dx * bv.y);
-      st[j + 2] = fmaf(as, st[j + 2], dx * bv.z);
-      st[j + 3] = fmaf(as, st[j + 3], dx * bv.w);
-      acc = fmaf(st[j], cv.x, acc);
-      acc = fmaf(st[j + 1], cv.y, acc);
-      acc = fmaf(st[j + 2], cv.z, acc);
-      acc = fmaf(st[j + 3], cv.w, acc);
-    }
-#pragma unroll
-    for (int off = TPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, TPR);
-    if (q == 0) s_y[s * P + p] = acc + Dh * x;
-  }
-  __syncthreads();
-  T* y = static_cast<T*>(a.y) + (static_cast<int64_t>(b) * S) * (H * P) + h * P;
-  for (int i = tid; i < S * P; i += kMThreads)
-    st_elt(y, static_cast<int64_t>(i / P) * (H * P) + i % P, s_y[i]);
-
-  // ---- the context tower's state update
-  if (a.ssm_state_out) {
-#pragma unroll
-    for (int j = 0; j < NPT; j += 4)
+    for (int j = 0; j < KS; j += 4)
       *reinterpret_cast<float4*>(a.ssm_state_out + sbase + j) = make_float4(st[j], st[j + 1], st[j + 2], st[j + 3]);
   }
   if (a.conv_state_out) {
     T* cso = static_cast<T*>(a.conv_state_out) + static_cast<int64_t>(b) * C * (W - 1);
-    // x channels by their head; B and C channels by the group's first head.
-    // New state = the last W-1 of [old state ; block inputs].
+    // x channels by their head; B and C channels by the group's first head
     const bool owns_bc = (h % (H / G)) == 0;
-    for (int cl = tid; cl < CH; cl += kMThreads) {
+    constexpr int CH = P + 2 * N;
+    for (int cl = tid; cl < CH; cl += NT) {
       if (cl >= P && !owns_bc) continue;
       const int c = cl < P ? h * P + cl
                            : (cl < P + N ? H * P + g * N + (cl - P) : H * P + G * N + g * N + (cl - P - N));
@@ -176,41 +322,67 @@ __global__ __launch_bounds__(kMThreads) void mamba_scan_kernel(MambaArgs a) {
 }
 
 template <typename T>
-hipError_t launch_t(const MambaArgs& a, hipStream_t st) {
-  const size_t lds = mamba_lds_bytes(a.S, a.P, a.N);
-  const dim3 grid(static_cast<unsigned>(a.B * a.H)), blk(kMThreads);
+hipError_t launch_t(const MambaArgs& a, void* ws, hipStream_t st) {
+  const size_t lds_g = mamba_group_lds_bytes(a.S, a.N);
+  const size_t lds_s = mamba_lds_bytes(a.S, a.P, a.N);
+  float* ws_bc = static_cast<float*>(ws);
+  float* ws_g = ws_bc + static_cast<size_t>(a.B) * a.G * a.S * 2 * a.N;
+  const dim3 blk(kMThreads);
   // more than 64 KB of dynamic LDS must be allowed per kernel (up to 160 KB)
-#define TT_MAMBA(PP, NN)                                                                   \
-  if (a.P == PP && a.N == NN) {                                                            \
-    if (lds > 65536) {                                                                     \
-      const hipError_t e = hipFuncSetAttribute(                                            \
-          reinterpret_cast<const void*>(&mamba_scan_kernel<T, PP, NN>),                    \
-          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));              \
-      if (e != hipSuccess) return e;                                                       \
-    }                                                                                      \
-    hipLaunchKernelGGL((mamba_scan_kernel<T, PP, NN>), grid, blk, lds, st, a);            \
-    return hipGetLastError();                                                              \
+  auto allow = [](const void* f, size_t bytes) {
+    return bytes > 65536 ? hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               static_cast<int>(bytes))
+                         : hipSuccess;
+  };
+#define TT_MAMBA(PP, NN, WW)                                                                    \
+  if (a.P == PP && a.N == NN && a.W == WW) {                                                    \
+    hipError_t e = allow(reinterpret_cast<const void*>(&mamba_group_kernel<T, NN, WW>), lds_g); \
+    if (e == hipSuccess)                                                                        \
+      e = allow(reinterpret_cast<const void*>(&mamba_scan_kernel<T, PP, NN, WW>), lds_s);       \
+    if (e != hipSuccess) return e;                                                              \
+    hipLaunchKernelGGL((mamba_group_kernel<T, NN, WW>), dim3(static_cast<unsigned>(a.B * a.G)), \
+                       blk, lds_g, st, a, ws_bc, ws_g);                                         \
+    e = hipGetLastError();                                                                      \
+    if (e != hipSuccess) return e;                                                              \
+    hipLaunchKernelGGL((mamba_scan_kernel<T, PP, NN, WW>), dim3(static_cast<unsigned>(a.B * a.H)), \
+                       dim3(4 * PP), lds_s, st, a, ws_bc, ws_g);                                \
+    return hipGetLastError();                                                                   \
   }
-  TT_MAMBA(64, 128)
-  TT_MAMBA(64, 64)
-  TT_MAMBA(32, 128)
-  TT_MAMBA(32, 64)
+#define TT_MAMBA_W(PP, NN) TT_MAMBA(PP, NN, 2) TT_MAMBA(PP, NN, 3) TT_MAMBA(PP, NN, 4)
+  TT_MAMBA_W(64, 128)
+  TT_MAMBA_W(64, 64)
+  TT_MAMBA_W(32, 128)
+  TT_MAMBA_W(32, 64)
+#undef TT_MAMBA_W
 #undef TT_MAMBA
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-bool mamba_supported(int P, int N) {
-  return (P == 64 || P == 32) && (N == 128 || N == 64);
+bool mamba_supported(int P, int N, int W) {
+  return (P == 64 || P == 32) && (N == 128 || N == 64) && W >= 2 && W <= 4;
 }
 
 size_t mamba_lds_bytes(int S, int P, int N) {
-  return (static_cast<size_t>(S) * (P + 2 * N) + 2 * S + static_cast<size_t>(S) * P) * sizeof(float);
+  // the scan kernel: the x window (S + 3 rows at most) and outputs (S
+  // rounded up to 16), B and C rows, dt, cum and M; the group kernel needs
+  // (2S + 3) (2N + 4) floats, checked separately
+  const size_t Sp = (S + 15) / 16 * 16;
+  return (static_cast<size_t>(S + 3 + Sp) * (P + 4) + static_cast<size_t>(S + Sp) * (N + 4) +
+          3 * static_cast<size_t>(S) + Sp * Sp) * sizeof(float);
 }
 
-hipError_t launch_mamba_scan(const MambaArgs& a, hipStream_t st) {
-  return a.dtype == 0 ? launch_t<uint16_t>(a, st) : launch_t<float>(a, st);
+size_t mamba_group_lds_bytes(int S, int N) {
+  return static_cast<size_t>(2 * S + 3) * (2 * N + 4) * sizeof(float);
+}
+
+size_t mamba_workspace_bytes(int B, int S, int G, int N) {
+  return static_cast<size_t>(B) * G * S * (2 * N + S) * sizeof(float);
+}
+
+hipError_t launch_mamba_scan(const MambaArgs& a, void* ws, hipStream_t st) {
+  return a.dtype == 0 ? launch_t<uint16_t>(a, ws, st) : launch_t<float>(a, ws, st);
 }
 
 }  // namespace tt

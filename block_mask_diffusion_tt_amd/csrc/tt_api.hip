@@ -207,13 +207,11 @@ tt_status tt_ctx_block_attn(const tt_attn_shape* shape, const void* q_blk, const
                            nullptr, residual, out, lse, 1, workspace, workspace_bytes, stream);
 }
 
-tt_status tt_mamba_block_scan(const tt_mamba_shape* shape, const void* xbc, const float* dt_raw,
-                              const void* conv_state, const float* ssm_state,
-                              const float* conv_w, const float* conv_b, const float* A_log,
-                              const float* dt_bias, const float* D, const uint8_t* active,
-                              void* y, void* conv_state_out, float* ssm_state_out,
-                              tt_stream stream) {
-  const char* fn = "tt_mamba_block_scan";
+}  // extern "C"
+
+namespace {
+
+tt_status check_mamba_shape(const char* fn, const tt_mamba_shape* shape) {
   if (!shape) return fail(TT_ERR_INVALID_ARG, "%s: shape is NULL", fn);
   const tt_mamba_shape& m = *shape;
   if (m.batch < 0 || m.n_heads < 1 || m.n_groups < 1 || m.head_dim < 1 || m.d_state < 1)
@@ -228,11 +226,41 @@ tt_status tt_mamba_block_scan(const tt_mamba_shape* shape, const void* xbc, cons
     return fail(TT_ERR_INVALID_ARG, "%s: block_size %d outside [1, 64]", fn, m.block_size);
   if (m.dtype != TT_BF16 && m.dtype != TT_F32)
     return fail(TT_ERR_INVALID_ARG, "%s: dtype %d is neither TT_BF16 nor TT_F32", fn, m.dtype);
-  if (!tt::mamba_supported(m.head_dim, m.d_state))
+  if (m.conv_width > 4)
+    return fail(TT_ERR_UNSUPPORTED, "%s: conv_width %d not supported (2 to 4)", fn, m.conv_width);
+  if (!tt::mamba_supported(m.head_dim, m.d_state, m.conv_width))
     return fail(TT_ERR_UNSUPPORTED, "%s: head_dim %d / d_state %d not supported (32 or 64 / 64 or 128)",
                 fn, m.head_dim, m.d_state);
   if (static_cast<int64_t>(m.n_heads) * m.head_dim + 2LL * m.n_groups * m.d_state > INT32_MAX / 64)
     return fail(TT_ERR_INVALID_ARG, "%s: too many channels", fn);
+  if (tt::mamba_lds_bytes(m.block_size, m.head_dim, m.d_state) > 160 * 1024 ||
+      tt::mamba_group_lds_bytes(m.block_size, m.d_state) > 160 * 1024)
+    return fail(TT_ERR_UNSUPPORTED, "%s: block too long for the LDS staging", fn);
+  return TT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tt_mamba_workspace_size(const tt_mamba_shape* shape) {
+  if (check_mamba_shape("tt_mamba_workspace_size", shape) != TT_OK) return 0;
+  ok();
+  const size_t n = tt::mamba_workspace_bytes(shape->batch, shape->block_size, shape->n_groups,
+                                             shape->d_state);
+  return n < 256 ? 256 : n;
+}
+
+tt_status tt_mamba_block_scan(const tt_mamba_shape* shape, const void* xbc, const float* dt_raw,
+                              const void* conv_state, const float* ssm_state,
+                              const float* conv_w, const float* conv_b, const float* A_log,
+                              const float* dt_bias, const float* D, const uint8_t* active,
+                              void* y, void* conv_state_out, float* ssm_state_out,
+                              void* workspace, size_t workspace_bytes, tt_stream stream) {
+  const char* fn = "tt_mamba_block_scan";
+  tt_status cs = check_mamba_shape(fn, shape);
+  if (cs != TT_OK) return cs;
+  const tt_mamba_shape& m = *shape;
   if (!xbc || !dt_raw || !conv_state || !ssm_state || !conv_w || !A_log || !y)
     return fail(TT_ERR_INVALID_ARG, "%s: xbc, dt_raw, conv_state, ssm_state, conv_w, A_log and y must be non-NULL", fn);
   if (!aligned(ssm_state, 16) || (ssm_state_out && !aligned(ssm_state_out, 16)))
@@ -252,16 +280,18 @@ tt_status tt_mamba_block_scan(const tt_mamba_shape* shape, const void* xbc, cons
     if (a0 < b0 + bytes && b0 < a0 + bytes)
       return fail(TT_ERR_INVALID_ARG, "%s: conv_state_out overlaps conv_state", fn);
   }
-  if (tt::mamba_lds_bytes(m.block_size, m.head_dim, m.d_state) > 160 * 1024)
-    return fail(TT_ERR_UNSUPPORTED, "%s: block too long for the LDS staging", fn);
   if (m.batch == 0) return ok();
+  const size_t need = tt::mamba_workspace_bytes(m.batch, m.block_size, m.n_groups, m.d_state);
+  if (!workspace || workspace_bytes < need)
+    return fail(TT_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
+  if (!aligned(workspace, 16)) return fail(TT_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
   tt::MambaArgs a{};
   a.B = m.batch; a.S = m.block_size; a.H = m.n_heads; a.P = m.head_dim; a.N = m.d_state;
   a.G = m.n_groups; a.W = m.conv_width; a.dtype = m.dtype;
   a.xbc = xbc; a.dt_raw = dt_raw; a.conv_state = conv_state; a.ssm_state = ssm_state;
   a.conv_w = conv_w; a.conv_b = conv_b; a.A_log = A_log; a.dt_bias = dt_bias; a.D = D;
   a.active = active; a.y = y; a.conv_state_out = conv_state_out; a.ssm_state_out = ssm_state_out;
-  const hipError_t he = tt::launch_mamba_scan(a, static_cast<hipStream_t>(stream));
+  const hipError_t he = tt::launch_mamba_scan(a, workspace, static_cast<hipStream_t>(stream));
   if (he != hipSuccess) return hip_fail(he, fn);
   return ok();
 }

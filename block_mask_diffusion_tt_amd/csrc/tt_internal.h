@@ -92,9 +92,11 @@ struct MambaArgs {
   void* y; void* conv_state_out; float* ssm_state_out;
 };
 
-bool mamba_supported(int P, int N);
+bool mamba_supported(int P, int N, int W);
 size_t mamba_lds_bytes(int S, int P, int N);
-hipError_t launch_mamba_scan(const MambaArgs& a, hipStream_t st);
+size_t mamba_group_lds_bytes(int S, int N);
+size_t mamba_workspace_bytes(int B, int S, int G, int N);
+hipError_t launch_mamba_scan(const MambaArgs& a, void* ws, hipStream_t st);
 
 // ---------------------------------------------------------------- adaLN
 hipError_t launch_timestep_embed(int B, const float* t, const int32_t* n_masked, int S,

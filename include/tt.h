@@ -453,7 +453,8 @@ tt_status tt_generate(const tt_attn_shape* shape, int32_t n_layers, int32_t n_bl
  * ssm_state: the final H) and conv_state_out (must not overlap conv_state:
  * the last W-1 rows of u).
  *   shape: batch B, n_heads H, head_dim P in {32, 64}, d_state N in
- *          {64, 128}, n_groups G (divides H), conv_width W in [2, 8],
+ *          {64, 128}, n_groups G (divides H), conv_width W in [2, 4]
+ *          (Mamba-2's is 4; [5, 8] returns TT_ERR_UNSUPPORTED),
  *          block_size S in [1, 64], dtype of xbc / conv states / y.
  *   xbc [B, S, C] and y [B, S, H*P] (dtype), C = H*P + 2*G*N;
  *   dt_raw [B, S, H] fp32; conv_state [B, C, W-1] (dtype);
@@ -461,9 +462,12 @@ tt_status tt_generate(const tt_attn_shape* shape, int32_t n_layers, int32_t n_bl
  *   conv_w [C, W], conv_b [C] or NULL, A_log [H], dt_bias [H] or NULL,
  *   D [H] or NULL: fp32;  active [B] uint8 or NULL (inactive: untouched).
  * All device pointers.  fp32 arithmetic throughout; y rounded to nearest
- * even for bf16.  Errors: TT_ERR_INVALID_ARG (NULL required pointer, bad
- * sizes, G not dividing H, misaligned state), TT_ERR_UNSUPPORTED (P or N
- * outside the sets above), TT_ERR_HIP.
+ * even for bf16.  The workspace (tt_mamba_workspace_size bytes, 16-byte
+ * aligned, no initialisation) holds the B/C conv outputs and C.B products
+ * the heads of a group share.  Errors: TT_ERR_INVALID_ARG (NULL required
+ * pointer, bad sizes, G not dividing H, misaligned state),
+ * TT_ERR_UNSUPPORTED (P, N or W outside the sets above), TT_ERR_WORKSPACE,
+ * TT_ERR_HIP.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t batch;
@@ -476,12 +480,14 @@ typedef struct {
   int32_t dtype;
 } tt_mamba_shape;
 
+size_t tt_mamba_workspace_size(const tt_mamba_shape* shape);
+
 tt_status tt_mamba_block_scan(const tt_mamba_shape* shape, const void* xbc, const float* dt_raw,
                               const void* conv_state, const float* ssm_state,
                               const float* conv_w, const float* conv_b, const float* A_log,
                               const float* dt_bias, const float* D, const uint8_t* active,
                               void* y, void* conv_state_out, float* ssm_state_out,
-                              tt_stream stream);
+                              void* workspace, size_t workspace_bytes, tt_stream stream);
 
 #ifdef __cplusplus
 }

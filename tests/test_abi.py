@@ -236,18 +236,22 @@ def test_generate_rejects_bad_arguments():
 def test_mamba_rejects_bad_arguments():
     L = tt.lib()
 
-    def call(shape=(2, 8, 64, 128, 2, 4, 16, 0), xbc=FAKE, ss=FAKE, cso=None, cs=FAKE):
+    def call(shape=(2, 8, 64, 128, 2, 4, 16, 0), xbc=FAKE, ss=FAKE, cso=None, cs=FAKE,
+             ws_bytes=1 << 30):
         s = tt.MambaShape(*shape)
         return L.tt_mamba_block_scan(ctypes.byref(s), xbc, FAKE, cs, ss, FAKE, None, FAKE, None,
-                                     None, None, FAKE, cso, None, None)
+                                     None, None, FAKE, cso, None, FAKE, ws_bytes, None)
     assert call(shape=(2, 8, 64, 128, 3, 4, 16, 0)) == tt.TT_ERR_INVALID_ARG     # G !| H
     assert call(shape=(2, 8, 48, 128, 2, 4, 16, 0)) == tt.TT_ERR_UNSUPPORTED     # P = 48
     assert call(shape=(2, 8, 64, 96, 2, 4, 16, 0)) == tt.TT_ERR_UNSUPPORTED      # N = 96
     assert call(shape=(2, 8, 64, 128, 2, 1, 16, 0)) == tt.TT_ERR_INVALID_ARG     # W = 1
+    assert call(shape=(2, 8, 64, 128, 2, 6, 16, 0)) == tt.TT_ERR_UNSUPPORTED     # W = 6
     assert call(shape=(2, 8, 64, 128, 2, 4, 65, 0)) == tt.TT_ERR_INVALID_ARG     # S = 65
     assert call(shape=(2, 8, 64, 128, 2, 4, 16, 9)) == tt.TT_ERR_INVALID_ARG     # dtype
     assert call(xbc=None) == tt.TT_ERR_INVALID_ARG
     assert call(ss=FAKE + 8) == tt.TT_ERR_INVALID_ARG                            # 16-byte state
     assert call(cso=FAKE) == tt.TT_ERR_INVALID_ARG                               # overlaps conv_state
     assert "tt_mamba_block_scan" in tt.last_error()
+    assert call(ws_bytes=16) == tt.TT_ERR_WORKSPACE
     assert call(shape=(0, 8, 64, 128, 2, 4, 16, 0)) == tt.TT_OK
+    assert tt.mamba_workspace_size(tt.MambaShape(2, 8, 64, 128, 2, 4, 16, 0)) >= 2 * 2 * 16 * 272 * 4

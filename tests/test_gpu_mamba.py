@@ -39,8 +39,9 @@ def run(c, states_out=False, in_place=True):
     if states_out:
         cso = torch.full_like(c["conv_state"], 5.0)
         sso = c["ssm_state"] if in_place else torch.full_like(c["ssm_state"], 5.0)
+    ws = torch.empty(tt.mamba_workspace_size(shape), dtype=torch.uint8, device=DEV)
     tt.mamba_block_scan(shape, c["xbc"], c["dt_raw"], c["conv_state"], c["ssm_state"], c["conv_w"],
-                        c["A_log"], y, conv_b=c["conv_b"], dt_bias=c["dt_bias"], D=c["D"],
+                        c["A_log"], y, ws, conv_b=c["conv_b"], dt_bias=c["dt_bias"], D=c["D"],
                         active=c["active"], conv_state_out=cso, ssm_state_out=sso)
     torch.cuda.synchronize()
     return y, cso, sso
@@ -77,7 +78,7 @@ def test_shapes(P, N, dtype):
     close(y, ref(c), dtype, f"P={P} N={N}")
 
 
-@pytest.mark.parametrize("S,W,G", [(1, 4, 1), (4, 2, 2), (5, 8, 4), (64, 4, 8)])
+@pytest.mark.parametrize("S,W,G", [(1, 4, 1), (4, 2, 2), (5, 3, 4), (64, 4, 8)])
 def test_block_lengths_and_conv_widths(S, W, G):
     c = mcase(2, S, 8, 64, 128, G, W=W, seed=30 + S + W)
     say("mamba S W G", S, W, G)
