@@ -45,11 +45,22 @@ namespace tt {
 namespace {
 
 constexpr int kMThreads = 256;
+// a native 4-float vector: arrays of it stay in registers (arrays of HIP's
+// float4 struct were left in scratch memory)
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float ld_elt(const uint16_t* p, int64_t i) {
   return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
 }
 __device__ __forceinline__ float ld_elt(const float* p, int64_t i) { return p[i]; }
+// raw bits of one element (converted later by raw_f32), so that nothing
+// between a load and its use needs the loaded register
+__device__ __forceinline__ uint32_t ld_raw(const uint16_t* p) { return *p; }
+__device__ __forceinline__ uint32_t ld_raw(const float* p) { return __float_as_uint(*p); }
+template <typename T>
+__device__ __forceinline__ float raw_f32(uint32_t r) {
+  return std::is_same<T, float>::value ? __uint_as_float(r) : __uint_as_float(r << 16);
+}
 __device__ __forceinline__ void st_elt(uint16_t* p, int64_t i, float v) {
   p[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
 }
@@ -58,32 +69,35 @@ __device__ __forceinline__ void st_elt(float* p, int64_t i, float v) { p[i] = v;
 __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
 __device__ __forceinline__ float softplus(float v) { return v > 20.f ? v : log1pf(expf(v)); }
 
-// The pre-convolution inputs of `nch` channels for window rows
-// t = -(KW-1) .. S-1 (the conv state, then the block), as fp32 into LDS at
-// dst[(t + KW-1) * stride + cc]; channel cc is global channel chan(cc).  Every
-// thread issues kU loads before it stores any (one latency round per kU).
-template <typename T, int KW, int NT, int nch, typename ChanFn>
-__device__ __forceinline__ void load_window(const T* xbc, const T* cst, int C, int S,
+// Slots are handled in rounds of 16 (one 16 x 16 output tile per wave).
+constexpr int kSC = 16;
+
+// The pre-convolution inputs of `nch` channels for the window rows
+// rw in [rw0, rw1) (rw = t + KW-1; t < 0 is the conv state, t >= 0 the
+// block), as fp32 into LDS at dst[rw * stride + cc]; channel cc is global
+// channel chan(cc).  Every load is unconditional (indexes past the end are
+// clamped onto the last element and their values dropped), so the kU loads
+// of a thread are in flight together and the thread waits once.
+template <typename T, int KW, int NT, int nch, int kU, typename ChanFn>
+__device__ __forceinline__ void load_window(const T* xbc, const T* cst, int C, int rw0, int rw1,
                                             ChanFn chan, float* dst, int stride) {
-  constexpr int kU = 8;
-  const int total = (S + KW - 1) * nch;
+  const int total = (rw1 - rw0) * nch;
   for (int base = 0; base < total; base += kU * NT) {
-    float v[kU];
+    uint32_t v[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int i = base + u * NT + threadIdx.x;
-      v[u] = 0.f;
-      if (i < total) {
-        const int r = i / nch, cc = i % nch, c = chan(cc);
-        const int t = r - (KW - 1);
-        v[u] = t < 0 ? ld_elt(cst, static_cast<int64_t>(c) * (KW - 1) + r)
-                     : ld_elt(xbc, static_cast<int64_t>(t) * C + c);
-      }
+      const int i = min(base + u * NT + static_cast<int>(threadIdx.x), total - 1);
+      const int r = rw0 + i / nch, cc = i % nch, c = chan(cc);
+      const int t = r - (KW - 1);
+      const T* src = t < 0 ? cst + static_cast<int64_t>(c) * (KW - 1) + r
+                           : xbc + static_cast<int64_t>(t) * C + c;
+      v[u] = ld_raw(src);
     }
+    __builtin_amdgcn_sched_barrier(0);   // every load before the first store
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int i = base + u * NT + threadIdx.x;
-      if (i < total) dst[(i / nch) * stride + i % nch] = v[u];
+    for (int u = 0; u < kU; ++u) {     // clamped like the loads (same bytes as the owner)
+      const int i = min(base + u * NT + static_cast<int>(threadIdx.x), total - 1);
+      dst[(rw0 + i / nch) * stride + i % nch] = raw_f32<T>(v[u]);
     }
   }
 }
@@ -92,87 +106,173 @@ __device__ __forceinline__ void load_window(const T* xbc, const T* cst, int C, i
 // out[s * ostride + cc] = SiLU(b[c] + sum_j w[c][j] win[(s + j) * stride + cc]).
 // nch divides the thread count NT, so each thread keeps one channel and its
 // taps.
-template <int KW, int NT, int nch, typename ChanFn>
-__device__ __forceinline__ void conv_window(const float* win, int stride, int S,
-                                            ChanFn chan, const float* conv_w, const float* conv_b,
+// The conv taps and bias of the thread's channel (channel threadIdx.x % nch).
+template <int KW>
+struct Taps {
+  float w[KW];
+  float bias;
+  __device__ __forceinline__ void load(const float* conv_w, const float* conv_b, int c) {
+#pragma unroll
+    for (int j = 0; j < KW; ++j) w[j] = conv_w[static_cast<int64_t>(c) * KW + j];
+    bias = conv_b ? conv_b[c] : 0.f;
+  }
+};
+
+// Conv + SiLU of `nch` channels over the S slots from a loaded window:
+// out[s * ostride + cc] = SiLU(b[c] + sum_j w[c][j] win[(s + j) * stride + cc]).
+// nch divides the thread count NT, so each thread keeps one channel and its
+// taps (cc = threadIdx.x % nch).
+template <int KW, int NT, int nch>
+__device__ __forceinline__ void conv_window(const float* win, int stride, int S, const Taps<KW>& tp,
                                             float* out, int ostride) {
   static_assert(NT % nch == 0, "one channel per thread");
   const int cc = threadIdx.x % nch;
-  const int c = chan(cc);
-  float w[KW];
-#pragma unroll
-  for (int j = 0; j < KW; ++j) w[j] = conv_w[static_cast<int64_t>(c) * KW + j];
-  const float bias = conv_b ? conv_b[c] : 0.f;
   for (int si = threadIdx.x / nch; si < S; si += NT / nch) {
-    float acc = bias;
+    float acc = tp.bias;
 #pragma unroll
-    for (int j = 0; j < KW; ++j) acc = fmaf(w[j], win[(si + j) * stride + cc], acc);
+    for (int j = 0; j < KW; ++j) acc = fmaf(tp.w[j], win[(si + j) * stride + cc], acc);
     out[si * ostride + cc] = silu(acc);
   }
 }
 
 // Per (sequence, group): the conv outputs of the group's B and C channels,
-// [S][2N] fp32, and G[s][j] = C_s . B_j for j <= s (0 above), [S][S] -- the
-// parts every head of the group shares.
+// [S][2N] fp32, and G[s][j] = C_s . B_j for j <= s, 0 elsewhere, as
+// [Sp][Sp] (S rounded up to 16) -- the parts every head of the group
+// shares.
 template <typename T, int N, int KW>
 __global__ __launch_bounds__(kMThreads) void mamba_group_kernel(MambaArgs a, float* ws_bc, float* ws_g) {
   const int b = blockIdx.x / a.G;
   const int g = blockIdx.x % a.G;
   if (a.active && !a.active[b]) return;
   const int S = a.S, H = a.H, G = a.G, P = a.P;
+  const int Sp = (S + kSC - 1) / kSC * kSC;
   const int C = H * P + 2 * G * N;
   constexpr int BCP = 2 * N + 4;         // LDS row stride (rows start 4 banks apart)
+  // one batch of loads covers the window of 16 slots
+  constexpr int kU = ((kSC + KW - 1) * 2 * N + kMThreads - 1) / kMThreads;
   extern __shared__ float lds[];
   float* win = lds;                      // [S + KW-1][BCP]
   float* out = lds + (S + KW - 1) * BCP; // [S][BCP]
   const T* xbc = static_cast<const T*>(a.xbc) + static_cast<int64_t>(b) * S * C;
   const T* cst = static_cast<const T*>(a.conv_state) + static_cast<int64_t>(b) * C * (KW - 1);
   auto chan = [&](int cc) { return H * P + (cc < N ? g * N + cc : G * N + g * N + (cc - N)); };
-  load_window<T, KW, kMThreads, 2 * N>(xbc, cst, C, S, chan, win, BCP);
+  Taps<KW> tp;
+  tp.load(a.conv_w, a.conv_b, chan(threadIdx.x % (2 * N)));
+  load_window<T, KW, kMThreads, 2 * N, kU>(xbc, cst, C, 0, S + KW - 1, chan, win, BCP);
   __syncthreads();
-  conv_window<KW, kMThreads, 2 * N>(win, BCP, S, chan, a.conv_w, a.conv_b, out, BCP);
+  conv_window<KW, kMThreads, 2 * N>(win, BCP, S, tp, out, BCP);
   __syncthreads();
   float* bc = ws_bc + (static_cast<int64_t>(b) * G + g) * S * 2 * N;
   for (int i = threadIdx.x; i < S * 2 * N / 4; i += kMThreads) {
     const int si = (4 * i) / (2 * N), cc = (4 * i) % (2 * N);
     *reinterpret_cast<float4*>(bc + 4 * i) = *reinterpret_cast<const float4*>(out + si * BCP + cc);
   }
-  float* gm = ws_g + (static_cast<int64_t>(b) * G + g) * S * S;
+  float* gm = ws_g + (static_cast<int64_t>(b) * G + g) * Sp * Sp;
   // (si, j) pairs, 16 j per pass over a row (no division by the runtime S)
-  for (int si = threadIdx.x >> 4; si < S; si += kMThreads >> 4)
-  for (int j = threadIdx.x & 15; j < S; j += 16) {
-    const int k = si * S + j;
-    float d = 0.f;
-    if (j <= si) {
-      const float* cs = out + si * BCP + N;
-      const float* bs = out + j * BCP;
+  for (int si = threadIdx.x >> 4; si < Sp; si += kMThreads >> 4)
+    for (int j = threadIdx.x & 15; j < Sp; j += 16) {
+      float d = 0.f;
+      if (j <= si && si < S) {
+        const float* cs = out + si * BCP + N;
+        const float* bs = out + j * BCP;
 #pragma unroll 4
-      for (int n = 0; n < N; n += 4) {
-        const float4 x4 = *reinterpret_cast<const float4*>(cs + n);
-        const float4 y4 = *reinterpret_cast<const float4*>(bs + n);
-        d = fmaf(x4.x, y4.x, fmaf(x4.y, y4.y, fmaf(x4.z, y4.z, fmaf(x4.w, y4.w, d))));
+        for (int n = 0; n < N; n += 4) {
+          const float4 x4 = *reinterpret_cast<const float4*>(cs + n);
+          const float4 y4 = *reinterpret_cast<const float4*>(bs + n);
+          d = fmaf(x4.x, y4.x, fmaf(x4.y, y4.y, fmaf(x4.z, y4.z, fmaf(x4.w, y4.w, d))));
+        }
       }
+      gm[si * Sp + j] = d;
     }
-    gm[k] = d;
-  }
 }
+
+// The global inputs of one round of 16 slots of the scan kernel: the
+// group's B/C rows, the head's x window rows and the G rows, held in
+// registers (the caller's arrays) between their loads and their LDS stores.
+template <typename T, int P, int N, int KW, int NT>
+struct ScanRound {
+  static constexpr int kBC = (kSC * 2 * N / 4 + NT - 1) / NT;       // float4 of B/C rows
+  static constexpr int kWn = ((kSC + KW - 1) * P + NT - 1) / NT;    // window elements
+  static constexpr int kG = (kSC * 64 / 4 + NT - 1) / NT;           // float4 of G rows (Sp <= 64)
+
+  // window rows [rw0, rw1) of round r0: round 0 also takes the W-1 rows of
+  // the conv state
+  static __device__ __forceinline__ int rw0(int r0) { return r0 == 0 ? 0 : r0 + KW - 1; }
+  static __device__ __forceinline__ int rw1(int r0, int S) { return min(r0 + kSC, S) + KW - 1; }
+
+  static __device__ __forceinline__ void issue(v4f (&bc)[kBC], uint32_t (&w)[kWn], v4f (&gv)[kG],
+                                               const float* bcg, const float* gmg, const T* xbc,
+                                               const T* cst, int C, int h, int S, int Sp, int r0) {
+    const int tid = threadIdx.x;
+    const int nbc = (min(r0 + kSC, S) - r0) * 2 * N / 4;
+#pragma unroll
+    for (int u = 0; u < kBC; ++u)
+      bc[u] = reinterpret_cast<const v4f*>(bcg + r0 * 2 * N)[min(u * NT + tid, nbc - 1)];
+    const int w0 = rw0(r0), nw = (rw1(r0, S) - w0) * P;
+#pragma unroll
+    for (int u = 0; u < kWn; ++u) {
+      const int i = min(u * NT + tid, nw - 1);
+      const int r = w0 + i / P, c = h * P + i % P;
+      const int t = r - (KW - 1);
+      const T* src = t < 0 ? cst + static_cast<int64_t>(c) * (KW - 1) + r
+                           : xbc + static_cast<int64_t>(t) * C + c;
+      w[u] = ld_raw(src);
+    }
+    const int ng = kSC * Sp / 4;           // 16 rows of G, each Sp wide
+#pragma unroll
+    for (int u = 0; u < kG; ++u)
+      gv[u] = reinterpret_cast<const v4f*>(gmg + r0 * Sp)[min(u * NT + tid, ng - 1)];
+  }
+
+  // Unconditional stores with the loads' clamped indexes: a lane past the
+  // end writes the last element's value to the last element's place (the
+  // same bytes its owner writes).  A conditional store would let the
+  // compiler sink each load into its branch, one wait per load.
+  static __device__ __forceinline__ void commit(const v4f (&bc)[kBC], const uint32_t (&w)[kWn],
+                                                const v4f (&gv)[kG], float* s_b, int c_off,
+                                                float* s_win, float* s_m, int S, int Sp, int r0,
+                                                int BP, int XP) {
+    const int tid = threadIdx.x;
+    const int nbc = (min(r0 + kSC, S) - r0) * 2 * N / 4;
+#pragma unroll
+    for (int u = 0; u < kBC; ++u) {
+      const int i = min(u * NT + tid, nbc - 1);
+      const int si = r0 + (4 * i) / (2 * N), cc = (4 * i) % (2 * N);
+      // B channels to s_b, C channels to s_b + c_off (a select, not a branch)
+      const int off = si * BP + cc + (cc >= N ? c_off - N : 0);
+      *reinterpret_cast<v4f*>(s_b + off) = bc[u];
+    }
+    const int w0 = rw0(r0), nw = (rw1(r0, S) - w0) * P;
+#pragma unroll
+    for (int u = 0; u < kWn; ++u) {
+      const int i = min(u * NT + tid, nw - 1);
+      s_win[(w0 + i / P) * XP + i % P] = raw_f32<T>(w[u]);
+    }
+    const int ng = kSC * Sp / 4;
+#pragma unroll
+    for (int u = 0; u < kG; ++u)
+      reinterpret_cast<v4f*>(s_m + r0 * Sp)[min(u * NT + tid, ng - 1)] = gv[u];
+  }
+};
 
 // Per (sequence, head): P/16 waves; wave w owns state rows 16w..16w+15, lane
 // l row p = 16w + l%16 and entries n in [kg*KS, kg*KS + KS), kg = l/16,
 // KS = N/4.  The outputs of 16 slots at a time are one 16 x 16 fp32 matrix
 // tile per wave, accumulated by v_mfma_f32_16x16x4f32 in two parts:
-//   H0 (exp(cum_s) C_s)  -- K = N, taken in the order n = kg*KS + t at step
+//   H0 C_s               -- K = N, taken in the order n = kg*KS + t at step
 //                            t, so each lane's A operand is its own state
-//                            entry t and its B operand C'[s][kg*KS + t];
+//                            entry t and its B operand C[s][kg*KS + t]; the
+//                            tile is then scaled by the decay exp(cum_s);
 //   X^T M^T              -- K = the slots j (4 per step), the in-block sum
 //                            sum_j M[s][j] x_j[p] (M is 0 for j > s).
 // Lane l then holds y at slot s0 + l%16 for rows 16w + 4 kg + r, r < 4.
+// Global loads: the round's inputs first, then the seed's state (most of
+// the bytes) -- waiting for the former leaves the latter in flight.
 template <typename T, int P, int N, int KW>
 __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const float* ws_bc,
                                                           const float* ws_g) {
   constexpr int NT = 4 * P;              // P/16 waves of 64
   constexpr int KS = N / 4;              // state entries per lane
-  constexpr int SC = 16;                 // slots per output tile
   static_assert(KS % 4 == 0, "16-byte state loads");
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   const int b = blockIdx.x / a.H;
@@ -180,7 +280,7 @@ __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const fl
   if (a.active && !a.active[b]) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.S, H = a.H, G = a.G;
-  const int Sp = (S + SC - 1) / SC * SC; // slots rounded up to whole tiles (zero padded)
+  const int Sp = (S + kSC - 1) / kSC * kSC; // slots rounded up to whole tiles (zero padded)
   constexpr int W = KW;
   const int g = h / (H / G);
   const int C = H * P + 2 * G * N;
@@ -190,73 +290,80 @@ __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const fl
   float* s_win = lds;                    // [S + W-1][XP]  x inputs
   float* s_x = s_win + (S + W - 1) * XP; // [Sp][XP]       conv outputs of the head's x
   float* s_b = s_x + Sp * XP;            // [S][BP]        the group's B
-  float* s_c = s_b + S * BP;             // [Sp][BP]       exp(cum_s) C_s
-  float* s_dt = s_c + Sp * BP;           // [S]  dt_s
-  float* s_cum = s_dt + S;               // [S]  sum_{k<=s} dt_k A  (log of the decay)
-  float* s_dec = s_cum + S;              // [S]  exp(cum_s)
-  float* s_m = s_dec + S;                // [Sp][Sp]  dt_j exp(cum_s - cum_j) G[s][j]
+  float* s_c = s_b + S * BP;             // [Sp][BP]       the group's C
+  float* s_dt = s_c + Sp * BP;           // [Sp] dt_s
+  float* s_cum = s_dt + Sp;              // [Sp] sum_{k<=s} dt_k A  (log of the decay)
+  float* s_dec = s_cum + Sp;             // [Sp] exp(cum_s), 0 past S
+  float* s_m = s_dec + Sp;               // [Sp][Sp]  G, then dt_j exp(cum_s - cum_j) G[s][j]
   const T* xbc = static_cast<const T*>(a.xbc) + static_cast<int64_t>(b) * S * C;
   const T* cst = static_cast<const T*>(a.conv_state) + static_cast<int64_t>(b) * C * (W - 1);
+  const float* bcg = ws_bc + (static_cast<int64_t>(b) * G + g) * S * 2 * N;
+  const float* gmg = ws_g + (static_cast<int64_t>(b) * G + g) * Sp * Sp;
 
-  // ---- every global load of the workgroup first: the seed's state (most
-  // of the HBM traffic), the group's B/C outputs, the x window, dt
+  // ---- global loads: dt of slot `lane`, round 0's inputs, the seed state
+  const float dtr = a.dt_raw[(static_cast<int64_t>(b) * S + min(lane, S - 1)) * H + h];
+  const float A = -expf(a.A_log[h]);
+  const float dtb = a.dt_bias ? a.dt_bias[h] : 0.f;
+  const float Dh = a.D ? a.D[h] : 0.f;
+  Taps<KW> tp;
+  tp.load(a.conv_w, a.conv_b, h * P + tid % P);
+  using RD = ScanRound<T, P, N, KW, NT>;
   const int pl = lane & 15, kg = lane >> 4;
   const int p = wave * 16 + pl;
   const int64_t sbase = ((static_cast<int64_t>(b) * H + h) * P + p) * N + kg * KS;
   float st[KS];
+  {
+    v4f bc[RD::kBC];
+    uint32_t w[RD::kWn];
+    v4f gv[RD::kG];
+    RD::issue(bc, w, gv, bcg, gmg, xbc, cst, C, h, S, Sp, 0);
+    // a scheduling fence keeps the round's loads ahead of the state's, so
+    // that waiting for the former leaves the latter in flight
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int j = 0; j < KS; j += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(a.ssm_state + sbase + j);
-    st[j] = v.x; st[j + 1] = v.y; st[j + 2] = v.z; st[j + 3] = v.w;
+    for (int j = 0; j < KS; j += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(a.ssm_state + sbase + j);
+      st[j] = v.x; st[j + 1] = v.y; st[j + 2] = v.z; st[j + 3] = v.w;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    RD::commit(bc, w, gv, s_b, S * BP, s_win, s_m, S, Sp, 0, BP, XP);
   }
-  const float* bc = ws_bc + (static_cast<int64_t>(b) * G + g) * S * 2 * N;
-  for (int i = tid; i < S * 2 * N / 4; i += NT) {
-    const int si = (4 * i) / (2 * N), cc = (4 * i) % (2 * N);
-    float* dst = cc < N ? s_b + si * BP + cc : s_c + si * BP + (cc - N);
-    *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(bc + 4 * i);
+  for (int r0 = kSC; r0 < S; r0 += kSC) {
+    v4f bc[RD::kBC];
+    uint32_t w[RD::kWn];
+    v4f gv[RD::kG];
+    RD::issue(bc, w, gv, bcg, gmg, xbc, cst, C, h, S, Sp, r0);
+    RD::commit(bc, w, gv, s_b, S * BP, s_win, s_m, S, Sp, r0, BP, XP);
   }
-  auto chan = [&](int cc) { return h * P + cc; };
-  load_window<T, KW, NT, P>(xbc, cst, C, S, chan, s_win, XP);
-  const float A = -expf(a.A_log[h]);
-  if (tid < S) {
-    s_dt[tid] = softplus(a.dt_raw[(static_cast<int64_t>(b) * S + tid) * H + h] +
-                         (a.dt_bias ? a.dt_bias[h] : 0.f));
+  // dt, and the decay's log as an inclusive prefix sum over the slots
+  // (wave 0, lane = slot; S <= 64)
+  if (wave == 0) {
+    const float dt = softplus(dtr + dtb);
+    float cum = lane < S ? dt * A : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float v = __shfl_up(cum, o);
+      if (lane >= o) cum += v;
+    }
+    if (lane < Sp) {
+      s_dt[lane] = dt;
+      s_cum[lane] = cum;
+      s_dec[lane] = lane < S ? expf(cum) : 0.f;
+    }
   }
   __syncthreads();
-  conv_window<KW, NT, P>(s_win, XP, S, chan, a.conv_w, a.conv_b, s_x, XP);
+  conv_window<KW, NT, P>(s_win, XP, S, tp, s_x, XP);
   for (int i = tid; i < (Sp - S) * XP; i += NT) s_x[S * XP + i] = 0.f;
-  if (tid == 0) {                        // prefix sum of the log decays (S <= 64)
-    float cum = 0.f;
-    for (int i = 0; i < S; ++i) {
-      cum = fmaf(s_dt[i], A, cum);
-      s_cum[i] = cum;
-      s_dec[i] = expf(cum);
-    }
-  }
-  __syncthreads();
-  // C rows scaled by the decay from the seed, zero rows past S; M
-  for (int i = tid; i < Sp * (N / 4); i += NT) {
-    const int si = i / (N / 4), n = 4 * (i % (N / 4));
-    float4* cp = reinterpret_cast<float4*>(s_c + si * BP + n);
-    if (si < S) {
-      const float dec = s_dec[si];
-      const float4 v = *cp;
-      *cp = make_float4(v.x * dec, v.y * dec, v.z * dec, v.w * dec);
-    } else {
-      *cp = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-  const float* gm = ws_g + (static_cast<int64_t>(b) * G + g) * S * S;
   for (int si = tid >> 4; si < Sp; si += NT >> 4)
-    for (int j = tid & 15; j < Sp; j += 16)
-      s_m[si * Sp + j] =
-          (j <= si && si < S) ? s_dt[j] * expf(s_cum[si] - s_cum[j]) * gm[si * S + j] : 0.f;
+    for (int j = tid & 15; j < Sp; j += 16) {
+      float* m = s_m + si * Sp + j;
+      *m = (j <= si && si < S) ? s_dt[j] * expf(s_cum[si] - s_cum[j]) * *m : 0.f;
+    }
   __syncthreads();
 
   // ---- outputs, one 16-slot tile at a time
-  const float Dh = a.D ? a.D[h] : 0.f;
   T* y = static_cast<T*>(a.y) + (static_cast<int64_t>(b) * S) * (H * P) + h * P + wave * 16 + 4 * kg;
-  for (int s0 = 0; s0 < Sp; s0 += SC) {
+  for (int s0 = 0; s0 < Sp; s0 += kSC) {
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
     const float* crow = s_c + (s0 + pl) * BP + kg * KS;
 #pragma unroll
@@ -267,14 +374,28 @@ __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const fl
       d = __builtin_amdgcn_mfma_f32_16x16x4f32(st[t + 2], cv.z, d, 0, 0, 0);
       d = __builtin_amdgcn_mfma_f32_16x16x4f32(st[t + 3], cv.w, d, 0, 0, 0);
     }
+    // rows of C past S hold stale values: they reach only the tile columns
+    // of slots past S, which nothing stores
+    const float dec = s_dec[s0 + pl];
+    d *= dec;
     const float* mrow = s_m + (s0 + pl) * Sp;
-    for (int j0 = 0; j0 < s0 + SC; j0 += 4)
+    for (int j0 = 0; j0 < s0 + kSC; j0 += 4)
       d = __builtin_amdgcn_mfma_f32_16x16x4f32(s_x[(j0 + kg) * XP + p], mrow[j0 + kg], d, 0, 0, 0);
     const int si = s0 + pl;
     if (si < S) {
-      const float* xr = s_x + si * XP + wave * 16 + 4 * kg;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) st_elt(y, static_cast<int64_t>(si) * (H * P) + r, d[r] + Dh * xr[r]);
+      const float4 xr = *reinterpret_cast<const float4*>(s_x + si * XP + wave * 16 + 4 * kg);
+      const float o0 = d[0] + Dh * xr.x, o1 = d[1] + Dh * xr.y;
+      const float o2 = d[2] + Dh * xr.z, o3 = d[3] + Dh * xr.w;
+      T* yo = y + static_cast<int64_t>(si) * (H * P);
+      if constexpr (std::is_same<T, float>::value) {
+        *reinterpret_cast<float4*>(yo) = make_float4(o0, o1, o2, o3);
+      } else {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(o0)) |
+                            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(o1))) << 16);
+        const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(o2)) |
+                            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(o3))) << 16);
+        *reinterpret_cast<uint2*>(yo) = make_uint2(lo, hi);
+      }
     }
   }
 
@@ -283,7 +404,7 @@ __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const fl
   // has read its part), and the conv state = the last W-1 inputs
   if (a.ssm_state_out) {
     const float last = s_cum[S - 1];
-    const float d0 = expf(last);
+    const float d0 = s_dec[S - 1];
 #pragma unroll
     for (int n = 0; n < KS; ++n) st[n] *= d0;
     for (int j = 0; j < S; ++j) {
@@ -370,7 +491,7 @@ size_t mamba_lds_bytes(int S, int P, int N) {
   // (2S + 3) (2N + 4) floats, checked separately
   const size_t Sp = (S + 15) / 16 * 16;
   return (static_cast<size_t>(S + 3 + Sp) * (P + 4) + static_cast<size_t>(S + Sp) * (N + 4) +
-          3 * static_cast<size_t>(S) + Sp * Sp) * sizeof(float);
+          3 * Sp + Sp * Sp) * sizeof(float);
 }
 
 size_t mamba_group_lds_bytes(int S, int N) {
@@ -378,7 +499,9 @@ size_t mamba_group_lds_bytes(int S, int N) {
 }
 
 size_t mamba_workspace_bytes(int B, int S, int G, int N) {
-  return static_cast<size_t>(B) * G * S * (2 * N + S) * sizeof(float);
+  // per (sequence, group): the B/C conv outputs [S][2N] and G [Sp][Sp]
+  const size_t Sp = (S + 15) / 16 * 16;
+  return static_cast<size_t>(B) * G * (static_cast<size_t>(S) * 2 * N + Sp * Sp) * sizeof(float);
 }
 
 hipError_t launch_mamba_scan(const MambaArgs& a, void* ws, hipStream_t st) {

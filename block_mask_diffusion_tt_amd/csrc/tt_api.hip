@@ -269,6 +269,8 @@ tt_status tt_mamba_block_scan(const tt_mamba_shape* shape, const void* xbc, cons
   const void* ptrs[] = {xbc, conv_state, y, conv_state_out};
   for (const void* t : ptrs)
     if (t && !aligned(t, e)) return fail(TT_ERR_INVALID_ARG, "%s: misaligned xbc/conv_state/y buffer", fn);
+  if (!aligned(y, 4 * e))
+    return fail(TT_ERR_INVALID_ARG, "%s: y must be aligned to 4 elements (%zu bytes)", fn, 4 * e);
   const void* fptrs[] = {dt_raw, conv_w, conv_b, A_log, dt_bias, D};
   for (const void* t : fptrs)
     if (t && !aligned(t, 4)) return fail(TT_ERR_INVALID_ARG, "%s: misaligned fp32 parameter", fn);

@@ -456,7 +456,8 @@ tt_status tt_generate(const tt_attn_shape* shape, int32_t n_layers, int32_t n_bl
  *          {64, 128}, n_groups G (divides H), conv_width W in [2, 4]
  *          (Mamba-2's is 4; [5, 8] returns TT_ERR_UNSUPPORTED),
  *          block_size S in [1, 64], dtype of xbc / conv states / y.
- *   xbc [B, S, C] and y [B, S, H*P] (dtype), C = H*P + 2*G*N;
+ *   xbc [B, S, C] and y [B, S, H*P] (dtype; y aligned to 4 elements),
+ *   C = H*P + 2*G*N;
  *   dt_raw [B, S, H] fp32; conv_state [B, C, W-1] (dtype);
  *   ssm_state [B, H, P, N] fp32 (16-byte aligned);
  *   conv_w [C, W], conv_b [C] or NULL, A_log [H], dt_bias [H] or NULL,
@@ -465,7 +466,7 @@ tt_status tt_generate(const tt_attn_shape* shape, int32_t n_layers, int32_t n_bl
  * even for bf16.  The workspace (tt_mamba_workspace_size bytes, 16-byte
  * aligned, no initialisation) holds the B/C conv outputs and C.B products
  * the heads of a group share.  Errors: TT_ERR_INVALID_ARG (NULL required
- * pointer, bad sizes, G not dividing H, misaligned state),
+ * pointer, bad sizes, G not dividing H, misaligned state or y),
  * TT_ERR_UNSUPPORTED (P, N or W outside the sets above), TT_ERR_WORKSPACE,
  * TT_ERR_HIP.
  * ---------------------------------------------------------------------- */
