@@ -66,7 +66,9 @@ __device__ __forceinline__ void st_elt(uint16_t* p, int64_t i, float v) {
 }
 __device__ __forceinline__ void st_elt(float* p, int64_t i, float v) { p[i] = v; }
 
-__device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
+// SiLU with the hardware reciprocal (about 1 ulp) instead of an IEEE
+// divide; v -> -inf gives v * rcp(inf) = -0
+__device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.f + __expf(-v)); }
 __device__ __forceinline__ float softplus(float v) { return v > 20.f ? v : log1pf(expf(v)); }
 
 // Slots are handled in rounds of 16 (one 16 x 16 output tile per wave).
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const fl
   for (int si = tid >> 4; si < Sp; si += NT >> 4)
     for (int j = tid & 15; j < Sp; j += 16) {
       float* m = s_m + si * Sp + j;
-      *m = (j <= si && si < S) ? s_dt[j] * expf(s_cum[si] - s_cum[j]) * *m : 0.f;
+      *m = (j <= si && si < S) ? s_dt[j] * __expf(s_cum[si] - s_cum[j]) * *m : 0.f;
     }
   __syncthreads();
 
