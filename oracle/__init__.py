@@ -51,6 +51,14 @@ What is pinned, and how (tests/test_oracle_*.py):
                     concatenation from zero states; the convolution against
                     numpy.convolve; closed forms (instant decay, zero step);
                     causality inside the block; brute force.
+  weighted       -- LayerNorm against torch's fp64 layer_norm, its D = 2
+  sublayer          closed form, zero mean / unit variance and affine
+                    invariance; modulation special cases; selection weights
+                    reducing the sublayer to the pinned block attention (q|k|v
+                    column order, head reshape, O projection, gate); scalar-
+                    loop brute force; block-slot permutation; gate = 0 and
+                    W_o = 0 leave x.  The placement (the published
+                    adaLN-single one) is a reading of the pages.
   adaLN-single   -- SiLU(0)=0, sinusoid special values, scalar-loop brute
                     force of the affine map.  The PLACEMENT of scale/shift/gate
                     and the timestep definition are readings the pages do not
@@ -81,6 +89,14 @@ from .sampling import (  # noqa: F401
     row_sample,
 )
 from .generate import generate  # noqa: F401
+from .sublayer import (  # noqa: F401
+    layer_norm,
+    ln_modulate,
+    linear,
+    split_qkv,
+    gate_residual,
+    adaln_attn_sublayer,
+)
 from .mamba import (  # noqa: F401
     causal_conv,
     mamba_block_scan,

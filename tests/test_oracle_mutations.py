@@ -12,6 +12,7 @@ import oracle.context as context_src
 import oracle.generate as generate_src
 import oracle.mamba as mamba_src
 import oracle.sampling as sampling_src
+import oracle.sublayer as sublayer_src
 import oracle.unmask as unmask_src
 
 from . import test_oracle_attention as TA
@@ -19,6 +20,7 @@ from . import test_oracle_context as TC
 from . import test_oracle_generate as TG
 from . import test_oracle_mamba as TM
 from . import test_oracle_sampling as TS
+from . import test_oracle_sublayer as TL
 from . import test_oracle_unmask as TU
 
 ATTN_PINS = [TA.test_p1_empty_context_is_library_attention,
@@ -128,6 +130,28 @@ MAMBA_MUTANTS = [
      "A = np.exp(_f64(A_log))\n    y = np.empty((Bn, S, H, P))\n    new_conv"),  # growing state
 ]
 
+SUBLAYER_PINS = [TL.test_l1_layer_norm_is_library_layer_norm,
+                 TL.test_l2_l3_layer_norm_closed_form_and_invariants,
+                 TL.test_m1_modulation_special_cases, TL.test_linear_and_split_brute_force,
+                 TL.test_s1_gate_and_inactive_special_cases,
+                 TL.test_s2_selection_weights_reduce_to_block_attention,
+                 TL.test_s3_brute_force_tiny, TL.test_s4_block_permutation]
+
+SUBLAYER_MUTANTS = [
+    ("var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)",
+     "var = ((x - mu) ** 2).sum(axis=-1, keepdims=True) / (x.shape[-1] - 1)"),   # sample variance
+    ("return (x - mu) / np.sqrt(var + eps)", "return (x - mu) / np.sqrt(var)"),  # eps dropped
+    ("(1.0 + _f64(scale)[:, None, :])", "_f64(scale)[:, None, :]"),              # dropped the 1
+    ("+ _f64(shift)[:, None, :]", "- _f64(shift)[:, None, :]"),                  # wrong sign of shift
+    ("k = qkv[..., nq:nq + nk]", "k = qkv[..., nq + nk:]"),                       # k takes v's columns
+    ("return _f64(x) @ _f64(w).T", "return _f64(x) @ _f64(w)[:, ::-1].T"),       # reversed input order
+    ("return _f64(x) + _f64(gate)[:, None, :] * _f64(y)", "return _f64(x) + _f64(y)"),  # no gate
+    ("y = linear(o.reshape(B, S, n_q_heads * head_dim), w_o)",
+     "y = linear(o.transpose(0, 1, 3, 2).reshape(B, S, n_q_heads * head_dim), w_o)"),  # head/channel order
+    ("o, _ = block_attn(q, k, v, k_ctx, v_ctx, ctx_start, ctx_len, active=active)",
+     "o, _ = block_attn(q, k, v, k_ctx, v_ctx, ctx_start, 0 * np.asarray(ctx_len), active=active)"),
+]
+
 UNMASK_MUTANTS = [
     ("conf[b, s] >= g or", "conf[b, s] > g or"),                # exclusive threshold
     ("np.flatnonzero(x == m)[0]", "np.flatnonzero(x == m)[-1]"),  # highest id on ties
@@ -198,6 +222,15 @@ def test_mamba_mutant_is_caught(monkeypatch, old, new):
     for name in ("softplus", "silu", "causal_conv", "mamba_block_scan"):
         monkeypatch.setattr(mamba_src, name, getattr(mod, name))
     assert _caught(MAMBA_PINS)
+
+
+@pytest.mark.parametrize("old,new", SUBLAYER_MUTANTS)
+def test_sublayer_mutant_is_caught(monkeypatch, old, new):
+    mod = _mutant(sublayer_src, old, new)
+    for name in ("layer_norm", "ln_modulate", "linear", "split_qkv", "gate_residual",
+                 "adaln_attn_sublayer"):
+        monkeypatch.setattr(sublayer_src, name, getattr(mod, name))
+    assert _caught(SUBLAYER_PINS)
 
 
 @pytest.mark.parametrize("old,new", UNMASK_MUTANTS)
