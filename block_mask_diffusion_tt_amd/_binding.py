@@ -29,7 +29,8 @@ EXPORTED = ["tt_last_error", "tt_abi_version", "tt_block_attn_workspace_size", "
             "tt_unmask_workspace_size", "tt_confidence_unmask", "tt_denoise_workspace_size",
             "tt_denoise_block", "tt_ctx_block_attn", "tt_ctx_advance", "tt_sample_unmask",
             "tt_generate_workspace_size", "tt_generate", "tt_mamba_workspace_size",
-            "tt_mamba_block_scan"]
+            "tt_mamba_block_scan", "tt_ln_modulate", "tt_qkv_proj", "tt_out_proj",
+            "tt_adaln_sublayer_workspace_size", "tt_adaln_attn_sublayer"]
 
 
 class TTError(RuntimeError):
@@ -107,6 +108,12 @@ def _load():
         "tt_mamba_workspace_size": (sz, [ctypes.POINTER(MambaShape)]),
         "tt_mamba_block_scan": (ctypes.c_int, [ctypes.POINTER(MambaShape), vp, vp, vp, vp, vp, vp,
                                                vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "tt_ln_modulate": (ctypes.c_int, [shp, i32, vp, vp, vp, vp, vp, vp]),
+        "tt_qkv_proj": (ctypes.c_int, [shp, i32, vp, vp, vp, vp, vp, vp, vp]),
+        "tt_out_proj": (ctypes.c_int, [shp, i32, vp, vp, vp, vp, vp, vp, vp]),
+        "tt_adaln_sublayer_workspace_size": (sz, [shp, i32, i32]),
+        "tt_adaln_attn_sublayer": (ctypes.c_int, [shp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                  vp, i32, vp, vp, vp, sz, vp]),
         "tt_generate": (ctypes.c_int, [shp, i32, i32, i32, f32, f32, i32, ctypes.c_uint64, i32,
                                        i32, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp,
                                        ctypes.POINTER(GenProvider), vp, vp, vp,
@@ -434,3 +441,36 @@ def mamba_block_scan(shape, xbc, dt_raw, conv_state, ssm_state, conv_w, A_log, y
                                     _ptr(dt_bias), _ptr(D), _ptr(active), _ptr(y),
                                     _ptr(conv_state_out), _ptr(ssm_state_out), _ptr(workspace),
                                     _nbytes(workspace), _stream(stream)))
+
+
+# ---------------------------------------------------- weighted adaLN sublayer
+
+def ln_modulate(shape, width, x, shift, scale, h, active=None, stream=None):
+    _check(_lib.tt_ln_modulate(ctypes.byref(shape), int(width), _ptr(x), _ptr(shift), _ptr(scale),
+                               _ptr(active), _ptr(h), _stream(stream)))
+
+
+def qkv_proj(shape, width, h, w_qkv, q_blk, k_blk, v_blk, active=None, stream=None):
+    _check(_lib.tt_qkv_proj(ctypes.byref(shape), int(width), _ptr(h), _ptr(w_qkv), _ptr(active),
+                            _ptr(q_blk), _ptr(k_blk), _ptr(v_blk), _stream(stream)))
+
+
+def out_proj(shape, width, o, w_o, gate, x, out, active=None, stream=None):
+    _check(_lib.tt_out_proj(ctypes.byref(shape), int(width), _ptr(o), _ptr(w_o), _ptr(gate),
+                            _ptr(x), _ptr(active), _ptr(out), _stream(stream)))
+
+
+def adaln_sublayer_workspace_size(shape, width, max_ctx_len):
+    n = _lib.tt_adaln_sublayer_workspace_size(ctypes.byref(shape), int(width), int(max_ctx_len))
+    if n == 0:
+        raise TTError(TT_ERR_INVALID_ARG, last_error())
+    return n
+
+
+def adaln_attn_sublayer(shape, width, x, shift, scale, gate, w_qkv, w_o, k_ctx, v_ctx, ctx_start,
+                        ctx_len, max_ctx_len, out, workspace, active=None, stream=None):
+    _check(_lib.tt_adaln_attn_sublayer(ctypes.byref(shape), int(width), _ptr(x), _ptr(shift),
+                                       _ptr(scale), _ptr(gate), _ptr(w_qkv), _ptr(w_o), _ptr(k_ctx),
+                                       _ptr(v_ctx), _ptr(ctx_start), _ptr(ctx_len),
+                                       int(max_ctx_len), _ptr(active), _ptr(out), _ptr(workspace),
+                                       _nbytes(workspace), _stream(stream)))

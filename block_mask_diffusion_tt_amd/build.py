@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtt.so")
-SOURCES = ["attn.hip", "unmask.hip", "adaln.hip", "context.hip", "mamba.hip", "tt_api.hip"]
+SOURCES = ["attn.hip", "unmask.hip", "adaln.hip", "context.hip", "mamba.hip", "sublayer.hip", "tt_api.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are disabled for every device pass.
@@ -40,10 +40,14 @@ def _run(cmd):
     return out
 
 
+# Files whose kernels write M0 themselves (inline asm right before each direct
+# global->LDS copy).
+M0_ASM = ["attn.hip", "sublayer.hip"]
+
+
 def _check_m0(asm_path):
-    """The attention kernel writes M0 itself (inline asm right before each
-    direct global->LDS copy).  Fail the build if the compiler also uses M0
-    anywhere in that file, since nothing would then preserve it."""
+    """Fail the build if the compiler also uses M0 anywhere in a file whose
+    kernels set it by hand, since nothing would then preserve it."""
     lines = open(asm_path).read().splitlines()
     for i, line in enumerate(lines):
         if re.search(r"\bm0\b", line.split(";")[0]):
@@ -68,10 +72,11 @@ def build(verbose=False):
             out = j.result()
             if verbose and out.strip():
                 print(out)
-    asm = os.path.join(BUILD, "attn.s")
-    _run([HIPCC] + CFLAGS + FILE_FLAGS["attn.hip"] +
-         ["--cuda-device-only", "-S", os.path.join(CSRC, "attn.hip"), "-o", asm])
-    _check_m0(asm)
+    for src in M0_ASM:
+        asm = os.path.join(BUILD, src.replace(".hip", ".s"))
+        _run([HIPCC] + CFLAGS + FILE_FLAGS.get(src, []) +
+             ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm])
+        _check_m0(asm)
     tmp = LIB + ".tmp"
     out = _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs)
     if verbose and out.strip():

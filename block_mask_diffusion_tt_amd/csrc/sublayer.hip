@@ -1,0 +1,298 @@
+// The denoiser's weighted adaLN-single attention sublayer around the block
+// attention:
+//   h   = LayerNorm(x) (1 + scale_b) + shift_b       ln_modulate_kernel
+//   q|k|v = h W_qkv^T                                gemm_kernel<kEpiQkv>
+//   o   = block attention (the attention kernels, identity modulation)
+//   out = x + gate_b (o W_o^T)                       gemm_kernel<kEpiGate>
+// [dothoosh] two-tower mechanism section and [modelcard] technical features:
+// every denoiser layer takes a timestep scale, shift and gate through
+// adaLN-single; the layer around them follows the published adaLN-single
+// placement (PixArt-alpha / DiT): LayerNorm without affine (eps 1e-6), the
+// modulation, bias-free projections, the gate on the projected attention
+// output before the residual add.
+//
+// ln_modulate_kernel: one wave per token row; the row stays in registers
+// (bf16, up to 8192 wide), mean and variance by exact two-pass sums and
+// wave reductions, output bf16 (the projection's operand).
+//
+// gemm_kernel: C[M, N] = A[M, K] W[N, K]^T in bf16 with fp32 accumulation
+// on the matrix cores (v_mfma_f32_32x32x16_bf16).  One workgroup of 4 waves
+// per 128 x 128 output tile; K in steps of 64.  A and W tiles stream
+// HBM -> LDS through the direct copy path into a 3-stage ring (two steps in
+// flight while one is multiplied).  LDS rows are 128 bytes (64 k); the
+// 16-byte slot of k-chunk c in row r is c ^ ((r >> 1) & 7), so the 16 rows
+// read together by a matrix-operand load hit 16 different bank groups.
+// Each wave computes a 64 x 64 piece as the transpose C^T = W A^T: the A
+// operand is 32 W rows x 16 k, the B operand 32 A rows x 16 k, so a lane's
+// 16 accumulators are 4 runs of 4 consecutive output columns of one output
+// row, stored as 8-byte groups by the epilogues.  Tiles are numbered
+// M-fastest and handed out in contiguous ranges per XCD (workgroup i runs
+// on XCD i % 8), so the tiles that share W columns share an L2.
+#include <math.h>
+
+#include "tt_internal.h"
+
+namespace tt {
+namespace {
+
+#define TT_LDS __attribute__((address_space(3)))
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 128, kBN = 128, kBK = 64, kNS = 3;
+constexpr int kGThreads = 256;
+constexpr int kTileBytes = kBM * kBK * 2;         // one operand tile: 16 KB
+constexpr int kStageBytes = 2 * kTileBytes;       // A tile, then W tile
+constexpr int kGemmLds = kNS * kStageBytes;       // 96 KB
+constexpr int kCopies = kTileBytes / 1024 / 4;    // 1 KB copies per wave per operand tile
+
+enum { kEpiQkv = 0, kEpiGate = 1 };
+
+// 16-byte global -> LDS copy through the direct path from a wave-uniform
+// base plus a per-lane byte offset: lane i writes LDS bytes
+// [lds + 16 i, lds + 16 i + 16).  In asm so that the compiler does not wait
+// for the copies in flight before every LDS read; the stage waits are
+// explicit.  No register result.
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "s"(lds) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// ------------------------------------------------------- LayerNorm + modulate
+template <int NCH>
+__global__ __launch_bounds__(256) void ln_modulate_kernel(LnArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int m = blockIdx.x * 4 + wave;
+  if (m >= a.M) return;
+  const int b = m / a.S;
+  if (a.active && !a.active[b]) return;
+  const int D = a.D;
+  const uint16_t* xr = a.x + static_cast<int64_t>(m) * D;
+  // 8 channels per lane per 512-wide chunk; the tail chunk's lanes past D
+  // load the row's last 8 channels (dropped below)
+  uint4 raw[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+    raw[c] = *reinterpret_cast<const uint4*>(xr + min(c * 512 + lane * 8, D - 8));
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (c * 512 + lane * 8 < D) {
+      const uint32_t w[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s += bf_lo(w[i]) + bf_hi(w[i]);
+    }
+  }
+  const float mean = wave_sum(s) / static_cast<float>(D);
+  float v = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (c * 512 + lane * 8 < D) {
+      const uint32_t w[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float d0 = bf_lo(w[i]) - mean, d1 = bf_hi(w[i]) - mean;
+        v = fmaf(d0, d0, fmaf(d1, d1, v));
+      }
+    }
+  }
+  const float rstd = 1.f / sqrtf(wave_sum(v) / static_cast<float>(D) + 1e-6f);
+  const float* sh = a.shift + static_cast<int64_t>(b) * D;
+  const float* sc = a.scale + static_cast<int64_t>(b) * D;
+  uint16_t* hr = a.h + static_cast<int64_t>(m) * D;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const int col = c * 512 + lane * 8;
+    if (col < D) {
+      const float4 s0 = *reinterpret_cast<const float4*>(sh + col);
+      const float4 s1 = *reinterpret_cast<const float4*>(sh + col + 4);
+      const float4 k0 = *reinterpret_cast<const float4*>(sc + col);
+      const float4 k1 = *reinterpret_cast<const float4*>(sc + col + 4);
+      const float shv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      const float scv[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+      const uint32_t w[4] = {raw[c].x, raw[c].y, raw[c].z, raw[c].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float y0 = fmaf((bf_lo(w[i]) - mean) * rstd, 1.f + scv[2 * i], shv[2 * i]);
+        const float y1 = fmaf((bf_hi(w[i]) - mean) * rstd, 1.f + scv[2 * i + 1], shv[2 * i + 1]);
+        o[i] = pack2(y0, y1);
+      }
+      *reinterpret_cast<uint4*>(hr + col) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+// --------------------------------------------------------------------- GEMM
+template <int EPI>
+__global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds];
+  const int tiles_m = (a.M + kBM - 1) / kBM;
+  const int tiles = tiles_m * ((a.N + kBN - 1) / kBN);
+  const int bid = blockIdx.x;
+  const int t = (tiles % 8 == 0) ? (bid % 8) * (tiles / 8) + bid / 8 : bid;
+  const int m0 = (t % tiles_m) * kBM, n0 = (t / tiles_m) * kBN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((TT_LDS uint8_t*)smem));
+  TT_LDS const uint8_t* lsm = (TT_LDS const uint8_t*)smem;
+
+  // copies: wave w, copy j fills tile rows (4w + j) * 8 .. +8; lane L row
+  // r = (4w + j) * 8 + L / 8, LDS slot L % 8 <- k-chunk (L % 8) ^ ((r >> 1) & 7);
+  // rows past the matrix end repeat its last row (never stored)
+  uint32_t offa[kCopies], offw[kCopies];
+#pragma unroll
+  for (int j = 0; j < kCopies; ++j) {
+    const int r = (wave * kCopies + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int ra = min(r, a.M - 1 - m0), rw = min(r, a.N - 1 - n0);
+    offa[j] = static_cast<uint32_t>(ra * a.K * 2 + c * 16);
+    offw[j] = static_cast<uint32_t>(rw * a.K * 2 + c * 16);
+  }
+  const uint16_t* abase = a.a + static_cast<int64_t>(m0) * a.K;
+  const uint16_t* wbase = a.w + static_cast<int64_t>(n0) * a.K;
+  auto issue = [&](int kt) {
+    const int st = kt % kNS;
+    const uint32_t la = __builtin_amdgcn_readfirstlane(lds0 + st * kStageBytes + wave * kCopies * 1024);
+    const uint32_t lw = la + kTileBytes;
+    const uint16_t* ab = abase + kt * kBK;
+    const uint16_t* wb = wbase + kt * kBK;
+#pragma unroll
+    for (int j = 0; j < kCopies; ++j) {
+      dma16s(ab, offa[j], la + j * 1024);
+      dma16s(wb, offw[j], lw + j * 1024);
+    }
+  };
+
+  // operand reads: W rows wn*64 + ns*32 + l%32 (A operand), A rows
+  // wm*64 + ms*32 + l%32 (B operand); k-chunk 2 ks + l/32 of step ks
+  const int wn = wave >> 1, wm = wave & 1;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int sw = (l32 >> 1) & 7;
+  int slot[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) slot[ks] = ((2 * ks + half) ^ sw) * 16;
+  const int wrow = (wn * 64 + l32) * 128, arow = (wm * 64 + l32) * 128;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int KT = a.K / kBK;
+  issue(0);
+  if (KT > 1) issue(1);
+  for (int kt = 0; kt < KT; ++kt) {
+    // this step's copies (this wave's) are done once at most the next
+    // step's are in flight; the barrier makes every wave's copies visible
+    // and frees the stage the copy below overwrites (read in step kt-1)
+    if (kt + 1 < KT) wait_vmem<2 * kCopies>(); else wait_vmem<0>();
+    __syncthreads();
+    if (kt + 2 < KT) issue(kt + 2);
+    TT_LDS const uint8_t* sa = lsm + (kt % kNS) * kStageBytes;
+    TT_LDS const uint8_t* sw_ = sa + kTileBytes;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 wf[2], af[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        wf[i] = *reinterpret_cast<TT_LDS const bf16x8*>(sw_ + wrow + i * 32 * 128 + slot[ks]);
+        af[i] = *reinterpret_cast<TT_LDS const bf16x8*>(sa + arow + i * 32 * 128 + slot[ks]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  // ---- epilogue: lane holds C[m][n .. n+3] for m = m0 + wm*64 + j*32 + l%32,
+  // n = n0 + wn*64 + i*32 + 8 g + 4 (l/32), g < 4
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int m = m0 + wm * 64 + j * 32 + l32;
+    if (m >= a.M) continue;
+    const int b = m / a.S;
+    if (a.active && !a.active[b]) continue;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * 64 + i * 32 + 8 * g + 4 * half;
+        if (n >= a.N) continue;
+        const float c0 = acc[i][j][4 * g], c1 = acc[i][j][4 * g + 1];
+        const float c2 = acc[i][j][4 * g + 2], c3 = acc[i][j][4 * g + 3];
+        if constexpr (EPI == kEpiQkv) {
+          uint16_t* dst;
+          if (n < a.nq) dst = a.q + static_cast<int64_t>(m) * a.nq + n;
+          else if (n < a.nq + a.nk) dst = a.k + static_cast<int64_t>(m) * a.nk + (n - a.nq);
+          else dst = a.v + static_cast<int64_t>(m) * a.nk + (n - a.nq - a.nk);
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(c0, c1), pack2(c2, c3));
+        } else {
+          const int64_t o = static_cast<int64_t>(m) * a.N + n;
+          const uint2 xv = *reinterpret_cast<const uint2*>(a.x + o);
+          const float4 gv = *reinterpret_cast<const float4*>(a.gate + static_cast<int64_t>(b) * a.N + n);
+          *reinterpret_cast<uint2*>(a.out + o) =
+              make_uint2(pack2(fmaf(gv.x, c0, bf_lo(xv.x)), fmaf(gv.y, c1, bf_hi(xv.x))),
+                         pack2(fmaf(gv.z, c2, bf_lo(xv.y)), fmaf(gv.w, c3, bf_hi(xv.y))));
+        }
+      }
+  }
+}
+
+}  // namespace
+
+bool ln_supported(int D) { return D >= 8 && D % 8 == 0 && D <= 8192; }
+
+hipError_t launch_ln_modulate(const LnArgs& a, hipStream_t st) {
+  const int nch = (a.D + 511) / 512;
+  const dim3 grid((a.M + 3) / 4), blk(256);
+  switch (nch) {
+#define TT_LN(K) \
+  case K: hipLaunchKernelGGL(ln_modulate_kernel<K>, grid, blk, 0, st, a); break;
+    TT_LN(1) TT_LN(2) TT_LN(3) TT_LN(4) TT_LN(5) TT_LN(6) TT_LN(7) TT_LN(8)
+    TT_LN(9) TT_LN(10) TT_LN(11) TT_LN(12) TT_LN(13) TT_LN(14) TT_LN(15) TT_LN(16)
+#undef TT_LN
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+bool gemm_supported(int M, int N, int K) {
+  // K in whole 64-steps; 4-column output groups; in-tile byte offsets of
+  // the copies fit 32 bits
+  return M >= 1 && N >= 4 && N % 4 == 0 && K >= kBK && K % kBK == 0 &&
+         static_cast<int64_t>(kBM) * K * 2 < (int64_t(1) << 31);
+}
+
+hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
+  const int tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
+  const dim3 grid(tiles), blk(kGThreads);
+  if (epi == kEpiQkv) hipLaunchKernelGGL(gemm_kernel<kEpiQkv>, grid, blk, 0, st, a);
+  else hipLaunchKernelGGL(gemm_kernel<kEpiGate>, grid, blk, 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace tt

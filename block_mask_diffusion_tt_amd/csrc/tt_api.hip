@@ -768,3 +768,228 @@ tt_status tt_generate(const tt_attn_shape* shape, int32_t n_layers, int32_t n_bl
 }
 
 }  // extern "C"
+
+// ------------------------------------------------- weighted adaLN sublayer
+
+namespace {
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const char* x = static_cast<const char*>(a);
+  const char* y = static_cast<const char*>(b);
+  return x < y + nb && y < x + na;
+}
+
+tt_status check_sublayer(const char* fn, const tt_attn_shape* s, int32_t width) {
+  tt_status st = check_shape(s);
+  if (st != TT_OK) return st;
+  if (s->dtype != TT_BF16)
+    return fail(TT_ERR_UNSUPPORTED, "%s: the weighted sublayer runs on bf16 storage only", fn);
+  if (width < 64 || width % 64 != 0 || !tt::ln_supported(width))
+    return fail(TT_ERR_UNSUPPORTED, "%s: width %d not supported (a multiple of 64, at most 8192)",
+                fn, width);
+  const int64_t M = static_cast<int64_t>(s->batch) * s->block_size;
+  if (M > (int64_t(1) << 24)) return fail(TT_ERR_INVALID_ARG, "%s: batch * block_size too large", fn);
+  const int nq = s->n_q_heads * s->head_dim, nk = s->n_kv_heads * s->head_dim;
+  if (M > 0 && (!tt::gemm_supported(static_cast<int>(M), nq + 2 * nk, width) ||
+                !tt::gemm_supported(static_cast<int>(M), width, nq)))
+    return fail(TT_ERR_UNSUPPORTED, "%s: projection sizes not supported", fn);
+  return TT_OK;
+}
+
+struct SubBufs {
+  uint16_t *h, *q, *k, *v, *o;
+  void* attn_ws;
+};
+
+size_t sublayer_bytes(const tt_attn_shape* s, int32_t width, int32_t max_ctx_len,
+                      SubBufs* bufs, void* base) {
+  const size_t M = static_cast<size_t>(s->batch) * s->block_size;
+  const size_t nq = static_cast<size_t>(s->n_q_heads) * s->head_dim;
+  const size_t nk = static_cast<size_t>(s->n_kv_heads) * s->head_dim;
+  Carver c{static_cast<char*>(base)};
+  void* h = c.take(M * width * 2);
+  void* q = c.take(M * nq * 2);
+  void* k = c.take(M * nk * 2);
+  void* v = c.take(M * nk * 2);
+  void* o = c.take(M * nq * 2);
+  const tt::AttnPlan ap = tt::attn_plan(s->batch, s->block_size, s->n_q_heads, s->n_kv_heads,
+                                        s->head_dim, s->dtype, max_ctx_len);
+  void* w = c.take(ap.total_bytes);
+  if (bufs) {
+    bufs->h = static_cast<uint16_t*>(h); bufs->q = static_cast<uint16_t*>(q);
+    bufs->k = static_cast<uint16_t*>(k); bufs->v = static_cast<uint16_t*>(v);
+    bufs->o = static_cast<uint16_t*>(o); bufs->attn_ws = w;
+  }
+  return c.off;
+}
+
+tt::GemmArgs qkv_args(const tt_attn_shape* s, int32_t width, const void* h, const void* w_qkv,
+                      const uint8_t* active, void* q, void* k, void* v) {
+  tt::GemmArgs g{};
+  g.M = s->batch * s->block_size; g.K = width; g.S = s->block_size;
+  g.nq = s->n_q_heads * s->head_dim; g.nk = s->n_kv_heads * s->head_dim;
+  g.N = g.nq + 2 * g.nk;
+  g.a = static_cast<const uint16_t*>(h); g.w = static_cast<const uint16_t*>(w_qkv);
+  g.active = active;
+  g.q = static_cast<uint16_t*>(q); g.k = static_cast<uint16_t*>(k); g.v = static_cast<uint16_t*>(v);
+  return g;
+}
+
+tt::GemmArgs out_args(const tt_attn_shape* s, int32_t width, const void* o, const void* w_o,
+                      const float* gate, const void* x, const uint8_t* active, void* out) {
+  tt::GemmArgs g{};
+  g.M = s->batch * s->block_size; g.N = width; g.S = s->block_size;
+  g.K = s->n_q_heads * s->head_dim;
+  g.a = static_cast<const uint16_t*>(o); g.w = static_cast<const uint16_t*>(w_o);
+  g.active = active;
+  g.x = static_cast<const uint16_t*>(x); g.gate = gate; g.out = static_cast<uint16_t*>(out);
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+tt_status tt_ln_modulate(const tt_attn_shape* shape, int32_t width, const void* x,
+                         const float* shift, const float* scale, const uint8_t* active, void* h,
+                         tt_stream stream) {
+  const char* fn = "tt_ln_modulate";
+  tt_status st = check_sublayer(fn, shape, width);
+  if (st != TT_OK) return st;
+  if (!x || !shift || !scale || !h)
+    return fail(TT_ERR_INVALID_ARG, "%s: x, shift, scale and h must be non-NULL", fn);
+  const void* ptrs[] = {x, shift, scale, h};
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return fail(TT_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
+  const size_t M = static_cast<size_t>(shape->batch) * shape->block_size;
+  if (x != h && overlaps(x, M * width * 2, h, M * width * 2))
+    return fail(TT_ERR_INVALID_ARG, "%s: h overlaps x without being x", fn);
+  if (M == 0) return ok();
+  tt::LnArgs a{};
+  a.M = static_cast<int>(M); a.S = shape->block_size; a.D = width;
+  a.x = static_cast<const uint16_t*>(x); a.shift = shift; a.scale = scale; a.active = active;
+  a.h = static_cast<uint16_t*>(h);
+  const hipError_t e = tt::launch_ln_modulate(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+tt_status tt_qkv_proj(const tt_attn_shape* shape, int32_t width, const void* h, const void* w_qkv,
+                      const uint8_t* active, void* q_blk, void* k_blk, void* v_blk,
+                      tt_stream stream) {
+  const char* fn = "tt_qkv_proj";
+  tt_status st = check_sublayer(fn, shape, width);
+  if (st != TT_OK) return st;
+  if (!h || !w_qkv || !q_blk || !k_blk || !v_blk)
+    return fail(TT_ERR_INVALID_ARG, "%s: h, w_qkv, q_blk, k_blk and v_blk must be non-NULL", fn);
+  const void* ptrs[] = {h, w_qkv, q_blk, k_blk, v_blk};
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return fail(TT_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
+  const size_t M = static_cast<size_t>(shape->batch) * shape->block_size;
+  const size_t nq = static_cast<size_t>(shape->n_q_heads) * shape->head_dim;
+  const size_t nk = static_cast<size_t>(shape->n_kv_heads) * shape->head_dim;
+  if (overlaps(h, M * width * 2, q_blk, M * nq * 2) || overlaps(h, M * width * 2, k_blk, M * nk * 2) ||
+      overlaps(h, M * width * 2, v_blk, M * nk * 2))
+    return fail(TT_ERR_INVALID_ARG, "%s: q/k/v overlap h", fn);
+  if (M == 0) return ok();
+  const tt::GemmArgs g = qkv_args(shape, width, h, w_qkv, active, q_blk, k_blk, v_blk);
+  const hipError_t e = tt::launch_gemm(g, 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+tt_status tt_out_proj(const tt_attn_shape* shape, int32_t width, const void* o, const void* w_o,
+                      const float* gate, const void* x, const uint8_t* active, void* out,
+                      tt_stream stream) {
+  const char* fn = "tt_out_proj";
+  tt_status st = check_sublayer(fn, shape, width);
+  if (st != TT_OK) return st;
+  if (!o || !w_o || !gate || !x || !out)
+    return fail(TT_ERR_INVALID_ARG, "%s: o, w_o, gate, x and out must be non-NULL", fn);
+  const void* ptrs[] = {o, w_o, gate, x, out};
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return fail(TT_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
+  const size_t M = static_cast<size_t>(shape->batch) * shape->block_size;
+  const size_t nq = static_cast<size_t>(shape->n_q_heads) * shape->head_dim;
+  if (overlaps(o, M * nq * 2, out, M * width * 2) ||
+      (x != out && overlaps(x, M * width * 2, out, M * width * 2)))
+    return fail(TT_ERR_INVALID_ARG, "%s: out overlaps o, or overlaps x without being x", fn);
+  if (M == 0) return ok();
+  const tt::GemmArgs g = out_args(shape, width, o, w_o, gate, x, active, out);
+  const hipError_t e = tt::launch_gemm(g, 1, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+size_t tt_adaln_sublayer_workspace_size(const tt_attn_shape* shape, int32_t width,
+                                        int32_t max_ctx_len) {
+  if (check_sublayer("tt_adaln_sublayer_workspace_size", shape, width) != TT_OK) return 0;
+  if (max_ctx_len < 0) {
+    fail(TT_ERR_INVALID_ARG, "max_ctx_len %d < 0", max_ctx_len);
+    return 0;
+  }
+  ok();
+  const size_t n = sublayer_bytes(shape, width, max_ctx_len, nullptr, nullptr);
+  return n < 256 ? 256 : n;
+}
+
+tt_status tt_adaln_attn_sublayer(const tt_attn_shape* shape, int32_t width, const void* x,
+                                 const float* shift, const float* scale, const float* gate,
+                                 const void* w_qkv, const void* w_o, const void* k_ctx,
+                                 const void* v_ctx, const int64_t* ctx_start,
+                                 const int32_t* ctx_len, int32_t max_ctx_len,
+                                 const uint8_t* active, void* out, void* workspace,
+                                 size_t workspace_bytes, tt_stream stream) {
+  const char* fn = "tt_adaln_attn_sublayer";
+  tt_status st = check_sublayer(fn, shape, width);
+  if (st != TT_OK) return st;
+  if (max_ctx_len < 0) return fail(TT_ERR_INVALID_ARG, "%s: max_ctx_len %d < 0", fn, max_ctx_len);
+  if (!x || !shift || !scale || !gate || !w_qkv || !w_o || !out)
+    return fail(TT_ERR_INVALID_ARG, "%s: x, shift, scale, gate, w_qkv, w_o and out must be non-NULL", fn);
+  if (!k_ctx || !v_ctx || !ctx_start || !ctx_len)
+    return fail(TT_ERR_INVALID_ARG, "%s: k_ctx, v_ctx, ctx_start and ctx_len must be non-NULL", fn);
+  const void* ptrs[] = {x, shift, scale, gate, w_qkv, w_o, k_ctx, v_ctx, out};
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return fail(TT_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", fn);
+  if (!aligned(ctx_start, 8) || !aligned(ctx_len, 4))
+    return fail(TT_ERR_INVALID_ARG, "%s: misaligned ctx_start/ctx_len", fn);
+  const size_t M = static_cast<size_t>(shape->batch) * shape->block_size;
+  if (x != out && overlaps(x, M * width * 2, out, M * width * 2))
+    return fail(TT_ERR_INVALID_ARG, "%s: out overlaps x without being x", fn);
+  if (M == 0) return ok();
+  const size_t need = sublayer_bytes(shape, width, max_ctx_len, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need)
+    return fail(TT_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
+  if (!aligned(workspace, 256))
+    return fail(TT_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  SubBufs w{};
+  sublayer_bytes(shape, width, max_ctx_len, &w, workspace);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  tt::LnArgs la{};
+  la.M = static_cast<int>(M); la.S = shape->block_size; la.D = width;
+  la.x = static_cast<const uint16_t*>(x); la.shift = shift; la.scale = scale; la.active = active;
+  la.h = w.h;
+  hipError_t e = tt::launch_ln_modulate(la, hs);
+  if (e == hipSuccess)
+    e = tt::launch_gemm(qkv_args(shape, width, w.h, w_qkv, active, w.q, w.k, w.v), 0, hs);
+  if (e == hipSuccess) {
+    tt::AttnArgs a{};
+    a.B = shape->batch; a.S = shape->block_size; a.Hq = shape->n_q_heads;
+    a.Hkv = shape->n_kv_heads; a.d = shape->head_dim; a.dtype = shape->dtype;
+    a.q = w.q; a.kb = w.k; a.vb = w.v; a.kc = k_ctx; a.vc = v_ctx;
+    a.ctx_start = ctx_start; a.ctx_len = ctx_len; a.active = active;
+    a.out = w.o;
+    a.kc_out = const_cast<void*>(k_ctx);
+    a.vc_out = const_cast<void*>(v_ctx);
+    const tt::AttnPlan p = tt::attn_plan(shape->batch, shape->block_size, shape->n_q_heads,
+                                         shape->n_kv_heads, shape->head_dim, shape->dtype,
+                                         max_ctx_len);
+    e = tt::launch_block_attn(a, p, w.attn_ws, hs);
+  }
+  if (e == hipSuccess)
+    e = tt::launch_gemm(out_args(shape, width, w.o, w_o, gate, x, active, out), 1, hs);
+  if (e != hipSuccess) return hip_fail(e, fn);
+  return ok();
+}
+
+}  // extern "C"

@@ -98,6 +98,30 @@ size_t mamba_group_lds_bytes(int S, int N);
 size_t mamba_workspace_bytes(int B, int S, int G, int N);
 hipError_t launch_mamba_scan(const MambaArgs& a, void* ws, hipStream_t st);
 
+// ------------------------------------------------- weighted adaLN sublayer
+// LayerNorm (no affine, eps 1e-6) + modulation of M = B*S token rows of
+// width D (bf16 in and out; shift/scale fp32 [B, D]).
+struct LnArgs {
+  int M, S, D;
+  const uint16_t* x; const float* shift; const float* scale; const uint8_t* active;
+  uint16_t* h;
+};
+bool ln_supported(int D);
+hipError_t launch_ln_modulate(const LnArgs& a, hipStream_t st);
+
+// C[M, N] = A[M, K] W[N, K]^T (bf16, fp32 accumulation) with an epilogue:
+// epi 0 scatters columns [0, nq) / [nq, nq+nk) / [nq+nk, N) to q [M, nq],
+// k [M, nk], v [M, nk]; epi 1 writes out = x + gate[m / S] * C ([M, N]).
+// Rows of inactive sequences are not written.
+struct GemmArgs {
+  int M, N, K, S;
+  const uint16_t* a; const uint16_t* w; const uint8_t* active;
+  int nq, nk; uint16_t* q; uint16_t* k; uint16_t* v;
+  const uint16_t* x; const float* gate; uint16_t* out;
+};
+bool gemm_supported(int M, int N, int K);
+hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st);
+
 // ---------------------------------------------------------------- adaLN
 hipError_t launch_timestep_embed(int B, const float* t, const int32_t* n_masked, int S,
                                  float* emb, hipStream_t st);

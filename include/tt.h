@@ -490,6 +490,75 @@ tt_status tt_mamba_block_scan(const tt_mamba_shape* shape, const void* xbc, cons
                               void* y, void* conv_state_out, float* ssm_state_out,
                               void* workspace, size_t workspace_bytes, tt_stream stream);
 
+/* ------------------------------------------------------------------------
+ * The weighted adaLN-single attention sublayer of a denoiser layer.
+ *
+ * [dothoosh] "two-tower mechanism" section and [modelcard] "technical
+ * features": every denoiser layer is conditioned on the diffusion timestep
+ * through adaLN-single, which injects a scale, a shift and a gate per
+ * timestep.  The pages do not show the layer around the three vectors; the
+ * published adaLN-single placement (PixArt-alpha / DiT) is taken:
+ *   h       = LayerNorm(x) * (1 + scale[b]) + shift[b]   (no affine, eps 1e-6)
+ *   q|k|v   = h W_qkv^T                                   (no bias)
+ *   o       = block attention of q over [context KV ; k, v] (tt_block_attn
+ *             with identity modulation and no residual)
+ *   out     = x + gate[b] * (o W_o^T)                     (no bias)
+ * The pages give no hidden size: `width` (D) is a parameter.
+ *
+ * Shapes (M = batch * block_size token rows, row m = (b, s), b = m / S):
+ *   x, h, out  [B, S, D] bf16;  shift, scale, gate [B, D] fp32 (for layer l
+ *              of tt_adaln_single's output: ada + (3l + j) * B * D, j = 0,
+ *              1, 2);
+ *   w_qkv      [(Hq + 2 Hkv) d, D] bf16, rows in the order q heads, k heads,
+ *              v heads (PyTorch Linear (out, in) storage);
+ *   w_o        [D, Hq d] bf16;
+ *   q_blk [B, S, Hq, d], k_blk / v_blk [B, S, Hkv, d], o [B, S, Hq, d] bf16;
+ *   the context arguments are those of tt_block_attn.
+ * Requirements: shape->dtype == TT_BF16 (else TT_ERR_UNSUPPORTED); D a
+ * multiple of 64 in [64, 8192]; every buffer 16-byte aligned.  Arithmetic:
+ * fp32 (LayerNorm statistics by exact two-pass sums; projections on the bf16
+ * matrix cores with fp32 accumulation); every bf16 output rounded to nearest
+ * even.  Sequences with active[b] == 0 are not written.  All calls are
+ * asynchronous on `stream`; deterministic.  Errors: TT_ERR_INVALID_ARG (NULL
+ * required pointer, misalignment, overlapping buffers as stated),
+ * TT_ERR_UNSUPPORTED, TT_ERR_WORKSPACE, TT_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+
+/* h = LayerNorm(x) (1 + scale) + shift.  h may be x itself (in place) but
+ * must not overlap it otherwise. */
+tt_status tt_ln_modulate(const tt_attn_shape* shape, int32_t width, const void* x,
+                         const float* shift, const float* scale, const uint8_t* active, void* h,
+                         tt_stream stream);
+
+/* q|k|v = h W_qkv^T, written as the attention's q_blk, k_blk, v_blk (none
+ * may overlap h). */
+tt_status tt_qkv_proj(const tt_attn_shape* shape, int32_t width, const void* h, const void* w_qkv,
+                      const uint8_t* active, void* q_blk, void* k_blk, void* v_blk,
+                      tt_stream stream);
+
+/* out = x + gate (o W_o^T).  out may be x itself (in place); it must not
+ * overlap o, nor x otherwise. */
+tt_status tt_out_proj(const tt_attn_shape* shape, int32_t width, const void* o, const void* w_o,
+                      const float* gate, const void* x, const uint8_t* active, void* out,
+                      tt_stream stream);
+
+/* Workspace of tt_adaln_attn_sublayer (256-byte aligned, no
+ * initialisation): h, q, k, v, o and the attention's partials.  0 on
+ * invalid arguments (tt_last_error says why). */
+size_t tt_adaln_sublayer_workspace_size(const tt_attn_shape* shape, int32_t width,
+                                        int32_t max_ctx_len);
+
+/* The whole sublayer: tt_ln_modulate, tt_qkv_proj, the block attention and
+ * tt_out_proj in stream order, intermediates in the workspace.  out may be x
+ * itself. */
+tt_status tt_adaln_attn_sublayer(const tt_attn_shape* shape, int32_t width, const void* x,
+                                 const float* shift, const float* scale, const float* gate,
+                                 const void* w_qkv, const void* w_o, const void* k_ctx,
+                                 const void* v_ctx, const int64_t* ctx_start,
+                                 const int32_t* ctx_len, int32_t max_ctx_len,
+                                 const uint8_t* active, void* out, void* workspace,
+                                 size_t workspace_bytes, tt_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -255,3 +255,44 @@ def test_mamba_rejects_bad_arguments():
     assert call(ws_bytes=16) == tt.TT_ERR_WORKSPACE
     assert call(shape=(0, 8, 64, 128, 2, 4, 16, 0)) == tt.TT_OK
     assert tt.mamba_workspace_size(tt.MambaShape(2, 8, 64, 128, 2, 4, 16, 0)) >= 2 * 2 * 16 * 272 * 4
+
+
+def test_sublayer_rejects_bad_arguments():
+    L = tt.lib()
+    F2 = FAKE * 2                      # a second, disjoint fake buffer
+
+    def shp(B=2, Hq=4, Hkv=2, d=64, S=16, dtype=0):
+        return tt.AttnShape(B, Hq, Hkv, d, S, dtype)
+
+    def ln(s=None, width=256, x=FAKE, h=F2):
+        s = s or shp()
+        return L.tt_ln_modulate(ctypes.byref(s), width, x, FAKE, FAKE, None, h, None)
+    assert ln(s=shp(dtype=1)) == tt.TT_ERR_UNSUPPORTED                # fp32 storage
+    assert ln(width=200) == tt.TT_ERR_UNSUPPORTED                     # not a multiple of 64
+    assert ln(width=8256) == tt.TT_ERR_UNSUPPORTED                    # wider than 8192
+    assert ln(x=None) == tt.TT_ERR_INVALID_ARG
+    assert ln(h=F2 + 8) == tt.TT_ERR_INVALID_ARG                      # misaligned
+    assert ln(h=FAKE + 256) == tt.TT_ERR_INVALID_ARG                  # partial overlap of x
+    assert "tt_ln_modulate" in tt.last_error()
+    assert ln(s=shp(B=0)) == tt.TT_OK
+
+    def qkv(h=FAKE, q=F2, k=F2 * 2, v=F2 * 3):
+        return L.tt_qkv_proj(ctypes.byref(shp()), 256, h, FAKE, None, q, k, v, None)
+    assert qkv(h=None) == tt.TT_ERR_INVALID_ARG
+    assert qkv(q=FAKE) == tt.TT_ERR_INVALID_ARG                       # q overlaps h
+
+    def outp(o=FAKE, x=F2, out=F2 * 2):
+        return L.tt_out_proj(ctypes.byref(shp()), 256, o, FAKE, FAKE, x, None, out, None)
+    assert outp(out=FAKE) == tt.TT_ERR_INVALID_ARG                    # out overlaps o
+    assert outp(out=F2 + 512) == tt.TT_ERR_INVALID_ARG                # partial overlap of x
+    assert outp(o=FAKE + 4) == tt.TT_ERR_INVALID_ARG
+
+    def sub(ws_bytes=1 << 30, maxl=64, out=F2):
+        return L.tt_adaln_attn_sublayer(ctypes.byref(shp()), 256, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, FAKE, FAKE, maxl, None, out, FAKE, ws_bytes, None)
+    assert sub(ws_bytes=256) == tt.TT_ERR_WORKSPACE
+    assert sub(maxl=-1) == tt.TT_ERR_INVALID_ARG
+    assert sub(out=F2 + 2) == tt.TT_ERR_INVALID_ARG
+    n = L.tt_adaln_sublayer_workspace_size(ctypes.byref(shp()), 256, 64)
+    assert n >= 2 * 16 * (256 + 2 * 256 + 2 * 128) * 2
+    assert L.tt_adaln_sublayer_workspace_size(ctypes.byref(shp(dtype=1)), 256, 64) == 0
