@@ -29,7 +29,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-ROW_REPS = 10          # calls per row in the per-row timing pass
+MFMA_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak
+ROW_REPS = 20          # calls per row in the per-row timing pass
 GEN_BLOCKS = 8         # generation row: max_new_tokens = 128 at S = 16
 ROW_WARM_CALLS = 250   # attention calls (~40 ms) before each row's timing
 METRIC = "block-denoise query-tokens/s + achieved HBM GB/s (S=16, ctx 8k, bf16)"
@@ -259,16 +260,18 @@ def main():
     torch.cuda.synchronize()
     committed = int(B * S - n_masked.sum().item())
 
-    # Per-row times, after the timed region: each row's calls alone, after
-    # ROW_WARM_CALLS back-to-back attention calls (the clocks drop while the
-    # host works between rows and take tens of ms of GPU work to come back)
-    # and one untimed call of the row (first launches load the kernel's
-    # code); then ROW_REPS calls bracketed by one event pair.
+    # Per-row times, after the timed region: each row's calls alone.  One
+    # untimed call first (a first launch loads the kernel's code), then
+    # ROW_WARM_CALLS back-to-back attention calls, not waited for: they bring
+    # the clocks back up (they drop while the host works between rows) and
+    # keep the GPU busy while the host queues the row's ROW_REPS calls
+    # behind them, so those run back to back (a short kernel would otherwise
+    # wait for each launch) between one event pair.
     def timed(fn):
-        for i in range(ROW_WARM_CALLS):
-            tt.block_attn(shape, qb[0], kb[0], vb[0], kc[0], vc[0], start, clen, max_len, out, aws)
         fn(-1)
         torch.cuda.synchronize()
+        for i in range(ROW_WARM_CALLS):
+            tt.block_attn(shape, qb[0], kb[0], vb[0], kc[0], vc[0], start, clen, max_len, out, aws)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -310,7 +313,20 @@ def main():
         us_mamba = timed(lambda r: tt.mamba_block_scan(*mb["args"], **mb["kw"]))
         us_mamba_ctx = timed(lambda r: tt.mamba_block_scan(
             *mb["args"], **mb["kw"], conv_state_out=mb["cso"], ssm_state_out=mb["sso"]))
-        return us_ada, us_sample, us_unmask, us_ctx, us_adv, loop, gen, us_mamba, us_mamba_ctx, mb
+        del mb["args"], mb["cso"], mb["sso"]
+        # weighted adaLN-single sublayer (one layer) at width Hq*d: its three
+        # kernels alone, then the whole sublayer over this workload's contexts
+        f3 = sublayer_inputs(tt, B, S, Hq, Hkv, d, max_len)
+        sh = f3["shape"]
+        us_ln = timed(lambda r: tt.ln_modulate(sh, W, f3["x"], ada[0, 0], ada[0, 1], f3["h"]))
+        us_qkv = timed(lambda r: tt.qkv_proj(sh, W, f3["h"], f3["w_qkv"], qb[0], kb[0], vb[0]))
+        us_o = timed(lambda r: tt.out_proj(sh, W, out, f3["w_o"], ada[0, 2], f3["x"], f3["out"]))
+        us_sub = timed(lambda r: tt.adaln_attn_sublayer(
+            sh, W, f3["x"], ada[0, 0], ada[0, 1], ada[0, 2], f3["w_qkv"], f3["w_o"], kc[0], vc[0],
+            start, clen, max_len, f3["out"], f3["ws"]))
+        del f3
+        f3_us = (us_ln, us_qkv, us_o, us_sub)
+        return us_ada, us_sample, us_unmask, us_ctx, us_adv, loop, gen, us_mamba, us_mamba_ctx, mb, f3_us
     rows_data = None if args.no_rows else collect_rows()
     ms = t0.elapsed_time(t1) / args.steps
     bounds = step_events + [t1]
@@ -359,12 +375,19 @@ def main():
     # block k/v written into the cache
     ctx_bytes = sum(2 * L * Hkv * d * 2 + S * Hq * d * 2 * 2 + 2 * 2 * S * Hkv * d * 2 for L in lens)
 
+    def mfma_row(us, flops, what):
+        tf = flops / (us * 1e-6) / 1e12
+        return {"calls": what, "us_per_call": round(us, 2), "flops": flops,
+                "tflops": round(tf, 1), "frac_mfma_bf16": round(tf / MFMA_BF16_TFLOPS, 4)}
+
     def row(us, nbytes, what):
         gbps = nbytes / (us * 1e-6) / 1e9
         return {"calls": what, "us_per_call": round(us, 2), "bytes": nbytes,
                 "gbps": round(gbps, 1), "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
     if rows_data is not None:
-        us_ada, us_sample, us_unmask, us_ctx, us_adv, loop, gen, us_mamba, us_mamba_ctx, mb = rows_data
+        us_ada, us_sample, us_unmask, us_ctx, us_adv, loop, gen, us_mamba, us_mamba_ctx, mb, f3_us = rows_data
+        us_ln, us_qkv, us_o, us_sub = f3_us
+        M, Nqkv = B * S, (Hq + 2 * Hkv) * d
         result["rows"] = {
             "a8_denoise_loop": loop,
             "a1_timestep_adaln": row(us_ada, ada_bytes, "tt_timestep_embed + tt_adaln_single"),
@@ -382,6 +405,16 @@ def main():
             "f4_mamba_scan_ctx": row(us_mamba_ctx, mb["bytes_ctx"],
                                      "tt_mamba_block_scan with the final states written "
                                      "(context tower), one layer"),
+            "f3_ln_modulate": row(us_ln, 2 * M * W * 2 + 2 * B * W * 4,
+                                  f"tt_ln_modulate, {M} rows of width {W}"),
+            "f3_qkv_proj": mfma_row(us_qkv, 2 * M * Nqkv * W,
+                                    f"tt_qkv_proj, [{M} x {W}] x [{W} x {Nqkv}]"),
+            "f3_out_proj": mfma_row(us_o, 2 * M * W * W,
+                                    f"tt_out_proj with gate and residual, [{M} x {W}] x [{W} x {W}]"),
+            "f3_sublayer": {"calls": "tt_adaln_attn_sublayer (LN+modulate, QKV, attention over the "
+                                     "contexts above, O + gate + residual), one layer",
+                            "us_per_call": round(us_sub, 2),
+                            "attention_share_us": round(attn_avg * 1e3, 2)},
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs, kc, vc, qb, kb, vb, ada,
@@ -434,6 +467,26 @@ def denoise_loop(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, 
 
 
 MAMBA = dict(H=64, P=64, N=128, G=8, W=4)   # assumed layer sizes (the pages give none)
+
+
+def sublayer_inputs(tt, B, S, Hq, Hkv, d, max_len):
+    """Seeded synthetic inputs of the weighted adaLN-single sublayer at width
+    D = Hq*d: block hidden states and the two projection weights (bf16,
+    std 1/sqrt(fan-in))."""
+    import math
+
+    import torch
+
+    import synth
+    dev, bf = "cuda", torch.bfloat16
+    D, N = Hq * d, (Hq + 2 * Hkv) * d
+    shape = tt.attn_shape(B, Hq, Hkv, d, S, bf)
+    x = synth.normal((B, S, D), 1.0, 901, bf, dev)
+    return {"shape": shape, "x": x, "h": torch.empty_like(x), "out": torch.empty_like(x),
+            "w_qkv": synth.normal((N, D), 1.0 / math.sqrt(D), 902, bf, dev),
+            "w_o": synth.normal((D, Hq * d), 1.0 / math.sqrt(Hq * d), 903, bf, dev),
+            "ws": torch.empty(tt.adaln_sublayer_workspace_size(shape, D, max_len),
+                              dtype=torch.uint8, device=dev)}
 
 
 def mamba_inputs(tt, B, S):

@@ -18,8 +18,9 @@
 // gemm_kernel: C[M, N] = A[M, K] W[N, K]^T in bf16 with fp32 accumulation
 // on the matrix cores (v_mfma_f32_32x32x16_bf16).  One workgroup of 4 waves
 // per 128 x 128 output tile; K in steps of 64.  A and W tiles stream
-// HBM -> LDS through the direct copy path into a 3-stage ring (two steps in
-// flight while one is multiplied).  LDS rows are 128 bytes (64 k); the
+// HBM -> LDS through the direct copy path into an NS-stage ring (NS - 1
+// steps in flight while one is multiplied; NS = 3 when the tiles fit one
+// per CU, else 2 so that two tiles share a CU).  LDS rows are 128 bytes (64 k); the
 // 16-byte slot of k-chunk c in row r is c ^ ((r >> 1) & 7), so the 16 rows
 // read together by a matrix-operand load hit 16 different bank groups.
 // Each wave computes a 64 x 64 piece as the transpose C^T = W A^T: the A
@@ -39,11 +40,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 64, kNS = 3;
+constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kGThreads = 256;
 constexpr int kTileBytes = kBM * kBK * 2;         // one operand tile: 16 KB
 constexpr int kStageBytes = 2 * kTileBytes;       // A tile, then W tile
-constexpr int kGemmLds = kNS * kStageBytes;       // 96 KB
 constexpr int kCopies = kTileBytes / 1024 / 4;    // 1 KB copies per wave per operand tile
 
 enum { kEpiQkv = 0, kEpiGate = 1 };
@@ -61,6 +61,17 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t 
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// wait until at most `later` pipeline steps' copies (2 kCopies each) of
+// this wave are in flight (later <= NS - 2, wave-uniform)
+template <int NS>
+__device__ __forceinline__ void wait_steps(int later) {
+  constexpr int c = 2 * kCopies;
+  static_assert(NS >= 2 && NS <= 4, "ring of 2 to 4 stages");
+  if (NS == 2 || later == 0) wait_vmem<0>();
+  else if (NS == 3 || later == 1) wait_vmem<c>();
+  else wait_vmem<2 * c>();
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -142,9 +153,9 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(LnArgs a) {
 }
 
 // --------------------------------------------------------------------- GEMM
-template <int EPI>
+template <int EPI, int NS>
 __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * kStageBytes];
   const int tiles_m = (a.M + kBM - 1) / kBM;
   const int tiles = tiles_m * ((a.N + kBN - 1) / kBN);
   const int bid = blockIdx.x;
@@ -170,7 +181,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
   const uint16_t* abase = a.a + static_cast<int64_t>(m0) * a.K;
   const uint16_t* wbase = a.w + static_cast<int64_t>(n0) * a.K;
   auto issue = [&](int kt) {
-    const int st = kt % kNS;
+    const int st = kt % NS;
     const uint32_t la = __builtin_amdgcn_readfirstlane(lds0 + st * kStageBytes + wave * kCopies * 1024);
     const uint32_t lw = la + kTileBytes;
     const uint16_t* ab = abase + kt * kBK;
@@ -201,16 +212,17 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int KT = a.K / kBK;
-  issue(0);
-  if (KT > 1) issue(1);
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0)
+    if (s0 < KT) issue(s0);
   for (int kt = 0; kt < KT; ++kt) {
-    // this step's copies (this wave's) are done once at most the next
-    // step's are in flight; the barrier makes every wave's copies visible
+    // this step's copies (this wave's) are done once at most the later
+    // steps' are in flight; the barrier makes every wave's copies visible
     // and frees the stage the copy below overwrites (read in step kt-1)
-    if (kt + 1 < KT) wait_vmem<2 * kCopies>(); else wait_vmem<0>();
+    wait_steps<NS>(min(NS - 2, KT - 1 - kt));
     __syncthreads();
-    if (kt + 2 < KT) issue(kt + 2);
-    TT_LDS const uint8_t* sa = lsm + (kt % kNS) * kStageBytes;
+    if (kt + NS - 1 < KT) issue(kt + NS - 1);
+    TT_LDS const uint8_t* sa = lsm + (kt % NS) * kStageBytes;
     TT_LDS const uint8_t* sw_ = sa + kTileBytes;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -289,9 +301,23 @@ bool gemm_supported(int M, int N, int K) {
 
 hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
   const int tiles = ((a.M + kBM - 1) / kBM) * ((a.N + kBN - 1) / kBN);
+  // Up to one tile per CU: a 3-stage ring (96 KB of LDS).  More tiles than
+  // CUs: a 2-stage ring (64 KB), so that two tiles share a CU and the tiles
+  // past the CU count run beside the others instead of in a second round
+  // (measured: 288 tiles on 256 CUs take 56 us instead of 80).
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const bool two = tiles > cus;
   const dim3 grid(tiles), blk(kGThreads);
-  if (epi == kEpiQkv) hipLaunchKernelGGL(gemm_kernel<kEpiQkv>, grid, blk, 0, st, a);
-  else hipLaunchKernelGGL(gemm_kernel<kEpiGate>, grid, blk, 0, st, a);
+  if (epi == kEpiQkv) {
+    if (two) hipLaunchKernelGGL((gemm_kernel<kEpiQkv, 2>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((gemm_kernel<kEpiQkv, 3>), grid, blk, 0, st, a);
+  } else {
+    if (two) hipLaunchKernelGGL((gemm_kernel<kEpiGate, 2>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((gemm_kernel<kEpiGate, 3>), grid, blk, 0, st, a);
+  }
   return hipGetLastError();
 }
 
