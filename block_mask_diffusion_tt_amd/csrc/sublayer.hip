@@ -64,12 +64,12 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 // wait until at most `later` pipeline steps' copies (2 kCopies each) of
-// this wave are in flight (later <= NS - 2, wave-uniform)
+// this wave are in flight (later <= NS - 2, wave-uniform; <= 0: all done)
 template <int NS>
 __device__ __forceinline__ void wait_steps(int later) {
   constexpr int c = 2 * kCopies;
   static_assert(NS >= 2 && NS <= 4, "ring of 2 to 4 stages");
-  if (NS == 2 || later == 0) wait_vmem<0>();
+  if (NS == 2 || later <= 0) wait_vmem<0>();
   else if (NS == 3 || later == 1) wait_vmem<c>();
   else wait_vmem<2 * c>();
 }
@@ -153,9 +153,12 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(LnArgs a) {
 }
 
 // --------------------------------------------------------------------- GEMM
-template <int EPI, int NS>
-__global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * kStageBytes];
+// NG groups of 4 waves; group g multiplies the K-steps kt = g (mod NG)
+// through its own NS-stage ring, and group 1's accumulators are added into
+// group 0's through LDS at the end (NG = 2: two copy streams per CU).
+template <int EPI, int NS, int NG>
+__global__ __launch_bounds__(kGThreads * NG) void gemm_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NG * NS * kStageBytes];
   const int tiles_m = (a.M + kBM - 1) / kBM;
   const int tiles = tiles_m * ((a.N + kBN - 1) / kBN);
   const int bid = blockIdx.x;
@@ -163,16 +166,18 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
   const int m0 = (t % tiles_m) * kBM, n0 = (t / tiles_m) * kBN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = NG == 1 ? 0 : wave >> 2, w4 = wave & 3;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((TT_LDS uint8_t*)smem));
   TT_LDS const uint8_t* lsm = (TT_LDS const uint8_t*)smem;
 
-  // copies: wave w, copy j fills tile rows (4w + j) * 8 .. +8; lane L row
-  // r = (4w + j) * 8 + L / 8, LDS slot L % 8 <- k-chunk (L % 8) ^ ((r >> 1) & 7);
-  // rows past the matrix end repeat its last row (never stored)
+  // copies: wave w4 of a group, copy j fills tile rows (4 w4 + j) * 8 .. +8;
+  // lane L row r = (4 w4 + j) * 8 + L / 8, LDS slot L % 8 <- k-chunk
+  // (L % 8) ^ ((r >> 1) & 7); rows past the matrix end repeat its last row
+  // (never stored)
   uint32_t offa[kCopies], offw[kCopies];
 #pragma unroll
   for (int j = 0; j < kCopies; ++j) {
-    const int r = (wave * kCopies + j) * 8 + (lane >> 3);
+    const int r = (w4 * kCopies + j) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int ra = min(r, a.M - 1 - m0), rw = min(r, a.N - 1 - n0);
     offa[j] = static_cast<uint32_t>(ra * a.K * 2 + c * 16);
@@ -180,9 +185,11 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
   }
   const uint16_t* abase = a.a + static_cast<int64_t>(m0) * a.K;
   const uint16_t* wbase = a.w + static_cast<int64_t>(n0) * a.K;
-  auto issue = [&](int kt) {
-    const int st = kt % NS;
-    const uint32_t la = __builtin_amdgcn_readfirstlane(lds0 + st * kStageBytes + wave * kCopies * 1024);
+  // the group's i-th step is K-step i * NG + grp, in stage i % NS of its ring
+  auto issue = [&](int i) {
+    const int kt = i * NG + grp;
+    const uint32_t la = __builtin_amdgcn_readfirstlane(
+        lds0 + (grp * NS + i % NS) * kStageBytes + w4 * kCopies * 1024);
     const uint32_t lw = la + kTileBytes;
     const uint16_t* ab = abase + kt * kBK;
     const uint16_t* wb = wbase + kt * kBK;
@@ -195,7 +202,7 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
 
   // operand reads: W rows wn*64 + ns*32 + l%32 (A operand), A rows
   // wm*64 + ms*32 + l%32 (B operand); k-chunk 2 ks + l/32 of step ks
-  const int wn = wave >> 1, wm = wave & 1;
+  const int wn = w4 >> 1, wm = w4 & 1;
   const int l32 = lane & 31, half = lane >> 5;
   const int sw = (l32 >> 1) & 7;
   int slot[4];
@@ -212,17 +219,20 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int KT = a.K / kBK;
+  const int steps = (KT - grp + NG - 1) / NG;   // this group's K-steps
+  const int iters = (KT + NG - 1) / NG;         // the same for every group
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0)
-    if (s0 < KT) issue(s0);
-  for (int kt = 0; kt < KT; ++kt) {
+    if (s0 < steps) issue(s0);
+  for (int i = 0; i < iters; ++i) {
     // this step's copies (this wave's) are done once at most the later
     // steps' are in flight; the barrier makes every wave's copies visible
-    // and frees the stage the copy below overwrites (read in step kt-1)
-    wait_steps<NS>(min(NS - 2, KT - 1 - kt));
+    // and frees the stage the copy below overwrites (read in step i-1)
+    wait_steps<NS>(min(NS - 2, steps - 1 - i));
     __syncthreads();
-    if (kt + NS - 1 < KT) issue(kt + NS - 1);
-    TT_LDS const uint8_t* sa = lsm + (kt % NS) * kStageBytes;
+    if (i + NS - 1 < steps) issue(i + NS - 1);
+    if (i >= steps) continue;            // a group with one step fewer
+    TT_LDS const uint8_t* sa = lsm + (grp * NS + i % NS) * kStageBytes;
     TT_LDS const uint8_t* sw_ = sa + kTileBytes;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -238,6 +248,29 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs a) {
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
     }
+  }
+
+  if constexpr (NG == 2) {
+    // group 1's partial sums into group 0's (64 KB of the ring, conflict
+    // free: consecutive lanes, consecutive words)
+    TT_LDS float* red = (TT_LDS float*)smem;
+    __syncthreads();                     // every wave is done with the ring
+    if (grp == 1) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[(((w4 * 2 + i) * 2 + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += red[(((w4 * 2 + i) * 2 + j) * 16 + r) * 64 + lane];
   }
 
   // ---- epilogue: lane holds C[m][n .. n+3] for m = m0 + wm*64 + j*32 + l%32,
@@ -310,13 +343,13 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
   const bool two = tiles > cus;
-  const dim3 grid(tiles), blk(kGThreads);
+  const dim3 grid(tiles);
   if (epi == kEpiQkv) {
-    if (two) hipLaunchKernelGGL((gemm_kernel<kEpiQkv, 2>), grid, blk, 0, st, a);
-    else hipLaunchKernelGGL((gemm_kernel<kEpiQkv, 3>), grid, blk, 0, st, a);
+    if (two) hipLaunchKernelGGL((gemm_kernel<kEpiQkv, 2, 1>), grid, dim3(kGThreads), 0, st, a);
+    else hipLaunchKernelGGL((gemm_kernel<kEpiQkv, 2, 2>), grid, dim3(2 * kGThreads), 0, st, a);
   } else {
-    if (two) hipLaunchKernelGGL((gemm_kernel<kEpiGate, 2>), grid, blk, 0, st, a);
-    else hipLaunchKernelGGL((gemm_kernel<kEpiGate, 3>), grid, blk, 0, st, a);
+    if (two) hipLaunchKernelGGL((gemm_kernel<kEpiGate, 2, 1>), grid, dim3(kGThreads), 0, st, a);
+    else hipLaunchKernelGGL((gemm_kernel<kEpiGate, 2, 2>), grid, dim3(2 * kGThreads), 0, st, a);
   }
   return hipGetLastError();
 }
