@@ -270,7 +270,10 @@ struct ScanRound {
 // Lane l then holds y at slot s0 + l%16 for rows 16w + 4 kg + r, r < 4.
 // Global loads: the round's inputs first, then the seed's state (most of
 // the bytes) -- waiting for the former leaves the latter in flight.
-template <typename T, int P, int N, int KW>
+// CTX: the context tower's form (final SSM state written; its own
+// instantiation, so that the denoiser's form keeps its smaller register
+// allocation)
+template <typename T, int P, int N, int KW, bool CTX>
 __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const float* ws_bc,
                                                           const float* ws_g) {
   constexpr int NT = 4 * P;              // P/16 waves of 64
@@ -312,7 +315,12 @@ __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const fl
   using RD = ScanRound<T, P, N, KW, NT>;
   const int pl = lane & 15, kg = lane >> 4;
   const int p = wave * 16 + pl;
-  const int64_t sbase = ((static_cast<int64_t>(b) * H + h) * P + p) * N + kg * KS;
+  // the lane's state entries, row p: n = kg KS + t (the denoiser's form), or
+  // n = 16 (t/4) + 4 kg + t%4 (the context tower's: the output layout of the
+  // final state's matrix products below); any order of K serves H0 C^T as
+  // long as C is read in the same one
+  constexpr int kStride = CTX ? 4 : 1;   // distance in n between consecutive float4 of a lane
+  const int64_t sbase = ((static_cast<int64_t>(b) * H + h) * P + p) * N + (CTX ? 4 * kg : kg * KS);
   float st[KS];
   {
     v4f bc[RD::kBC];
@@ -324,7 +332,7 @@ __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const fl
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < KS; j += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(a.ssm_state + sbase + j);
+      const float4 v = *reinterpret_cast<const float4*>(a.ssm_state + sbase + kStride * j);
       st[j] = v.x; st[j + 1] = v.y; st[j + 2] = v.z; st[j + 3] = v.w;
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -367,10 +375,10 @@ __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const fl
   T* y = static_cast<T*>(a.y) + (static_cast<int64_t>(b) * S) * (H * P) + h * P + wave * 16 + 4 * kg;
   for (int s0 = 0; s0 < Sp; s0 += kSC) {
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
-    const float* crow = s_c + (s0 + pl) * BP + kg * KS;
+    const float* crow = s_c + (s0 + pl) * BP + (CTX ? 4 * kg : kg * KS);
 #pragma unroll
     for (int t = 0; t < KS; t += 4) {
-      const float4 cv = *reinterpret_cast<const float4*>(crow + t);
+      const float4 cv = *reinterpret_cast<const float4*>(crow + kStride * t);
       d = __builtin_amdgcn_mfma_f32_16x16x4f32(st[t], cv.x, d, 0, 0, 0);
       d = __builtin_amdgcn_mfma_f32_16x16x4f32(st[t + 1], cv.y, d, 0, 0, 0);
       d = __builtin_amdgcn_mfma_f32_16x16x4f32(st[t + 2], cv.z, d, 0, 0, 0);
@@ -404,26 +412,34 @@ __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const fl
   // ---- the context tower's final state: H_S = exp(cum_S) H0 +
   // sum_j dt_j exp(cum_S - cum_j) x_j B_j^T (in place allowed: every thread
   // has read its part), and the conv state = the last W-1 inputs
-  if (a.ssm_state_out) {
+  // on the matrix cores: per 16-entry tile nt of n, the wave's 16 x 16
+  // block of H_S^T = d0 H0^T + sum_j (w_j B_j)[16 nt + i] x_j[p], K = the
+  // slots j four at a time, w_j = dt_j exp(cum_S - cum_j); the accumulator
+  // starts from the lane's own state entries (d0 = exp(cum_S))
+  if constexpr (CTX) {
     const float last = s_cum[S - 1];
     const float d0 = s_dec[S - 1];
+    f32x4 hs[KS / 4];
 #pragma unroll
-    for (int n = 0; n < KS; ++n) st[n] *= d0;
-    for (int j = 0; j < S; ++j) {
-      const float coef = s_dt[j] * expf(last - s_cum[j]) * s_x[j * XP + p];
-      const float* bs = s_b + j * BP + kg * KS;
+    for (int nt = 0; nt < KS / 4; ++nt)
+      hs[nt] = f32x4{st[4 * nt] * d0, st[4 * nt + 1] * d0, st[4 * nt + 2] * d0, st[4 * nt + 3] * d0};
+    for (int j0 = 0; j0 < Sp; j0 += 4) {
+      const int j = j0 + kg;
+      // slots past S: a select, not a product (the LDS rows read there may
+      // be stale); x is 0 there
+      const float w = j < S ? s_dt[j] * expf(last - s_cum[j]) : 0.f;
+      const float xv = s_x[j * XP + p];
+      const float* brow = s_b + j * BP + pl;
 #pragma unroll
-      for (int n = 0; n < KS; n += 4) {
-        const float4 bv = *reinterpret_cast<const float4*>(bs + n);
-        st[n] = fmaf(coef, bv.x, st[n]);
-        st[n + 1] = fmaf(coef, bv.y, st[n + 1]);
-        st[n + 2] = fmaf(coef, bv.z, st[n + 2]);
-        st[n + 3] = fmaf(coef, bv.w, st[n + 3]);
+      for (int nt = 0; nt < KS / 4; ++nt) {
+        const float av = j < S ? brow[16 * nt] * w : 0.f;
+        hs[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, xv, hs[nt], 0, 0, 0);
       }
     }
 #pragma unroll
-    for (int j = 0; j < KS; j += 4)
-      *reinterpret_cast<float4*>(a.ssm_state_out + sbase + j) = make_float4(st[j], st[j + 1], st[j + 2], st[j + 3]);
+    for (int nt = 0; nt < KS / 4; ++nt)
+      *reinterpret_cast<float4*>(a.ssm_state_out + sbase + 16 * nt) =
+          make_float4(hs[nt][0], hs[nt][1], hs[nt][2], hs[nt][3]);
   }
   if (a.conv_state_out) {
     T* cso = static_cast<T*>(a.conv_state_out) + static_cast<int64_t>(b) * C * (W - 1);
@@ -459,16 +475,23 @@ hipError_t launch_t(const MambaArgs& a, void* ws, hipStream_t st) {
   };
 #define TT_MAMBA(PP, NN, WW)                                                                    \
   if (a.P == PP && a.N == NN && a.W == WW) {                                                    \
+    const void* scan = a.ssm_state_out                                                          \
+        ? reinterpret_cast<const void*>(&mamba_scan_kernel<T, PP, NN, WW, true>)                \
+        : reinterpret_cast<const void*>(&mamba_scan_kernel<T, PP, NN, WW, false>);              \
     hipError_t e = allow(reinterpret_cast<const void*>(&mamba_group_kernel<T, NN, WW>), lds_g); \
-    if (e == hipSuccess)                                                                        \
-      e = allow(reinterpret_cast<const void*>(&mamba_scan_kernel<T, PP, NN, WW>), lds_s);       \
+    if (e == hipSuccess) e = allow(scan, lds_s);                                                \
     if (e != hipSuccess) return e;                                                              \
     hipLaunchKernelGGL((mamba_group_kernel<T, NN, WW>), dim3(static_cast<unsigned>(a.B * a.G)), \
                        blk, lds_g, st, a, ws_bc, ws_g);                                         \
     e = hipGetLastError();                                                                      \
     if (e != hipSuccess) return e;                                                              \
-    hipLaunchKernelGGL((mamba_scan_kernel<T, PP, NN, WW>), dim3(static_cast<unsigned>(a.B * a.H)), \
-                       dim3(4 * PP), lds_s, st, a, ws_bc, ws_g);                                \
+    const dim3 grid(static_cast<unsigned>(a.B * a.H));                                          \
+    if (a.ssm_state_out)                                                                        \
+      hipLaunchKernelGGL((mamba_scan_kernel<T, PP, NN, WW, true>), grid, dim3(4 * PP), lds_s,   \
+                         st, a, ws_bc, ws_g);                                                   \
+    else                                                                                        \
+      hipLaunchKernelGGL((mamba_scan_kernel<T, PP, NN, WW, false>), grid, dim3(4 * PP), lds_s,  \
+                         st, a, ws_bc, ws_g);                                                   \
     return hipGetLastError();                                                                   \
   }
 #define TT_MAMBA_W(PP, NN) TT_MAMBA(PP, NN, 2) TT_MAMBA(PP, NN, 3) TT_MAMBA(PP, NN, 4)
