@@ -135,6 +135,8 @@ CASES = [
     (40, 5, 64, 2, 1, 64, [7 * i % 50 for i in range(40)]),   # K = 64 (a single step), 2 m-tiles
     (2, 16, 2688, 8, 2, 128, (300, 17)),       # width not a power of two (42 k-steps)
     (8, 16, 512, 4, 2, 128, [64] * 8),         # 8 tiles: the per-XCD tile numbering
+    (1, 1, 64, 1, 1, 64, (5,)),                # a single token row (M = 1)
+    (2, 64, 128, 2, 1, 128, (10, 300)),        # the longest block (S = 64)
 ]
 
 
