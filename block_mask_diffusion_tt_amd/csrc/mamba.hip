@@ -258,13 +258,15 @@ struct ScanRound {
 };
 
 // Per (sequence, head): P/16 waves; wave w owns state rows 16w..16w+15, lane
-// l row p = 16w + l%16 and entries n in [kg*KS, kg*KS + KS), kg = l/16,
-// KS = N/4.  The outputs of 16 slots at a time are one 16 x 16 fp32 matrix
+// l row p = 16w + l%16 and KS = N/4 entries of it: n in [kg*KS, kg*KS + KS),
+// kg = l/16 (or, in the context tower's form, n = 16 (t/4) + 4 kg + t%4 for
+// its t-th entry).  The outputs of 16 slots at a time are one 16 x 16 fp32 matrix
 // tile per wave, accumulated by v_mfma_f32_16x16x4f32 in two parts:
-//   H0 C_s               -- K = N, taken in the order n = kg*KS + t at step
-//                            t, so each lane's A operand is its own state
-//                            entry t and its B operand C[s][kg*KS + t]; the
-//                            tile is then scaled by the decay exp(cum_s);
+//   H0 C_s               -- K = N, taken in the order of the lanes' own
+//                            entries: at step t each lane's A operand is its
+//                            state entry t and its B operand C[s][n] for the
+//                            same n; the tile is then scaled by the decay
+//                            exp(cum_s);
 //   X^T M^T              -- K = the slots j (4 per step), the in-block sum
 //                            sum_j M[s][j] x_j[p] (M is 0 for j > s).
 // Lane l then holds y at slot s0 + l%16 for rows 16w + 4 kg + r, r < 4.

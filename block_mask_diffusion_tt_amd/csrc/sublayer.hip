@@ -31,6 +31,8 @@
 // on XCD i % 8), so the tiles that share W columns share an L2.
 #include <math.h>
 
+#include <atomic>
+
 #include "tt_internal.h"
 
 namespace tt {
@@ -338,10 +340,18 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
   // CUs: a 2-stage ring (64 KB), so that two tiles share a CU and the tiles
   // past the CU count run beside the others instead of in a second round
   // (measured: 288 tiles on 256 CUs take 56 us instead of 80).
-  int dev = 0, cus = 0;
+  int dev = 0;
   hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
+  // CU count per device, asked once (concurrent first calls store the same
+  // value)
+  static std::atomic<int> cu_count[64];
+  int cus = dev < 64 ? cu_count[dev].load(std::memory_order_relaxed) : 0;
+  if (cus == 0) {
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (dev < 64) cu_count[dev].store(cus, std::memory_order_relaxed);
+  }
   const bool two = tiles > cus;
   const dim3 grid(tiles);
   if (epi == kEpiQkv) {
