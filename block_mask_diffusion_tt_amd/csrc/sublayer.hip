@@ -226,15 +226,15 @@ __global__ __launch_bounds__(kGThreads * NG) void gemm_kernel(GemmArgs a) {
 #pragma unroll
   for (int s0 = 0; s0 < NS - 1; ++s0)
     if (s0 < steps) issue(s0);
-  for (int i = 0; i < iters; ++i) {
+  for (int it = 0; it < iters; ++it) {
     // this step's copies (this wave's) are done once at most the later
     // steps' are in flight; the barrier makes every wave's copies visible
-    // and frees the stage the copy below overwrites (read in step i-1)
-    wait_steps<NS>(min(NS - 2, steps - 1 - i));
+    // and frees the stage the copy below overwrites (read in step it-1)
+    wait_steps<NS>(min(NS - 2, steps - 1 - it));
     __syncthreads();
-    if (i + NS - 1 < steps) issue(i + NS - 1);
-    if (i >= steps) continue;            // a group with one step fewer
-    TT_LDS const uint8_t* sa = lsm + (grp * NS + i % NS) * kStageBytes;
+    if (it + NS - 1 < steps) issue(it + NS - 1);
+    if (it >= steps) continue;           // a group with one step fewer
+    TT_LDS const uint8_t* sa = lsm + (grp * NS + it % NS) * kStageBytes;
     TT_LDS const uint8_t* sw_ = sa + kTileBytes;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
