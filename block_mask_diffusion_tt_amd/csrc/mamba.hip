@@ -160,9 +160,38 @@ __global__ __launch_bounds__(kMThreads) void mamba_group_kernel(MambaArgs a, flo
   auto chan = [&](int cc) { return H * P + (cc < N ? g * N + cc : G * N + g * N + (cc - N)); };
   Taps<KW> tp;
   tp.load(a.conv_w, a.conv_b, chan(threadIdx.x % (2 * N)));
-  load_window<T, KW, kMThreads, 2 * N, kU>(xbc, cst, C, 0, S + KW - 1, chan, win, BCP);
-  __syncthreads();
-  conv_window<KW, kMThreads, 2 * N>(win, BCP, S, tp, out, BCP);
+  // One thread per B/C channel and S <= 16: element u * 2N + tid of the
+  // window is row u of channel tid, so the thread's own loads hold its
+  // channel's whole window and the conv runs from registers (rows past
+  // the window load a clamped element and are never used).
+  if (kMThreads == 2 * N && S <= kSC) {
+    constexpr int kRows = kSC + KW - 1;
+    const int tid = threadIdx.x;
+    const int total = (S + KW - 1) * 2 * N;
+    uint32_t v[kRows];
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const int i = min(u * 2 * N + tid, total - 1);
+      const int r = i / (2 * N), c = chan(i % (2 * N));
+      const int t = r - (KW - 1);
+      const T* src = t < 0 ? cst + static_cast<int64_t>(c) * (KW - 1) + r
+                           : xbc + static_cast<int64_t>(t) * C + c;
+      v[u] = ld_raw(src);
+    }
+#pragma unroll
+    for (int si = 0; si < kSC; ++si) {   // unrolled: constant register indexes
+      if (si < S) {
+        float acc = tp.bias;
+#pragma unroll
+        for (int j = 0; j < KW; ++j) acc = fmaf(tp.w[j], raw_f32<T>(v[si + j]), acc);
+        out[si * BCP + tid] = silu(acc);
+      }
+    }
+  } else {
+    load_window<T, KW, kMThreads, 2 * N, kU>(xbc, cst, C, 0, S + KW - 1, chan, win, BCP);
+    __syncthreads();
+    conv_window<KW, kMThreads, 2 * N>(win, BCP, S, tp, out, BCP);
+  }
   __syncthreads();
   float* bc = ws_bc + (static_cast<int64_t>(b) * G + g) * S * 2 * N;
   for (int i = threadIdx.x; i < S * 2 * N / 4; i += kMThreads) {
