@@ -154,6 +154,28 @@ __global__ __launch_bounds__(256) void ln_modulate_kernel(LnArgs a) {
   }
 }
 
+// The epilogues for the 4 output columns n..n+3 of row m (sequence b):
+// kEpiQkv scatters them to q, k or v (a group never straddles: the
+// boundaries are multiples of 64); kEpiGate writes x + gate * C.
+template <int EPI>
+__device__ __forceinline__ void store4(const GemmArgs& a, int m, int b, int n, float c0, float c1,
+                                       float c2, float c3) {
+  if constexpr (EPI == kEpiQkv) {
+    uint16_t* dst;
+    if (n < a.nq) dst = a.q + static_cast<int64_t>(m) * a.nq + n;
+    else if (n < a.nq + a.nk) dst = a.k + static_cast<int64_t>(m) * a.nk + (n - a.nq);
+    else dst = a.v + static_cast<int64_t>(m) * a.nk + (n - a.nq - a.nk);
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(c0, c1), pack2(c2, c3));
+  } else {
+    const int64_t o = static_cast<int64_t>(m) * a.N + n;
+    const uint2 xv = *reinterpret_cast<const uint2*>(a.x + o);
+    const float4 gv = *reinterpret_cast<const float4*>(a.gate + static_cast<int64_t>(b) * a.N + n);
+    *reinterpret_cast<uint2*>(a.out + o) =
+        make_uint2(pack2(fmaf(gv.x, c0, bf_lo(xv.x)), fmaf(gv.y, c1, bf_hi(xv.x))),
+                   pack2(fmaf(gv.z, c2, bf_lo(xv.y)), fmaf(gv.w, c3, bf_hi(xv.y))));
+  }
+}
+
 // --------------------------------------------------------------------- GEMM
 // NG groups of 4 waves; group g multiplies the K-steps kt = g (mod NG)
 // through its own NS-stage ring, and group 1's accumulators are added into
@@ -289,23 +311,139 @@ __global__ __launch_bounds__(kGThreads * NG) void gemm_kernel(GemmArgs a) {
       for (int g = 0; g < 4; ++g) {
         const int n = n0 + wn * 64 + i * 32 + 8 * g + 4 * half;
         if (n >= a.N) continue;
-        const float c0 = acc[i][j][4 * g], c1 = acc[i][j][4 * g + 1];
-        const float c2 = acc[i][j][4 * g + 2], c3 = acc[i][j][4 * g + 3];
-        if constexpr (EPI == kEpiQkv) {
-          uint16_t* dst;
-          if (n < a.nq) dst = a.q + static_cast<int64_t>(m) * a.nq + n;
-          else if (n < a.nq + a.nk) dst = a.k + static_cast<int64_t>(m) * a.nk + (n - a.nq);
-          else dst = a.v + static_cast<int64_t>(m) * a.nk + (n - a.nq - a.nk);
-          *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(c0, c1), pack2(c2, c3));
-        } else {
-          const int64_t o = static_cast<int64_t>(m) * a.N + n;
-          const uint2 xv = *reinterpret_cast<const uint2*>(a.x + o);
-          const float4 gv = *reinterpret_cast<const float4*>(a.gate + static_cast<int64_t>(b) * a.N + n);
-          *reinterpret_cast<uint2*>(a.out + o) =
-              make_uint2(pack2(fmaf(gv.x, c0, bf_lo(xv.x)), fmaf(gv.y, c1, bf_hi(xv.x))),
-                         pack2(fmaf(gv.z, c2, bf_lo(xv.y)), fmaf(gv.w, c3, bf_hi(xv.y))));
-        }
+        store4<EPI>(a, m, b, n, acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                    acc[i][j][4 * g + 3]);
       }
+  }
+}
+
+// 128 x 144 tiles, for shapes whose tile count fits the CUs at this width
+// but not at 128 (N = 4608 at M = 1024: 256 tiles instead of 288): two
+// groups of 4 waves as in gemm_kernel<EPI, 2, 2>; each wave multiplies all
+// 144 W rows of the tile against its 32 A rows with
+// v_mfma_f32_16x16x32_bf16 (9 x 2 accumulator tiles of 16 x 16).  A stage
+// holds the A tile (16 KB), the W tile (18 KB) and 2 KB that two padding
+// copies fill (so that every wave issues 9 copies).
+constexpr int kBN144 = 144;
+constexpr int kStage144 = 36 * 1024;
+constexpr int kCopies144 = 9;            // per wave per stage: 36 copies / 4 waves
+
+template <int EPI>
+__global__ __launch_bounds__(2 * kGThreads) void gemm144_kernel(GemmArgs a) {
+  constexpr int NS = 2, NG = 2, NT = kBN144 / 16;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NG * NS * kStage144];
+  const int tiles_m = (a.M + kBM - 1) / kBM;
+  const int tiles = tiles_m * (a.N / kBN144);
+  const int bid = blockIdx.x;
+  const int t = (tiles % 8 == 0) ? (bid % 8) * (tiles / 8) + bid / 8 : bid;
+  const int m0 = (t % tiles_m) * kBM, n0 = (t / tiles_m) * kBN144;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, w4 = wave & 3;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((TT_LDS uint8_t*)smem));
+  TT_LDS const uint8_t* lsm = (TT_LDS const uint8_t*)smem;
+
+  // copy q = 9 w4 + j fills stage bytes [q KB, q KB + 1 KB): A rows 8q..
+  // (q < 16), W rows 8 (q - 16).. (q < 34), or W rows 0..7 again (padding);
+  // lane L: row + L / 8, LDS slot L % 8 <- k-chunk (L % 8) ^ ((row >> 1) & 7)
+  uint32_t off[kCopies144];
+  bool isw[kCopies144];
+#pragma unroll
+  for (int j = 0; j < kCopies144; ++j) {
+    const int q = w4 * kCopies144 + j;
+    isw[j] = q >= 16;
+    const int r = (q < 16 ? 8 * q : (q < 34 ? 8 * (q - 16) : 0)) + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int rc = q < 16 ? min(r, a.M - 1 - m0) : r;     // N is a multiple of 144
+    off[j] = static_cast<uint32_t>(rc * a.K * 2 + c * 16);
+  }
+  const uint16_t* abase = a.a + static_cast<int64_t>(m0) * a.K;
+  const uint16_t* wbase = a.w + static_cast<int64_t>(n0) * a.K;
+  auto issue = [&](int i) {
+    const int kt = i * NG + grp;
+    const uint32_t l0 = __builtin_amdgcn_readfirstlane(
+        lds0 + (grp * NS + i % NS) * kStage144 + w4 * kCopies144 * 1024);
+#pragma unroll
+    for (int j = 0; j < kCopies144; ++j)
+      dma16s((isw[j] ? wbase : abase) + kt * kBK, off[j], l0 + j * 1024);
+  };
+
+  // operand reads, k-substep ks of 32: W rows 16 nt + l%16 (A operand), A
+  // rows 32 w4 + 16 mt + l%16 (B operand), k-chunk 4 ks + l/16
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int sw = (l16 >> 1) & 7;
+  const int slot0 = ((kq) ^ sw) * 16, slot1 = ((4 + kq) ^ sw) * 16;
+  const int wrow = l16 * 128, arow = (w4 * 32 + l16) * 128;
+
+  f32x4 acc[NT][2];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) acc[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int KT = a.K / kBK;
+  const int steps = (KT - grp + NG - 1) / NG;
+  const int iters = (KT + NG - 1) / NG;
+  if (steps > 0) issue(0);
+  for (int it = 0; it < iters; ++it) {
+    wait_vmem<0>();                      // this wave's copies of step it
+    __syncthreads();                     // everyone's; step it-1's stage is free
+    if (it + 1 < steps) issue(it + 1);
+    if (it >= steps) continue;
+    TT_LDS const uint8_t* sa = lsm + (grp * NS + it % NS) * kStage144;
+    TT_LDS const uint8_t* sw_ = sa + kTileBytes;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int slot = ks ? slot1 : slot0;
+      bf16x8 af[2], wf[NT];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        af[mt] = *reinterpret_cast<TT_LDS const bf16x8*>(sa + arow + mt * 16 * 128 + slot);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        wf[nt] = *reinterpret_cast<TT_LDS const bf16x8*>(sw_ + wrow + nt * 16 * 128 + slot);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[nt], af[mt], acc[nt][mt], 0, 0, 0);
+    }
+  }
+
+  // group 1's partial sums into group 0's
+  TT_LDS float* red = (TT_LDS float*)smem;
+  __syncthreads();
+  if (grp == 1) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[(((w4 * NT + nt) * 2 + mt) * 4 + r) * 64 + lane] = acc[nt][mt][r];
+  }
+  __syncthreads();
+  if (grp == 1) return;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[nt][mt][r] += red[(((w4 * NT + nt) * 2 + mt) * 4 + r) * 64 + lane];
+
+  // ---- epilogue: lane holds C[m][n .. n+3] for m = m0 + 32 w4 + 16 mt + l%16,
+  // n = n0 + 16 nt + 4 (l/16)
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int m = m0 + w4 * 32 + mt * 16 + l16;
+    if (m >= a.M) continue;
+    const int b = m / a.S;
+    if (a.active && !a.active[b]) continue;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int n = n0 + nt * 16 + 4 * kq;
+      store4<EPI>(a, m, b, n, acc[nt][mt][0], acc[nt][mt][1], acc[nt][mt][2], acc[nt][mt][3]);
+    }
   }
 }
 
@@ -353,6 +491,12 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
     if (dev < 64) cu_count[dev].store(cus, std::memory_order_relaxed);
   }
   const bool two = tiles > cus;
+  const int tiles144 = a.N % kBN144 == 0 ? ((a.M + kBM - 1) / kBM) * (a.N / kBN144) : 0;
+  if (two && tiles144 > 0 && tiles144 <= cus) {
+    if (epi == kEpiQkv) hipLaunchKernelGGL(gemm144_kernel<kEpiQkv>, dim3(tiles144), dim3(2 * kGThreads), 0, st, a);
+    else hipLaunchKernelGGL(gemm144_kernel<kEpiGate>, dim3(tiles144), dim3(2 * kGThreads), 0, st, a);
+    return hipGetLastError();
+  }
   const dim3 grid(tiles);
   if (epi == kEpiQkv) {
     if (two) hipLaunchKernelGGL((gemm_kernel<kEpiQkv, 2, 1>), grid, dim3(kGThreads), 0, st, a);

@@ -185,15 +185,17 @@ def test_end_to_end_against_oracle():
 
 
 # Full size: 64 sequences, S = 16, width 4096, 32 / 2 heads of 128, 1024
-# context tokens each (the launch shapes the benchmark times: 288 and 256
-# tiles), checked on sampled sequences.
+# context tokens each (the launch shapes the benchmark times: the QKV
+# projection in 256 tiles of 128 x 144, the O projection in 256 of
+# 128 x 128).  The QKV projection is checked on every row (an fp64 product
+# of 19 GFLOP on the host), the other stages on sampled sequences.
 def test_full_size_sampled():
     c = scase(64, 16, 4096, 32, 2, 128, [1024] * 64, seed=41)
     say("sublayer full size")
     st = chain(c)
     seqs = [0, 29, 63]
     check_ln(dict(c, x=c["x"][seqs], shift=c["shift"][seqs], scale=c["scale"][seqs]), st["h"][seqs])
-    check_qkv(c, st, seqs)
+    check_qkv(c, st)
     check_attn(c, st, seqs)
     check_out(c, st, seqs)
     got = composite(c)
