@@ -506,14 +506,14 @@ __device__ double recheck_row(const T* x, int V, float m, double tau, double* re
     const double a = (static_cast<double>(v) - md) * inv;
     return a > -50.0 ? exp(a) : 0.0;
   };
-  // scalar head up to 16-byte alignment, then 8 logits per thread per
-  // iteration (one or two 16-byte loads), then a scalar tail
+  // scalar head up to 16-byte alignment, then groups of 8 logits with four
+  // groups' loads in flight per thread (the scan is a full read of the row
+  // by one workgroup: one load at a time left it waiting on memory), then
+  // the remaining groups and a scalar tail
   const int head = min(V, static_cast<int>(((16 - reinterpret_cast<uintptr_t>(x) % 16) % 16) / sizeof(T)));
   if (static_cast<int>(threadIdx.x) < head) acc += term(load1(x, threadIdx.x));
   const int nvec = (V - head) / 8;
-  for (int j = threadIdx.x; j < nvec; j += kThreads) {
-    float v[8];
-    load8<T>(x, head + 8 * static_cast<int64_t>(j), v);
+  auto group = [&](const float (&v)[8]) {
     double s8 = 0.0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -521,6 +521,19 @@ __device__ double recheck_row(const T* x, int V, float m, double tau, double* re
       if (a > -50.0) s8 += exp(a);
     }
     acc += s8;
+  };
+  int j = threadIdx.x;
+  for (; j + 3 * kThreads < nvec; j += 4 * kThreads) {
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load8<T>(x, head + 8 * static_cast<int64_t>(j + u * kThreads), v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) group(v[u]);
+  }
+  for (; j < nvec; j += kThreads) {
+    float v[8];
+    load8<T>(x, head + 8 * static_cast<int64_t>(j), v);
+    group(v);
   }
   for (int i = head + 8 * nvec + threadIdx.x; i < V; i += kThreads) acc += term(load1(x, i));
 #pragma unroll
