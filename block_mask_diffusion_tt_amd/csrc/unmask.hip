@@ -326,6 +326,8 @@ struct Chunk<float> {
 // and the Gumbel-max candidates x >= M - cand_margin(M): the token holding
 // M was itself a candidate when it arrived, and it outscores every token
 // left out, so the best perturbed score of the slice is among the candidates.
+// (A running maximum per wave instead, with no barrier, was slower: the
+// waves' maxima grow later, so more tokens pass as candidates.)
 template <typename T>
 __global__ __launch_bounds__(kThreads) void rowsample_kernel(
     const T* __restrict__ logits, int64_t row_stride, int V, const uint8_t* __restrict__ masked,
@@ -374,9 +376,10 @@ __global__ __launch_bounds__(kThreads) void rowsample_kernel(
       for (int j = 0; j < 8; ++j) e[j] = fast_exp2((cur.get(8 * u + j) - M) * c);
       z += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
     }
-    // a bit per candidate, then one loop body for all of them (the logit is
-    // read again -- from the cache, it was just loaded -- rather than
-    // indexed out of the registers)
+    // a bit per candidate, then one loop body for all of them; the logit is
+    // picked out of the loaded registers by a select over the 32 slots (a
+    // reload from memory made every pass with a candidate wait a full memory
+    // round trip before the next barrier)
     const float thr = M - cand_margin(M, tau);
     uint32_t cand = 0;
 #pragma unroll
@@ -388,7 +391,9 @@ __global__ __launch_bounds__(kThreads) void rowsample_kernel(
       const int i = __builtin_ctz(cand);
       cand &= cand - 1;
       const int t = cb + 8 * (tid + kThreads * (i >> 3)) + (i & 7);
-      const float l = load1(x, t);
+      float l = 0.f;
+#pragma unroll
+      for (int k = 0; k < kPerThread; ++k) l = (k == i) ? cur.get(k) : l;
       const float sc = l + tau * gumbel32(noise_word(rk, t));
       merge_best(key, key2, idx, lx, sc, -INFINITY, t, l);
     }
