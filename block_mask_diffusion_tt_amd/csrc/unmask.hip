@@ -422,6 +422,12 @@ __global__ __launch_bounds__(kThreads) void rowsample_kernel(
   }
 }
 
+// The decision kernel runs one workgroup per sequence; its fp64 full-row
+// scans (rescoring near-tied Gumbel scores, rechecking confidences near a
+// decision boundary) are reads of a whole row by that one workgroup, so it is
+// a large one: 16 waves keep 64 KB of the row in flight.
+constexpr int kDecideThreads = 1024;
+
 // fp64 rescoring of one row's candidates (those within cand_margin of the
 // row maximum m): the token of the largest l + tau G in fp64, lowest token on
 // equal scores.  All threads take part; every thread returns the result.
@@ -447,24 +453,24 @@ __device__ void rescore_row64(const T* x, int V, float m, float tau, double tau6
   if (static_cast<int>(threadIdx.x) < head) visit(load1(x, threadIdx.x), threadIdx.x);
   const int nvec = (V - head) / 8;
   int j = threadIdx.x;
-  for (; j + 3 * kThreads < nvec; j += 4 * kThreads) {
+  for (; j + 3 * kDecideThreads < nvec; j += 4 * kDecideThreads) {
     float v[4][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) load8<T>(x, head + 8 * static_cast<int64_t>(j + u * kThreads), v[u]);
+    for (int u = 0; u < 4; ++u) load8<T>(x, head + 8 * static_cast<int64_t>(j + u * kDecideThreads), v[u]);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       float g = fmaxf(fmaxf(fmaxf(v[u][0], v[u][1]), fmaxf(v[u][2], v[u][3])),
                       fmaxf(fmaxf(v[u][4], v[u][5]), fmaxf(v[u][6], v[u][7])));
       if (g >= thr)
-        for (int k = 0; k < 8; ++k) visit(v[u][k], head + 8 * (j + u * kThreads) + k);
+        for (int k = 0; k < 8; ++k) visit(v[u][k], head + 8 * (j + u * kDecideThreads) + k);
     }
   }
-  for (; j < nvec; j += kThreads) {
+  for (; j < nvec; j += kDecideThreads) {
     float v[8];
     load8<T>(x, head + 8 * static_cast<int64_t>(j), v);
     for (int k = 0; k < 8; ++k) visit(v[k], head + 8 * j + k);
   }
-  for (int t = head + 8 * nvec + threadIdx.x; t < V; t += kThreads) visit(load1(x, t), t);
+  for (int t = head + 8 * nvec + threadIdx.x; t < V; t += kDecideThreads) visit(load1(x, t), t);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const double ob = __shfl_xor(best, off);
@@ -483,7 +489,7 @@ __device__ void rescore_row64(const T* x, int V, float m, float tau, double tau6
   __syncthreads();
   best = red_k[0];
   bi = red_i[0];
-  for (int w = 1; w < kThreads / 64; ++w)
+  for (int w = 1; w < kDecideThreads / 64; ++w)
     if (red_k[w] > best || (red_k[w] == best && red_i[w] < bi)) {
       best = red_k[w];
       bi = red_i[w];
@@ -528,32 +534,38 @@ __device__ double recheck_row(const T* x, int V, float m, double tau, double* re
     acc += s8;
   };
   int j = threadIdx.x;
-  for (; j + 3 * kThreads < nvec; j += 4 * kThreads) {
+  for (; j + 3 * kDecideThreads < nvec; j += 4 * kDecideThreads) {
     float v[4][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) load8<T>(x, head + 8 * static_cast<int64_t>(j + u * kThreads), v[u]);
+    for (int u = 0; u < 4; ++u) load8<T>(x, head + 8 * static_cast<int64_t>(j + u * kDecideThreads), v[u]);
 #pragma unroll
     for (int u = 0; u < 4; ++u) group(v[u]);
   }
-  for (; j < nvec; j += kThreads) {
+  for (; j < nvec; j += kDecideThreads) {
     float v[8];
     load8<T>(x, head + 8 * static_cast<int64_t>(j), v);
     group(v);
   }
-  for (int i = head + 8 * nvec + threadIdx.x; i < V; i += kThreads) acc += term(load1(x, i));
+  for (int i = head + 8 * nvec + threadIdx.x; i < V; i += kDecideThreads) acc += term(load1(x, i));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
   if (lane == 0) red[wave] = acc;
   __syncthreads();
-  double tot = ((red[0] + red[1]) + (red[2] + red[3]));
+  double t[kDecideThreads / 64];
+#pragma unroll
+  for (int w = 0; w < kDecideThreads / 64; ++w) t[w] = red[w];
+#pragma unroll
+  for (int h = kDecideThreads / 128; h >= 1; h >>= 1)   // fixed pairwise tree
+#pragma unroll
+    for (int w = 0; w < h; ++w) t[w] += t[w + h];
   __syncthreads();
-  return 1.0 / tot;
+  return 1.0 / t[0];
 }
 
 template <typename T, bool SAMPLE>
-__global__ __launch_bounds__(kThreads) void decide_kernel(
+__global__ __launch_bounds__(kDecideThreads) void decide_kernel(
     const T* __restrict__ logits, int64_t row_stride, int S, int V,
     const void* __restrict__ parts, int splits, float c, float gamma, float tau, double tau64,
     NoiseKey nk, int mask_id, int step, int32_t* tokens, uint8_t* masked, uint8_t* committed_now,
@@ -566,8 +578,8 @@ __global__ __launch_bounds__(kThreads) void decide_kernel(
   __shared__ int s_checked[64];
   __shared__ int s_msk[64];
   __shared__ int s_rescore[64];
-  __shared__ double red[kThreads / 64];
-  __shared__ int red_i[kThreads / 64];
+  __shared__ double red[kDecideThreads / 64];
+  __shared__ int red_i[kDecideThreads / 64];
   __shared__ int s_choice;        // -1: threshold set; else the single slot
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -731,7 +743,7 @@ void launch_unmask_t(const UnmaskArgs& a, const UnmaskPlan& p, void* ws, int vec
     RowPart* part = static_cast<RowPart*>(ws);
     hipLaunchKernelGGL(rowreduce_kernel<T>, dim3(p.splits, a.B * a.S), blk, 0, st, x, a.row_stride,
                        a.V, a.masked, c, p.split_len, p.splits, vec, part);
-    hipLaunchKernelGGL((decide_kernel<T, false>), dim3(a.B), blk, 0, st, x, a.row_stride, a.S, a.V,
+    hipLaunchKernelGGL((decide_kernel<T, false>), dim3(a.B), dim3(kDecideThreads), 0, st, x, a.row_stride, a.S, a.V,
                        static_cast<const void*>(part), p.splits, c, a.gamma, a.temperature, tau64,
                        nk, a.mask_id, a.step, a.tokens, a.masked, a.committed_now, a.conf, a.pred,
                        a.commit_step, a.n_masked);
@@ -740,7 +752,7 @@ void launch_unmask_t(const UnmaskArgs& a, const UnmaskPlan& p, void* ws, int vec
     hipLaunchKernelGGL(rowsample_kernel<T>, dim3(p.s_splits, a.B * a.S), blk, 0, st, x,
                        a.row_stride, a.V, a.masked, c, a.temperature, nk, p.split_len, p.s_splits,
                        vec, part);
-    hipLaunchKernelGGL((decide_kernel<T, true>), dim3(a.B), blk, 0, st, x, a.row_stride, a.S, a.V,
+    hipLaunchKernelGGL((decide_kernel<T, true>), dim3(a.B), dim3(kDecideThreads), 0, st, x, a.row_stride, a.S, a.V,
                        static_cast<const void*>(part), p.s_splits, c, a.gamma, a.temperature,
                        tau64, nk, a.mask_id, a.step, a.tokens, a.masked, a.committed_now, a.conf,
                        a.pred, a.commit_step, a.n_masked);
