@@ -113,25 +113,32 @@ def test_row_stride():
 # Planted near-ties of the perturbed scores: token 1's logit is set so that
 # l_1 + tau G_1 lies within a few fp32 ulps of l_0 + tau G_0 (the noise taken
 # from the oracle's generator for that slot), far below the fp32 decision
-# band: the fp64 rescoring path must pick the oracle's token.
-def test_planted_score_near_ties():
-    B, S, V, tau, seed, block, step = 1, 8, 64, 0.5, 77, 3, 2
+# band: the fp64 rescoring path must pick the oracle's token.  At V = 40003
+# the pair sits mid-row and the rows are not 16-byte aligned, so the fp64 scan
+# runs its head, its four-groups-in-flight loop, its one-group loop and its
+# scalar tail.
+@pytest.mark.parametrize("V", [64, 40003])
+def test_planted_score_near_ties(V):
+    B, S, tau, seed, block, step = 1, 8, 0.5, 77, 3, 2
     tau32 = f32(tau)
     lg = np.full((B, S, V), -30.0)
+    pairs = []
     for s in range(S):
+        i0 = 0 if V == 64 else 20000 + 37 * s
         g = sampling.gumbel_noise(seed, s, step, block, V)
-        lg[0, s, 0] = 1.0
-        target = 1.0 + tau32 * (g[0] - g[1])
+        lg[0, s, i0] = 1.0
+        target = 1.0 + tau32 * (g[i0] - g[i0 + 1])
         l1 = np.float32(target)
         # step to the float32 neighbour on the side the slot asks for
         for _ in range(s % 3):
             l1 = np.nextafter(l1, np.float32(np.inf) if s % 2 else np.float32(-np.inf))
-        lg[0, s, 1] = float(l1)
+        lg[0, s, i0 + 1] = float(l1)
+        pairs.append({i0, i0 + 1})
     logits = torch.tensor(lg, dtype=torch.float32, device=DEV)
     masked = torch.ones((B, S), dtype=torch.uint8)
     g, r = check(logits, _tokens(B, S, masked, V), masked, 0.8, tau, seed, block, step,
-                 what="planted near-ties")
-    assert set(r["pred"][0].tolist()) <= {0, 1}
+                 what=f"planted near-ties V={V}")
+    assert all(int(t) in pairs[s] for s, t in enumerate(r["pred"][0].tolist()))
 
 
 # Planted confidences next to gamma (V = 2, logits (a, 0), p = sigmoid(a/tau)

@@ -124,9 +124,13 @@ def test_identical_rows_below_gamma_commit_lowest_slot():
 
 
 # Rows whose p sits within 1e-7 of gamma: only the fp64 recheck decides them.
+# V = 40003: rows not 16-byte aligned, and the recheck's full-row scan runs
+# every loop of its strided read (head, four groups in flight, one group,
+# scalar tail).
 @pytest.mark.parametrize("side", [-1, 1])
-def test_near_threshold_rows_decided_in_fp64(side):
-    V, S = 1024, 8
+@pytest.mark.parametrize("V", [1024, 40003])
+def test_near_threshold_rows_decided_in_fp64(side, V):
+    S = 8
     lg = torch.zeros((1, S, V), dtype=torch.float32)
     target = [0.8, 0.7, 0.9, 0.8, 0.5, 0.8, 0.3, 0.8]
     for s, p in enumerate(target):
