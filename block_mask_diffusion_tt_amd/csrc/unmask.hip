@@ -96,6 +96,38 @@ __device__ __forceinline__ void load8<float>(const float* x, int64_t i, float (&
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// Eight consecutive logits as loaded (raw words), unpacked to fp32 when used,
+// so a load can stay in flight while earlier data is processed.
+template <typename T>
+struct Raw8;
+
+template <>
+struct Raw8<uint16_t> {
+  uint4 w;
+  __device__ __forceinline__ void load(const uint16_t* x, int64_t i) {
+    w = *reinterpret_cast<const uint4*>(x + i);
+  }
+  __device__ __forceinline__ void unpack(float (&v)[8]) const {
+    v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
+    v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
+    v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xffff0000u);
+    v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xffff0000u);
+  }
+};
+
+template <>
+struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* x, int64_t i) {
+    a = *reinterpret_cast<const float4*>(x + i);
+    b = *reinterpret_cast<const float4*>(x + i + 4);
+  }
+  __device__ __forceinline__ void unpack(float (&v)[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
 __device__ __forceinline__ float load1(const uint16_t* x, int64_t i) {
   return __uint_as_float(static_cast<uint32_t>(x[i]) << 16);
 }
@@ -134,13 +166,38 @@ __global__ __launch_bounds__(kThreads) void rowreduce_kernel(
   if (vec_ok) {
     const int ngroups = (end - beg) >> 3;
     int gi = threadIdx.x;
-    // four 16-byte loads in flight per thread, consumed in index order
-    for (; gi + 3 * kThreads < ngroups; gi += 4 * kThreads) {
-      float v[4][8];
+    // uniform trips of four groups per thread (each lane still takes its
+    // groups tid, tid + 256, ... in index order, the remainder in the loop
+    // below); the next trip's loads are issued before this trip's arithmetic,
+    // into the other of two raw buffers (a copy between buffers would wait for
+    // its loads).  The last trip's fetch repeats its own addresses (in bounds,
+    // unused).
+    const int trips = ngroups / (4 * kThreads);
+    auto fetch = [&](Raw8<T> (&r)[4], int g) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) load8<T>(x, beg + ((gi + u * kThreads) << 3), v[u]);
+      for (int u = 0; u < 4; ++u) r[u].load(x, beg + ((g + u * kThreads) << 3));
+    };
+    auto trip = [&](const Raw8<T> (&r)[4], int g) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) group(v[u], beg + ((gi + u * kThreads) << 3));
+      for (int u = 0; u < 4; ++u) {
+        float v[8];
+        r[u].unpack(v);
+        group(v, beg + ((g + u * kThreads) << 3));
+      }
+    };
+    if (trips > 0) {
+      Raw8<T> ra[4], rb[4];
+      fetch(ra, gi);
+      for (int t = 0;;) {
+        fetch(rb, t + 1 < trips ? gi + 4 * kThreads : gi);
+        trip(ra, gi);
+        gi += 4 * kThreads;
+        if (++t == trips) break;
+        fetch(ra, t + 1 < trips ? gi + 4 * kThreads : gi);
+        trip(rb, gi);
+        gi += 4 * kThreads;
+        if (++t == trips) break;
+      }
     }
     for (; gi < ngroups; gi += kThreads) {
       float v[8];
