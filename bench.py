@@ -577,6 +577,18 @@ def generate_row(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, 
             "generated_tokens_per_s": round(tokens / sec, 1)}
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, n_seq, kc, vc, qb, kb, vb, ada, logits, start):
     """The fp64 oracle on the host cores: attention of n_seq sequences over all
     layers plus their unmasking pass, on D2H copies of the same inputs, scaled
@@ -613,7 +625,7 @@ def cpu_baseline(w, n_seq, kc, vc, qb, kb, vb, ada, logits, start):
     all_tokens = sum(L + S for L in w["lens"])
     t_step = t_attn * all_tokens / sample_tokens + t_unmask * B / len(seqs)
     return {"value": round(B * S / t_step, 3), "unit": "query-tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpu_count": os.cpu_count(), "host_cpu_model": cpu_model(),
             "sample": (f"{len(seqs)} of {B} sequences x {NL} layers attention + their unmasking "
                        f"rows (fp64 NumPy, {t_attn + t_unmask:.1f} s measured: attention "
                        f"{t_attn:.1f} s on {threads} BLAS threads, unmasking {t_unmask:.1f} s "

@@ -11,6 +11,7 @@ from ._binding import (AttnShape, StepProvider, TTError, abi_version, adaln_sing
                        mamba_workspace_size,
                        MambaShape, ln_modulate, qkv_proj, out_proj,
                        adaln_sublayer_workspace_size, adaln_attn_sublayer,
-                       denoise_block, denoise_workspace_size, dtype_code, last_error, lib,
+                       denoise_block, denoise_block_resume, denoise_workspace_size, dtype_code,
+                       last_error, lib,
                        timestep_embed, unmask_workspace_size, workspace_clear, EXPORTED,
                        LIB_PATH, TT_BF16, TT_F32)

@@ -27,7 +27,7 @@ _STATUS_NAMES = {0: "TT_OK", 1: "TT_ERR_INVALID_ARG", 2: "TT_ERR_UNSUPPORTED",
 EXPORTED = ["tt_last_error", "tt_abi_version", "tt_block_attn_workspace_size", "tt_block_attn",
             "tt_workspace_clear", "tt_timestep_embed", "tt_adaln_single",
             "tt_unmask_workspace_size", "tt_confidence_unmask", "tt_denoise_workspace_size",
-            "tt_denoise_block", "tt_ctx_block_attn", "tt_ctx_advance", "tt_sample_unmask",
+            "tt_denoise_block", "tt_denoise_block_resume", "tt_ctx_block_attn", "tt_ctx_advance", "tt_sample_unmask",
             "tt_generate_workspace_size", "tt_generate", "tt_mamba_workspace_size",
             "tt_mamba_block_scan", "tt_ln_modulate", "tt_qkv_proj", "tt_out_proj",
             "tt_adaln_sublayer_workspace_size", "tt_adaln_attn_sublayer"]
@@ -121,6 +121,11 @@ def _load():
         "tt_denoise_block": (ctypes.c_int, [shp, i32, i32, f32, f32, i32, i32, vp, vp, vp, vp,
                                             i32, vp, vp, vp, ctypes.POINTER(StepProvider), vp,
                                             vp, vp, ctypes.POINTER(i32), vp, sz, vp]),
+        "tt_denoise_block_resume": (ctypes.c_int, [shp, i32, i32, i32, f32, f32, i32,
+                                                   ctypes.c_uint64, i32, i32, i32, vp, vp, vp,
+                                                   vp, i32, vp, vp, vp,
+                                                   ctypes.POINTER(StepProvider), vp, vp, vp,
+                                                   ctypes.POINTER(i32), vp, sz, vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -163,6 +168,15 @@ def _stream(stream):
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def _on_stream(st):
+    """A torch stream context for the library's hipStream_t `st` (0 / None:
+    the null stream), so that a provider's copies are ordered with the
+    library's launches on that stream."""
+    if not st:
+        return torch.cuda.stream(torch.cuda.default_stream())
+    return torch.cuda.stream(torch.cuda.ExternalStream(st))
 
 
 def dtype_code(dtype):
@@ -275,12 +289,39 @@ def denoise_block(shape, n_layers, max_steps, gamma, temperature, mask_token_id,
                   k_ctx_layers, v_ctx_layers, ctx_start, ctx_len, max_ctx_len, provider,
                   tokens, masked, workspace, commit_step=None, ada_w=None, ada_bias=None,
                   ada_table=None, stream=None):
-    """Runs tt_denoise_block.  `provider` has two methods, called from inside
-    the loop with tensor views of the library's workspace buffers:
+    """Runs tt_denoise_block (see denoise_block_resume for the provider)."""
+    return _denoise(None, shape, n_layers, max_steps, gamma, temperature, mask_token_id, vocab,
+                    k_ctx_layers, v_ctx_layers, ctx_start, ctx_len, max_ctx_len, provider,
+                    tokens, masked, workspace, commit_step, ada_w, ada_bias, ada_table, stream)
+
+
+def denoise_block_resume(shape, n_layers, first_step, max_steps, gamma, temperature,
+                         mask_token_id, vocab, k_ctx_layers, v_ctx_layers, ctx_start, ctx_len,
+                         max_ctx_len, provider, tokens, masked, workspace, commit_step=None,
+                         seed=None, block_index=0, ada_w=None, ada_bias=None, ada_table=None,
+                         stream=None):
+    """Runs tt_denoise_block_resume: steps first_step .. first_step+max_steps-1
+    (seed None: argmax predictions; else temperature sampling with that seed
+    and block_index).  Returns the number of steps this call ran."""
+    resume = (int(first_step), 0 if seed is None else 1, 0 if seed is None else int(seed),
+              int(block_index))
+    return _denoise(resume, shape, n_layers, max_steps, gamma, temperature, mask_token_id, vocab,
+                    k_ctx_layers, v_ctx_layers, ctx_start, ctx_len, max_ctx_len, provider,
+                    tokens, masked, workspace, commit_step, ada_w, ada_bias, ada_table, stream)
+
+
+def _denoise(resume, shape, n_layers, max_steps, gamma, temperature, mask_token_id, vocab,
+             k_ctx_layers, v_ctx_layers, ctx_start, ctx_len, max_ctx_len, provider, tokens,
+             masked, workspace, commit_step, ada_w, ada_bias, ada_table, stream):
+    """The loop of tt_denoise_block (resume None) or of tt_denoise_block_resume
+    (resume = (first_step, sample, seed, block_index)).  `provider` has two
+    methods, called from inside the loop with tensor views of the library's
+    workspace buffers:
         provider.layer_inputs(step, layer, prev_out, q_blk, k_blk, v_blk)
         provider.logits(step, last_out, logits)
-    each filling its output tensors in place on the current stream (prev_out
-    is None for layer 0).  Returns the number of steps taken."""
+    each filling its output tensors in place on the current stream, which is
+    the library's stream while a callback runs (prev_out is None for layer
+    0).  Returns the number of steps taken."""
     B, S, Hq, Hkv, d = shape.batch, shape.block_size, shape.n_q_heads, shape.n_kv_heads, shape.head_dim
     tdtype = torch.bfloat16 if shape.dtype == TT_BF16 else torch.float32
     esz = 2 if shape.dtype == TT_BF16 else 4
@@ -300,9 +341,10 @@ def denoise_block(shape, n_layers, max_steps, gamma, temperature, mask_token_id,
 
     def _layer_inputs(user, step, layer, prev_out, q, kb, vb, st):
         try:
-            provider.layer_inputs(int(step), int(layer), view(prev_out, (B, S, Hq, d)),
-                                  view(q, (B, S, Hq, d)), view(kb, (B, S, Hkv, d)),
-                                  view(vb, (B, S, Hkv, d)))
+            with _on_stream(st):
+                provider.layer_inputs(int(step), int(layer), view(prev_out, (B, S, Hq, d)),
+                                      view(q, (B, S, Hq, d)), view(kb, (B, S, Hkv, d)),
+                                      view(vb, (B, S, Hkv, d)))
             return 0
         except Exception as e:  # reported through TT_ERR_CALLBACK
             errors.append(e)
@@ -310,7 +352,8 @@ def denoise_block(shape, n_layers, max_steps, gamma, temperature, mask_token_id,
 
     def _logits(user, step, last_out, lg, st):
         try:
-            provider.logits(int(step), view(last_out, (B, S, Hq, d)), view(lg, (B, S, vocab)))
+            with _on_stream(st):
+                provider.logits(int(step), view(last_out, (B, S, Hq, d)), view(lg, (B, S, vocab)))
             return 0
         except Exception as e:
             errors.append(e)
@@ -320,13 +363,18 @@ def denoise_block(shape, n_layers, max_steps, gamma, temperature, mask_token_id,
     kptrs = (ctypes.c_void_p * n_layers)(*[_ptr(t) for t in k_ctx_layers])
     vptrs = (ctypes.c_void_p * n_layers)(*[_ptr(t) for t in v_ctx_layers])
     taken = ctypes.c_int32(0)
-    status = _lib.tt_denoise_block(ctypes.byref(shape), int(n_layers), int(max_steps),
-                                   float(gamma), float(temperature), int(mask_token_id),
-                                   int(vocab), kptrs, vptrs, _ptr(ctx_start), _ptr(ctx_len),
-                                   int(max_ctx_len), _ptr(ada_w), _ptr(ada_bias), _ptr(ada_table),
-                                   ctypes.byref(cb), _ptr(tokens), _ptr(masked),
-                                   _ptr(commit_step), ctypes.byref(taken), _ptr(workspace),
-                                   _nbytes(workspace), _stream(stream))
+    rest = (int(mask_token_id), int(vocab), kptrs, vptrs, _ptr(ctx_start), _ptr(ctx_len),
+            int(max_ctx_len), _ptr(ada_w), _ptr(ada_bias), _ptr(ada_table), ctypes.byref(cb),
+            _ptr(tokens), _ptr(masked), _ptr(commit_step), ctypes.byref(taken), _ptr(workspace),
+            _nbytes(workspace), _stream(stream))
+    if resume is None:
+        status = _lib.tt_denoise_block(ctypes.byref(shape), int(n_layers), int(max_steps),
+                                       float(gamma), float(temperature), *rest)
+    else:
+        first, sample, seed, blk = resume
+        status = _lib.tt_denoise_block_resume(ctypes.byref(shape), int(n_layers), first,
+                                              int(max_steps), float(gamma), float(temperature),
+                                              sample, seed, blk, *rest)
     if status != TT_OK:
         msg = last_error()
         if errors:
@@ -353,8 +401,9 @@ def generate(shape, n_layers, n_blocks, steps_per_block, gamma, temperature, mas
         provider.layer_inputs(block, step, layer, prev_out, q_blk, k_blk, v_blk)
         provider.logits(block, step, last_out, logits)
         provider.ctx_inputs(block, layer, tokens, prev_out, q_blk, k_blk, v_blk)
-    each filling its output tensors in place on the current stream (prev_out
-    is None for layer 0; tokens is the committed block [B, S] int32).
+    each filling its output tensors in place on the current stream, which is
+    the library's stream while a callback runs (prev_out is None for layer
+    0; tokens is the committed block [B, S] int32).
     Returns the number of blocks taken."""
     B, S, Hq, Hkv, d = shape.batch, shape.block_size, shape.n_q_heads, shape.n_kv_heads, shape.head_dim
     tdtype = torch.bfloat16 if shape.dtype == TT_BF16 else torch.float32
@@ -376,7 +425,8 @@ def generate(shape, n_layers, n_blocks, steps_per_block, gamma, temperature, mas
     def _wrap(fn):
         def inner(*a):
             try:
-                fn(*a)
+                with _on_stream(a[-1]):   # the library's stream is the last argument
+                    fn(*a)
                 return 0
             except Exception as e:  # reported through TT_ERR_CALLBACK
                 errors.append(e)

@@ -48,14 +48,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kTK = 64;          // keys per LDS tile
 constexpr int kKPad = 8;         // bf16 padding of an LDS K row
 constexpr int kVPad = 4;         // bf16 padding of an LDS V^T row
-constexpr int kRowsBf16 = 256;   // rows per bf16 workgroup (8 waves x 32)
+constexpr int kMaxWaves = 8;     // bf16 workgroups: up to 8 waves of 32 rows
 constexpr int kRowsF32 = 64;     // rows per fp32 workgroup (1 wave, 1 row per lane)
 constexpr float kRescaleTh = 8.f;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct KParams {
   int B, S, Hq, Hkv, G, R;
-  int rows_per_unit, RB, NC, chunk;
+  int rows_per_unit, RB, NC, chunk, units;
   const uint16_t* q; const uint16_t* kb; const uint16_t* vb;
   const uint16_t* kc; const uint16_t* vc;
   const void* qf; const void* kbf; const void* vbf; const void* kcf; const void* vcf;
@@ -86,6 +86,18 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
   return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }
 
+// Logical unit of workgroup i (units are numbered (b, g, c, rb), row block
+// fastest).  With several row blocks per group, workgroup i runs logical
+// unit (i % 8) * ceil(U / 8) + i / 8: workgroups are dispatched to the 8 XCDs
+// round-robin, so the row blocks of one context chunk start together on one
+// XCD and read each K/V tile through its L2.  The grid then has 8 * ceil(U/8)
+// workgroups and those past U have nothing to do.
+__device__ __forceinline__ int unit_of_block(int i, int units, int RB) {
+  if (RB == 1) return i;
+  const int q = (units + 7) / 8;
+  return (i % 8) * q + i / 8;
+}
+
 // Decode the unit of this workgroup; false when it has nothing to do.
 struct Unit {
   int b, g, rb, c, nunits;
@@ -96,10 +108,10 @@ struct Unit {
 __device__ __forceinline__ bool decode_unit(int u, int Hkv, int RB, int NC, int chunk,
                                             const int32_t* ctx_len, const uint8_t* active,
                                             Unit& un) {
-  un.c = u % NC;
-  int t = u / NC;
-  un.rb = t % RB;
-  t /= RB;
+  un.rb = u % RB;
+  int t = u / RB;
+  un.c = t % NC;
+  t /= NC;
   un.g = t % Hkv;
   un.b = t / Hkv;
   if (active && !active[un.b]) return false;
@@ -165,6 +177,10 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t 
                :: "v"(off), "s"(base), "s"(lds) : "memory");
 }
 
+// Waits until at most N vector memory operations of this wave are in flight.
+// The stage waits count the copies only: the loops that use them issue no
+// other vector memory operation (operands come from LDS and registers; the
+// build checks that the kernels neither spill nor use M0 elsewhere).
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
@@ -203,13 +219,42 @@ constexpr int kSchedMfma = 0x8, kSchedValu = 0x402, kSchedLdsRead = 0x100;
 // produces it into a later basic block.
 #define TT_PIN(x) asm volatile("" : "+v"(x))
 
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. N-1.
+template <int B, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < N) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, N>(f);
+  }
+}
+
+// Slot order of the matrix products of a pipeline step (d/16 QK^T products
+// kk and 2 * d/32 PV^T products j = ks * d/32 + dt, alternating, opening
+// with two PV^T products): whether slot s is a QK^T product, and its kk or j.
 template <int D>
+struct SlotOrder;
+template <>
+struct SlotOrder<128> {
+  static constexpr int N = 16;
+  static constexpr int isq[16] = {0, 0, 1, 0, 1, 0, 1, 0, 1, 0, 1, 0, 1, 0, 1, 1};
+  static constexpr int idx[16] = {0, 1, 0, 2, 1, 3, 2, 4, 3, 5, 4, 6, 5, 7, 6, 7};
+};
+template <>
+struct SlotOrder<64> {
+  static constexpr int N = 8;
+  static constexpr int isq[8] = {0, 0, 1, 0, 1, 0, 1, 1};
+  static constexpr int idx[8] = {0, 1, 0, 2, 1, 3, 2, 3};
+};
+
+template <int D, int NW>
 struct Bf16Cfg {
   static constexpr int CH = D / 8;                 // 16-byte chunks per key row
   static constexpr int TILE = 64 * D * 2;          // bytes of one K (or V) tile of 64 keys
   static constexpr int NST = 4;                    // pipeline stages
   static constexpr int VREG = NST * TILE;          // V tiles follow the NST K tiles
-  static constexpr int CPT = 64 * CH / 512;        // copies per thread per tile tensor
+  static constexpr int ROWS = 32 * NW;             // rows per workgroup (32 per wave)
+  static constexpr int NT = 64 * NW;               // threads per workgroup
+  static constexpr int CPT = 64 * CH / NT;         // copies per thread per tile tensor
   static constexpr int SMEM = 2 * NST * TILE;
 };
 
@@ -228,71 +273,36 @@ __device__ __forceinline__ int vslot(int key, int c) {
   return (key >> 2) * 4 * (D / 8) + c * 4 + (key & 3);
 }
 
-
-template <int D>
-__global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
-  using C = Bf16Cfg<D>;
+// NW waves of 32 rows (NW = 8 for the 256 rows of S = 16 slots x 16 heads;
+// fewer for smaller blocks, so that no wave multiplies rows that do not exist).
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void attn_bf16_kernel(KParams p) {
+  using C = Bf16Cfg<D, NW>;
   constexpr int KSTEPS = D / 16;   // MFMA k-steps of QK^T
   constexpr int DT = D / 32;       // 32-channel tiles of the output
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::SMEM];
 
   Unit un;
-  if (!decode_unit(blockIdx.x, p.Hkv, p.RB, p.NC, p.chunk, p.ctx_len, p.active, un)) return;
+  const int ul = unit_of_block(blockIdx.x, p.units, p.RB);
+  if (ul >= p.units || !decode_unit(ul, p.Hkv, p.RB, p.NC, p.chunk, p.ctx_len, p.active, un)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31, grp = lane >> 4, li = lane & 15;
   const int64_t kstride = static_cast<int64_t>(p.Hkv) * D;
   TT_LDS uint8_t* const lsm = (TT_LDS uint8_t*)(smem);  // address-space cast
   append_block_kv(p, un, D, 2);
+  // this lane's row: rl within the unit's row block, row within the group
+  const int rl = wave * 32 + l32;
+  const int row = un.rb * C::ROWS + rl;
   // block keys visible to this lane's row: all S, or slots 0..s when causal
   // (rows past R take all S, so every row has a finite maximum)
-  int blk_valid = p.S;
-  if (p.causal) {
-    const int row = un.rb * kRowsBf16 + wave * 32 + l32;
-    blk_valid = row < p.R ? row / p.G + 1 : p.S;
-  }
+  const int blk_valid = (p.causal && row < p.R) ? row / p.G + 1 : p.S;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lsm));
-
-  // ---- Q' = (q * (1 + scale) + shift) * log2(e)/sqrt(d), rounded to bf16;
-  // this wave's 32 rows, lane l32 holding row wave*32 + l32
-  bf16x8 qf[KSTEPS];
-  {
-    const int row = un.rb * kRowsBf16 + wave * 32 + l32;
-    const bool valid = row < p.R;
-    const int s = valid ? row / p.G : 0;
-    const int h = un.g * p.G + (valid ? row % p.G : 0);
-    const uint16_t* qrow = p.q + ((static_cast<int64_t>(un.b) * p.S + s) * p.Hq + h) * D;
-    const float* sc = p.scale ? p.scale + (static_cast<int64_t>(un.b) * p.Hq + h) * D : nullptr;
-    const float* sh = p.shift ? p.shift + (static_cast<int64_t>(un.b) * p.Hq + h) * D : nullptr;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const int d0 = kk * 16 + half * 8;
-      float v[8];
-      const uint4 w = valid ? *reinterpret_cast<const uint4*>(qrow + d0) : make_uint4(0, 0, 0, 0);
-      v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
-      v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
-      v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xffff0000u);
-      v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xffff0000u);
-      if (sc && valid) {
-        const float4 a = *reinterpret_cast<const float4*>(sc + d0);
-        const float4 b = *reinterpret_cast<const float4*>(sc + d0 + 4);
-        v[0] *= 1.f + a.x; v[1] *= 1.f + a.y; v[2] *= 1.f + a.z; v[3] *= 1.f + a.w;
-        v[4] *= 1.f + b.x; v[5] *= 1.f + b.y; v[6] *= 1.f + b.z; v[7] *= 1.f + b.w;
-      }
-      if (sh && valid) {
-        const float4 a = *reinterpret_cast<const float4*>(sh + d0);
-        const float4 b = *reinterpret_cast<const float4*>(sh + d0 + 4);
-        v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
-        v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qf[kk][i] = static_cast<__bf16>(v[i] * p.qscale);
-    }
-  }
 
   // ---- tiles: the block's S keys first (chunk 0), then 64-key context tiles
   const int n_ctx_tiles = (un.k_end - un.k_beg + kTK - 1) / kTK;
   const int n_tiles = (un.has_blk ? 1 : 0) + n_ctx_tiles;
+  const int nh = 2 * n_tiles;   // 32-key halves
   const int64_t ctx0 = p.ctx_start[un.b];
   auto tile_valid = [&](int t) {
     return (un.has_blk && t == 0) ? blk_valid
@@ -362,252 +372,311 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
   const int vlo = 2 * (grp & 1) + ((li & 3) >> 1);
   const int vbase = C::VREG + vslot<D>(4 * half + (li >> 2), vlo) * 16 + ((li & 1) << 3);
 
+  // Scores are kept relative to each row's running reference mu: the QK^T
+  // accumulation starts from -mu (negmu, all 16 entries of a lane belong to
+  // one row), so no subtraction is needed before the exponentials.
   f32x16 acc[DT];
+  float mu = 0.f, lsum = 0.f;
+  f32x16 negmu;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negmu[r] = 0.f;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-  // Scores are kept relative to the row's running reference mu: the QK^T
-  // accumulation starts from -mu (negmu, all 16 entries of a lane belong to
-  // one row), so no subtraction is needed before the exponentials.
-  float mu = 0.f;
-  float lsum = 0.f;
-  f32x16 negmu;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) negmu[r] = 0.f;
 
-  // K operands of half kt of the tile in `stage` (A of S^T = K Q'^T)
-  auto kload = [&](int stage, int kt, bf16x8 (&ko)[KSTEPS]) {
-    TT_LDS const uint8_t* kb = lsm + stage * C::TILE + kt * 32 * C::CH * 16 + kbase;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
-      ko[kk] = *reinterpret_cast<TT_LDS const bf16x8*>(kb + kk * 2 * 16 * 16);
+  // Half g (32 keys) of the unit is half g & 1 of tile g >> 1, in stage
+  // (g >> 1) % NST.  K operand kk of half g (A of S^T = K Q'^T):
+  auto kread = [&](int g, int kk) {
+    TT_LDS const uint8_t* a = lsm + ((g >> 1) % C::NST) * C::TILE + (g & 1) * 32 * C::CH * 16 + kbase + kk * 2 * 16 * 16;
+    return *reinterpret_cast<TT_LDS const bf16x8*>(a);
   };
-  // S^T of 32 keys x this wave's 32 rows
-  auto qk = [&](const bf16x8 (&ko)[KSTEPS], f32x16& sc) {
-    sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ko[0], qf[0], negmu, 0, 0, 0);
-#pragma unroll
-    for (int kk = 1; kk < KSTEPS; ++kk)
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ko[kk], qf[kk], sc, 0, 0, 0);
-  };
-  // V^T operands of k-step ks (keys 16ks..16ks+15) of half kt (A of
-  // O^T += V^T P^T), two transpose reads each
-  auto vload = [&](int stage, int kt, int ks, bf16x8 (&vo)[2][DT]) {
+  // V^T operand (A of O^T += V^T P^T) of 16-key step ks, channel tile dt of
+  // half g: two transpose reads
+  auto vread = [&](int g, int ks, int dt) {
     typedef short v8i16 __attribute__((ext_vector_type(8)));
-    TT_LDS uint8_t* vb = lsm + stage * C::TILE + kt * 8 * 4 * C::CH * 16 + vbase + ks * 4 * 4 * C::CH * 16;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      TT_LDS uint8_t* a = vb + dt * 4 * 4 * 16;
-      const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<TT_LDS v4i16*>(a));
-      const v4i16 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          reinterpret_cast<TT_LDS v4i16*>(a + 2 * 4 * C::CH * 16));
-      const v8i16 w8 = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
-      vo[ks][dt] = __builtin_bit_cast(bf16x8, w8);
-    }
+    TT_LDS uint8_t* a = lsm + ((g >> 1) % C::NST) * C::TILE + (g & 1) * 8 * 4 * C::CH * 16 + vbase +
+                        ks * 4 * 4 * C::CH * 16 + dt * 4 * 4 * 16;
+    const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<TT_LDS v4i16*>(a));
+    const v4i16 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<TT_LDS v4i16*>(a + 2 * 4 * C::CH * 16));
+    const v8i16 w8 = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
+    return __builtin_bit_cast(bf16x8, w8);
   };
-  auto pv = [&](const bf16x8 (&vo)[2][DT], const bf16x8 (&pb)[2], int ks) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vo[ks][dt], pb[ks], acc[dt], 0, 0, 0);
-  };
-  // mask keys at or past nvalid in half kt, return the maximum of this
-  // lane's 16 scores (lanes l and l^32 hold the two halves of a row)
-  auto rowmax = [&](f32x16& sc, int kt, int nvalid) {
-    if (__builtin_expect(nvalid < kt * 32 + 32, 0)) {
-      // key of accumulator r is kt*32 + 4*half + 8*(r/4) + r%4
-      const int lim = nvalid - kt * 32 - 4 * ((static_cast<int>(threadIdx.x) >> 5) & 1);
+  // keys at or past the valid count of the tile holding half g are masked to
+  // -inf (key of accumulator r in half g&1 is (g&1)*32 + 4*half + 8*(r/4) + r%4)
+  auto mask_half = [&](f32x16& sc, int g) {
+    const int nvalid = tile_valid(g >> 1);
+    const int lim = nvalid - (g & 1) * 32 - 4 * half;
+    if (lim < 32) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (8 * (r >> 2) + (r & 3) >= lim) sc[r] = -INFINITY;
     }
-    float m = fmaxf(sc[0], sc[1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(sc[r], sc[r + 1]));
-    return m;
   };
-  auto rowmax_full = [&](const f32x16& sc) {
-    float m = fmaxf(sc[0], sc[1]);
+  // P = 2^S (scores relative to mu), rounded to bf16: the B operand of P^T
+  auto pack = [&](const f32x16& e, int r0) {
+    uint32_t pk[4];
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(sc[r], sc[r + 1]));
-    return m;
-  };
-  // raise the reference only when a half-tile exceeds it by more than 2^8
-  // (scores are relative to mu): the lane maxima decide, and only then are
-  // the two halves of each row combined, so both lanes of a row move mu
-  // together; sc is shifted to the new reference
-  auto rescale = [&](float lmax, f32x16& sc) {
-    if (__any(lmax > kRescaleTh)) {
-      const float up = fmaxf(xhalf_max(lmax), 0.f);
-      const float alpha = __builtin_amdgcn_exp2f(-up);
-      lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-      mu += up;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sc[r] -= up;
-        negmu[r] = -mu;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const bf16x2 pr = {static_cast<__bf16>(e[r0 + 2 * i]), static_cast<__bf16>(e[r0 + 2 * i + 1])};
+      pk[i] = __builtin_bit_cast(uint32_t, pr);
     }
+    return __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
   };
-  // P = 2^S (scores relative to mu) rounded to bf16, the B operand of P^T,
-  // in two parts: exponentials 0..kExpA-1 and the k-step-0 operand pb[0]
-  // (overlapped with the QK^T products), then the rest and pb[1]
-  // (overlapped with the first PV^T products).  The row sum adds the fp32
-  // values in two chains of plain adds: the dot-product instruction would
-  // serialize with the matrix products.
-  constexpr int kExpA = 10;
-  auto softmax_a = [&](const f32x16& sc, float (&e)[16], bf16x8 (&pb)[2]) {
-#pragma unroll
-    for (int r = 0; r < kExpA; ++r) e[r] = __builtin_amdgcn_exp2f(sc[r]);
-    pb[0] = pack_bf16(e, 0);
-  };
-  auto softmax_b = [&](const f32x16& sc, float (&e)[16], bf16x8 (&pb)[2]) {
-#pragma unroll
-    for (int r = kExpA; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(sc[r]);
-    pb[1] = pack_bf16(e, 8);
-  };
-  auto row_sum = [&](const float (&e)[16]) {
+  auto row_sum = [&](const f32x16& e) {
     float s0 = e[0], s1 = e[1];
 #pragma unroll
     for (int r = 2; r < 16; r += 2) {
       s0 += e[r];
       s1 += e[r + 1];
     }
-    lsum += s0 + s1;
+    return s0 + s1;
   };
   constexpr int LD = 2 * C::CPT;  // copies per thread per tile
-  // wait until this thread's copies of tile t have landed (`later` tiles
-  // issued after it may still be in flight), then make everyone's visible
-  auto wait_tile = [&](int later) {
-    if (later >= 1) wait_vmem<LD>();
-    else wait_vmem<0>();
-    __syncthreads();
-  };
 
-  // Pipeline (per wave; tile t in stage t % 4, halves h = 0, 1).  Each
-  // half-tile runs three phases, each a run of matrix products with the
-  // vector work that does not feed them interleaved:
-  //   1. S(next) = QK (8 products)    with exponentials 0..9 of P(h), pb[0]
-  //   2. O += PV(h) k-step 0 (4)      with exponentials 10..15, pb[1]; the
-  //                                   K operands of the next QK are read
-  //   3. O += PV(h) k-step 1 (4)      with the row sum of P(h) and the row
-  //                                   maximum of S(next); the V^T operands of
-  //                                   the next half's k-step 0 are read
-  // where S(next) is S(t,1) in half 0 and S(t+1,0) in half 1.  At the start
-  // of tile t the workgroup waits until tile t+1 is visible and issues the
-  // copies of tile t+3 into the stage of tile t-1, so every LDS operand read
-  // has a full phase or more before its products.  Only the first tile (the
-  // block's S keys) and the last context tile can hold fewer than 64 keys;
-  // the steps that touch them mask scores, the others do not.
-  const int pre = n_tiles < C::NST - 1 ? n_tiles : C::NST - 1;
-  for (int t = 0; t < pre; ++t) issue(t);
-  wait_tile(n_tiles > 2 ? 1 : (n_tiles - 1));   // tile 0 (tiles 1..2 may fly)
-  f32x16 sA, sB;
-  bf16x8 pb[2];
-  bf16x8 ko[KSTEPS];
-  bf16x8 vo[2][DT];
-  kload(0, 0, ko);
-  qk(ko, sA);
-  kload(0, 1, ko);
-  vload(0, 0, 0, vo);
-  float tmax = xhalf_max(rowmax(sA, 0, tile_valid(0)));
-  // the first half-tile sets the reference to its row maximum (finite: the
-  // first half of a unit's first tile always holds a valid key)
-  mu = tmax;
+  // Software pipeline over halves (per wave).  Step h runs one stream of
+  // matrix products that interleaves the PV^T products of half h (DT channel
+  // tiles x 2 k-steps, independent) with the dependent QK^T chain of half
+  // h+2 (D/16 products), while the vector unit turns the scores of half h+1
+  // into P(h+1)
+  // (exponentials, packs, the row sum): no product waits for the softmax and
+  // no exponential for a product.  The stream opens with two PV^T products,
+  // which gives the previous step's last QK^T products time to land before
+  // the exponentials need their scores.  Every operand is read from LDS two
+  // product slots before its use.
+  //   The running reference mu is raised only when a half's row sum
+  // exceeds 2^8 (some probability above 2^8, or many large ones): that rare
+  // step recomputes S(h+1) relative to the old mu, raises mu to the row
+  // maximum, rescales the accumulator and the sum, and shifts S(h+2).
+  //   Tiles stream HBM -> LDS in a 4-stage ring.  At the start of tile t
+  // (step 2t) the workgroup waits until tile t+1 is visible (the K operands
+  // of steps 2t and 2t+1) and refills the stage of tile t-1, whose last
+  // reads were in step 2t-1, with tile t+3: two tiles are in flight while
+  // two are read.
+  bf16x8 kop[KSTEPS];      // K operands of the QK^T chain in flight
+  bf16x8 vop[2 * DT];      // V^T operands of the PV^T products, j = ks * DT + dt
+  f32x16 scr[2];           // scores of halves of even / odd index
+  bf16x8 pb[2][2];         // P of halves of even / odd index (two k-steps)
+  // Q' = (q * (1 + scale) + shift) * log2(e)/sqrt(d), rounded to bf16;
+  // lane l32 holds its row.  All loads of q, scale and shift are issued at
+  // once (rows past R read row 0 and are zeroed), after the copies of tiles
+  // 0 and 1: the waits for the query loads also cover them (loads complete
+  // in order), and S(0) needs them.
+  bf16x8 qf[KSTEPS];
+  for (int t = 0; t < (n_tiles < 2 ? n_tiles : 2); ++t) issue(t);
+  const bool has_sc = p.scale != nullptr, has_sh = p.shift != nullptr;
+  {
+    uint4 qraw[KSTEPS];
+    float4 sca[KSTEPS][2], sha[KSTEPS][2];
+    const bool valid = row < p.R;
+    const int s = valid ? row / p.G : 0;
+    const int h = un.g * p.G + (valid ? row % p.G : 0);
+    const uint16_t* qrow = p.q + ((static_cast<int64_t>(un.b) * p.S + s) * p.Hq + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      qraw[kk] = *reinterpret_cast<const uint4*>(qrow + kk * 16 + half * 8);
+    // a missing vector reads the present one (ignored below), so that one
+    // branch holds every modulation load
+    if (has_sc || has_sh) {
+      const int64_t ada = (static_cast<int64_t>(un.b) * p.Hq + h) * D + half * 8;
+      const float* scp = (has_sc ? p.scale : p.shift) + ada;
+      const float* shp = (has_sh ? p.shift : p.scale) + ada;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          sca[kk][i] = *reinterpret_cast<const float4*>(scp + kk * 16 + 4 * i);
+          sha[kk][i] = *reinterpret_cast<const float4*>(shp + kk * 16 + 4 * i);
+        }
+    }
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const uint4 w = qraw[kk];
+      float v[8] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                    __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u),
+                    __uint_as_float(w.z << 16), __uint_as_float(w.z & 0xffff0000u),
+                    __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xffff0000u)};
+      if (has_sc || has_sh) {
+        const float4 a0 = sca[kk][0], a1 = sca[kk][1];
+        const float4 b0 = sha[kk][0], b1 = sha[kk][1];
+        const float sc8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float sh8[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (has_sc) v[i] *= 1.f + sc8[i];
+          if (has_sh) v[i] += sh8[i];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[kk][i] = static_cast<__bf16>(valid ? v[i] * p.qscale : 0.f);
+    }
+  }
+  // tiles 0 and 1 visible, then tiles 2 and 3 start
+  wait_vmem<0>();
+  __syncthreads();
+  for (int t = 2; t < (n_tiles < C::NST ? n_tiles : C::NST); ++t) issue(t);
+  // prologue: S(0), S(1); the reference mu is S(0)'s row maximum (finite:
+  // the first half of a unit's first tile always holds a valid key)
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) kop[kk] = kread(0, kk);
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk)
+    scr[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[kk], kk == 0 ? negmu : scr[0], 0, 0, 0);
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) kop[kk] = kread(1, kk);
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk)
+    scr[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kk], qf[kk], kk == 0 ? negmu : scr[1], 0, 0, 0);
+  vop[0] = vread(0, 0, 0);
+  vop[1] = vread(0, 0, 1);
+  mask_half(scr[0], 0);
+  {
+    float m = fmaxf(scr[0][0], scr[0][1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(scr[0][r], scr[0][r + 1]));
+    mu = xhalf_max(m);
+  }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    sA[r] -= tmax;
+    scr[0][r] = __builtin_amdgcn_exp2f(scr[0][r] - mu);
+    scr[1][r] -= mu;
     negmu[r] = -mu;
   }
-  tmax = 0.f;
-  // interleaving of the three phases (one product, then vector or LDS work)
-  auto sched_phase1 = [&]() {
+  pb[0][0] = pack(scr[0], 0);
+  pb[0][1] = pack(scr[0], 8);
+  lsum = row_sum(scr[0]);
+
+  // The rare step: S(g) = scores of half g relative to the old mu,
+  // recomputed from LDS (sn already holds its exponentials); mu is raised to
+  // the row maximum where that is positive, and S(g+1) (s2) shifted along.
+  auto raise_mu = [&](int g, f32x16& sn, f32x16& s2, bf16x8 (&pn)[2], float& esum) {
 #pragma unroll
-    for (int i = 0; i < KSTEPS - 1; ++i) {
-      TT_SCHED_GROUP(kSchedMfma, 1);
-      TT_SCHED_GROUP(kSchedValu, 2);
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const bf16x8 k1 = kread(g, kk);
+      sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[kk], kk == 0 ? negmu : sn, 0, 0, 0);
     }
-    TT_SCHED_GROUP(kSchedMfma, 1);
-  };
-  auto sched_phase2 = [&](bool kreads) {
+    mask_half(sn, g);
+    float m = fmaxf(sn[0], sn[1]);
 #pragma unroll
-    for (int i = 0; i < DT; ++i) {
-      TT_SCHED_GROUP(kSchedMfma, 1);
-      TT_SCHED_GROUP(kSchedValu, 3);
-      if (kreads) TT_SCHED_GROUP(kSchedLdsRead, KSTEPS / DT);
-    }
-  };
-  auto sched_phase3 = [&]() {
+    for (int r = 2; r < 16; r += 2) m = fmaxf(m, fmaxf(sn[r], sn[r + 1]));
+    const float up = fmaxf(xhalf_max(m), 0.f);
+    const float alpha = __builtin_amdgcn_exp2f(-up);
+    lsum *= alpha;
 #pragma unroll
-    for (int i = 0; i < DT; ++i) {
-      TT_SCHED_GROUP(kSchedMfma, 1);
-      TT_SCHED_GROUP(kSchedValu, 6);
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+    mu += up;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sn[r] = __builtin_amdgcn_exp2f(sn[r] - up);
+      s2[r] -= up;
+      negmu[r] = -mu;
     }
+    pn[0] = pack(sn, 0);
+    pn[1] = pack(sn, 8);
+    esum = row_sum(sn);
   };
-  auto tile_step = [&](int t, auto more_c, auto mask_c) {
-    constexpr bool MORE = decltype(more_c)::value;   // a tile t+1 follows
-    constexpr bool MASK = decltype(mask_c)::value;   // tile t or t+1 may be partial
-    const int st = t % C::NST;
-    const int st1 = (t + 1) % C::NST;
-    if (MORE) {
-      wait_tile(t + 2 < n_tiles ? 1 : 0);          // tile t+1 visible
+
+  // Step h (E = h & 1).  EDGE: half h+1 may be partial (first or last tile)
+  // or missing, half h+2 may be missing (its products then run on stale LDS
+  // data and are never used).
+  auto step = [&](int h, auto odd_c, auto edge_c) {
+    constexpr int E = decltype(odd_c)::value;
+    constexpr bool EDGE = decltype(edge_c)::value;
+    f32x16& sn = scr[E ^ 1];       // S(h+1) -> exponentials
+    f32x16& s2 = scr[E];           // S(h+2) (the stale S(h) dies here)
+    bf16x8 (&pc)[2] = pb[E];       // P(h)
+    bf16x8 (&pn)[2] = pb[E ^ 1];
+    const int t = h >> 1;
+    if (!E && t > 0) {
+      if (t + 2 < n_tiles) wait_vmem<LD>();
+      else wait_vmem<0>();
+      __syncthreads();
       if (t + C::NST - 1 < n_tiles) issue(t + C::NST - 1);
     }
-    float e[16];
-    // ---- half 0: P(t,0) from sA; S(t,1) into sB
-    vload(st, 0, 1, vo);
-    rescale(tmax, sA);
-    softmax_a(sA, e, pb);
-    qk(ko, sB);                                    // K(t,1)
-    sched_phase1();
-    softmax_b(sA, e, pb);
-    pv(vo, pb, 0);
-    if (MORE) kload(st1, 0, ko);                   // K(t+1,0)
-    sched_phase2(MORE);
-    pv(vo, pb, 1);
-    vload(st, 1, 0, vo);
-    row_sum(e);
-    tmax = MASK ? rowmax(sB, 1, tile_valid(t)) : rowmax_full(sB);
-    sched_phase3();
-    TT_PIN(tmax);
-    TT_PIN(lsum);
-    // ---- half 1: P(t,1) from sB; S(t+1,0) into sA
-    vload(st, 1, 1, vo);
-    rescale(tmax, sB);
-    softmax_a(sB, e, pb);
-    if (MORE) {
-      qk(ko, sA);                                  // K(t+1,0)
-      sched_phase1();
+    if (EDGE) mask_half(sn, h + 1);
+    // vector work: the 16 exponentials spread over the slots (from slot 1;
+    // the previous step's last QK^T products land meanwhile), each one's
+    // row-sum term two slots later, the packs once the values exist
+    using SO = SlotOrder<D>;
+    constexpr int NS = SO::N;
+    constexpr int EPS = 16 / NS;      // exponentials per slot
+    float rs0, rs1;                   // the row sum of P(h+1), two chains
+    static_for<0, NS>([&](auto s_c) {
+      constexpr int s = decltype(s_c)::value;
+      constexpr int x = SO::idx[s];
+      if constexpr (SO::isq[s] != 0)
+        s2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[x], qf[x], x == 0 ? negmu : s2, 0, 0, 0);
+      else
+        acc[x % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[x], pc[x / DT], acc[x % DT], 0, 0, 0);
+      // the operand of the product two slots ahead (the next step's first
+      // two PV^T products for the last two slots)
+      if constexpr (s + 2 < NS) {
+        constexpr int y = SO::idx[s + 2];
+        if constexpr (SO::isq[s + 2] != 0) kop[y] = kread(h + 2, y);
+        else vop[y] = vread(h, y / DT, y % DT);
+      } else {
+        constexpr int y = SO::idx[s + 2 - NS];
+        vop[y] = vread(h + 1, y / DT, y % DT);
+      }
+      // exponentials e0 .. e1-1 in this slot (none in slot 0, the rest in
+      // the last one); the row-sum terms of those of two slots back
+      constexpr int e0 = s == 0 ? 0 : (s - 1) * EPS;
+      constexpr int e1 = s == 0 ? 0 : (s == NS - 1 ? 16 : s * EPS);
+      constexpr int a0 = s < 3 ? 0 : (s - 3) * EPS;
+      constexpr int a1 = s < 3 ? 0 : (s - 2) * EPS;
+      static_for<e0, e1>([&](auto r_c) {
+        constexpr int r = decltype(r_c)::value;
+        sn[r] = __builtin_amdgcn_exp2f(sn[r]);
+      });
+      static_for<a0, a1>([&](auto r_c) {
+        constexpr int r = decltype(r_c)::value;
+        if constexpr (r == 0) rs0 = sn[0];
+        else if constexpr (r == 1) rs1 = sn[1];
+        else if constexpr (r & 1) rs1 += sn[r];
+        else rs0 += sn[r];
+      });
+      if constexpr (s == 8 / EPS + 1) {   // e0..e7 exist
+        pn[0] = pack(sn, 0);
+        // kept here: the rare branch below redefines pn, and the compiler
+        // would otherwise sink the packs to the next step's first products
+        asm volatile("" : "+v"(pn[0]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    static_for<(NS - 3) * EPS, 16>([&](auto r_c) {
+      constexpr int r = decltype(r_c)::value;
+      if constexpr (r & 1) rs1 += sn[r];
+      else rs0 += sn[r];
+    });
+    pn[1] = pack(sn, 8);
+    asm volatile("" : "+v"(pn[1]));
+    float esum = rs0 + rs1;
+    if (!EDGE || h + 1 < nh) {
+      if (__builtin_expect(__any(esum > 256.f), 0)) raise_mu(h + 1, sn, s2, pn, esum);
+      lsum += esum;
     }
-    softmax_b(sB, e, pb);
-    pv(vo, pb, 0);
-    if (MORE) kload(st1, 1, ko);                   // K(t+1,1)
-    sched_phase2(MORE);
-    pv(vo, pb, 1);
-    if (MORE) {
-      vload(st1, 0, 0, vo);                        // V(t+1,0), k-step 0
-      row_sum(e);
-      tmax = MASK ? rowmax(sA, 0, tile_valid(t + 1)) : rowmax_full(sA);
-      sched_phase3();
-      TT_PIN(tmax);
-    } else {
-      row_sum(e);
-    }
-    TT_PIN(lsum);
   };
-  if (n_tiles >= 2) tile_step(0, std::true_type{}, std::true_type{});
-  for (int t = 1; t + 2 < n_tiles; ++t) tile_step(t, std::true_type{}, std::false_type{});
-  if (n_tiles >= 3) tile_step(n_tiles - 2, std::true_type{}, std::true_type{});
-  tile_step(n_tiles - 1, std::false_type{}, std::true_type{});
+  // tile 0 and the last two tiles take the edge steps, the rest the
+  // steady-state ones (three loops, so each has one body)
+  step(0, std::integral_constant<int, 0>{}, std::true_type{});
+  step(1, std::integral_constant<int, 1>{}, std::true_type{});
+  int t = 1;
+  for (; t + 2 < n_tiles; ++t) {
+    step(2 * t, std::integral_constant<int, 0>{}, std::false_type{});
+    step(2 * t + 1, std::integral_constant<int, 1>{}, std::false_type{});
+  }
+  for (; t < n_tiles; ++t) {
+    step(2 * t, std::integral_constant<int, 0>{}, std::true_type{});
+    step(2 * t + 1, std::integral_constant<int, 1>{}, std::true_type{});
+  }
 
-  // ---- partials: (max, sum) per row and the unnormalised accumulator
-  const int64_t u = blockIdx.x;
+  // ---- partials: (max, sum) per row and the unnormalised accumulator, in
+  // the unit's slot ((b * Hkv + g) * RB + rb) * NC + c
   const float ltot = xhalf_sum(lsum);
-  const int rl = wave * 32 + l32;
-  if (un.rb * kRowsBf16 + rl >= p.R) return;
+  if (row >= p.R) return;
+  const int64_t u = ((static_cast<int64_t>(un.b) * p.Hkv + un.g) * p.RB + un.rb) * p.NC + un.c;
   // o = acc / l in fp16, scaled by 2^-k so the row's largest |o| lands in
   // [2^14, 2^15): full fp16 precision (2^-11 relative) whatever the scale of
   // V, no overflow; (m, l, k) in fp32.  k stays in [-100, 127] so that 2^-k
@@ -623,17 +692,17 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(KParams p) {
   const int k = min(max(ex - 15, -100), 127);
   const float sc = ldexpf(inv, -k);
   if (half == 0)
-    *reinterpret_cast<float4*>(p.part_ml + (u * kRowsBf16 + rl) * 4) =
+    *reinterpret_cast<float4*>(p.part_ml + (u * C::ROWS + rl) * 4) =
         make_float4(mu, ltot, static_cast<float>(k), 0.f);
-  uint16_t* dst = static_cast<uint16_t*>(p.part_acc) + (u * kRowsBf16 + rl) * D;
+  uint16_t* dst = static_cast<uint16_t*>(p.part_acc) + (u * C::ROWS + rl) * D;
   typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const half4 h = {static_cast<_Float16>(acc[dt][4 * j] * sc), static_cast<_Float16>(acc[dt][4 * j + 1] * sc),
-                       static_cast<_Float16>(acc[dt][4 * j + 2] * sc), static_cast<_Float16>(acc[dt][4 * j + 3] * sc)};
-      *reinterpret_cast<uint2*>(dst + dt * 32 + 8 * j + 4 * half) = __builtin_bit_cast(uint2, h);
+      const half4 hv = {static_cast<_Float16>(acc[dt][4 * j] * sc), static_cast<_Float16>(acc[dt][4 * j + 1] * sc),
+                        static_cast<_Float16>(acc[dt][4 * j + 2] * sc), static_cast<_Float16>(acc[dt][4 * j + 3] * sc)};
+      *reinterpret_cast<uint2*>(dst + dt * 32 + 8 * j + 4 * half) = __builtin_bit_cast(uint2, hv);
     }
 }
 
@@ -647,7 +716,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(KParams p) {
   __shared__ float ks[TKF][D];
   __shared__ float vs[TKF][D];
   Unit un;
-  if (!decode_unit(blockIdx.x, p.Hkv, p.RB, p.NC, p.chunk, p.ctx_len, p.active, un)) return;
+  const int ul = unit_of_block(blockIdx.x, p.units, p.RB);
+  if (ul >= p.units || !decode_unit(ul, p.Hkv, p.RB, p.NC, p.chunk, p.ctx_len, p.active, un)) return;
   const int tid = threadIdx.x;
   const float* q = static_cast<const float*>(p.qf);
   const float* kb = static_cast<const float*>(p.kbf);
@@ -719,7 +789,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(KParams p) {
     }
   }
   if (!valid) return;
-  const int64_t u = blockIdx.x;
+  const int64_t u = ((static_cast<int64_t>(un.b) * p.Hkv + un.g) * p.RB + un.rb) * p.NC + un.c;
   *reinterpret_cast<float4*>(p.part_ml + (u * kRowsF32 + tid) * 4) = make_float4(m, l, 0.f, 0.f);
   float* dst = static_cast<float*>(p.part_acc) + (u * kRowsF32 + tid) * D;
   const float inv = 1.f / l;
@@ -856,10 +926,14 @@ AttnPlan attn_plan(int B, int S, int Hq, int Hkv, int d, int dtype, int max_ctx_
   AttnPlan pl{};
   const int G = Hq / Hkv;
   pl.rows = S * G;
-  pl.rows_per_unit = dtype == 0 ? kRowsBf16 : kRowsF32;
+  // bf16: waves of 32 rows, as few as the rows need (a power of two from 2
+  // to kMaxWaves); fp32: one wave of 64 rows
+  int nw = 2;
+  while (nw < kMaxWaves && 32 * nw < pl.rows) nw *= 2;
+  pl.rows_per_unit = dtype == 0 ? 32 * nw : kRowsF32;
   pl.row_blocks = static_cast<int>(ceil_div(pl.rows, pl.rows_per_unit));
   const int64_t groups = static_cast<int64_t>(B) * Hkv * pl.row_blocks;
-  const int64_t want = ceil_div(kNumCUs, groups);
+  const int64_t want = ceil_div(device_cus(), groups);
   int64_t chunk = max_ctx_len > 0 ? ceil_div(max_ctx_len, want < 1 ? 1 : want) : kTK;
   chunk = static_cast<int64_t>(align_up(static_cast<size_t>(chunk), kTK));
   if (chunk < kTK) chunk = kTK;
@@ -893,16 +967,26 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& pl, void* ws, hi
   kp.causal = a.causal;
   kp.ctx_end = a.ctx_end; kp.kc_out = a.kc_out; kp.vc_out = a.vc_out;
   const int64_t units = static_cast<int64_t>(a.B) * a.Hkv * pl.row_blocks * pl.n_chunks;
+  kp.units = static_cast<int>(units);
+  // several row blocks per group: the grid is padded to a multiple of 8 for
+  // the XCD-aware unit order (unit_of_block)
+  const unsigned grid = static_cast<unsigned>(pl.row_blocks > 1 ? 8 * ceil_div(units, 8) : units);
   if (a.dtype == 0) {
-    if (a.d == 128)
-      hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(static_cast<unsigned>(units)), dim3(512), 0, st, kp);
-    else
-      hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(static_cast<unsigned>(units)), dim3(512), 0, st, kp);
+    const int nw = pl.rows_per_unit / 32;
+    if (a.d == 128) {
+      if (nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<128, 8>), dim3(grid), dim3(512), 0, st, kp);
+      else if (nw == 4) hipLaunchKernelGGL((attn_bf16_kernel<128, 4>), dim3(grid), dim3(256), 0, st, kp);
+      else hipLaunchKernelGGL((attn_bf16_kernel<128, 2>), dim3(grid), dim3(128), 0, st, kp);
+    } else {
+      if (nw == 8) hipLaunchKernelGGL((attn_bf16_kernel<64, 8>), dim3(grid), dim3(512), 0, st, kp);
+      else if (nw == 4) hipLaunchKernelGGL((attn_bf16_kernel<64, 4>), dim3(grid), dim3(256), 0, st, kp);
+      else hipLaunchKernelGGL((attn_bf16_kernel<64, 2>), dim3(grid), dim3(128), 0, st, kp);
+    }
   } else {
     if (a.d == 128)
-      hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(static_cast<unsigned>(units)), dim3(64), 0, st, kp);
+      hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(grid), dim3(64), 0, st, kp);
     else
-      hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(static_cast<unsigned>(units)), dim3(64), 0, st, kp);
+      hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(grid), dim3(64), 0, st, kp);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -60,6 +60,10 @@ __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t 
                :: "v"(off), "s"(base), "s"(lds) : "memory");
 }
 
+// Waits until at most N vector memory operations of this wave are in flight.
+// The stage waits count the copies only: the loops that use them issue no
+// other vector memory operation (operands come from LDS and registers; the
+// build checks that the kernels neither spill nor use M0 elsewhere).
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
@@ -478,18 +482,7 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
   // CUs: a 2-stage ring (64 KB), so that two tiles share a CU and the tiles
   // past the CU count run beside the others instead of in a second round
   // (measured: 288 tiles on 256 CUs take 56 us instead of 80).
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  // CU count per device, asked once (concurrent first calls store the same
-  // value)
-  static std::atomic<int> cu_count[64];
-  int cus = dev < 64 ? cu_count[dev].load(std::memory_order_relaxed) : 0;
-  if (cus == 0) {
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    if (dev < 64) cu_count[dev].store(cus, std::memory_order_relaxed);
-  }
+  const int cus = device_cus();
   const bool two = tiles > cus;
   const int tiles144 = a.N % kBN144 == 0 ? ((a.M + kBM - 1) / kBM) * (a.N / kBN144) : 0;
   if (two && tiles144 > 0 && tiles144 <= cus) {

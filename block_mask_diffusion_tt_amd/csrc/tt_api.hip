@@ -5,10 +5,35 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
 #include <string>
 
 #include "../../include/tt.h"
 #include "tt_internal.h"
+
+namespace tt {
+
+int device_cus() {
+  constexpr int kDefault = 256;   // MI355X
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return kDefault;
+  }
+  // asked once per device (concurrent first calls store the same value)
+  static std::atomic<int> cus[64];
+  int n = dev < 64 ? cus[dev].load(std::memory_order_relaxed) : 0;
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+      (void)hipGetLastError();
+      return kDefault;
+    }
+    if (dev < 64) cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+}  // namespace tt
 
 namespace {
 
@@ -482,6 +507,7 @@ DenoiseBufs carve_denoise(Carver& cv, const tt_attn_shape* shape, int n_layers, 
 }
 
 struct LoopOpts {
+  int first_step;     // absolute index of the loop's first step
   int n_layers, max_steps, vocab, mask_id;
   float gamma, temperature;
   int sample; uint64_t seed; int block;
@@ -507,7 +533,8 @@ tt_status denoise_loop(const char* fn, const tt_attn_shape* shape, const LoopOpt
   hipStream_t hs = static_cast<hipStream_t>(stream);
   hipError_t he = tt::launch_count_masked(B, S, masked, z.n_masked, hs);
   if (he != hipSuccess) return hip_fail(he, fn);
-  for (int k = 0; k < o.max_steps; ++k) {
+  const int k_end = o.first_step + o.max_steps;
+  for (int k = o.first_step; k < k_end; ++k) {
     he = tt::launch_active_from_masked(B, z.n_masked, z.active, z.total, hs);
     if (he != hipSuccess) return hip_fail(he, fn);
     int32_t host_total = 0;
@@ -544,14 +571,14 @@ tt_status denoise_loop(const char* fn, const tt_attn_shape* shape, const LoopOpt
     tt::UnmaskArgs ua{};
     ua.B = B; ua.S = S; ua.V = o.vocab; ua.dtype = shape->dtype; ua.logits = z.logits;
     ua.row_stride = o.vocab;
-    ua.gamma = (o.finish_block && k == o.max_steps - 1) ? -INFINITY : o.gamma;
+    ua.gamma = (o.finish_block && k == k_end - 1) ? -INFINITY : o.gamma;
     ua.temperature = o.temperature;
     ua.mask_id = o.mask_id; ua.step = k; ua.tokens = tokens; ua.masked = masked;
     ua.commit_step = commit_step; ua.n_masked = z.n_masked;
     ua.sample = o.sample; ua.seed = o.seed; ua.block_index = o.block;
     he = tt::launch_confidence_unmask(ua, z.up, z.unmask_ws, hs);
     if (he != hipSuccess) return hip_fail(he, fn);
-    if (steps_taken) *steps_taken = k + 1;
+    if (steps_taken) *steps_taken = k + 1 - o.first_step;
   }
   return TT_OK;
 }
@@ -594,22 +621,32 @@ size_t generate_bytes(const tt_attn_shape* s, int n_layers, int n_blocks, int ma
 
 extern "C" {
 
-tt_status tt_denoise_block(const tt_attn_shape* shape, int32_t n_layers, int32_t max_steps,
-                           float gamma, float temperature, int32_t mask_token_id, int32_t vocab,
-                           const void* const* k_ctx_layers, const void* const* v_ctx_layers,
-                           const int64_t* ctx_start, const int32_t* ctx_len, int32_t max_ctx_len,
-                           const void* ada_w, const float* ada_bias, const float* ada_table,
-                           const tt_step_provider* provider, int32_t* tokens, uint8_t* masked,
-                           int8_t* commit_step, int32_t* steps_taken, void* workspace,
-                           size_t workspace_bytes, tt_stream stream) {
-  const char* fn = "tt_denoise_block";
+}  // extern "C"
+
+namespace {
+
+tt_status denoise_common(const char* fn, const tt_attn_shape* shape, int32_t n_layers,
+                         int32_t first_step, int32_t max_steps, float gamma, float temperature,
+                         int32_t sample, uint64_t seed, int32_t block_index,
+                         int32_t mask_token_id, int32_t vocab, const void* const* k_ctx_layers,
+                         const void* const* v_ctx_layers, const int64_t* ctx_start,
+                         const int32_t* ctx_len, int32_t max_ctx_len, const void* ada_w,
+                         const float* ada_bias, const float* ada_table,
+                         const tt_step_provider* provider, int32_t* tokens, uint8_t* masked,
+                         int8_t* commit_step, int32_t* steps_taken, void* workspace,
+                         size_t workspace_bytes, tt_stream stream) {
   if (steps_taken) *steps_taken = 0;
   tt_status st = check_shape(shape);
   if (st != TT_OK) return st;
   const int S = shape->block_size;
   if (n_layers < 1) return fail(TT_ERR_INVALID_ARG, "%s: n_layers %d < 1", fn, n_layers);
-  if (max_steps < 0 || max_steps > S)
-    return fail(TT_ERR_INVALID_ARG, "%s: max_steps %d outside [0, block_size=%d]", fn, max_steps, S);
+  if (first_step < 0 || first_step > S)
+    return fail(TT_ERR_INVALID_ARG, "%s: first_step %d outside [0, block_size=%d]", fn, first_step, S);
+  if (max_steps < 0 || max_steps > S - first_step)
+    return fail(TT_ERR_INVALID_ARG, "%s: max_steps %d outside [0, block_size - first_step = %d]", fn,
+                max_steps, S - first_step);
+  if (sample && block_index < 0)
+    return fail(TT_ERR_INVALID_ARG, "%s: block_index %d < 0", fn, block_index);
   if (max_ctx_len < 0) return fail(TT_ERR_INVALID_ARG, "%s: max_ctx_len %d < 0", fn, max_ctx_len);
   st = check_unmask_scalars(shape->batch, S, vocab, vocab, gamma, temperature);
   if (st != TT_OK) return st;
@@ -630,8 +667,10 @@ tt_status tt_denoise_block(const tt_attn_shape* shape, int32_t n_layers, int32_t
   Carver cv{static_cast<char*>(workspace)};
   const DenoiseBufs z = carve_denoise(cv, shape, n_layers, max_ctx_len, vocab);
   LoopOpts o{};
+  o.first_step = first_step;
   o.n_layers = n_layers; o.max_steps = max_steps; o.vocab = vocab; o.mask_id = mask_token_id;
   o.gamma = gamma; o.temperature = temperature;
+  o.sample = sample != 0; o.seed = seed; o.block = block_index;
   auto layer_inputs = [&](int k, int l, const void* prev) {
     return provider->layer_inputs(provider->user, k, l, prev, z.q, z.kb, z.vb, stream);
   };
@@ -641,8 +680,44 @@ tt_status tt_denoise_block(const tt_attn_shape* shape, int32_t n_layers, int32_t
                     stream);
   if (st != TT_OK) return st;
   const hipError_t he = hipStreamSynchronize(static_cast<hipStream_t>(stream));
-  if (he != hipSuccess) return hip_fail(he, "tt_denoise_block final sync");
+  if (he != hipSuccess) return hip_fail(he, fn);
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+tt_status tt_denoise_block(const tt_attn_shape* shape, int32_t n_layers, int32_t max_steps,
+                           float gamma, float temperature, int32_t mask_token_id, int32_t vocab,
+                           const void* const* k_ctx_layers, const void* const* v_ctx_layers,
+                           const int64_t* ctx_start, const int32_t* ctx_len, int32_t max_ctx_len,
+                           const void* ada_w, const float* ada_bias, const float* ada_table,
+                           const tt_step_provider* provider, int32_t* tokens, uint8_t* masked,
+                           int8_t* commit_step, int32_t* steps_taken, void* workspace,
+                           size_t workspace_bytes, tt_stream stream) {
+  return denoise_common("tt_denoise_block", shape, n_layers, 0, max_steps, gamma, temperature, 0,
+                        0, 0, mask_token_id, vocab, k_ctx_layers, v_ctx_layers, ctx_start,
+                        ctx_len, max_ctx_len, ada_w, ada_bias, ada_table, provider, tokens, masked,
+                        commit_step, steps_taken, workspace, workspace_bytes, stream);
+}
+
+tt_status tt_denoise_block_resume(const tt_attn_shape* shape, int32_t n_layers,
+                                  int32_t first_step, int32_t max_steps, float gamma,
+                                  float temperature, int32_t sample, uint64_t seed,
+                                  int32_t block_index, int32_t mask_token_id, int32_t vocab,
+                                  const void* const* k_ctx_layers,
+                                  const void* const* v_ctx_layers, const int64_t* ctx_start,
+                                  const int32_t* ctx_len, int32_t max_ctx_len, const void* ada_w,
+                                  const float* ada_bias, const float* ada_table,
+                                  const tt_step_provider* provider, int32_t* tokens,
+                                  uint8_t* masked, int8_t* commit_step, int32_t* steps_taken,
+                                  void* workspace, size_t workspace_bytes, tt_stream stream) {
+  return denoise_common("tt_denoise_block_resume", shape, n_layers, first_step, max_steps, gamma,
+                        temperature, sample, seed, block_index, mask_token_id, vocab,
+                        k_ctx_layers, v_ctx_layers, ctx_start, ctx_len, max_ctx_len, ada_w,
+                        ada_bias, ada_table, provider, tokens, masked, commit_step, steps_taken,
+                        workspace, workspace_bytes, stream);
 }
 
 size_t tt_generate_workspace_size(const tt_attn_shape* shape, int32_t n_layers, int32_t n_blocks,

@@ -9,9 +9,11 @@
 
 namespace tt {
 
-// The launch-shape rules are fixed for the 256-CU MI355X so that a workspace
-// size computed on any host matches what the launch uses.
-constexpr int kNumCUs = 256;
+// Compute units of the current device (asked once per device); the MI355X's
+// 256 when no device can be asked (a workspace size computed on a host
+// without a GPU).  Launch plans, and so workspace sizes, follow the device
+// that is current when they are computed.
+int device_cus();
 
 constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

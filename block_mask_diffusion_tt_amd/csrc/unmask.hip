@@ -773,7 +773,7 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(
 UnmaskPlan unmask_plan(int B, int S, int V) {
   UnmaskPlan p{};
   const int64_t rows = static_cast<int64_t>(B) * S;
-  int splits = static_cast<int>(ceil_div(2 * kNumCUs, rows));
+  int splits = static_cast<int>(ceil_div(2 * device_cus(), rows));
   splits = splits < 1 ? 1 : (splits > 64 ? 64 : splits);
   int64_t len = align_up(static_cast<size_t>(ceil_div(V, splits)), 8);
   if (len < 2048) len = 2048;

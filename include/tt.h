@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define TT_ABI_VERSION 2
+#define TT_ABI_VERSION 3
 #define TT_TIMESTEP_DIM 256 /* width of the timestep embedding */
 
 typedef enum {
@@ -358,6 +358,38 @@ tt_status tt_denoise_block(const tt_attn_shape* shape, int32_t n_layers, int32_t
                            const tt_step_provider* provider, int32_t* tokens,
                            uint8_t* masked, int8_t* commit_step, int32_t* steps_taken,
                            void* workspace, size_t workspace_bytes, tt_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tt_denoise_block_resume -- the same loop started at step first_step: the
+ * block refined step by step until final ([dothoosh] two-tower mechanism
+ * section) can be stopped after any step and continued later from its state
+ * (tokens, masked, commit_step), which is all the loop carries between steps
+ * (the timestep of a step is the masked fraction at its start).  It runs
+ * steps k = first_step .. first_step + max_steps - 1 while any slot is
+ * masked: the provider is called with the absolute step k, commit_step
+ * records k, and with sample != 0 the unmasking pass is tt_sample_unmask
+ * (seed, block_index, step = k), else the argmax of tt_confidence_unmask.
+ * A run of n steps therefore gives bit for bit the state that a run of j
+ * steps followed by a resumed run from first_step = j with n - j steps gives,
+ * whatever j.  tt_denoise_block is this call with first_step = 0, sample = 0.
+ *   first_step  in [0, S]; max_steps in [0, S - first_step]
+ *   *steps_taken (host, may be NULL): steps run by this call.
+ * Arguments, layouts, workspace (tt_denoise_workspace_size) and errors are
+ * those of tt_denoise_block, plus TT_ERR_INVALID_ARG for first_step or
+ * max_steps outside their ranges, or block_index < 0 with sample != 0.
+ * ---------------------------------------------------------------------- */
+tt_status tt_denoise_block_resume(const tt_attn_shape* shape, int32_t n_layers,
+                                  int32_t first_step, int32_t max_steps, float gamma,
+                                  float temperature, int32_t sample, uint64_t seed,
+                                  int32_t block_index, int32_t mask_token_id, int32_t vocab,
+                                  const void* const* k_ctx_layers,
+                                  const void* const* v_ctx_layers, const int64_t* ctx_start,
+                                  const int32_t* ctx_len, int32_t max_ctx_len,
+                                  const void* ada_w, const float* ada_bias,
+                                  const float* ada_table, const tt_step_provider* provider,
+                                  int32_t* tokens, uint8_t* masked, int8_t* commit_step,
+                                  int32_t* steps_taken, void* workspace, size_t workspace_bytes,
+                                  tt_stream stream);
 
 /* ------------------------------------------------------------------------
  * tt_generate -- multi-block generation: denoise a block, let the context

@@ -23,6 +23,29 @@ def say(*a):
     sys.stdout.flush()
 
 
+def record(what, **values):
+    """Prints a measured quantity of a test and, when TT_TEST_RECORD names a
+    file, appends it there as one JSON line (for numbers that are reported
+    rather than asserted, such as the peaked cases' exact-oracle error)."""
+    import json
+    import os
+    say(what, values)
+    path = os.environ.get("TT_TEST_RECORD")
+    if path:
+        with open(path, "a") as fh:
+            fh.write(json.dumps(dict(what=what, **values)) + "\n")
+
+
+def peaked_errors(out, eo, ro_rounded_q):
+    """Max-abs errors of a peaked case: the kernel against the exact oracle,
+    and how far the operand rounding of q' alone moves the exact result (the
+    oracle on the rounded query against the exact oracle)."""
+    o = np64(out) if isinstance(out, torch.Tensor) else out
+    return dict(exact_max_abs=float(np.abs(o - eo).max()),
+                rounding_shift_max_abs=float(np.abs(ro_rounded_q - eo).max()),
+                exact_rel_fro=float(np.linalg.norm(o - eo) / np.linalg.norm(eo)))
+
+
 def np64(t):
     return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
 

@@ -30,7 +30,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version():
-    assert tt.abi_version() == 2
+    assert tt.abi_version() == 3
 
 
 def _status(fn, *args):
@@ -147,6 +147,29 @@ def test_denoise_rejects_bad_arguments():
     assert call(provider=ctypes.byref(prov)) == tt.TT_ERR_INVALID_ARG    # NULL callbacks
     assert call(k=(ctypes.c_void_p * 1)(None)) == tt.TT_ERR_INVALID_ARG
     assert tt.denoise_workspace_size(s, 1, 8, 64) > 0
+
+
+def test_denoise_resume_rejects_bad_arguments():
+    s = tt.AttnShape(2, 4, 1, 64, 16, 1)
+    L = tt.lib()
+    ptrs = (ctypes.c_void_p * 1)(FAKE)
+
+    def call(first=0, max_steps=16, sample=0, block=0):
+        taken = ctypes.c_int32(-5)
+        st = L.tt_denoise_block_resume(ctypes.byref(s), 1, first, max_steps, 0.8, 1.0, sample, 9,
+                                       block, 3, 64, ptrs, ptrs, FAKE, FAKE, 8, None, None, None,
+                                       None, FAKE, FAKE, None, ctypes.byref(taken), FAKE, 1 << 30,
+                                       None)
+        assert taken.value == 0
+        return st
+    assert call(first=-1) == tt.TT_ERR_INVALID_ARG
+    assert call(first=17, max_steps=0) == tt.TT_ERR_INVALID_ARG
+    assert call(first=4, max_steps=13) == tt.TT_ERR_INVALID_ARG     # past the block's S steps
+    assert call(first=4, max_steps=12, sample=1, block=-1) == tt.TT_ERR_INVALID_ARG
+    assert "first_step" in tt.last_error() or "block_index" in tt.last_error()
+    # in range: it gets as far as the NULL provider
+    assert call(first=4, max_steps=12) == tt.TT_ERR_INVALID_ARG
+    assert "provider" in tt.last_error()
 
 
 def test_binding_raises_with_message():

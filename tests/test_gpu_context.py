@@ -99,7 +99,7 @@ def test_causal_shapes_fp32(S, heads, d):
 # held to the relative-Frobenius bound.
 @pytest.mark.parametrize("L", [0, 8, 100])
 def test_causal_peaked_short_context(L):
-    from .gpu_cases import TOL, rounded_query
+    from .gpu_cases import TOL, peaked_errors, record, rounded_query
     c = attn_case(4, 16, 32, 2, 128, [L, L // 2, 0, L], dtype=BF16, seed=2300 + L, qscale=4.0)
     say("ctx-tower peaked", L)
     out, lse = _run(c)
@@ -107,8 +107,9 @@ def test_causal_peaked_short_context(L):
     ro, rl = _oracle(dict(c, q=torch.from_numpy(qr)))
     assert_attn_close(out, lse, ro, rl, BF16, f"ctx-tower peaked L={L} (rounded q)")
     eo, _ = _oracle(c)
-    fro = np.linalg.norm(np64(out) - eo) / np.linalg.norm(eo)
-    assert fro <= TOL[BF16]["rel_fro"]
+    e = peaked_errors(out, eo, ro)
+    record(f"ctx-tower peaked L={L}", **e)
+    assert e["exact_rel_fro"] <= TOL[BF16]["rel_fro"], e
 
 
 # The cache append: bit-exact copies at the right rows, nothing else written;

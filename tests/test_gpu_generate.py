@@ -62,7 +62,7 @@ class Provider:
 
 def _run(B=3, S=16, Hq=8, Hkv=2, d=64, V=2048, NL=2, lens=(100, 0, 37), room=(3, 3, 3),
          n_blocks=3, steps=16, gamma=0.8, tau=1.0, seed=None, dtype=torch.bfloat16,
-         logit_std=8.5, eos_plan=((0, 1, 5),), what=""):
+         logit_std=8.5, eos_plan=((0, 1, 5),), what="", stream=None):
     say("generate", what, dict(B=B, S=S, V=V, NL=NL, lens=lens, n_blocks=n_blocks, steps=steps,
                                tau=tau, seed=seed))
     lens = list(lens)
@@ -83,9 +83,11 @@ def _run(B=3, S=16, Hq=8, Hkv=2, d=64, V=2048, NL=2, lens=(100, 0, 37), room=(3,
     n_gen = torch.full((B,), -1, dtype=torch.int32, device=DEV)
     stop = torch.full((B,), -1, dtype=torch.int8, device=DEV)
     prov = Provider(B, S, Hq, Hkv, d, V, dtype, logit_std, eos_plan, 4242)
+    if stream is not None:
+        torch.cuda.synchronize()     # inputs were made on torch's current stream
     taken = tt.generate(shape, NL, n_blocks, steps, gamma, tau, MASK, EOS, V, kc, vc, ctx_start,
                         ctx_end, ctx_len, max(lens), prov, out, n_gen, ws, stop_reason=stop,
-                        seed=seed)
+                        seed=seed, stream=stream)
     torch.cuda.synchronize()
 
     def ctx_inputs(blk, layer, tokens):
@@ -162,3 +164,10 @@ def test_generate_fp32_small():
 def test_generate_all_stop_early():
     r = _run(eos_plan=((0, 0, 1), (1, 0, 15), (2, 0, 0)), n_blocks=4, what="all EOS")
     assert r["blocks_taken"] == 1 and r["stop"].tolist() == [1, 1, 1]
+
+
+# Generation on a stream other than torch's current one (sampled at the pages'
+# temperature 0.1): every callback's copies run on the library's stream.
+def test_generate_on_a_side_stream():
+    r = _run(tau=0.1, seed=31, what="side stream", stream=torch.cuda.Stream())
+    assert r["stop"].tolist() == [1, 0, 0]

@@ -145,6 +145,44 @@ def test_near_threshold_rows_decided_in_fp64(side, V):
     assert np.any(np.abs(p - gamma) < 1e-6)
 
 
+# No row reaches gamma, and the two most confident rows differ in fp64 p by
+# about 1e-9: far below the error of an fp32 sum over the vocabulary, so only
+# the decision kernel's fp64 recheck of the rows within its band of the best
+# fp32 p can order them.  Every row has logit a at one token and 0 elsewhere
+# (p = 1 / (1 + (V-1) e^-a) < gamma); the runner-up row also carries eps at
+# one other token, which lowers its p by about p^2 e^-a eps.  The more
+# confident row sits at the higher slot in sequence 0 and at the lower slot
+# in sequence 1, so neither "lowest slot" nor a flipped fp32 order can pass
+# by luck; the other rows have logit a - 0.5 (clearly lower p).
+@pytest.mark.parametrize("V", [131072, 40003])
+@pytest.mark.parametrize("eps_exp", [-11, -13])
+def test_top_two_rows_ordered_in_fp64(V, eps_exp):
+    B, S = 2, 16
+    a, eps = 11.75, 2.0 ** eps_exp        # both exact in bf16
+    lg = torch.zeros((B, S, V), dtype=torch.float32)
+    for b in range(B):
+        for s in range(S):
+            lg[b, s, (101 * s + 7 + b) % V] = a - 0.5
+    best, second = {0: (9, 3), 1: (2, 11)}, {}
+    for b, (hi, lo) in best.items():
+        lg[b, hi, (101 * hi + 7 + b) % V] = a
+        lg[b, lo, (101 * lo + 7 + b) % V] = a
+        lg[b, lo, (101 * lo + 500 + b) % V] = eps
+        second[b] = lo
+    logits = lg.to(torch.bfloat16)
+    assert torch.equal(logits.float(), lg)
+    masked = torch.ones((B, S), dtype=torch.uint8)
+    r0 = oracle.confidence_unmask(lg.double().numpy(), np.full((B, S), 3), masked.numpy(), 0.8,
+                                  1.0, 3, 0)
+    for b, (hi, lo) in best.items():
+        gap = r0["conf"][b, hi] - r0["conf"][b, lo]
+        assert 1e-10 < gap < 1e-8 and r0["conf"][b].max() < 0.8, (b, gap)
+    g, r = check(logits.to(DEV), _tokens(B, S, masked, V), masked, 0.8, 1.0,
+                 what=f"top-2 rows 2^{eps_exp} apart, V={V}")
+    for b, (hi, lo) in best.items():
+        assert g["committed_now"][b].tolist() == [int(s == hi) for s in range(S)], b
+
+
 def test_row_stride_and_scalar_path():
     B, S, V, stride = 2, 5, 1000, 1003        # stride not a multiple of 8 -> scalar loads
     logits = synth.normal((B * S * stride,), 3.0, 51, torch.bfloat16, DEV)
