@@ -5,7 +5,7 @@ memory and streams only.  Importing this package requires the built library;
 there is no CPU fallback."""
 from ._binding import *  # noqa: F401,F403
 from ._binding import (AttnShape, StepProvider, TTError, abi_version, adaln_single,  # noqa: F401
-                       attn_shape, block_attn, block_attn_workspace_size, confidence_unmask,
+                       attn_shape, block_attn, block_attn_noalloc, block_attn_workspace_size, confidence_unmask,
                        ctx_advance, ctx_block_attn, sample_unmask, generate,
                        generate_workspace_size, GenProvider, mamba_shape, mamba_block_scan,
                        mamba_workspace_size,

@@ -25,7 +25,7 @@ _STATUS_NAMES = {0: "TT_OK", 1: "TT_ERR_INVALID_ARG", 2: "TT_ERR_UNSUPPORTED",
 
 # Every symbol include/tt.h declares.
 EXPORTED = ["tt_last_error", "tt_abi_version", "tt_block_attn_workspace_size", "tt_block_attn",
-            "tt_workspace_clear", "tt_timestep_embed", "tt_adaln_single",
+            "tt_block_attn_noalloc", "tt_workspace_clear", "tt_timestep_embed", "tt_adaln_single",
             "tt_unmask_workspace_size", "tt_confidence_unmask", "tt_denoise_workspace_size",
             "tt_denoise_block", "tt_denoise_block_resume", "tt_ctx_block_attn", "tt_ctx_advance", "tt_sample_unmask",
             "tt_generate_workspace_size", "tt_generate", "tt_mamba_workspace_size",
@@ -91,6 +91,8 @@ def _load():
         "tt_block_attn_workspace_size": (sz, [shp, i32]),
         "tt_block_attn": (ctypes.c_int, [shp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp,
                                          vp, vp, vp, vp, sz, vp]),
+        "tt_block_attn_noalloc": (ctypes.c_int, [shp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp,
+                                                 vp, vp, vp, vp, vp]),
         "tt_ctx_block_attn": (ctypes.c_int, [shp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, vp,
                                              vp, vp, vp, sz, vp]),
         "tt_ctx_advance": (ctypes.c_int, [i32, i32, vp, vp, vp, vp, vp, vp]),
@@ -207,6 +209,16 @@ def block_attn(shape, q_blk, k_blk, v_blk, k_ctx, v_ctx, ctx_start, ctx_len, max
                               int(max_ctx_len), _ptr(active), _ptr(ada_shift), _ptr(ada_scale),
                               _ptr(ada_gate), _ptr(residual), _ptr(out), _ptr(lse),
                               _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
+def block_attn_noalloc(shape, q_blk, k_blk, v_blk, k_ctx, v_ctx, ctx_start, ctx_len, max_ctx_len,
+                       out, active=None, ada_shift=None, ada_scale=None, ada_gate=None,
+                       residual=None, lse=None, stream=None):
+    _check(_lib.tt_block_attn_noalloc(ctypes.byref(shape), _ptr(q_blk), _ptr(k_blk), _ptr(v_blk),
+                                      _ptr(k_ctx), _ptr(v_ctx), _ptr(ctx_start), _ptr(ctx_len),
+                                      int(max_ctx_len), _ptr(active), _ptr(ada_shift),
+                                      _ptr(ada_scale), _ptr(ada_gate), _ptr(residual), _ptr(out),
+                                      _ptr(lse), _stream(stream)))
 
 
 def ctx_block_attn(shape, q_blk, k_blk, v_blk, k_ctx, v_ctx, ctx_start, ctx_len, max_ctx_len,

@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <atomic>
+#include <mutex>
 #include <string>
 
 #include "../../include/tt.h"
@@ -151,17 +152,55 @@ size_t tt_block_attn_workspace_size(const tt_attn_shape* shape, int32_t max_ctx_
 
 }  // extern "C"
 
+// ------------------------------------------------- allocation-free attention
+// Workspace of tt_block_attn_noalloc: one array in every GPU's memory, held
+// by the library until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in); it uses the device
+// address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[TT_BLOCK_ATTN_SCRATCH_BYTES];
+
 namespace {
 
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device (looked up once per
+// device, with that device current); NULL after a failure, reported in *e.
+void* scratch_of_current_device(hipError_t* e) {
+  int dev = 0;
+  *e = hipGetDevice(&dev);
+  if (*e != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *e = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    *e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (*e != hipSuccess || !p) {
+      if (*e == hipSuccess) *e = hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 // Validation and launch shared by the denoiser's and the context tower's
-// attention calls.
+// attention calls.  use_scratch: the workspace is this device's `scratch`
+// (looked up after every argument has been checked).
 tt_status block_attn_common(const char* fn, const tt_attn_shape* shape, const void* q_blk,
                             const void* k_blk, const void* v_blk, const void* k_ctx,
                             const void* v_ctx, const int64_t* ctx_start, const int32_t* ctx_len,
                             const int64_t* ctx_end, int32_t max_ctx_len, const uint8_t* active,
                             const float* ada_shift, const float* ada_scale, const float* ada_gate,
                             const void* residual, void* out, float* lse, int causal,
-                            void* workspace, size_t workspace_bytes, tt_stream stream) {
+                            void* workspace, size_t workspace_bytes, tt_stream stream,
+                            bool use_scratch = false) {
   tt_status st = check_shape(shape);
   if (st != TT_OK) return st;
   if (max_ctx_len < 0) return fail(TT_ERR_INVALID_ARG, "%s: max_ctx_len %d < 0", fn, max_ctx_len);
@@ -185,6 +224,16 @@ tt_status block_attn_common(const char* fn, const tt_attn_shape* shape, const vo
   const tt::AttnPlan p = tt::attn_plan(shape->batch, shape->block_size, shape->n_q_heads,
                                        shape->n_kv_heads, shape->head_dim, shape->dtype,
                                        max_ctx_len);
+  if (use_scratch) {
+    if (p.total_bytes > TT_BLOCK_ATTN_SCRATCH_BYTES)
+      return fail(TT_ERR_WORKSPACE, "%s: the launch needs %zu bytes of workspace, more than the "
+                  "%llu-byte scratch; use tt_block_attn with a workspace", fn, p.total_bytes,
+                  static_cast<unsigned long long>(TT_BLOCK_ATTN_SCRATCH_BYTES));
+    hipError_t se = hipSuccess;
+    workspace = scratch_of_current_device(&se);
+    if (!workspace) return hip_fail(se, fn);
+    workspace_bytes = TT_BLOCK_ATTN_SCRATCH_BYTES;
+  }
   if (!workspace || workspace_bytes < p.total_bytes)
     return fail(TT_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes,
                 p.total_bytes);
@@ -230,6 +279,22 @@ tt_status tt_ctx_block_attn(const tt_attn_shape* shape, const void* q_blk, const
   return block_attn_common("tt_ctx_block_attn", shape, q_blk, k_blk, v_blk, k_ctx, v_ctx,
                            ctx_start, ctx_len, ctx_end, max_ctx_len, active, nullptr, nullptr,
                            nullptr, residual, out, lse, 1, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+tt_status tt_block_attn_noalloc(const tt_attn_shape* shape, const void* q_blk, const void* k_blk,
+                                const void* v_blk, const void* k_ctx, const void* v_ctx,
+                                const int64_t* ctx_start, const int32_t* ctx_len,
+                                int32_t max_ctx_len, const uint8_t* active,
+                                const float* ada_shift, const float* ada_scale,
+                                const float* ada_gate, const void* residual, void* out,
+                                float* lse, tt_stream stream) {
+  return block_attn_common("tt_block_attn_noalloc", shape, q_blk, k_blk, v_blk, k_ctx, v_ctx,
+                           ctx_start, ctx_len, nullptr, max_ctx_len, active, ada_shift, ada_scale,
+                           ada_gate, residual, out, lse, 0, nullptr, 0, stream, true);
 }
 
 }  // extern "C"

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define TT_ABI_VERSION 3
+#define TT_ABI_VERSION 4
 #define TT_TIMESTEP_DIM 256 /* width of the timestep embedding */
 
 typedef enum {
@@ -135,6 +135,36 @@ tt_status tt_block_attn(const tt_attn_shape* shape,
                         const float* ada_gate, const void* residual,
                         void* out, float* lse,
                         void* workspace, size_t workspace_bytes, tt_stream stream);
+
+/* ------------------------------------------------------------------------
+ * tt_block_attn_noalloc -- tt_block_attn for callers that cannot allocate:
+ * code under HIP graph capture, tight serving loops and harnesses that forbid
+ * hipMalloc.  It computes exactly what tt_block_attn computes (same kernels,
+ * same launch, identical bits) but takes no workspace: its partial results go
+ * to a scratch array of TT_BLOCK_ATTN_SCRATCH_BYTES that the library keeps in
+ * each GPU's memory until the process ends.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine); its first call on a
+ * device looks up that device's copy of the array.
+ * Arguments, layouts, precision and errors are tt_block_attn's, plus
+ * TT_ERR_WORKSPACE when tt_block_attn_workspace_size(shape, max_ctx_len)
+ * exceeds TT_BLOCK_ATTN_SCRATCH_BYTES (64 MiB: every shape whose
+ * B * Hkv * ceil(S * Hq / Hkv / 256) stays within the compute-unit count,
+ * e.g. B = 64, S = 16, Hq = 32, Hkv = 2, d = 128 at any context length,
+ * needs at most 17 MiB).  The scratch needs no initialisation.
+ * All calls on one GPU share its scratch: two calls that overlap in time on
+ * one GPU (different streams or threads without ordering between them) race
+ * and may return wrong results; calls in one stream's order are safe.
+ * ---------------------------------------------------------------------- */
+#define TT_BLOCK_ATTN_SCRATCH_BYTES (64ull << 20)
+
+tt_status tt_block_attn_noalloc(const tt_attn_shape* shape,
+                                const void* q_blk, const void* k_blk, const void* v_blk,
+                                const void* k_ctx, const void* v_ctx,
+                                const int64_t* ctx_start, const int32_t* ctx_len,
+                                int32_t max_ctx_len, const uint8_t* active,
+                                const float* ada_shift, const float* ada_scale,
+                                const float* ada_gate, const void* residual,
+                                void* out, float* lse, tt_stream stream);
 
 /* ------------------------------------------------------------------------
  * tt_ctx_block_attn -- one attention layer of the frozen context tower over

@@ -30,7 +30,7 @@ def test_header_symbols_exported():
 
 
 def test_abi_version():
-    assert tt.abi_version() == 3
+    assert tt.abi_version() == 4
 
 
 def _status(fn, *args):
@@ -63,6 +63,24 @@ def test_block_attn_rejects_bad_shapes(shape, status):
     s = tt.AttnShape(*shape)
     assert _attn(s) == status
     assert tt.last_error() != ""
+
+
+def test_block_attn_noalloc_rejects_bad_calls_before_any_launch():
+    lib = tt.lib()
+
+    def call(s, q=FAKE, maxl=128):
+        return lib.tt_block_attn_noalloc(ctypes.byref(s), q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                         maxl, None, None, None, None, None, FAKE, None, None)
+    assert call(tt.AttnShape(1, 32, 3, 128, 16, 0)) == tt.TT_ERR_INVALID_ARG
+    assert call(tt.AttnShape(2, 32, 2, 128, 16, 0), q=None) == tt.TT_ERR_INVALID_ARG
+    assert call(tt.AttnShape(2, 32, 2, 128, 16, 0), maxl=-1) == tt.TT_ERR_INVALID_ARG
+    # a launch whose partials exceed the 64 MiB scratch
+    big = tt.AttnShape(2048, 64, 8, 128, 64, 0)
+    assert tt.block_attn_workspace_size(big, 1 << 16) > (64 << 20)
+    assert call(big, maxl=1 << 16) == tt.TT_ERR_WORKSPACE
+    assert "scratch" in tt.last_error()
+    # an empty batch is a no-op
+    assert call(tt.AttnShape(0, 32, 2, 128, 16, 0)) == tt.TT_OK
 
 
 def test_block_attn_rejects_bad_pointers_and_workspace():
