@@ -10,7 +10,18 @@ layer, block S = 16 with all 16 slots masked, 32 query / 2 KV heads, d = 128,
 6 attention layers, bf16, logits 64 x 16 x 131072 bf16 drawn as N(0, 8.5^2)
 (about 30% of rows reach p >= 0.8 at temperature 1).  --workload ragged64
 draws contexts uniform in [1024, 8192] instead; --workload batch128 uses 128
-sequences with contexts uniform in [2048, 16384].
+sequences with contexts uniform in [2048, 16384]; --workload single4k is one
+sequence with 4096 context tokens, adaLN from a random N(0, 1) 256-d
+timestep embedding and logits N(0, 4^2), its K/V rotated over 24 sets (623 MB)
+so that the 256 MB last-level cache cannot hold them.
+
+--workload sweep32k is the block-size sweep: 8 sequences x 32768 context
+tokens, S in {4, 16, 64} x gamma in {0.6, 0.8, 0.95}, each cell a whole
+tt_denoise_block loop (all S slots masked at the start, adaLN from the masked
+fraction every step, fresh logits N(0, 8.5^2) every step from a pool of
+distinct draws, copied in by the step provider), plus the attention and
+unmasking calls of each S timed alone (HBM fraction, and the matrix-core
+fraction that bounds S = 64).
 
 Prints one JSON line (rank 0): the metric, the dominant kernel's roofline
 (attention: algorithmic bytes per launch / mean launch time from HIP events on
@@ -44,7 +55,10 @@ def parse():
     # sustained rate
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="ctx8k", choices=["ctx8k", "ragged64", "batch128"])
+    ap.add_argument("--workload", default="ctx8k",
+                    choices=["ctx8k", "ragged64", "batch128", "single4k", "sweep32k"])
+    ap.add_argument("--loops", type=int, default=2,
+                    help="sweep32k: timed denoise loops per (S, gamma) cell, after one untimed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the per-row timings after the timed region (counter runs)")
@@ -138,16 +152,21 @@ def counted_traffic():
 
 def workload(name):
     import synth
+    extra = {}
+    std = 8.5
     if name == "ctx8k":
         B, lens = 64, [8192] * 64
     elif name == "ragged64":
         B = 64
         lens = synth.uniform_int(B, 1024, 8192, seed=3).tolist()
+    elif name == "single4k":
+        B, lens, std = 1, [4096], 4.0
+        extra = dict(kv_sets=24, random_emb=True)
     else:
         B = 128
         lens = synth.uniform_int(B, 2048, 16384, seed=5).tolist()
     return dict(name=name, B=B, lens=lens, S=16, Hq=32, Hkv=2, d=128, layers=6, V=131072,
-                logit_std=8.5, gamma=0.8, tau=1.0, seed=1234)
+                logit_std=std, gamma=0.8, tau=1.0, seed=1234, **extra)
 
 
 def algorithmic_bytes(w, n_masked_rows):
@@ -176,6 +195,9 @@ def main():
     import block_mask_diffusion_tt_amd as tt
     import synth
 
+    if args.workload == "sweep32k":
+        sweep_main(args)
+        return
     dev = "cuda"
     w = workload(args.workload)
     B, S, Hq, Hkv, d, NL, V = w["B"], w["S"], w["Hq"], w["Hkv"], w["d"], w["layers"], w["V"]
@@ -192,8 +214,14 @@ def main():
     start = torch.tensor(np.concatenate([[0], np.cumsum(region)[:-1]]), dtype=torch.int64, device=dev)
     ctx_end = start + torch.tensor(region, dtype=torch.int64, device=dev)
     clen = torch.tensor(lens, dtype=torch.int32, device=dev)
-    kc = [synth.normal((total, Hkv, d), 1.0, sd + 10 + l, bf, dev) for l in range(NL)]
-    vc = [synth.normal((total, Hkv, d), 1.0, sd + 20 + l, bf, dev) for l in range(NL)]
+    # K/V sets rotated over the steps (one unless the whole cache would fit
+    # in the last-level cache)
+    n_sets = w.get("kv_sets", 1)
+    kcs = [[synth.normal((total, Hkv, d), 1.0, sd + 10 + l + 100 * j, bf, dev) for l in range(NL)]
+           for j in range(n_sets)]
+    vcs = [[synth.normal((total, Hkv, d), 1.0, sd + 20 + l + 100 * j, bf, dev) for l in range(NL)]
+           for j in range(n_sets)]
+    kc, vc = kcs[0], vcs[0]
     qb = [synth.normal((B, S, Hq, d), 1.0, sd + 30 + l, bf, dev) for l in range(NL)]
     kb = [synth.normal((B, S, Hkv, d), 1.0, sd + 40 + l, bf, dev) for l in range(NL)]
     vb = [synth.normal((B, S, Hkv, d), 1.0, sd + 50 + l, bf, dev) for l in range(NL)]
@@ -209,6 +237,8 @@ def main():
     n_masked = torch.empty((B,), dtype=torch.int32, device=dev)
     t_step = torch.full((B,), 1.0, dtype=torch.float32, device=dev)   # n_masked / S at step 0
     emb = torch.empty((B, 256), dtype=torch.float32, device=dev)
+    if w.get("random_emb"):
+        emb.copy_(synth.normal((B, 256), 1.0, sd + 63, torch.float32, dev))
     ada = torch.empty((NL, 3, B, W), dtype=torch.float32, device=dev)
     out = torch.empty((B, S, Hq, d), dtype=bf, device=dev)
     shape = tt.attn_shape(B, Hq, Hkv, d, S, bf)
@@ -224,8 +254,10 @@ def main():
             ev = torch.cuda.Event(enable_timing=True)
             ev.record(stream)
             step_events.append(ev)
-        tt.timestep_embed(B, t_step, emb)
+        if not w.get("random_emb"):
+            tt.timestep_embed(B, t_step, emb)
         tt.adaln_single(B, W, NL, emb, ada_w, ada_b, ada_t, ada)
+        kcl, vcl = kcs[i % n_sets], vcs[i % n_sets]
         # one event pair brackets the six back-to-back attention calls of the
         # step (an event between every call would add its own gaps)
         if record:
@@ -233,7 +265,7 @@ def main():
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
         for l in range(NL):
-            tt.block_attn(shape, qb[l], kb[l], vb[l], kc[l], vc[l], start, clen, max_len, out, aws,
+            tt.block_attn(shape, qb[l], kb[l], vb[l], kcl[l], vcl[l], start, clen, max_len, out, aws,
                           ada_shift=ada[l, 0], ada_scale=ada[l, 1], ada_gate=ada[l, 2])
         if record:
             e1.record(stream)
@@ -575,6 +607,189 @@ def generate_row(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, 
             "blocks": blocks, "denoise_steps": steps, "generated_tokens": tokens,
             "ms_per_call": round(sec * 1e3, 2), "ms_per_step": round(sec * 1e3 / max(steps, 1), 4),
             "generated_tokens_per_s": round(tokens / sec, 1)}
+
+
+SWEEP_S = (4, 16, 64)
+SWEEP_GAMMA = (0.6, 0.8, 0.95)
+SWEEP_POOL = 8      # distinct logit draws per block size, used in turn by the steps
+
+
+def sweep_main(args):
+    """Block-size sweep over 8 sequences x 32768 context tokens (6 layers,
+    32/2 heads, d = 128, bf16, V = 131072).  For every S: the attention call
+    and the unmasking call timed alone (HIP events around back-to-back
+    calls), then for every gamma whole tt_denoise_block loops from a fully
+    masked block.  Inside a loop the provider copies each step's logits (and
+    the step-0 q/k/v) into the library's buffers; those copies stand for the
+    layers this path leaves out and are timed with their own event pairs and
+    reported apart.  Events recorded by the provider at layer 0 and at the
+    logits callback bracket each step's six attention calls, which gives the
+    attention time inside the loop."""
+    import numpy as np
+    import torch
+
+    import block_mask_diffusion_tt_amd as tt
+    import synth
+
+    dev, bf = "cuda", torch.bfloat16
+    B, L, Hq, Hkv, d, NL, V = 8, 32768, 32, 2, 128, 6, 131072
+    W, sd, tau = Hq * d, 4321, 1.0
+    lens = [L] * B
+    start = torch.arange(B, dtype=torch.int64, device=dev) * L
+    clen = torch.full((B,), L, dtype=torch.int32, device=dev)
+    kc = [synth.normal((B * L, Hkv, d), 1.0, sd + 10 + l, bf, dev) for l in range(NL)]
+    vc = [synth.normal((B * L, Hkv, d), 1.0, sd + 20 + l, bf, dev) for l in range(NL)]
+    ada_w = synth.normal((256, 3 * W), 0.05, sd + 60, bf, dev)
+    ada_b = synth.normal((3 * W,), 0.1, sd + 61, torch.float32, dev)
+    ada_t = synth.normal((NL, 3, W), 0.1, sd + 62, torch.float32, dev)
+    emb = torch.empty((B, 256), dtype=torch.float32, device=dev)
+    ada = torch.empty((NL, 3, B, W), dtype=torch.float32, device=dev)
+    tt.timestep_embed(B, torch.ones((B,), dtype=torch.float32, device=dev), emb)
+    tt.adaln_single(B, W, NL, emb, ada_w, ada_b, ada_t, ada)
+    stream = torch.cuda.current_stream()
+
+    def event_time(fn, reps, warm):
+        for r in range(warm):
+            fn(r)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for r in range(reps):
+            fn(r)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3   # us per call
+
+    per_s, cells = {}, []
+    for S in SWEEP_S:
+        shape = tt.attn_shape(B, Hq, Hkv, d, S, bf)
+        qb = [synth.normal((B, S, Hq, d), 1.0, sd + 30 + l, bf, dev) for l in range(NL)]
+        kb = [synth.normal((B, S, Hkv, d), 1.0, sd + 40 + l, bf, dev) for l in range(NL)]
+        vb = [synth.normal((B, S, Hkv, d), 1.0, sd + 50 + l, bf, dev) for l in range(NL)]
+        pool = [synth.normal((B, S, V), 8.5, sd + 70 + j, bf, dev) for j in range(SWEEP_POOL)]
+        aws = torch.zeros(tt.block_attn_workspace_size(shape, L), dtype=torch.uint8, device=dev)
+        out = torch.empty((B, S, Hq, d), dtype=bf, device=dev)
+
+        def attn(r):
+            l = r % NL
+            tt.block_attn(shape, qb[l], kb[l], vb[l], kc[l], vc[l], start, clen, L, out, aws,
+                          ada_shift=ada[l, 0], ada_scale=ada[l, 1], ada_gate=ada[l, 2])
+        us_attn = event_time(attn, reps=60, warm=120)
+        reps = 20
+        tok = torch.full((reps + 4, B, S), 3, dtype=torch.int32, device=dev)
+        msk = torch.ones((reps + 4, B, S), dtype=torch.uint8, device=dev)
+        uws = torch.empty(tt.unmask_workspace_size(B, S, V), dtype=torch.uint8, device=dev)
+        us_unmask = event_time(lambda r: tt.confidence_unmask(
+            B, S, V, pool[r % SWEEP_POOL], V, 0.8, tau, 3, 0, tok[r + 2], msk[r + 2], uws),
+            reps=reps, warm=2)
+        nbytes = sum(2 * x * Hkv * d * 2 + S * Hq * d * 2 * 2 + 2 * S * Hkv * d * 2 + 3 * Hq * d * 4
+                     for x in lens)
+        flops = 4 * S * Hq * d * sum(x + S for x in lens)
+        gbps = nbytes / (us_attn * 1e-6) / 1e9
+        tfs = flops / (us_attn * 1e-6) / 1e12
+        per_s[S] = {"attn_us_per_call": round(us_attn, 2), "attn_bytes": nbytes,
+                    "attn_gbps": round(gbps, 1), "attn_frac_hbm": round(gbps / HBM_PEAK_GBPS, 4),
+                    "attn_flops": flops, "attn_tflops": round(tfs, 1),
+                    "attn_frac_mfma_bf16": round(tfs / MFMA_BF16_TFLOPS, 4),
+                    "unmask_us_per_call": round(us_unmask, 2),
+                    "unmask_frac_hbm": round(B * S * V * 2 / (us_unmask * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+        del tok, msk, uws, aws, out
+        dws = torch.empty(tt.denoise_workspace_size(shape, NL, L, V), dtype=torch.uint8, device=dev)
+
+        class Provider:
+            def __init__(self):
+                self.copies, self.attn = [], []
+                self.mark = None
+
+            def _ev(self):
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(torch.cuda.current_stream())
+                return e
+
+            def layer_inputs(self, step, layer, prev_out, q, k, v):
+                if layer == 0:
+                    self.mark = self._ev()
+                if step == 0:
+                    a = self._ev()
+                    q.copy_(qb[layer])
+                    k.copy_(kb[layer])
+                    v.copy_(vb[layer])
+                    self.copies.append((a, self._ev()))
+
+            def logits(self, step, last_out, lg):
+                a = self._ev()
+                if step > 0:    # step 0's interval also holds the q/k/v copies
+                    self.attn.append((self.mark, a))
+                lg.copy_(pool[step % SWEEP_POOL])
+                self.copies.append((a, self._ev()))
+
+        for gamma in SWEEP_GAMMA:
+            runs = []
+            for rep in range(1 + args.loops):
+                tokens = torch.full((B, S), 3, dtype=torch.int32, device=dev)
+                masked = torch.ones((B, S), dtype=torch.uint8, device=dev)
+                prov = Provider()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                steps = tt.denoise_block(shape, NL, S, gamma, tau, 3, V, kc, vc, start, clen, L,
+                                         prov, tokens, masked, dws, ada_w=ada_w, ada_bias=ada_b,
+                                         ada_table=ada_t)
+                torch.cuda.synchronize()
+                sec = time.perf_counter() - t0
+                copy_ms = sum(a.elapsed_time(b) for a, b in prov.copies)
+                attn_us = [a.elapsed_time(b) * 1e3 / NL for a, b in prov.attn]
+                if rep > 0:
+                    runs.append((steps, sec * 1e3, copy_ms, attn_us, int(masked.sum().item())))
+            steps = runs[0][0]
+            loop_ms = float(np.median([r[1] for r in runs]))
+            copy_ms = float(np.median([r[2] for r in runs]))
+            attn_in = [x for r in runs for x in r[3]]
+            net = loop_ms - copy_ms
+            cells.append({"S": S, "gamma": gamma, "steps": steps, "masked_left": runs[0][4],
+                          "loops_timed": len(runs), "ms_per_loop": round(loop_ms, 3),
+                          "provider_copy_ms": round(copy_ms, 3),
+                          "ms_per_step": round(net / steps, 4),
+                          "query_tokens_per_s": round(steps * B * S / (net * 1e-3), 1),
+                          "attn_us_in_loop": round(float(np.mean(attn_in)), 2) if attn_in else None})
+        del dws, pool, qb, kb, vb
+        torch.cuda.empty_cache()
+    head = next(c for c in cells if c["S"] == 16 and c["gamma"] == 0.8)
+    a16 = per_s[16]
+    us16 = head["attn_us_in_loop"] or a16["attn_us_per_call"]
+    gb16 = a16["attn_bytes"] / (us16 * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": head["query_tokens_per_s"],
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": head["steps"] * head["loops_timed"],
+        "warmup": head["steps"],
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "sweep32k (B=8, L=32768, S in {4, 16, 64}, gamma in {0.6, 0.8, "
+                               "0.95}, whole denoise loops; value: the S=16, gamma=0.8 cell, "
+                               "provider logit copies excluded)",
+                   "batch": B, "ctx": L, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "layers": NL, "vocab": V, "temperature": tau, "logit_std": 8.5},
+        "roofline": {"kernel": "tt_block_attn (attention + merge) at S=16 inside the loop",
+                     "bound": "hbm", "achieved": round(gb16, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gb16 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": a16["attn_bytes"], "mean_launch_ms": round(us16 * 1e-3, 4)},
+        "sweep": {"per_block_size": {str(k): v for k, v in per_s.items()}, "loops": cells},
+    }
+    if not args.no_cpu_baseline:
+        S = 16
+        w = dict(B=B, S=S, layers=NL, lens=lens, gamma=0.8, tau=tau)
+        qb = [synth.normal((B, S, Hq, d), 1.0, sd + 30 + l, bf, dev) for l in range(NL)]
+        kb = [synth.normal((B, S, Hkv, d), 1.0, sd + 40 + l, bf, dev) for l in range(NL)]
+        vb = [synth.normal((B, S, Hkv, d), 1.0, sd + 50 + l, bf, dev) for l in range(NL)]
+        lg = synth.normal((B, S, V), 8.5, sd + 70, bf, dev)
+        result["cpu_baseline"] = cpu_baseline(w, 1, kc, vc, qb, kb, vb, ada, lg, start)
+    print(json.dumps(result), flush=True)
 
 
 def cpu_model():

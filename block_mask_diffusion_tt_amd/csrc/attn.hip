@@ -15,10 +15,12 @@
 //     read from HBM once per layer;
 //   * a unit = (sequence b, KV head g, row block rb, context chunk c); chunk 0
 //     also takes the S block keys; units write (max, sum, accumulator)
-//     partials that the merge kernel combines in chunk order (deterministic).
+//     partials that the merge kernel combines in a fixed chunk order
+//     (deterministic).
 //
-// bf16 kernel (gfx950 matrix cores, 64-wide waves): 8 waves x 32 rows, one
-// workgroup per CU (two waves per SIMD).
+// bf16 kernel (gfx950 matrix cores, 64-wide waves): waves of 32 rows, 2, 4
+// or 8 of them per workgroup (as many as the R rows of a KV head need, up to
+// 256 rows; more rows make several row blocks), one workgroup per CU.
 //   S^T = K Q'^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 channels
 //   straight from the LDS K tile, B = the wave's pre-modulated Q' held in
 //   registers), so each lane ends with 16 scores of one row; the online
@@ -50,6 +52,8 @@ constexpr int kKPad = 8;         // bf16 padding of an LDS K row
 constexpr int kVPad = 4;         // bf16 padding of an LDS V^T row
 constexpr int kMaxWaves = 8;     // bf16 workgroups: up to 8 waves of 32 rows
 constexpr int kRowsF32 = 64;     // rows per fp32 workgroup (1 wave, 1 row per lane)
+constexpr int kMinChunk = 256;   // fewest context keys per unit (multiple of kTK): below
+                                 // that, the fixed cost of a unit and of its partial dominate
 constexpr float kRescaleTh = 8.f;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -858,10 +862,14 @@ __device__ __forceinline__ void load_part<uint16_t, 8>(const void* part, int64_t
 // head, row block) group.  Two quads per thread measured fastest (1, 2, 4
 // and 8 tried at the headline shape: 10.1, 8.6, 10.1, 13.0 us).
 constexpr int kMergeQuads = 2;
+template <typename T>
+struct TypeTag { using type = T; };
 template <int D>
 constexpr int merge_rows_per_wg() { return 256 / (D / (4 * kMergeQuads)); }
 
-template <typename OutT, int D>
+// NB: chunk partials loaded together (2, 4 or 8: the smallest that covers
+// the plan's chunks, 8 beyond).
+template <typename OutT, int D, int NB>
 __global__ __launch_bounds__(256) void merge_kernel(MParams p) {
   constexpr int CPT = 4 * kMergeQuads;   // channels per thread
   constexpr int Q = kMergeQuads;         // 16-byte loads per thread per chunk
@@ -878,24 +886,45 @@ __global__ __launch_bounds__(256) void merge_kernel(MParams p) {
   if (row >= p.R) return;
   const int n = units_of(p.ctx_len[b], p.chunk, p.NC);
   const int64_t u0 = static_cast<int64_t>(grp) * p.NC;
-  // chunk c contributes w_c l_c o_c with w_c = 2^(m_c - M); its stored
-  // partial is o_c 2^-k_c (fp16 for bf16 output, fp32 for fp32 output)
-  float M = -INFINITY;
-  for (int c = 0; c < n; ++c) M = fmaxf(M, p.part_ml[((u0 + c) * p.rows_per_unit + rl) * 4]);
-  float L = 0.f;
+  // chunk c contributes 2^(m_c - M) l_c o_c, M the largest m_c; its stored
+  // partial is o_c 2^-k_c (fp16 for bf16 output, fp32 for fp32 output).
+  // One pass over the chunks, NB at a time (all their loads issued
+  // together), the running sums rescaled when a batch raises the maximum.
+  float M = -INFINITY, L = 0.f;
   float o[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) o[i] = 0.f;
-  for (int c = 0; c < n; ++c) {
-    const int64_t base = (u0 + c) * p.rows_per_unit + rl;
-    const float4 ml = *reinterpret_cast<const float4*>(p.part_ml + base * 4);
-    const float wl = exp2f(ml.x - M) * ml.y;
-    L += wl;
-    const float coef = ldexpf(wl, static_cast<int>(ml.z));
-    float a[CPT];
-    load_part<OutT, CPT>(p.part_acc, base * D + c0, a);
+  for (int cb = 0; cb < n; cb += NB) {
+    float4 ml[NB];
+    float a[NB][CPT];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) o[i] = fmaf(coef, a[i], o[i]);
+    for (int j = 0; j < NB; ++j) {
+      if (cb + j < n) {
+        const int64_t base = (u0 + cb + j) * p.rows_per_unit + rl;
+        ml[j] = *reinterpret_cast<const float4*>(p.part_ml + base * 4);
+        load_part<OutT, CPT>(p.part_acc, base * D + c0, a[j]);
+      } else {
+        ml[j] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) a[j][i] = 0.f;
+      }
+    }
+    float Mb = M;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) Mb = fmaxf(Mb, ml[j].x);
+    const float r = exp2f(M - Mb);   // 0 on the first batch (M = -inf)
+    L *= r;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) o[i] *= r;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const float wl = exp2f(ml[j].x - Mb) * ml[j].y;
+      L += wl;
+      const float coef = ldexpf(wl, static_cast<int>(ml[j].z));
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) o[i] = fmaf(coef, a[j][i], o[i]);
+    }
+    M = Mb;
   }
   const float inv = 1.f / L;
   const int s = row / p.G, h = g * p.G + row % p.G;
@@ -936,7 +965,7 @@ AttnPlan attn_plan(int B, int S, int Hq, int Hkv, int d, int dtype, int max_ctx_
   const int64_t want = ceil_div(device_cus(), groups);
   int64_t chunk = max_ctx_len > 0 ? ceil_div(max_ctx_len, want < 1 ? 1 : want) : kTK;
   chunk = static_cast<int64_t>(align_up(static_cast<size_t>(chunk), kTK));
-  if (chunk < kTK) chunk = kTK;
+  if (chunk < kMinChunk) chunk = kMinChunk;
   pl.chunk = static_cast<int>(chunk);
   int64_t nc = max_ctx_len > 0 ? ceil_div(max_ctx_len, chunk) : 1;
   pl.n_chunks = static_cast<int>(nc < 1 ? 1 : nc);
@@ -999,13 +1028,23 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& pl, void* ws, hi
   const dim3 mg(static_cast<unsigned>(ceil_div(pl.rows_per_unit, a.d == 128 ? merge_rows_per_wg<128>()
                                                                          : merge_rows_per_wg<64>())),
                 static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * pl.row_blocks));
-  if (a.dtype == 0) {
-    if (a.d == 128) hipLaunchKernelGGL((merge_kernel<uint16_t, 128>), mg, dim3(256), 0, st, mp);
-    else hipLaunchKernelGGL((merge_kernel<uint16_t, 64>), mg, dim3(256), 0, st, mp);
-  } else {
-    if (a.d == 128) hipLaunchKernelGGL((merge_kernel<float, 128>), mg, dim3(256), 0, st, mp);
-    else hipLaunchKernelGGL((merge_kernel<float, 64>), mg, dim3(256), 0, st, mp);
-  }
+  const int nb = pl.n_chunks <= 2 ? 2 : pl.n_chunks <= 4 ? 4 : 8;
+  auto merge = [&](auto out_c, auto d_c, auto nb_c) {
+    using OutT = typename decltype(out_c)::type;
+    hipLaunchKernelGGL((merge_kernel<OutT, decltype(d_c)::value, decltype(nb_c)::value>), mg,
+                       dim3(256), 0, st, mp);
+  };
+  auto by_nb = [&](auto out_c, auto d_c) {
+    if (nb == 2) merge(out_c, d_c, std::integral_constant<int, 2>{});
+    else if (nb == 4) merge(out_c, d_c, std::integral_constant<int, 4>{});
+    else merge(out_c, d_c, std::integral_constant<int, 8>{});
+  };
+  auto by_d = [&](auto out_c) {
+    if (a.d == 128) by_nb(out_c, std::integral_constant<int, 128>{});
+    else by_nb(out_c, std::integral_constant<int, 64>{});
+  };
+  if (a.dtype == 0) by_d(TypeTag<uint16_t>{});
+  else by_d(TypeTag<float>{});
   return hipGetLastError();
 }
 
