@@ -69,14 +69,20 @@ __global__ __launch_bounds__(256) void adaln_kernel(int B, int width, int n_laye
 #pragma unroll
     for (int kk = 0; kk < kPerSlice; ++kk) wv[kk] = make_uint2(0, 0);
   }
-  for (int idx = threadIdx.x; idx < kRows * kEmb; idx += 256) {
+  // SiLU of the tile's embeddings into LDS: every load issued before the
+  // first use (one round trip)
+  constexpr int kEPer = kRows * kEmb / 256;
+  float ev[kEPer];
+#pragma unroll
+  for (int i = 0; i < kEPer; ++i) {
+    const int idx = threadIdx.x + 256 * i;
     const int r = idx / kEmb, k = idx % kEmb;
-    float v = 0.f;
-    if (r < nb) {
-      const float e = emb[static_cast<int64_t>(b0 + r) * kEmb + k];
-      v = e / (1.f + expf(-e));
-    }
-    s_e[r][k] = v;
+    ev[i] = r < nb ? emb[static_cast<int64_t>(b0 + r) * kEmb + k] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < kEPer; ++i) {
+    const int idx = threadIdx.x + 256 * i;
+    s_e[idx / kEmb][idx % kEmb] = ev[i] / (1.f + expf(-ev[i]));
   }
   __syncthreads();
   float acc[kRows][4];
