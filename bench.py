@@ -74,7 +74,7 @@ def parse():
 
 
 COUNTERS_JSON = os.path.join(ROOT, "profiles", "attn_ctx8k_hbm_counters.json")
-ATTN_KERNELS = ("attn_bf16_kernel<128>", "merge_kernel<unsigned short, 128>")
+ATTN_KERNELS = ("attn_bf16_kernel<128, 8>", "merge_kernel<unsigned short, 128, 2>")
 
 
 def attn_source_hash():
@@ -148,6 +148,20 @@ def counted_traffic():
     if rec.get("source_sha256") != attn_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def calibration_copy(args):
+    """One plain device copy of --calib-copy-mb MiB (its hardware byte
+    counters calibrate the kernels' FETCH_SIZE / WRITE_SIZE readings)."""
+    import torch
+    if not args.calib_copy_mb:
+        return
+    src = torch.ones(args.calib_copy_mb << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def workload(name):
@@ -273,13 +287,7 @@ def main():
         tt.confidence_unmask(B, S, V, logits, V, w["gamma"], w["tau"], 3, 0, tokens_all[i],
                              masked_all[i], uws, n_masked=n_masked)
 
-    if args.calib_copy_mb:
-        src = torch.ones(args.calib_copy_mb << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    calibration_copy(args)
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
@@ -632,6 +640,7 @@ def sweep_main(args):
     import synth
 
     dev, bf = "cuda", torch.bfloat16
+    calibration_copy(args)
     B, L, Hq, Hkv, d, NL, V = 8, 32768, 32, 2, 128, 6, 131072
     W, sd, tau = Hq * d, 4321, 1.0
     lens = [L] * B
