@@ -47,8 +47,17 @@ M0_ASM = ["attn.hip", "sublayer.hip"]
 
 def _check_m0(asm_path):
     """Fail the build if the compiler also uses M0 anywhere in a file whose
-    kernels set it by hand, since nothing would then preserve it."""
-    lines = open(asm_path).read().splitlines()
+    kernels set it by hand, since nothing would then preserve it, or if any
+    of its kernels spills to scratch: their copy waits count the copies in
+    flight (s_waitcnt vmcnt(N)), and a spill reload is a memory operation the
+    count does not know of."""
+    text = open(asm_path).read()
+    for m in re.finditer(r"^\s*\.amdhsa_private_segment_fixed_size\s+(\d+)", text, re.M):
+        if int(m.group(1)) != 0:
+            raise RuntimeError(f"{asm_path}: a kernel uses {m.group(1)} bytes of scratch")
+    if re.search(r"^\s*scratch_(load|store)", text, re.M):
+        raise RuntimeError(f"{asm_path}: a kernel spills to scratch")
+    lines = text.splitlines()
     for i, line in enumerate(lines):
         if re.search(r"\bm0\b", line.split(";")[0]):
             ok = (re.match(r"\s*s_mov_b32 m0, s\d+\s*$", line) and i + 2 < len(lines)
