@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <atomic>
 #include <mutex>
@@ -63,6 +65,37 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t elt_size(int dtype) { return dtype == TT_BF16 ? 2 : 4; }
 
+// TT_VALIDATE set (and not "0"): check the context arrays on the device
+// before a call's kernels, and wait for the verdict.
+bool validate_enabled() {
+  const char* v = getenv("TT_VALIDATE");
+  return v && v[0] && strcmp(v, "0") != 0;
+}
+
+tt_status check_ctx_on_device(const char* fn, int B, const int64_t* ctx_start,
+                              const int32_t* ctx_len, const int64_t* ctx_end,
+                              const uint8_t* active, tt_stream stream) {
+  if (!validate_enabled() || B == 0) return TT_OK;
+  int64_t v[4];
+  const hipError_t e = tt::validate_ctx(B, ctx_start, ctx_len, ctx_end, active, v,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, fn);
+  if (v[0] < 0) return TT_OK;
+  const long long b = v[0], x = v[2], y = v[3];
+  switch (v[1]) {
+    case 1: return fail(TT_ERR_INVALID_ARG, "%s: TT_VALIDATE: ctx_len[%lld] = %lld < 0", fn, b, x);
+    case 2: return fail(TT_ERR_INVALID_ARG, "%s: TT_VALIDATE: ctx_start[%lld] = %lld < 0", fn, b, x);
+    case 3:
+      return fail(TT_ERR_INVALID_ARG,
+                  "%s: TT_VALIDATE: ctx_end[%lld] = %lld is below ctx_start + ctx_len = %lld", fn,
+                  b, x, y);
+    default:
+      return fail(TT_ERR_INVALID_ARG,
+                  "%s: TT_VALIDATE: the reserved regions of sequences %lld and %lld overlap", fn, b,
+                  x);
+  }
+}
+
 tt_status check_shape(const tt_attn_shape* s) {
   if (!s) return fail(TT_ERR_INVALID_ARG, "shape is NULL");
   if (s->batch < 0) return fail(TT_ERR_INVALID_ARG, "batch %d < 0", s->batch);
@@ -96,11 +129,13 @@ tt_status check_unmask_scalars(int32_t batch, int32_t S, int32_t V, int64_t row_
   return TT_OK;
 }
 
+// Hands out 256-byte-aligned pieces of a workspace in order.  With a NULL
+// base it only counts (a size query), without forming pointers from NULL.
 struct Carver {
   char* base;
   size_t off = 0;
   void* take(size_t bytes) {
-    void* p = base + off;
+    void* p = base ? base + off : nullptr;
     off += tt::align_up(bytes, 256);
     return p;
   }
@@ -250,6 +285,8 @@ tt_status block_attn_common(const char* fn, const tt_attn_shape* shape, const vo
   a.ctx_end = ctx_end;
   a.kc_out = const_cast<void*>(k_ctx);
   a.vc_out = const_cast<void*>(v_ctx);
+  st = check_ctx_on_device(fn, shape->batch, ctx_start, ctx_len, ctx_end, active, stream);
+  if (st != TT_OK) return st;
   const hipError_t e = tt::launch_block_attn(a, p, workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, fn);
   return ok();
@@ -399,6 +436,9 @@ tt_status tt_ctx_advance(int32_t batch, int32_t block_size, const int64_t* ctx_s
   if (!aligned(ctx_start, 8) || !aligned(ctx_end, 8) || !aligned(ctx_len, 4))
     return fail(TT_ERR_INVALID_ARG, "tt_ctx_advance: misaligned ctx_start/ctx_end/ctx_len");
   if (batch == 0) return ok();
+  const tt_status vs = check_ctx_on_device("tt_ctx_advance", batch, ctx_start, ctx_len, ctx_end,
+                                           active, stream);
+  if (vs != TT_OK) return vs;
   const hipError_t e = tt::launch_ctx_advance(batch, block_size, ctx_start, ctx_end, ctx_len,
                                               active, appended, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "tt_ctx_advance launch");
@@ -729,6 +769,8 @@ tt_status denoise_common(const char* fn, const tt_attn_shape* shape, int32_t n_l
     return fail(TT_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
   if (!aligned(workspace, 256)) return fail(TT_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
 
+  st = check_ctx_on_device(fn, shape->batch, ctx_start, ctx_len, nullptr, nullptr, stream);
+  if (st != TT_OK) return st;
   Carver cv{static_cast<char*>(workspace)};
   const DenoiseBufs z = carve_denoise(cv, shape, n_layers, max_ctx_len, vocab);
   LoopOpts o{};
@@ -843,6 +885,8 @@ tt_status tt_generate(const tt_attn_shape* shape, int32_t n_layers, int32_t n_bl
     return fail(TT_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
   if (!aligned(workspace, 256)) return fail(TT_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
 
+  st = check_ctx_on_device(fn, B, ctx_start, ctx_len, ctx_end, nullptr, stream);
+  if (st != TT_OK) return st;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const int hint = max_ctx_len + n_blocks * S;
   Carver cv{static_cast<char*>(workspace)};
@@ -1102,6 +1146,8 @@ tt_status tt_adaln_attn_sublayer(const tt_attn_shape* shape, int32_t width, cons
     return fail(TT_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, workspace_bytes, need);
   if (!aligned(workspace, 256))
     return fail(TT_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  st = check_ctx_on_device(fn, shape->batch, ctx_start, ctx_len, nullptr, active, stream);
+  if (st != TT_OK) return st;
   SubBufs w{};
   sublayer_bytes(shape, width, max_ctx_len, &w, workspace);
   const hipStream_t hs = static_cast<hipStream_t>(stream);

@@ -149,4 +149,14 @@ hipError_t launch_ctx_advance(int B, int S, const int64_t* ctx_start, const int6
                               int32_t* ctx_len, const uint8_t* active, uint8_t* appended,
                               hipStream_t st);
 
+// ---------------------------------------------------------------- TT_VALIDATE
+// Checks the context arrays on the device (csrc/validate.hip) and waits for
+// the verdict: verdict[0] = the first failing sequence or -1, verdict[1] the
+// rule (1 ctx_len < 0, 2 ctx_start < 0, 3 ctx_end below start + len, 4 two
+// reserved regions overlap, verdict[2] = the other sequence), verdict[2..3]
+// the values involved.
+hipError_t validate_ctx(int B, const int64_t* ctx_start, const int32_t* ctx_len,
+                        const int64_t* ctx_end, const uint8_t* active, int64_t verdict[4],
+                        hipStream_t st);
+
 }  // namespace tt

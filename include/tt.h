@@ -23,8 +23,21 @@
  *     An invalid call returns a status, stores a message readable through
  *     tt_last_error() and launches nothing.  A failing HIP call returns
  *     TT_ERR_HIP.
- *   - No global mutable state besides the thread-local error message; calls
- *     on different streams with different workspaces may run concurrently.
+ *   - Device-side checks (debugging aid): with the environment variable
+ *     TT_VALIDATE set to anything but "" or "0", every call that takes the
+ *     context arrays (the attention calls, tt_ctx_advance, the denoise and
+ *     generation loops, the weighted sublayer) first runs one small kernel
+ *     over them and waits for its verdict.  It returns TT_ERR_INVALID_ARG,
+ *     naming the first offending sequence, when for an active sequence b
+ *     ctx_len[b] < 0, ctx_start[b] < 0, ctx_end[b] < ctx_start[b] +
+ *     ctx_len[b], or (with ctx_end, up to 8192 sequences) its reserved
+ *     region overlaps another active sequence's; nothing else of the call is
+ *     launched then.  Checked calls are synchronous.  The verdict lives in a
+ *     small array in each GPU's memory, so two checked calls on one GPU must
+ *     not overlap in time.
+ *   - No global mutable state besides the thread-local error message (and
+ *     the per-GPU arrays of TT_VALIDATE and tt_block_attn_noalloc); calls on
+ *     different streams with different workspaces may run concurrently.
  *     Two calls in flight must not share one workspace.
  *   - bf16 is IEEE-754 binary32 truncated to its upper 16 bits (bfloat16).
  *   - Limits: head_dim in {64, 128}; block_size S in [1, 64]; n_q_heads a
