@@ -55,6 +55,9 @@ constexpr int kRowsF32 = 64;     // rows per fp32 workgroup (1 wave, 1 row per l
 constexpr int kMinChunk = 256;   // fewest context keys per unit (multiple of kTK): below
                                  // that, the fixed cost of a unit and of its partial dominate
 constexpr float kRescaleTh = 8.f;
+constexpr int kModHeads = 16;    // largest query-head group whose adaLN vectors are staged in LDS
+template <int D>
+constexpr int kModStride = D + 4;   // floats per staged head (padded)
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct KParams {
@@ -285,6 +288,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bf16_kernel(KParams p) {
   constexpr int KSTEPS = D / 16;   // MFMA k-steps of QK^T
   constexpr int DT = D / 32;       // 32-channel tiles of the output
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::SMEM];
+  __shared__ __attribute__((aligned(16))) float smod[2 * kModHeads * kModStride<D>];
 
   Unit un;
   const int ul = unit_of_block(blockIdx.x, p.units, p.RB);
@@ -462,63 +466,98 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bf16_kernel(KParams p) {
   f32x16 scr[2];           // scores of halves of even / odd index
   bf16x8 pb[2][2];         // P of halves of even / odd index (two k-steps)
   // Q' = (q * (1 + scale) + shift) * log2(e)/sqrt(d), rounded to bf16;
-  // lane l32 holds its row.  All loads of q, scale and shift are issued at
-  // once (rows past R read row 0 and are zeroed), after the copies of tiles
-  // 0 and 1: the waits for the query loads also cover them (loads complete
-  // in order), and S(0) needs them.
+  // lane l32 holds its row.  The loads of q are issued after the copies of
+  // tiles 0 and 1: the waits for them also cover the copies (loads complete
+  // in order), and S(0) needs both.  Rows past R read row 0 and are zeroed.
+  //   The modulation vectors depend on the head only, so every wave would
+  // load the same G heads: with G <= kModHeads the workgroup stages the
+  // unit's G x d scale and shift in LDS once (contiguous in memory, one
+  // 16-byte load per thread and vector at the headline shape; rows padded by
+  // 16 bytes to spread the heads over the banks) and every lane reads its
+  // head from there after the barrier that makes tiles 0 and 1 visible.
+  // Larger groups load per lane (each lane its row's head).
   bf16x8 qf[KSTEPS];
   for (int t = 0; t < (n_tiles < 2 ? n_tiles : 2); ++t) issue(t);
   const bool has_sc = p.scale != nullptr, has_sh = p.shift != nullptr;
+  const bool has_mod = has_sc || has_sh;
+  const bool staged = has_mod && p.G <= kModHeads;
+  const bool valid = row < p.R;
+  const int h = un.g * p.G + (valid ? row % p.G : 0);
+  uint4 qraw[KSTEPS];
   {
-    uint4 qraw[KSTEPS];
-    float4 sca[KSTEPS][2], sha[KSTEPS][2];
-    const bool valid = row < p.R;
     const int s = valid ? row / p.G : 0;
-    const int h = un.g * p.G + (valid ? row % p.G : 0);
     const uint16_t* qrow = p.q + ((static_cast<int64_t>(un.b) * p.S + s) * p.Hq + h) * D;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk)
       qraw[kk] = *reinterpret_cast<const uint4*>(qrow + kk * 16 + half * 8);
-    // a missing vector reads the present one (ignored below), so that one
-    // branch holds every modulation load
-    if (has_sc || has_sh) {
-      const int64_t ada = (static_cast<int64_t>(un.b) * p.Hq + h) * D + half * 8;
-      const float* scp = (has_sc ? p.scale : p.shift) + ada;
-      const float* shp = (has_sh ? p.shift : p.scale) + ada;
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          sca[kk][i] = *reinterpret_cast<const float4*>(scp + kk * 16 + 4 * i);
-          sha[kk][i] = *reinterpret_cast<const float4*>(shp + kk * 16 + 4 * i);
-        }
-    }
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      const uint4 w = qraw[kk];
-      float v[8] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                    __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u),
-                    __uint_as_float(w.z << 16), __uint_as_float(w.z & 0xffff0000u),
-                    __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xffff0000u)};
-      if (has_sc || has_sh) {
-        const float4 a0 = sca[kk][0], a1 = sca[kk][1];
-        const float4 b0 = sha[kk][0], b1 = sha[kk][1];
-        const float sc8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        const float sh8[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (has_sc) v[i] *= 1.f + sc8[i];
-          if (has_sh) v[i] += sh8[i];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qf[kk][i] = static_cast<__bf16>(valid ? v[i] * p.qscale : 0.f);
-    }
   }
-  // tiles 0 and 1 visible, then tiles 2 and 3 start
+  // a missing vector reads the present one (ignored below), so that one
+  // branch holds every modulation load
+  const float* scv = has_sc ? p.scale : p.shift;
+  const float* shv = has_sh ? p.shift : p.scale;
+  float4 sca[KSTEPS][2], sha[KSTEPS][2];
+  if (staged) {
+    constexpr int PER = (kModHeads * D / 4 + C::NT - 1) / C::NT;
+    const int n4 = p.G * D / 4;
+    const int64_t base = (static_cast<int64_t>(un.b) * p.Hq + un.g * p.G) * D;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + i * C::NT;
+      if (e < n4) {
+        const float4 a = *reinterpret_cast<const float4*>(scv + base + 4 * e);
+        const float4 b = *reinterpret_cast<const float4*>(shv + base + 4 * e);
+        const int j = (4 * e) / D, c = (4 * e) % D;
+        *reinterpret_cast<float4*>(&smod[j * kModStride<D> + c]) = a;
+        *reinterpret_cast<float4*>(&smod[(kModHeads + j) * kModStride<D> + c]) = b;
+      }
+    }
+  } else if (has_mod) {
+    const int64_t ada = (static_cast<int64_t>(un.b) * p.Hq + h) * D + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        sca[kk][i] = *reinterpret_cast<const float4*>(scv + ada + kk * 16 + 4 * i);
+        sha[kk][i] = *reinterpret_cast<const float4*>(shv + ada + kk * 16 + 4 * i);
+      }
+  }
+  // tiles 0 and 1 (and the staged vectors) visible, then tiles 2 and 3 start
   wait_vmem<0>();
   __syncthreads();
   for (int t = 2; t < (n_tiles < C::NST ? n_tiles : C::NST); ++t) issue(t);
+  if (staged) {
+    const int j = h - un.g * p.G;
+    const float* scl = &smod[j * kModStride<D> + half * 8];
+    const float* shl = &smod[(kModHeads + j) * kModStride<D> + half * 8];
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        sca[kk][i] = *reinterpret_cast<const float4*>(scl + kk * 16 + 4 * i);
+        sha[kk][i] = *reinterpret_cast<const float4*>(shl + kk * 16 + 4 * i);
+      }
+  }
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    const uint4 w = qraw[kk];
+    float v[8] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                  __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u),
+                  __uint_as_float(w.z << 16), __uint_as_float(w.z & 0xffff0000u),
+                  __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xffff0000u)};
+    if (has_mod) {
+      const float4 a0 = sca[kk][0], a1 = sca[kk][1];
+      const float4 b0 = sha[kk][0], b1 = sha[kk][1];
+      const float sc8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float sh8[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (has_sc) v[i] *= 1.f + sc8[i];
+        if (has_sh) v[i] += sh8[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qf[kk][i] = static_cast<__bf16>(valid ? v[i] * p.qscale : 0.f);
+  }
   // prologue: S(0), S(1); the reference mu is S(0)'s row maximum (finite:
   // the first half of a unit's first tile always holds a valid key)
 #pragma unroll
