@@ -290,18 +290,73 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bf16_kernel(KParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::SMEM];
   __shared__ __attribute__((aligned(16))) float smod[2 * kModHeads * kModStride<D>];
 
-  Unit un;
   const int ul = unit_of_block(blockIdx.x, p.units, p.RB);
-  if (ul >= p.units || !decode_unit(ul, p.Hkv, p.RB, p.NC, p.chunk, p.ctx_len, p.active, un)) return;
+  if (ul >= p.units) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31, grp = lane >> 4, li = lane & 15;
   const int64_t kstride = static_cast<int64_t>(p.Hkv) * D;
   TT_LDS uint8_t* const lsm = (TT_LDS uint8_t*)(smem);  // address-space cast
-  append_block_kv(p, un, D, 2);
   // this lane's row: rl within the unit's row block, row within the group
   const int rl = wave * 32 + l32;
-  const int row = un.rb * C::ROWS + rl;
+  const int row = (ul % p.RB) * C::ROWS + rl;
+
+  // Q' = (q * (1 + scale) + shift) * log2(e)/sqrt(d), rounded to bf16;
+  // lane l32 holds its row.  The query and modulation loads depend on the
+  // unit's sequence, head and row block only (its number), so they go out
+  // first, before the lengths decide whether the unit has work.  Rows past R
+  // read row 0 and are zeroed.
+  //   The modulation vectors depend on the head only, so every wave would
+  // load the same G heads: with G <= kModHeads the workgroup stages the
+  // unit's G x d scale and shift in LDS once (contiguous in memory, one
+  // 16-byte load per thread and vector at the headline shape; rows padded by
+  // 16 bytes to spread the heads over the banks) and every lane reads its
+  // head from there after the barrier that makes tiles 0 and 1 visible.
+  // Larger groups load per lane (each lane its row's head).
+  constexpr int MPER = (kModHeads * D / 4 + C::NT - 1) / C::NT;
+  const bool has_sc = p.scale != nullptr, has_sh = p.shift != nullptr;
+  const bool has_mod = has_sc || has_sh;
+  const bool staged = has_mod && p.G <= kModHeads;
+  const bool valid = row < p.R;
+  uint4 qraw[KSTEPS];
+  float4 sca[KSTEPS][2], sha[KSTEPS][2];
+  float4 msc[MPER], msh[MPER];
+  {
+    const int t = ul / p.RB / p.NC;
+    const int ug = t % p.Hkv, ub = t / p.Hkv;
+    const int h = ug * p.G + (valid ? row % p.G : 0);
+    const int s = valid ? row / p.G : 0;
+    const uint16_t* qrow = p.q + ((static_cast<int64_t>(ub) * p.S + s) * p.Hq + h) * D;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      qraw[kk] = *reinterpret_cast<const uint4*>(qrow + kk * 16 + half * 8);
+    // a missing vector reads the present one (ignored below), so that one
+    // branch holds every modulation load
+    const float* scv = has_sc ? p.scale : p.shift;
+    const float* shv = has_sh ? p.shift : p.scale;
+    if (staged) {
+      const int n4 = p.G * D / 4;
+      const int64_t base = (static_cast<int64_t>(ub) * p.Hq + ug * p.G) * D;
+#pragma unroll
+      for (int i = 0; i < MPER; ++i) {
+        const int e = tid + i * C::NT;
+        msc[i] = e < n4 ? *reinterpret_cast<const float4*>(scv + base + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
+        msh[i] = e < n4 ? *reinterpret_cast<const float4*>(shv + base + 4 * e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    } else if (has_mod) {
+      const int64_t ada = (static_cast<int64_t>(ub) * p.Hq + h) * D + half * 8;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          sca[kk][i] = *reinterpret_cast<const float4*>(scv + ada + kk * 16 + 4 * i);
+          sha[kk][i] = *reinterpret_cast<const float4*>(shv + ada + kk * 16 + 4 * i);
+        }
+    }
+  }
+  Unit un;
+  if (!decode_unit(ul, p.Hkv, p.RB, p.NC, p.chunk, p.ctx_len, p.active, un)) return;
+  append_block_kv(p, un, D, 2);
   // block keys visible to this lane's row: all S, or slots 0..s when causal
   // (rows past R take all S, so every row has a finite maximum)
   const int blk_valid = (p.causal && row < p.R) ? row / p.G + 1 : p.S;
@@ -465,68 +520,26 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bf16_kernel(KParams p) {
   bf16x8 vop[2 * DT];      // V^T operands of the PV^T products, j = ks * DT + dt
   f32x16 scr[2];           // scores of halves of even / odd index
   bf16x8 pb[2][2];         // P of halves of even / odd index (two k-steps)
-  // Q' = (q * (1 + scale) + shift) * log2(e)/sqrt(d), rounded to bf16;
-  // lane l32 holds its row.  The loads of q are issued after the copies of
-  // tiles 0 and 1: the waits for them also cover the copies (loads complete
-  // in order), and S(0) needs both.  Rows past R read row 0 and are zeroed.
-  //   The modulation vectors depend on the head only, so every wave would
-  // load the same G heads: with G <= kModHeads the workgroup stages the
-  // unit's G x d scale and shift in LDS once (contiguous in memory, one
-  // 16-byte load per thread and vector at the headline shape; rows padded by
-  // 16 bytes to spread the heads over the banks) and every lane reads its
-  // head from there after the barrier that makes tiles 0 and 1 visible.
-  // Larger groups load per lane (each lane its row's head).
   bf16x8 qf[KSTEPS];
   for (int t = 0; t < (n_tiles < 2 ? n_tiles : 2); ++t) issue(t);
-  const bool has_sc = p.scale != nullptr, has_sh = p.shift != nullptr;
-  const bool has_mod = has_sc || has_sh;
-  const bool staged = has_mod && p.G <= kModHeads;
-  const bool valid = row < p.R;
-  const int h = un.g * p.G + (valid ? row % p.G : 0);
-  uint4 qraw[KSTEPS];
-  {
-    const int s = valid ? row / p.G : 0;
-    const uint16_t* qrow = p.q + ((static_cast<int64_t>(un.b) * p.S + s) * p.Hq + h) * D;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
-      qraw[kk] = *reinterpret_cast<const uint4*>(qrow + kk * 16 + half * 8);
-  }
-  // a missing vector reads the present one (ignored below), so that one
-  // branch holds every modulation load
-  const float* scv = has_sc ? p.scale : p.shift;
-  const float* shv = has_sh ? p.shift : p.scale;
-  float4 sca[KSTEPS][2], sha[KSTEPS][2];
   if (staged) {
-    constexpr int PER = (kModHeads * D / 4 + C::NT - 1) / C::NT;
-    const int n4 = p.G * D / 4;
-    const int64_t base = (static_cast<int64_t>(un.b) * p.Hq + un.g * p.G) * D;
+    // (the wait for these values also covers the copies just issued)
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
+    for (int i = 0; i < MPER; ++i) {
       const int e = tid + i * C::NT;
-      if (e < n4) {
-        const float4 a = *reinterpret_cast<const float4*>(scv + base + 4 * e);
-        const float4 b = *reinterpret_cast<const float4*>(shv + base + 4 * e);
+      if (e < p.G * D / 4) {
         const int j = (4 * e) / D, c = (4 * e) % D;
-        *reinterpret_cast<float4*>(&smod[j * kModStride<D> + c]) = a;
-        *reinterpret_cast<float4*>(&smod[(kModHeads + j) * kModStride<D> + c]) = b;
+        *reinterpret_cast<float4*>(&smod[j * kModStride<D> + c]) = msc[i];
+        *reinterpret_cast<float4*>(&smod[(kModHeads + j) * kModStride<D> + c]) = msh[i];
       }
     }
-  } else if (has_mod) {
-    const int64_t ada = (static_cast<int64_t>(un.b) * p.Hq + h) * D + half * 8;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk)
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        sca[kk][i] = *reinterpret_cast<const float4*>(scv + ada + kk * 16 + 4 * i);
-        sha[kk][i] = *reinterpret_cast<const float4*>(shv + ada + kk * 16 + 4 * i);
-      }
   }
   // tiles 0 and 1 (and the staged vectors) visible, then tiles 2 and 3 start
   wait_vmem<0>();
   __syncthreads();
   for (int t = 2; t < (n_tiles < C::NST ? n_tiles : C::NST); ++t) issue(t);
   if (staged) {
-    const int j = h - un.g * p.G;
+    const int j = valid ? row % p.G : 0;
     const float* scl = &smod[j * kModStride<D> + half * 8];
     const float* shl = &smod[(kModHeads + j) * kModStride<D> + half * 8];
 #pragma unroll
