@@ -164,6 +164,8 @@ __device__ __forceinline__ void append_block_kv(const KParams& p, const Unit& un
 // ------------------------------------------------------------------ bf16
 #define TT_LDS __attribute__((address_space(3)))
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // 16-byte global -> LDS copy through the direct path: lane i writes LDS bytes
@@ -729,9 +731,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bf16_kernel(KParams p) {
   }
 
   // ---- partials: (max, sum) per row and the unnormalised accumulator, in
-  // the unit's slot ((b * Hkv + g) * RB + rb) * NC + c
+  // the unit's slot ((b * Hkv + g) * RB + rb) * NC + c.  Lanes of rows past R
+  // compute along (their values are finite) but store nothing.
   const float ltot = xhalf_sum(lsum);
-  if (row >= p.R) return;
+  const bool live = row < p.R;
   const int64_t u = ((static_cast<int64_t>(un.b) * p.Hkv + un.g) * p.RB + un.rb) * p.NC + un.c;
   // o = acc / l in fp16, scaled by 2^-k so the row's largest |o| lands in
   // [2^14, 2^15): full fp16 precision (2^-11 relative) whatever the scale of
@@ -747,19 +750,48 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bf16_kernel(KParams p) {
   frexpf(xhalf_max(amax) * inv, &ex);
   const int k = min(max(ex - 15, -100), 127);
   const float sc = ldexpf(inv, -k);
-  if (half == 0)
+  if (live && half == 0)
     *reinterpret_cast<float4*>(p.part_ml + (u * C::ROWS + rl) * 4) =
         make_float4(mu, ltot, static_cast<float>(k), 0.f);
-  uint16_t* dst = static_cast<uint16_t*>(p.part_acc) + (u * C::ROWS + rl) * D;
-  typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+  // The fp16 rows go out through LDS: each wave writes its 32 rows x d into
+  // a private half of a K or V tile region of a stage that no wave reads or
+  // copies into any more (the stages of the three tiles before the last: no
+  // copy is pending after the last tiles' waits, and after the barrier at the
+  // last tile's start every wave reads that tile only; a unit with fewer
+  // tiles never filled them), then stores whole 16-byte row chunks, 1 KB per
+  // instruction, instead of 8-byte pieces scattered over 32 rows.  The
+  // 16-byte chunk index is XOR-swizzled with the row to spread the rows over
+  // the LDS banks.
+  {
+    constexpr int RB16 = D / 8;            // 16-byte chunks per row
+    const int tl = n_tiles - 1;
+    const int piece = wave >> 1;           // K, V of stage tl+1, then K, V of stage tl+2
+    const int stage = (tl + 1 + (piece >> 1)) % C::NST;
+    TT_LDS uint8_t* const wb = lsm + (piece & 1) * C::VREG + stage * C::TILE + (wave & 1) * (C::TILE / 2);
+    typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const half4 hv = {static_cast<_Float16>(acc[dt][4 * j] * sc), static_cast<_Float16>(acc[dt][4 * j + 1] * sc),
-                        static_cast<_Float16>(acc[dt][4 * j + 2] * sc), static_cast<_Float16>(acc[dt][4 * j + 3] * sc)};
-      *reinterpret_cast<uint2*>(dst + dt * 32 + 8 * j + 4 * half) = __builtin_bit_cast(uint2, hv);
+      for (int j = 0; j < 4; ++j) {
+        const half4 hv = {static_cast<_Float16>(acc[dt][4 * j] * sc), static_cast<_Float16>(acc[dt][4 * j + 1] * sc),
+                          static_cast<_Float16>(acc[dt][4 * j + 2] * sc), static_cast<_Float16>(acc[dt][4 * j + 3] * sc)};
+        const int c = dt * 4 + j;
+        *reinterpret_cast<TT_LDS u32x2*>(wb + l32 * (D * 2) + ((c ^ (l32 & (RB16 - 1))) * 16) + half * 8) =
+            __builtin_bit_cast(u32x2, hv);
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint16_t* const dst = static_cast<uint16_t*>(p.part_acc) + (u * C::ROWS + wave * 32) * D;
+#pragma unroll
+    for (int i = 0; i < 32 * RB16 / 64; ++i) {
+      const int idx = i * 64 + lane;
+      const int r = idx / RB16, c = idx % RB16;
+      const u32x4 v = *reinterpret_cast<const TT_LDS u32x4*>(wb + r * (D * 2) + ((c ^ (r & (RB16 - 1))) * 16));
+      if (un.rb * C::ROWS + wave * 32 + r < p.R)
+        *reinterpret_cast<u32x4*>(dst + r * D + c * 8) = v;
     }
+  }
 }
 
 // ------------------------------------------------------------------ fp32
