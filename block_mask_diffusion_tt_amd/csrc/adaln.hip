@@ -33,116 +33,210 @@ __global__ void timestep_embed_kernel(int B, const float* t, const int32_t* n_ma
   emb[static_cast<int64_t>(b) * kEmb + kEmb / 2 + i] = static_cast<float>(sn);
 }
 
-// u = SiLU(emb) @ W for a tile of kRows sequences x 128 columns per
-// workgroup: 256 threads = 8 k-slices x 32 column quads.  Each thread owns 4
-// adjacent columns for the tile's rows and 32 values of k; its 32 loads of W
-// (8 bytes each) are issued before any arithmetic.  The 8 k-slices are summed
-// in LDS in a fixed order (deterministic), then the epilogue adds the bias and
-// writes every layer's copy with its table row.
-constexpr int kRows = 8;   // 16 rows halve the W re-reads but their LDS allows one
-                           // workgroup per CU: twice as slow, measured
-constexpr int kCols = 128;
-constexpr int kSlices = 8;
-constexpr int kPerSlice = kEmb / kSlices;
+// u = SiLU(emb) W (+ bias) on the matrix cores (v_mfma_f32_32x32x16_bf16).
+// W is bf16; each fp32 value x of SiLU(emb) is split exactly into three
+// bf16 parts, x = hi + mid + lo (hi the top 8 significant bits of x, mid the
+// top 8 of x - hi, lo the at most 8 bits left), so every product of the
+// three bf16 matrix products is exact and only the fp32 accumulation rounds,
+// as in a fp32 dot product.
+//   Workgroup = 8 waves over a tile of 32 sequences x 128 columns: wave
+// (nt, kh) multiplies the 32 columns of n-tile nt over the 128 values of k in
+// half kh, and the two halves are summed through LDS in a fixed order.  Every
+// workgroup computes SiLU for its rows itself, so the tile is wide in
+// columns (fewer workgroups repeat that work).  The 512 threads copy the
+// tile's W slab (256 x 128 bf16) into LDS and compute the split SiLU values
+// of its 32 rows into LDS once; the B operands (W, column per lane) come out
+// of the slab through the transposing ds_read_b64_tr_b16.  The time goes to
+// fetching the W slab and writing the n_layers copies, not to arithmetic, so
+// every load of the kernel is issued before its first wait.
+// The epilogue adds the bias and writes every layer's copy with its table
+// row: wave (nt, kh) writes the layers l with l % 2 == kh, 32 consecutive
+// columns (128 bytes) per row and store.
+//   Operand layout: lane l holds row (A) or column (B) l % 32 and 8 values of
+// k; element e of lane l is k = 16 m + 4 (l / 32) + (e % 4) + 8 (e / 4) for
+// k-step m, on both sides.  The accumulator holds column l % 32 and rows
+// 8 (r / 4) + 4 (l / 32) + r % 4, r = 0..15.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void adaln_kernel(int B, int width, int n_layers,
+constexpr int kTileB = 32;                // sequences per workgroup
+constexpr int kTileN = 128;               // columns per workgroup (4 n-tiles)
+constexpr int kSplits = 3;                // bf16 parts of each SiLU value
+constexpr int kEPitch = kEmb + 8;         // bf16 per LDS row of a part (16 bytes of
+                                          // padding spread 16 rows over all banks)
+constexpr int kKSteps = kEmb / 16 / 2;    // k-steps per wave (one half of k)
+constexpr int kPreLayers = 8;             // table values loaded up front per lane
+                                          // (layers kh, kh + 2, ...: up to 16 layers)
+
+// Position of k within its 16-block in the SiLU rows: groups of 4 in the
+// order 0, 2, 1, 3, so that a lane's 8 values are 16 contiguous bytes.
+__device__ __forceinline__ int epos(int k) {
+  const int g = (k >> 2) & 3;
+  return (k & ~15) + 4 * ((g & 1) * 2 + (g >> 1)) + (k & 3);
+}
+
+// Byte offset of W slab element (k, c), c < 128: rows of 256 bytes, the
+// 64-byte chunk of each n-tile XOR-swizzled with k % 4 so that the 8 rows
+// of one transposing read hit all banks.
+__device__ __forceinline__ int wpos(int k, int c) {
+  return k * (kTileN * 2) + ((((c >> 5) ^ k) & 3) << 6) + (c & 31) * 2;
+}
+
+__global__ __launch_bounds__(512) void adaln_kernel(int B, int width, int n_layers,
                                                     const float* __restrict__ emb,
                                                     const uint16_t* __restrict__ w,
                                                     const float* __restrict__ bias,
                                                     const float* __restrict__ table,
                                                     float* __restrict__ ada) {
-  __shared__ float s_e[kRows][kEmb];
-  __shared__ float s_part[kSlices][kRows][kCols + 4];
+  __shared__ __attribute__((aligned(16))) uint16_t s_e[kSplits][kTileB][kEPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t s_w[kEmb * kTileN * 2];
+  __shared__ float s_red[4][2][16][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform in the wave
+  const int nt = wave & 3, kh = wave >> 2;
+  const int l32 = lane & 31, half = lane >> 5, grp = lane >> 4, li = lane & 15;
   const int N = 3 * width;
-  const int n0 = blockIdx.x * kCols;
-  const int b0 = blockIdx.y * kRows;
-  const int nb = min(kRows, B - b0);
-  const int slice = threadIdx.x >> 5, cq = threadIdx.x & 31;
-  const int n = n0 + 4 * cq;
-  uint2 wv[kPerSlice];
-  if (n < N) {   // width is a multiple of 4, so a quad never straddles N
-    const uint16_t* wp = w + static_cast<int64_t>(slice * kPerSlice) * N + n;
+  const int b0 = blockIdx.y * kTileB;
+  const int n0 = blockIdx.x * kTileN;
+
+  // All loads are issued up front and without branches (out-of-range rows,
+  // columns and layers read a valid element that is then replaced by zero),
+  // so that the compiler's waits can count them in order: the SiLU work
+  // waits for the embedding rows only, while W, the bias and the table rows
+  // are still in flight, and the kernel waits for memory once.
+  //   The tile's embedding rows: thread t takes row t / 16 and the 4-value
+  // groups k = 64 i + 4 (t % 16).
+  const int er_row = tid >> 4, er_q = tid & 15;
+  const bool rv = b0 + er_row < B;
+  float x[kEmb / 64][4];
+  {
+    const float* er = emb + static_cast<int64_t>(rv ? b0 + er_row : 0) * kEmb + 4 * er_q;
 #pragma unroll
-    for (int kk = 0; kk < kPerSlice; ++kk)
-      wv[kk] = *reinterpret_cast<const uint2*>(wp + static_cast<int64_t>(kk) * N);
-  } else {
+    for (int i = 0; i < kEmb / 64; ++i)
 #pragma unroll
-    for (int kk = 0; kk < kPerSlice; ++kk) wv[kk] = make_uint2(0, 0);
+      for (int j = 0; j < 4; ++j) x[i][j] = er[64 * i + j];
   }
-  // SiLU of the tile's embeddings into LDS: every load issued before the
-  // first use (one round trip)
-  constexpr int kEPer = kRows * kEmb / 256;
-  float ev[kEPer];
+
+  // W slab: 8-byte pieces (4 columns; w is 8-byte aligned and N a multiple
+  // of 4), 16 rows per pass
+  const int wc = 4 * (tid & 31), wr = tid >> 5;
+  const bool cv = n0 + wc < N;
+  uint2 wv[kEmb * kTileN / 4 / 512];
+  {
+    const uint16_t* const wp = w + static_cast<int64_t>(wr) * N + (cv ? n0 + wc : 0);
 #pragma unroll
-  for (int i = 0; i < kEPer; ++i) {
-    const int idx = threadIdx.x + 256 * i;
-    const int r = idx / kEmb, k = idx % kEmb;
-    ev[i] = r < nb ? emb[static_cast<int64_t>(b0 + r) * kEmb + k] : 0.f;
+    for (int i = 0; i < kEmb * kTileN / 4 / 512; ++i)
+      wv[i] = *reinterpret_cast<const uint2*>(wp + static_cast<int64_t>(16 * i) * N);
+  }
+
+  // what the epilogue adds: the bias and the table rows of this wave's
+  // layers kh, kh + 2, ... (a missing vector reads emb[0])
+  const int n = n0 + 32 * nt + l32;   // this lane's column
+  const bool ncol = n < N;
+  const int which = ncol ? n / width : 0;   // shift, scale or gate
+  const int c = ncol ? n - which * width : 0;
+  float bv = (bias ? bias : emb)[bias ? c + which * width : 0];
+  float tv[kPreLayers];
+#pragma unroll
+  for (int p = 0; p < kPreLayers; ++p) {
+    const int l = min(kh + 2 * p, n_layers - 1);
+    tv[p] = (table ? table : emb)[table ? (static_cast<int64_t>(l) * 3 + which) * width + c : 0];
+  }
+
+  // SiLU of the tile's rows, split into three bf16 parts, into LDS
+  {
+    const int r = er_row, q = er_q;
+#pragma unroll
+    for (int i = 0; i < kEmb / 64; ++i) {
+      uint32_t part[kSplits][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // hardware exp2 and reciprocal: a few ulp, far inside the fp32 sum's error
+        const float v = rv ? x[i][j] : 0.f;
+        const float s = v * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(v * -1.44269504f));
+        const uint32_t h = __float_as_uint(s) & 0xffff0000u;
+        const float r1 = s - __uint_as_float(h);
+        const uint32_t m = __float_as_uint(r1) & 0xffff0000u;
+        const float r2 = r1 - __uint_as_float(m);   // at most 8 significant bits
+        part[0][j] = h;
+        part[1][j] = m;
+        part[2][j] = __float_as_uint(r2);
+      }
+      const int pos = epos(64 * i + 4 * q);
+#pragma unroll
+      for (int sp = 0; sp < kSplits; ++sp) {
+        const u32x2 pk = {__builtin_amdgcn_perm(part[sp][1], part[sp][0], 0x07060302u),
+                          __builtin_amdgcn_perm(part[sp][3], part[sp][2], 0x07060302u)};
+        *reinterpret_cast<u32x2*>(&s_e[sp][r][pos]) = pk;
+      }
+    }
   }
 #pragma unroll
-  for (int i = 0; i < kEPer; ++i) {
-    const int idx = threadIdx.x + 256 * i;
-    s_e[idx / kEmb][idx % kEmb] = ev[i] / (1.f + expf(-ev[i]));
+  for (int i = 0; i < kEmb * kTileN / 4 / 512; ++i) {
+    const u32x2 v = {cv ? wv[i].x : 0u, cv ? wv[i].y : 0u};
+    *reinterpret_cast<u32x2*>(&s_w[wpos(wr + 16 * i, wc)]) = v;
   }
   __syncthreads();
-  float acc[kRows][4];
+
+  // three accumulators (one per part): independent chains of 8 products
+  f32x16 acc[kSplits];
 #pragma unroll
-  for (int r = 0; r < kRows; ++r)
+  for (int sp = 0; sp < kSplits; ++sp)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[r][j] = 0.f;
+    for (int i = 0; i < 16; ++i) acc[sp][i] = 0.f;
+  // this lane's transposing reads: rows 16 m + 4 half + li / 4 (+ 8), columns
+  // 32 nt + 16 (grp & 1) + 4 (li & 3); lane j of each 16-lane group receives
+  // column j of the 4 rows
+  const int wcol = 32 * nt + 16 * (grp & 1) + 4 * (li & 3);
+  typedef __attribute__((address_space(3))) uint8_t LdsU8;
+  typedef __attribute__((address_space(3))) v4i16 LdsV4;
+  LdsU8* const lw = (LdsU8*)(s_w);   // address-space cast
 #pragma unroll
-  for (int kk = 0; kk < kPerSlice; kk += 4) {
-    float wf[4][4];
+  for (int ks = 0; ks < kKSteps; ++ks) {
+    const int m = kh * kKSteps + ks;
+    const int k = 16 * m + 4 * half + (li >> 2);
+    const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<LdsV4*>(lw + wpos(k, wcol)));
+    const v4i16 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<LdsV4*>(lw + wpos(k + 8, wcol)));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 wb = {x1[0], x1[1], x1[2], x1[3], x2[0], x2[1], x2[2], x2[3]};
+    const bf16x8 bop = __builtin_bit_cast(bf16x8, wb);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      wf[q][0] = __uint_as_float(wv[kk + q].x << 16);
-      wf[q][1] = __uint_as_float(wv[kk + q].x & 0xffff0000u);
-      wf[q][2] = __uint_as_float(wv[kk + q].y << 16);
-      wf[q][3] = __uint_as_float(wv[kk + q].y & 0xffff0000u);
-    }
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      const float4 e = *reinterpret_cast<const float4*>(&s_e[r][slice * kPerSlice + kk]);
-      const float ev[4] = {e.x, e.y, e.z, e.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[r][j] = fmaf(ev[q], wf[q][j], acc[r][j]);
+    for (int sp = 0; sp < kSplits; ++sp) {
+      const u32x4 av = *reinterpret_cast<const u32x4*>(&s_e[sp][l32][16 * m + 8 * half]);
+      acc[sp] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), bop,
+                                                        acc[sp], 0, 0, 0);
     }
   }
 #pragma unroll
-  for (int r = 0; r < kRows; ++r)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s_part[slice][r][4 * cq + j] = acc[r][j];
+  for (int i = 0; i < 16; ++i) s_red[nt][kh][i][lane] = (acc[2][i] + acc[1][i]) + acc[0][i];
   __syncthreads();
-  // epilogue: one 4-column quad of one row per thread and pass (8 rows x 32
-  // quads per pass); width is a multiple of 4, so a quad never straddles
-  // shift/scale/gate
-  for (int r = threadIdx.x >> 5; r < kRows; r += 256 / 32) {
-    const int q = threadIdx.x & 31;
-    const int col = n0 + 4 * q;
-    if (r < nb && col < N) {
-      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (!ncol) return;
+  if (!bias) bv = 0.f;
+  float u[16];
 #pragma unroll
-      for (int sl = 0; sl < kSlices; ++sl) {
-        const float4 v = *reinterpret_cast<const float4*>(&s_part[sl][r][4 * q]);
-        u.x += v.x; u.y += v.y; u.z += v.z; u.w += v.w;
-      }
-      if (bias) {
-        const float4 bv = *reinterpret_cast<const float4*>(bias + col);
-        u.x += bv.x; u.y += bv.y; u.z += bv.z; u.w += bv.w;
-      }
-      const int j = col / width, cc = col % width;
-      for (int l = 0; l < n_layers; ++l) {
-        float4 o = u;
-        if (table) {
-          const float4 tv = *reinterpret_cast<const float4*>(table + (static_cast<int64_t>(l) * 3 + j) * width + cc);
-          o.x += tv.x; o.y += tv.y; o.z += tv.z; o.w += tv.w;
-        }
-        *reinterpret_cast<float4*>(ada + ((static_cast<int64_t>(l) * 3 + j) * B + b0 + r) * width + cc) = o;
-      }
+  for (int i = 0; i < 16; ++i) u[i] = (s_red[nt][0][i][lane] + s_red[nt][1][i][lane]) + bv;
+  const int nrows = min(kTileB, B - b0) - 4 * half;   // rows left from this lane's first
+  float* const base = ada + (static_cast<int64_t>(which) * B + b0 + 4 * half) * width + c;
+  const int64_t layer = static_cast<int64_t>(3) * B * width;
+  auto store_layer = [&](int l, float t) {
+    float* const dst = base + l * layer;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      // row offset, the same in every lane (kept scalar: a 32-bit scalar
+      // product per row instead of a 64-bit vector one per row and lane)
+      const int rb = 8 * (i >> 2) + (i & 3);
+      const int off = __builtin_amdgcn_readfirstlane(rb * width);
+      if (rb < nrows) dst[off] = u[i] + t;
     }
-  }
+  };
+#pragma unroll
+  for (int p = 0; p < kPreLayers; ++p)
+    if (kh + 2 * p < n_layers) store_layer(kh + 2 * p, table ? tv[p] : 0.f);
+  for (int l = kh + 2 * kPreLayers; l < n_layers; l += 2)
+    store_layer(l, table ? table[(static_cast<int64_t>(l) * 3 + which) * width + c] : 0.f);
 }
 
 __global__ void active_kernel(int B, const int32_t* n_masked, uint8_t* active, int32_t* total) {
@@ -190,8 +284,8 @@ hipError_t launch_adaln_single(int B, int width, int n_layers, const float* emb,
                                const float* bias, const float* table, float* ada,
                                hipStream_t st) {
   const int N = 3 * width;
-  const dim3 grid(static_cast<unsigned>(ceil_div(N, kCols)), static_cast<unsigned>(ceil_div(B, kRows)));
-  hipLaunchKernelGGL(adaln_kernel, grid, dim3(256), 0, st, B, width, n_layers, emb,
+  const dim3 grid(static_cast<unsigned>(ceil_div(N, kTileN)), static_cast<unsigned>(ceil_div(B, kTileB)));
+  hipLaunchKernelGGL(adaln_kernel, grid, dim3(512), 0, st, B, width, n_layers, emb,
                      static_cast<const uint16_t*>(w), bias, table, ada);
   return hipGetLastError();
 }

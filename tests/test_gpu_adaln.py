@@ -39,3 +39,23 @@ def test_adaln_single(B, width, n_layers):
     torch.cuda.synchronize()
     ref0 = oracle.adaln_single(np64(emb), np64(w), np.zeros(3 * width), np.zeros((n_layers, 3, width)))
     np.testing.assert_allclose(np64(ada), ref0, rtol=1e-5, atol=2e-6)
+
+
+@pytest.mark.parametrize("B,width,n_layers", [(33, 260, 17), (2, 4, 1), (64, 4096, 6)])
+def test_adaln_single_edges(B, width, n_layers):
+    """Ragged tiles (33 sequences, 780 columns), a width that is not a
+    multiple of 8, more layers than the kernel preloads table rows for, one
+    layer, and an embedding that is 4-byte but not 16-byte aligned (a view one
+    float into a larger buffer, which the interface allows)."""
+    say("adaln_single edges", B, width, n_layers)
+    buf = synth.normal((B * 256 + 1,), 1.0, 11, torch.float32, DEV)
+    emb = buf[1:].view(B, 256)
+    assert emb.data_ptr() % 16 == 4
+    w = synth.normal((256, 3 * width), 0.05, 12, torch.bfloat16, DEV)
+    bias = synth.normal((3 * width,), 0.1, 13, torch.float32, DEV)
+    table = synth.normal((n_layers, 3, width), 0.1, 14, torch.float32, DEV)
+    ada = torch.full((n_layers, 3, B, width), 7.0, dtype=torch.float32, device=DEV)
+    tt.adaln_single(B, width, n_layers, emb, w, bias, table, ada)
+    torch.cuda.synchronize()
+    ref = oracle.adaln_single(np64(emb), np64(w), np64(bias), np64(table))
+    np.testing.assert_allclose(np64(ada), ref, rtol=1e-5, atol=2e-6)
