@@ -164,6 +164,38 @@ def calibration_copy(args):
     del src, dst
 
 
+def reference_streams():
+    """HBM rates of plain streams by another implementation on the same GPU in
+    the same run (torch's own kernels over 2 GiB, median of 10 after 3
+    warm-up calls): a read-only reduction (bytes read) and a copy (bytes
+    read + written).  Context for roofline.frac, which is taken against the
+    published peak."""
+    import numpy as np
+    import torch
+    x = torch.ones((1 << 30,), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    out = {}
+    for name, fn, nbytes in (("torch_sum_read_gbps", lambda: x.sum(dtype=torch.float32), 2 << 30),
+                             ("torch_copy_gbps", lambda: y.copy_(x), 4 << 30)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(10):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        out[name] = round(nbytes / (float(np.median(ts)) * 1e-3) / 1e9, 1)
+    del x, y
+    torch.cuda.empty_cache()
+    out["what"] = "2 GiB bf16: sum to fp32 (read), copy (read + write); median of 10"
+    return out
+
+
 def workload(name):
     import synth
     extra = {}
@@ -368,6 +400,7 @@ def main():
         f3_us = (us_ln, us_qkv, us_o, us_sub)
         return us_ada, us_sample, us_unmask, us_ctx, us_adv, loop, gen, us_mamba, us_mamba_ctx, mb, f3_us
     rows_data = None if args.no_rows else collect_rows()
+    streams = None if args.no_rows else reference_streams()
     ms = t0.elapsed_time(t1) / args.steps
     bounds = step_events + [t1]
     step_ms = [a.elapsed_time(b) for a, b in zip(bounds[:-1], bounds[1:])]
@@ -406,6 +439,8 @@ def main():
                      "bytes_per_launch": per_launch, "mean_launch_ms": round(attn_avg, 4),
                      "launch_ms_p10_p50_p90": pct(attn_ms)},
     }
+    if streams is not None:
+        result["roofline"]["reference_streams"] = streams
     # algorithmic bytes of the other rows: adaLN reads W, bias and the table
     # and writes every layer's vectors; unmasking reads the masked rows'
     # logits once (the state arrays are a few KB)
@@ -458,7 +493,7 @@ def main():
         }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs, kc, vc, qb, kb, vb, ada,
-                                              logits, start)
+                                              logits, start, t_step, emb, ada_w, ada_b, ada_t)
     print(json.dumps(result), flush=True)
 
 
@@ -813,11 +848,13 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(w, n_seq, kc, vc, qb, kb, vb, ada, logits, start):
-    """The fp64 oracle on the host cores: attention of n_seq sequences over all
-    layers plus their unmasking pass, on D2H copies of the same inputs, scaled
-    linearly (in context tokens for attention, in rows for unmasking) to the
-    whole step."""
+def cpu_baseline(w, n_seq, kc, vc, qb, kb, vb, ada, logits, start, t_step, emb, ada_w, ada_b,
+                 ada_t):
+    """The fp64 oracle on the host cores: the timestep embedding and
+    adaLN-single, attention over all layers and the unmasking pass of n_seq
+    sequences, on D2H copies of the same inputs, scaled linearly (in
+    sequences for adaLN, context tokens for attention, rows for unmasking) to
+    the whole step."""
     import numpy as np
 
     import oracle
@@ -830,6 +867,13 @@ def cpu_baseline(w, n_seq, kc, vc, qb, kb, vb, ada, logits, start):
     B, S, NL = w["B"], w["S"], w["layers"]
     seqs = list(range(min(n_seq, B)))
     st = start.cpu().numpy()
+    n = len(seqs)
+    ada_in = (f64(emb[:n]) if w.get("random_emb") else f64(t_step[:n]), f64(ada_w), f64(ada_b),
+              f64(ada_t))
+    t0 = time.perf_counter()
+    e = ada_in[0] if w.get("random_emb") else oracle.timestep_embedding(ada_in[0])
+    oracle.adaln_single(e, *ada_in[1:])
+    t_ada = time.perf_counter() - t0
     t_attn = 0.0
     for l in range(NL):
         for b in seqs:
@@ -847,14 +891,15 @@ def cpu_baseline(w, n_seq, kc, vc, qb, kb, vb, ada, logits, start):
     t_unmask = time.perf_counter() - t0
     sample_tokens = sum(w["lens"][b] + S for b in seqs)
     all_tokens = sum(L + S for L in w["lens"])
-    t_step = t_attn * all_tokens / sample_tokens + t_unmask * B / len(seqs)
-    return {"value": round(B * S / t_step, 3), "unit": "query-tokens/s", "cores": threads,
+    t_total = (t_ada * B / n + t_attn * all_tokens / sample_tokens + t_unmask * B / n)
+    return {"value": round(B * S / t_total, 3), "unit": "query-tokens/s", "cores": threads,
             "kind": "oracle", "host_cpu_count": os.cpu_count(), "host_cpu_model": cpu_model(),
-            "sample": (f"{len(seqs)} of {B} sequences x {NL} layers attention + their unmasking "
-                       f"rows (fp64 NumPy, {t_attn + t_unmask:.1f} s measured: attention "
+            "sample": (f"{n} of {B} sequences: timestep embedding + adaLN-single, {NL} layers "
+                       "attention and their unmasking rows (fp64 NumPy, "
+                       f"{t_ada + t_attn + t_unmask:.1f} s measured: adaLN {t_ada:.2f} s, attention "
                        f"{t_attn:.1f} s on {threads} BLAS threads, unmasking {t_unmask:.1f} s "
-                       "single-threaded), scaled linearly in context tokens and rows to the full "
-                       "step")}
+                       "single-threaded), scaled linearly in sequences, context tokens and rows "
+                       "to the full step")}
 
 
 if __name__ == "__main__":
