@@ -832,7 +832,9 @@ def sweep_main(args):
         kb = [synth.normal((B, S, Hkv, d), 1.0, sd + 40 + l, bf, dev) for l in range(NL)]
         vb = [synth.normal((B, S, Hkv, d), 1.0, sd + 50 + l, bf, dev) for l in range(NL)]
         lg = synth.normal((B, S, V), 8.5, sd + 70, bf, dev)
-        result["cpu_baseline"] = cpu_baseline(w, 1, kc, vc, qb, kb, vb, ada, lg, start)
+        result["cpu_baseline"] = cpu_baseline(w, 1, kc, vc, qb, kb, vb, ada, lg, start,
+                                              torch.ones((B,), dtype=torch.float32, device=dev),
+                                              emb, ada_w, ada_b, ada_t)
     print(json.dumps(result), flush=True)
 
 
