@@ -48,13 +48,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kTK = 64;          // keys per LDS tile
-constexpr int kKPad = 8;         // bf16 padding of an LDS K row
-constexpr int kVPad = 4;         // bf16 padding of an LDS V^T row
 constexpr int kMaxWaves = 8;     // bf16 workgroups: up to 8 waves of 32 rows
 constexpr int kRowsF32 = 64;     // rows per fp32 workgroup (1 wave, 1 row per lane)
 constexpr int kMinChunk = 256;   // fewest context keys per unit (multiple of kTK): below
                                  // that, the fixed cost of a unit and of its partial dominate
-constexpr float kRescaleTh = 8.f;
 constexpr int kModHeads = 16;    // largest query-head group whose adaLN vectors are staged in LDS
 template <int D>
 constexpr int kModStride = D + 4;   // floats per staged head (padded)
@@ -87,10 +84,6 @@ __device__ __forceinline__ int units_of(int L, int chunk, int NC) {
   int n = (L + chunk - 1) / chunk;
   n = n < 1 ? 1 : n;
   return n > NC ? NC : n;
-}
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
-  return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }
 
 // Logical unit of workgroup i (units are numbered (b, g, c, rb), row block
@@ -168,19 +161,14 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// 16-byte global -> LDS copy through the direct path: lane i writes LDS bytes
-// [lds + 16 i, lds + 16 i + 16).  Written in asm because the compiler would
-// otherwise wait for every such copy in flight before any LDS read (it cannot
-// tell the pipeline stages apart); the stage waits below are explicit.  The
-// instruction has no register result.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(lds) : "memory");
-}
-
-// The same copy from a wave-uniform base plus a per-lane byte offset (the
-// SGPR-base form: no per-copy address arithmetic), marked non-temporal: the
-// context K/V is read once per layer, so the caches need not keep it.
+// 16-byte global -> LDS copy through the direct path, from a wave-uniform
+// base plus a per-lane byte offset (the SGPR-base form: no per-copy address
+// arithmetic): lane i writes LDS bytes [lds + 16 i, lds + 16 i + 16).  Written
+// in asm because the compiler would otherwise wait for every such copy in
+// flight before any LDS read (it cannot tell the pipeline stages apart); the
+// stage waits below are explicit.  The instruction has no register result.
+// Marked non-temporal: the context K/V is read once per layer, so the caches
+// need not keep it.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                :: "v"(off), "s"(base), "s"(lds) : "memory");
@@ -204,24 +192,6 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-
-// e[r0..r0+7] rounded to bf16 (round to nearest even), packed in order
-__device__ __forceinline__ bf16x8 pack_bf16(const float (&e)[16], int r0) {
-  uint32_t pk[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16x2 pr = {static_cast<__bf16>(e[r0 + 2 * i]), static_cast<__bf16>(e[r0 + 2 * i + 1])};
-    pk[i] = __builtin_bit_cast(uint32_t, pr);
-  }
-  return __builtin_bit_cast(bf16x8, make_uint4(pk[0], pk[1], pk[2], pk[3]));
-}
-
-// Instruction interleaving requests for the machine scheduler: groups of
-// `n` instructions of one class, in the order requested (class masks of
-// the scheduler: 0x8 matrix products, 0x402 vector ALU incl. transcendental,
-// 0x100 LDS reads).
-constexpr int kSchedMfma = 0x8, kSchedValu = 0x402, kSchedLdsRead = 0x100;
-#define TT_SCHED_GROUP(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
 
 // Keeps a value's computation before this point: an empty asm that reads and
 // "writes" the register, so the compiler cannot sink the arithmetic that
@@ -699,7 +669,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bf16_kernel(KParams p) {
         pn[0] = pack(sn, 0);
         // kept here: the rare branch below redefines pn, and the compiler
         // would otherwise sink the packs to the next step's first products
-        asm volatile("" : "+v"(pn[0]));
+        TT_PIN(pn[0]);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -709,7 +679,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attn_bf16_kernel(KParams p) {
       else rs0 += sn[r];
     });
     pn[1] = pack(sn, 8);
-    asm volatile("" : "+v"(pn[1]));
+    TT_PIN(pn[1]);
     float esum = rs0 + rs1;
     if (!EDGE || h + 1 < nh) {
       if (__builtin_expect(__any(esum > 256.f), 0)) raise_mu(h + 1, sn, s2, pn, esum);
@@ -951,13 +921,23 @@ struct TypeTag { using type = T; };
 template <int D>
 constexpr int merge_rows_per_wg() { return 256 / (D / (4 * kMergeQuads)); }
 
-// NB: chunk partials loaded together (2, 4 or 8: the smallest that covers
-// the plan's chunks, 8 beyond).
+// NB: chunk partials loaded together (2, 4, 8 or 16: the smallest that
+// covers the plan's chunks, 16 beyond).
+//   kMany (NB = 16, plans of more than 8 chunks: few rows, many partials per
+// row, a latency-bound merge): the gate and residual loads go out before the
+// chunks are combined, and the chunk loads carry no branches (chunks past n
+// read chunk n - 1 again and are dropped by selection; a missing gate or
+// residual reads a valid stand-in row that is ignored), so the merge waits
+// for memory once instead of three times (one sequence of 4096 tokens, 16
+// chunks per KV head: 8.7 -> 5.6 us).  With few chunks the merge is
+// bandwidth-bound and keeps its loads as they are (the same change there
+// cost 0.5 us at 64 x 8192 tokens).
 template <typename OutT, int D, int NB>
 __global__ __launch_bounds__(256) void merge_kernel(MParams p) {
   constexpr int CPT = 4 * kMergeQuads;   // channels per thread
   constexpr int Q = kMergeQuads;         // 16-byte loads per thread per chunk
   constexpr int TPR = D / CPT;           // threads per row
+  constexpr bool kMany = NB >= 16;
   const int grp = blockIdx.y;  // (b, g, rb)
   const int rb = grp % p.RB;
   const int g = (grp / p.RB) % p.Hkv;
@@ -970,6 +950,23 @@ __global__ __launch_bounds__(256) void merge_kernel(MParams p) {
   if (row >= p.R) return;
   const int n = units_of(p.ctx_len[b], p.chunk, p.NC);
   const int64_t u0 = static_cast<int64_t>(grp) * p.NC;
+  float gv[CPT], rv[CPT];
+  if constexpr (kMany) {
+    const int s = row / p.G, h = g * p.G + row % p.G;
+    const int64_t orow = (static_cast<int64_t>(b) * p.S + s) * p.Hq + h;
+    const float* const gp = p.gate ? p.gate + (static_cast<int64_t>(b) * p.Hq + h) * D + c0 : p.part_ml;
+    const OutT* const rp = (p.residual ? static_cast<const OutT*>(p.residual)
+                                       : static_cast<const OutT*>(p.out)) + orow * D + c0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const float4 x = *reinterpret_cast<const float4*>(gp + 4 * q);
+      gv[4 * q] = x.x; gv[4 * q + 1] = x.y; gv[4 * q + 2] = x.z; gv[4 * q + 3] = x.w;
+      float r4[4];
+      load4<OutT>(rp + 4 * q, r4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rv[4 * q + i] = r4[i];
+    }
+  }
   // chunk c contributes 2^(m_c - M) l_c o_c, M the largest m_c; its stored
   // partial is o_c 2^-k_c (fp16 for bf16 output, fp32 for fp32 output).
   // One pass over the chunks, NB at a time (all their loads issued
@@ -983,7 +980,11 @@ __global__ __launch_bounds__(256) void merge_kernel(MParams p) {
     float a[NB][CPT];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      if (cb + j < n) {
+      if constexpr (kMany) {
+        const int64_t base = (u0 + min(cb + j, n - 1)) * p.rows_per_unit + rl;
+        ml[j] = *reinterpret_cast<const float4*>(p.part_ml + base * 4);
+        load_part<OutT, CPT>(p.part_acc, base * D + c0, a[j]);
+      } else if (cb + j < n) {
         const int64_t base = (u0 + cb + j) * p.rows_per_unit + rl;
         ml[j] = *reinterpret_cast<const float4*>(p.part_ml + base * 4);
         load_part<OutT, CPT>(p.part_acc, base * D + c0, a[j]);
@@ -991,6 +992,16 @@ __global__ __launch_bounds__(256) void merge_kernel(MParams p) {
         ml[j] = make_float4(-INFINITY, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int i = 0; i < CPT; ++i) a[j][i] = 0.f;
+      }
+    }
+    if constexpr (kMany) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const bool in = cb + j < n;
+        ml[j].x = in ? ml[j].x : -INFINITY;
+        ml[j].y = in ? ml[j].y : 0.f;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) a[j][i] = in ? a[j][i] : 0.f;
       }
     }
     float Mb = M;
@@ -1020,13 +1031,22 @@ __global__ __launch_bounds__(256) void merge_kernel(MParams p) {
   for (int q = 0; q < Q; ++q) {
     float v[4] = {o[4 * q] * inv, o[4 * q + 1] * inv, o[4 * q + 2] * inv, o[4 * q + 3] * inv};
     if (gp) {
-      const float4 gv = *reinterpret_cast<const float4*>(gp + 4 * q);
-      v[0] *= gv.x; v[1] *= gv.y; v[2] *= gv.z; v[3] *= gv.w;
+      if constexpr (!kMany) {
+        const float4 x = *reinterpret_cast<const float4*>(gp + 4 * q);
+        gv[4 * q] = x.x; gv[4 * q + 1] = x.y; gv[4 * q + 2] = x.z; gv[4 * q + 3] = x.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] *= gv[4 * q + i];
     }
     if (rp) {
-      float r[4];
-      load4<OutT>(rp + 4 * q, r);
-      v[0] += r[0]; v[1] += r[1]; v[2] += r[2]; v[3] += r[3];
+      if constexpr (!kMany) {
+        float r4[4];
+        load4<OutT>(rp + 4 * q, r4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rv[4 * q + i] = r4[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += rv[4 * q + i];
     }
     store4<OutT>(op + 4 * q, v[0], v[1], v[2], v[3]);
   }
@@ -1112,7 +1132,7 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& pl, void* ws, hi
   const dim3 mg(static_cast<unsigned>(ceil_div(pl.rows_per_unit, a.d == 128 ? merge_rows_per_wg<128>()
                                                                          : merge_rows_per_wg<64>())),
                 static_cast<unsigned>(static_cast<int64_t>(a.B) * a.Hkv * pl.row_blocks));
-  const int nb = pl.n_chunks <= 2 ? 2 : pl.n_chunks <= 4 ? 4 : 8;
+  const int nb = pl.n_chunks <= 2 ? 2 : pl.n_chunks <= 4 ? 4 : pl.n_chunks <= 8 ? 8 : 16;
   auto merge = [&](auto out_c, auto d_c, auto nb_c) {
     using OutT = typename decltype(out_c)::type;
     hipLaunchKernelGGL((merge_kernel<OutT, decltype(d_c)::value, decltype(nb_c)::value>), mg,
@@ -1121,7 +1141,8 @@ hipError_t launch_block_attn(const AttnArgs& a, const AttnPlan& pl, void* ws, hi
   auto by_nb = [&](auto out_c, auto d_c) {
     if (nb == 2) merge(out_c, d_c, std::integral_constant<int, 2>{});
     else if (nb == 4) merge(out_c, d_c, std::integral_constant<int, 4>{});
-    else merge(out_c, d_c, std::integral_constant<int, 8>{});
+    else if (nb == 8) merge(out_c, d_c, std::integral_constant<int, 8>{});
+    else merge(out_c, d_c, std::integral_constant<int, 16>{});
   };
   auto by_d = [&](auto out_c) {
     if (a.d == 128) by_nb(out_c, std::integral_constant<int, 128>{});
