@@ -927,7 +927,7 @@ constexpr int merge_rows_per_wg() { return 256 / (D / (4 * kMergeQuads)); }
 // row, a latency-bound merge): the gate and residual loads go out before the
 // chunks are combined, and the chunk loads carry no branches (chunks past n
 // read chunk n - 1 again and are dropped by selection; a missing gate or
-// residual reads a valid stand-in row that is ignored), so the merge waits
+// residual reads a valid stand-in that is ignored), so the merge waits
 // for memory once instead of three times (one sequence of 4096 tokens, 16
 // chunks per KV head: 8.7 -> 5.6 us).  With few chunks the merge is
 // bandwidth-bound and keeps its loads as they are (the same change there
@@ -955,8 +955,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MParams p) {
     const int s = row / p.G, h = g * p.G + row % p.G;
     const int64_t orow = (static_cast<int64_t>(b) * p.S + s) * p.Hq + h;
     const float* const gp = p.gate ? p.gate + (static_cast<int64_t>(b) * p.Hq + h) * D + c0 : p.part_ml;
-    const OutT* const rp = (p.residual ? static_cast<const OutT*>(p.residual)
-                                       : static_cast<const OutT*>(p.out)) + orow * D + c0;
+    // stand-ins: the records' first floats, and this row's chunk-0 partial
+    // (same element width as OutT, loaded by this thread anyway)
+    const OutT* const rp = p.residual ? static_cast<const OutT*>(p.residual) + orow * D + c0
+                                      : static_cast<const OutT*>(p.part_acc) + (u0 * p.rows_per_unit + rl) * D + c0;
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
       const float4 x = *reinterpret_cast<const float4*>(gp + 4 * q);
