@@ -484,6 +484,7 @@ __global__ __launch_bounds__(kThreads) void rowsample_kernel(
 // decision boundary) are reads of a whole row by that one workgroup, so it is
 // a large one: 16 waves keep 64 KB of the row in flight.
 constexpr int kDecideThreads = 1024;
+constexpr int kPartBatch = 8;   // slice records loaded together per row
 
 // fp64 rescoring of one row's candidates (those within cand_margin of the
 // row maximum m): the token of the largest l + tau G in fp64, lowest token on
@@ -646,11 +647,30 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(
     s_msk[tid] = msk;
     s_checked[tid] = 0;
     s_rescore[tid] = 0;
+    // The slice records are loaded kPartBatch at a time (the loads of a
+    // batch in flight together; indices past the last slice re-read it and
+    // are ignored) and folded in slice order as one by one: one memory round
+    // trip per batch instead of one per slice (32 slices per row for a
+    // single sequence).
     if (msk && !SAMPLE) {
       const RowPart* p = static_cast<const RowPart*>(parts) + (row0 + tid) * splits;
-      float m = p[0].m, z = p[0].z;
-      int a = p[0].arg;
-      for (int k = 1; k < splits; ++k) merge(m, z, a, p[k].m, p[k].z, p[k].arg, c);
+      float m = 0.f, z = 0.f;
+      int a = INT_MAX;
+      for (int k0 = 0; k0 < splits; k0 += kPartBatch) {
+        RowPart q[kPartBatch];
+#pragma unroll
+        for (int j = 0; j < kPartBatch; ++j) q[j] = p[min(k0 + j, splits - 1)];
+#pragma unroll
+        for (int j = 0; j < kPartBatch; ++j) {
+          if (k0 + j == 0) {
+            m = q[j].m;
+            z = q[j].z;
+            a = q[j].arg;
+          } else if (k0 + j < splits) {
+            merge(m, z, a, q[j].m, q[j].z, q[j].arg, c);
+          }
+        }
+      }
       s_m[tid] = m;
       s_lx[tid] = m;
       s_pred[tid] = a;
@@ -658,13 +678,35 @@ __global__ __launch_bounds__(kDecideThreads) void decide_kernel(
     } else if (msk) {
       // slices in order: row maximum, Z relative to it, best perturbed score
       const SamplePart* p = static_cast<const SamplePart*>(parts) + (row0 + tid) * splits;
-      float m = p[0].m;
-      for (int k = 1; k < splits; ++k) m = fmaxf(m, p[k].m);
-      float z = 0.f, key = p[0].key, key2 = p[0].key2, lx = p[0].lx;
-      int idx = p[0].idx;
-      for (int k = 0; k < splits; ++k) {
-        z += p[k].z * fast_exp2((p[k].m - m) * c);
-        if (k) merge_best(key, key2, idx, lx, p[k].key, p[k].key2, p[k].idx, p[k].lx);
+      float m = -INFINITY;
+      for (int k0 = 0; k0 < splits; k0 += kPartBatch) {
+        float mk[kPartBatch];
+#pragma unroll
+        for (int j = 0; j < kPartBatch; ++j) mk[j] = p[min(k0 + j, splits - 1)].m;
+#pragma unroll
+        for (int j = 0; j < kPartBatch; ++j)
+          if (k0 + j < splits) m = k0 + j == 0 ? mk[j] : fmaxf(m, mk[j]);
+      }
+      float z = 0.f, key = 0.f, key2 = 0.f, lx = 0.f;
+      int idx = INT_MAX;
+      for (int k0 = 0; k0 < splits; k0 += kPartBatch) {
+        SamplePart q[kPartBatch];
+#pragma unroll
+        for (int j = 0; j < kPartBatch; ++j) q[j] = p[min(k0 + j, splits - 1)];
+#pragma unroll
+        for (int j = 0; j < kPartBatch; ++j) {
+          const int k = k0 + j;
+          if (k >= splits) continue;
+          z += q[j].z * fast_exp2((q[j].m - m) * c);
+          if (k == 0) {
+            key = q[j].key;
+            key2 = q[j].key2;
+            idx = q[j].idx;
+            lx = q[j].lx;
+          } else {
+            merge_best(key, key2, idx, lx, q[j].key, q[j].key2, q[j].idx, q[j].lx);
+          }
+        }
       }
       s_m[tid] = m;
       s_z[tid] = z;
