@@ -103,7 +103,8 @@ __global__ __launch_bounds__(512) void adaln_kernel(int B, int width, int n_laye
   const int n0 = blockIdx.x * kTileN;
 
   // All loads are issued up front and without branches (out-of-range rows,
-  // columns and layers read a valid element that is then replaced by zero),
+  // columns and layers read a valid element whose value is then replaced by
+  // zero or not used),
   // so that the compiler's waits can count them in order: the SiLU work
   // waits for the embedding rows only, while W, the bias and the table rows
   // are still in flight, and the kernel waits for memory once.
