@@ -66,7 +66,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 size_t elt_size(int dtype) { return dtype == TT_BF16 ? 2 : 4; }
 
 // TT_VALIDATE set (and not "0"): check the context arrays on the device
-// before a call's kernels, and wait for the verdict.
+// before a call's kernels, and wait for the outcome.
 bool validate_enabled() {
   const char* v = getenv("TT_VALIDATE");
   return v && v[0] && strcmp(v, "0") != 0;

@@ -151,12 +151,12 @@ hipError_t launch_ctx_advance(int B, int S, const int64_t* ctx_start, const int6
 
 // ---------------------------------------------------------------- TT_VALIDATE
 // Checks the context arrays on the device (csrc/validate.hip) and waits for
-// the verdict: verdict[0] = the first failing sequence or -1, verdict[1] the
+// the outcome: outcome[0] = the first failing sequence or -1, outcome[1] the
 // rule (1 ctx_len < 0, 2 ctx_start < 0, 3 ctx_end below start + len, 4 two
-// reserved regions overlap, verdict[2] = the other sequence), verdict[2..3]
+// reserved regions overlap, outcome[2] = the other sequence), outcome[2..3]
 // the values involved.
 hipError_t validate_ctx(int B, const int64_t* ctx_start, const int32_t* ctx_len,
-                        const int64_t* ctx_end, const uint8_t* active, int64_t verdict[4],
+                        const int64_t* ctx_end, const uint8_t* active, int64_t outcome[4],
                         hipStream_t st);
 
 }  // namespace tt

@@ -10,10 +10,10 @@
 namespace tt {
 namespace {
 
-// The verdict of the last check on this device: the first failing sequence
+// The outcome of the last check on this device: the first failing sequence
 // (-1 if none), the failed rule, two values for the message.  Only device
 // code writes it; the host copies it out through the symbol.
-__device__ int64_t g_verdict[4];
+__device__ int64_t g_outcome[4];
 
 constexpr int kOverlapMaxB = 8192;   // pairwise region check up to this batch
 
@@ -59,23 +59,23 @@ __global__ __launch_bounds__(1024) void validate_ctx_kernel(int B, const int64_t
     int64_t v1 = 0, v2 = 0;
     int rule = 0;
     if (first != INT_MAX) rule = ctx_rule(first, B, ctx_start, ctx_len, ctx_end, active, v1, v2);
-    g_verdict[0] = first == INT_MAX ? -1 : first;
-    g_verdict[1] = rule;
-    g_verdict[2] = v1;
-    g_verdict[3] = v2;
+    g_outcome[0] = first == INT_MAX ? -1 : first;
+    g_outcome[1] = rule;
+    g_outcome[2] = v1;
+    g_outcome[3] = v2;
   }
 }
 
 }  // namespace
 
 hipError_t validate_ctx(int B, const int64_t* ctx_start, const int32_t* ctx_len,
-                        const int64_t* ctx_end, const uint8_t* active, int64_t verdict[4],
+                        const int64_t* ctx_end, const uint8_t* active, int64_t outcome[4],
                         hipStream_t st) {
   hipLaunchKernelGGL(validate_ctx_kernel, dim3(1), dim3(1024), 0, st, B, ctx_start, ctx_len,
                      ctx_end, active);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = hipMemcpyFromSymbolAsync(verdict, HIP_SYMBOL(g_verdict), 4 * sizeof(int64_t), 0,
+  e = hipMemcpyFromSymbolAsync(outcome, HIP_SYMBOL(g_outcome), 4 * sizeof(int64_t), 0,
                                hipMemcpyDeviceToHost, st);
   if (e != hipSuccess) return e;
   return hipStreamSynchronize(st);

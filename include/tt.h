@@ -27,12 +27,12 @@
  *     TT_VALIDATE set to anything but "" or "0", every call that takes the
  *     context arrays (the attention calls, tt_ctx_advance, the denoise and
  *     generation loops, the weighted sublayer) first runs one small kernel
- *     over them and waits for its verdict.  It returns TT_ERR_INVALID_ARG,
+ *     over them and waits for its outcome.  It returns TT_ERR_INVALID_ARG,
  *     naming the first offending sequence, when for an active sequence b
  *     ctx_len[b] < 0, ctx_start[b] < 0, ctx_end[b] < ctx_start[b] +
  *     ctx_len[b], or (with ctx_end, up to 8192 sequences) its reserved
  *     region overlaps another active sequence's; nothing else of the call is
- *     launched then.  Checked calls are synchronous.  The verdict lives in a
+ *     launched then.  Checked calls are synchronous.  The outcome lives in a
  *     small array in each GPU's memory, so two checked calls on one GPU must
  *     not overlap in time.
  *   - No global mutable state besides the thread-local error message (and
