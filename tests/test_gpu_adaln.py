@@ -59,3 +59,33 @@ def test_adaln_single_edges(B, width, n_layers):
     torch.cuda.synchronize()
     ref = oracle.adaln_single(np64(emb), np64(w), np64(bias), np64(table))
     np.testing.assert_allclose(np64(ada), ref, rtol=1e-5, atol=2e-6)
+
+
+def _shapes(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        out.append((int(rng.integers(1, 201)), 4 * int(rng.integers(1, 257)),
+                    int(rng.integers(1, 21)), bool(rng.integers(0, 2)), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("B,width,n_layers,has_bias,has_table", _shapes(2024, 6))
+def test_adaln_single_random_shapes(B, width, n_layers, has_bias, has_table):
+    """Seeded shapes across the kernel's tiling: batches that end mid-tile
+    (32 sequences per tile), widths whose 3 * width columns end mid-tile (128
+    per tile), layer counts on both sides of the 16 whose table rows are
+    loaded up front, and a missing bias or table."""
+    say("adaln_single random", B, width, n_layers, has_bias, has_table)
+    seed = B * 7919 + width * 31 + n_layers
+    emb = synth.normal((B, 256), 1.0, seed, torch.float32, DEV)
+    w = synth.normal((256, 3 * width), 0.05, seed + 1, torch.bfloat16, DEV)
+    bias = synth.normal((3 * width,), 0.1, seed + 2, torch.float32, DEV) if has_bias else None
+    table = synth.normal((n_layers, 3, width), 0.1, seed + 3, torch.float32, DEV) if has_table else None
+    ada = torch.full((n_layers, 3, B, width), 7.0, dtype=torch.float32, device=DEV)
+    tt.adaln_single(B, width, n_layers, emb, w, bias, table, ada)
+    torch.cuda.synchronize()
+    ref = oracle.adaln_single(np64(emb), np64(w),
+                              np64(bias) if has_bias else np.zeros(3 * width),
+                              np64(table) if has_table else np.zeros((n_layers, 3, width)))
+    np.testing.assert_allclose(np64(ada), ref, rtol=1e-5, atol=2e-6)

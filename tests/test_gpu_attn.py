@@ -219,3 +219,26 @@ def test_headline_batch64_ctx8192_sampled():
 def test_context_32768_sampled(S):
     c = attn_case(8, S, 32, 2, 128, [32768] * 8, dtype=BF16, seed=1200 + S)
     _check(c, f"ctx 32768 S={S}", seqs=[0, 7])
+
+
+def _many_chunk_cases(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B = int(rng.integers(1, 4))
+        lens = [int(x) for x in rng.integers(0, 9217, size=B)]
+        lens[int(rng.integers(0, B))] = int(rng.integers(2304, 9217))   # at least 9 chunks
+        out.append((B, int(rng.choice([4, 16])), lens, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("B,S,lens,dtype_f32", _many_chunk_cases(77, 6))
+def test_many_chunk_merge(B, S, lens, dtype_f32):
+    """Plans of more than 8 chunks per KV head (a few sequences, long ragged
+    contexts: 9 to 36 chunks of 256 keys), where the merge folds 16 chunks
+    per batch: sequences with fewer chunks than the batch, several batches,
+    empty contexts, with the adaLN vectors and a residual; bf16 and fp32."""
+    dtype = F32 if dtype_f32 else BF16
+    c = attn_case(B, S, 32, 2, 128, lens, dtype=dtype, seed=sum(lens) + B + S, ada=True,
+                  residual=True)
+    _check(c, f"many chunks B={B} S={S}")
