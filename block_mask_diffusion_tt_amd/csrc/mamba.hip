@@ -18,7 +18,10 @@
 //         + D x_s
 // which needs one multiply-add per state entry and slot (H0 C_s) instead of
 // the recurrence's three, and no state update unless the final state is
-// asked for.  Two kernels:
+// asked for.  Where S <= 16 and 2N = 4P (the bench's N = 128, P = 64) one
+// launch of mamba_scan_kernel does everything, each head also convolving its
+// group's B/C channels and forming G itself (the FUSED form below); else two
+// kernels:
 //   mamba_group_kernel, one workgroup per (sequence, group): the conv + SiLU
 //     outputs of the group's B and C channels, [S][2N] fp32, and
 //     G[s][j] = C_s . B_j, into the workspace -- shared by the group's heads;
@@ -231,14 +234,10 @@ struct ScanRound {
   static __device__ __forceinline__ int rw0(int r0) { return r0 == 0 ? 0 : r0 + KW - 1; }
   static __device__ __forceinline__ int rw1(int r0, int S) { return min(r0 + kSC, S) + KW - 1; }
 
-  static __device__ __forceinline__ void issue(v4f (&bc)[kBC], uint32_t (&w)[kWn], v4f (&gv)[kG],
-                                               const float* bcg, const float* gmg, const T* xbc,
-                                               const T* cst, int C, int h, int S, int Sp, int r0) {
+  // the head's x window rows of the round
+  static __device__ __forceinline__ void issue_x(uint32_t (&w)[kWn], const T* xbc, const T* cst, int C,
+                                                 int h, int S, int r0) {
     const int tid = threadIdx.x;
-    const int nbc = (min(r0 + kSC, S) - r0) * 2 * N / 4;
-#pragma unroll
-    for (int u = 0; u < kBC; ++u)
-      bc[u] = reinterpret_cast<const v4f*>(bcg + r0 * 2 * N)[min(u * NT + tid, nbc - 1)];
     const int w0 = rw0(r0), nw = (rw1(r0, S) - w0) * P;
 #pragma unroll
     for (int u = 0; u < kWn; ++u) {
@@ -249,6 +248,17 @@ struct ScanRound {
                            : xbc + static_cast<int64_t>(t) * C + c;
       w[u] = ld_raw(src);
     }
+  }
+
+  static __device__ __forceinline__ void issue(v4f (&bc)[kBC], uint32_t (&w)[kWn], v4f (&gv)[kG],
+                                               const float* bcg, const float* gmg, const T* xbc,
+                                               const T* cst, int C, int h, int S, int Sp, int r0) {
+    const int tid = threadIdx.x;
+    const int nbc = (min(r0 + kSC, S) - r0) * 2 * N / 4;
+#pragma unroll
+    for (int u = 0; u < kBC; ++u)
+      bc[u] = reinterpret_cast<const v4f*>(bcg + r0 * 2 * N)[min(u * NT + tid, nbc - 1)];
+    issue_x(w, xbc, cst, C, h, S, r0);
     const int ng = kSC * Sp / 4;           // 16 rows of G, each Sp wide
 #pragma unroll
     for (int u = 0; u < kG; ++u)
@@ -259,6 +269,17 @@ struct ScanRound {
   // end writes the last element's value to the last element's place (the
   // same bytes its owner writes).  A conditional store would let the
   // compiler sink each load into its branch, one wait per load.
+  static __device__ __forceinline__ void commit_x(const uint32_t (&w)[kWn], float* s_win, int S, int r0,
+                                                  int XP) {
+    const int tid = threadIdx.x;
+    const int w0 = rw0(r0), nw = (rw1(r0, S) - w0) * P;
+#pragma unroll
+    for (int u = 0; u < kWn; ++u) {
+      const int i = min(u * NT + tid, nw - 1);
+      s_win[(w0 + i / P) * XP + i % P] = raw_f32<T>(w[u]);
+    }
+  }
+
   static __device__ __forceinline__ void commit(const v4f (&bc)[kBC], const uint32_t (&w)[kWn],
                                                 const v4f (&gv)[kG], float* s_b, int c_off,
                                                 float* s_win, float* s_m, int S, int Sp, int r0,
@@ -273,12 +294,7 @@ struct ScanRound {
       const int off = si * BP + cc + (cc >= N ? c_off - N : 0);
       *reinterpret_cast<v4f*>(s_b + off) = bc[u];
     }
-    const int w0 = rw0(r0), nw = (rw1(r0, S) - w0) * P;
-#pragma unroll
-    for (int u = 0; u < kWn; ++u) {
-      const int i = min(u * NT + tid, nw - 1);
-      s_win[(w0 + i / P) * XP + i % P] = raw_f32<T>(w[u]);
-    }
+    commit_x(w, s_win, S, r0, XP);
     const int ng = kSC * Sp / 4;
 #pragma unroll
     for (int u = 0; u < kG; ++u)
@@ -287,9 +303,8 @@ struct ScanRound {
 };
 
 // Per (sequence, head): P/16 waves; wave w owns state rows 16w..16w+15, lane
-// l row p = 16w + l%16 and KS = N/4 entries of it: n in [kg*KS, kg*KS + KS),
-// kg = l/16 (or, in the context tower's form, n = 16 (t/4) + 4 kg + t%4 for
-// its t-th entry).  The outputs of 16 slots at a time are one 16 x 16 fp32 matrix
+// l row p = 16w + l%16 and KS = N/4 entries of it: n = 16 (t/4) + 4 kg + t%4
+// for its t-th entry, kg = l/16.  The outputs of 16 slots at a time are one 16 x 16 fp32 matrix
 // tile per wave, accumulated by v_mfma_f32_16x16x4f32 in two parts:
 //   H0 C_s               -- K = N, taken in the order of the lanes' own
 //                            entries: at step t each lane's A operand is its
@@ -304,15 +319,29 @@ struct ScanRound {
 // CTX: the context tower's form (final SSM state written; its own
 // instantiation, so that the denoiser's form keeps its smaller register
 // allocation)
-template <typename T, int P, int N, int KW, bool CTX>
+// FUSED (S <= 16 and one thread per B/C channel, NT == 2N): the kernel
+// also does the group kernel's part for its own head -- the conv + SiLU of
+// the group's B/C channels from registers, and G = C B^T on the matrix cores,
+// each wave over N/(P/16) state entries, its partial tile summed in LDS --
+// so one launch does the whole layer and the workspace is not used.  The
+// B/C window is read by all H/G heads of the group, which the XCD-aware
+// order below runs on one XCD, so seven of the eight reads hit its L2.
+template <typename T, int P, int N, int KW, bool CTX, bool FUSED>
 __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const float* ws_bc,
                                                           const float* ws_g) {
   constexpr int NT = 4 * P;              // P/16 waves of 64
   constexpr int KS = N / 4;              // state entries per lane
   static_assert(KS % 4 == 0, "16-byte state loads");
+  static_assert(!FUSED || NT == 2 * N, "one thread per B/C channel");
   typedef float f32x4 __attribute__((ext_vector_type(4)));
-  const int b = blockIdx.x / a.H;
-  const int h = blockIdx.x % a.H;
+  // XCD-aware order: workgroups go to the 8 XCDs round-robin, so workgroup
+  // i runs (sequence, head) unit (i % 8) * ceil(n/8) + i / 8 and the heads of
+  // one group (consecutive units) share an XCD and its L2
+  const int n_units = a.B * a.H;
+  const int unit = (blockIdx.x % 8) * ((n_units + 7) / 8) + blockIdx.x / 8;
+  if (unit >= n_units) return;
+  const int b = unit / a.H;
+  const int h = unit % a.H;
   if (a.active && !a.active[b]) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.S, H = a.H, G = a.G;
@@ -325,12 +354,13 @@ __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const fl
   extern __shared__ float lds[];
   float* s_win = lds;                    // [S + W-1][XP]  x inputs
   float* s_x = s_win + (S + W - 1) * XP; // [Sp][XP]       conv outputs of the head's x
-  float* s_b = s_x + Sp * XP;            // [S][BP]        the group's B
-  float* s_c = s_b + S * BP;             // [Sp][BP]       the group's C
+  float* s_b = s_x + Sp * XP;            // [Sp][BP]       the group's B
+  float* s_c = s_b + Sp * BP;            // [Sp][BP]       the group's C
   float* s_dt = s_c + Sp * BP;           // [Sp] dt_s
   float* s_cum = s_dt + Sp;              // [Sp] sum_{k<=s} dt_k A  (log of the decay)
   float* s_dec = s_cum + Sp;             // [Sp] exp(cum_s), 0 past S
   float* s_m = s_dec + Sp;               // [Sp][Sp]  G, then dt_j exp(cum_s - cum_j) G[s][j]
+  float* s_gp = s_m + Sp * Sp;           // FUSED: [P/16][16][16] the waves' partial G tiles
   const T* xbc = static_cast<const T*>(a.xbc) + static_cast<int64_t>(b) * S * C;
   const T* cst = static_cast<const T*>(a.conv_state) + static_cast<int64_t>(b) * C * (W - 1);
   const float* bcg = ws_bc + (static_cast<int64_t>(b) * G + g) * S * 2 * N;
@@ -346,35 +376,75 @@ __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const fl
   using RD = ScanRound<T, P, N, KW, NT>;
   const int pl = lane & 15, kg = lane >> 4;
   const int p = wave * 16 + pl;
-  // the lane's state entries, row p: n = kg KS + t (the denoiser's form), or
-  // n = 16 (t/4) + 4 kg + t%4 (the context tower's: the output layout of the
-  // final state's matrix products below); any order of K serves H0 C^T as
-  // long as C is read in the same one
-  constexpr int kStride = CTX ? 4 : 1;   // distance in n between consecutive float4 of a lane
-  const int64_t sbase = ((static_cast<int64_t>(b) * H + h) * P + p) * N + (CTX ? 4 * kg : kg * KS);
+  // the lane's state entries, row p: n = 16 (t/4) + 4 kg + t%4 (the output
+  // layout of the final state's matrix products below; any order of K
+  // serves H0 C^T as long as C is read in the same one).  Each 16-byte load
+  // of a wave then covers 64 consecutive bytes of each of its 16 rows: 16
+  // cache lines per load instruction, half of each, where runs of KS
+  // entries per lane touched 64 lines a sixteenth at a time (measured 2 us
+  // faster from HBM at the bench shape).
+  constexpr int kStride = 4;             // distance in n between consecutive float4 of a lane
+  const int64_t sbase = ((static_cast<int64_t>(b) * H + h) * P + p) * N + 4 * kg;
   float st[KS];
-  {
-    v4f bc[RD::kBC];
-    uint32_t w[RD::kWn];
-    v4f gv[RD::kG];
-    RD::issue(bc, w, gv, bcg, gmg, xbc, cst, C, h, S, Sp, 0);
-    // a scheduling fence keeps the round's loads ahead of the state's, so
-    // that waiting for the former leaves the latter in flight
-    __builtin_amdgcn_sched_barrier(0);
+  auto load_state = [&]() {
 #pragma unroll
     for (int j = 0; j < KS; j += 4) {
       const float4 v = *reinterpret_cast<const float4*>(a.ssm_state + sbase + kStride * j);
       st[j] = v.x; st[j + 1] = v.y; st[j + 2] = v.z; st[j + 3] = v.w;
     }
-    __builtin_amdgcn_sched_barrier(0);
-    RD::commit(bc, w, gv, s_b, S * BP, s_win, s_m, S, Sp, 0, BP, XP);
-  }
-  for (int r0 = kSC; r0 < S; r0 += kSC) {
-    v4f bc[RD::kBC];
+  };
+  if constexpr (FUSED) {
+    // the thread's B/C channel cb over the window rows (clamped onto the
+    // last row; rows past the window only feed slots past S), its taps, and
+    // the head's x window
+    constexpr int kRows = kSC + KW - 1;
+    const int cb = H * P + (tid < N ? g * N + tid : G * N + g * N + (tid - N));
+    Taps<KW> tb;
+    tb.load(a.conv_w, a.conv_b, cb);
     uint32_t w[RD::kWn];
-    v4f gv[RD::kG];
-    RD::issue(bc, w, gv, bcg, gmg, xbc, cst, C, h, S, Sp, r0);
-    RD::commit(bc, w, gv, s_b, S * BP, s_win, s_m, S, Sp, r0, BP, XP);
+    uint32_t vb[kRows];
+    RD::issue_x(w, xbc, cst, C, h, S, 0);
+#pragma unroll
+    for (int u = 0; u < kRows; ++u) {
+      const int r = min(u, S + KW - 2);
+      const int t = r - (KW - 1);
+      const T* src = t < 0 ? cst + static_cast<int64_t>(cb) * (KW - 1) + r
+                           : xbc + static_cast<int64_t>(t) * C + cb;
+      vb[u] = ld_raw(src);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_state();
+    __builtin_amdgcn_sched_barrier(0);
+    RD::commit_x(w, s_win, S, 0, XP);
+    // conv + SiLU of the channel; slots past S are stored as 0
+    float* dst = tid < N ? s_b + tid : s_c + (tid - N);
+#pragma unroll
+    for (int si = 0; si < kSC; ++si) {
+      float acc = tb.bias;
+#pragma unroll
+      for (int j = 0; j < KW; ++j) acc = fmaf(tb.w[j], raw_f32<T>(vb[si + j]), acc);
+      dst[si * BP] = si < S ? silu(acc) : 0.f;
+    }
+  } else {
+    {
+      v4f bc[RD::kBC];
+      uint32_t w[RD::kWn];
+      v4f gv[RD::kG];
+      RD::issue(bc, w, gv, bcg, gmg, xbc, cst, C, h, S, Sp, 0);
+      // a scheduling fence keeps the round's loads ahead of the state's, so
+      // that waiting for the former leaves the latter in flight
+      __builtin_amdgcn_sched_barrier(0);
+      load_state();
+      __builtin_amdgcn_sched_barrier(0);
+      RD::commit(bc, w, gv, s_b, Sp * BP, s_win, s_m, S, Sp, 0, BP, XP);
+    }
+    for (int r0 = kSC; r0 < S; r0 += kSC) {
+      v4f bc[RD::kBC];
+      uint32_t w[RD::kWn];
+      v4f gv[RD::kG];
+      RD::issue(bc, w, gv, bcg, gmg, xbc, cst, C, h, S, Sp, r0);
+      RD::commit(bc, w, gv, s_b, Sp * BP, s_win, s_m, S, Sp, r0, BP, XP);
+    }
   }
   // dt, and the decay's log as an inclusive prefix sum over the slots
   // (wave 0, lane = slot; S <= 64)
@@ -395,10 +465,41 @@ __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const fl
   __syncthreads();
   conv_window<KW, NT, P>(s_win, XP, S, tp, s_x, XP);
   for (int i = tid; i < (Sp - S) * XP; i += NT) s_x[S * XP + i] = 0.f;
+  if constexpr (FUSED) {
+    // this wave's part of G = C B^T (16 x 16, Sp = 16): D[s][j] over the
+    // entries n in [wave KW4, wave KW4 + KW4), lane group kg taking KQ
+    // consecutive ones; A = C[s = lane%16][n], B = B_j[n] for j = lane%16
+    constexpr int KW4 = N / (P / 16), KQ = KW4 / 4;
+    static_assert(KQ % 4 == 0, "16-byte operand reads");
+    const float* ca = s_c + pl * BP + wave * KW4 + kg * KQ;
+    const float* ba = s_b + pl * BP + wave * KW4 + kg * KQ;
+    f32x4 gd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < KQ; t += 4) {
+      const float4 cv = *reinterpret_cast<const float4*>(ca + t);
+      const float4 bv = *reinterpret_cast<const float4*>(ba + t);
+      gd = __builtin_amdgcn_mfma_f32_16x16x4f32(cv.x, bv.x, gd, 0, 0, 0);
+      gd = __builtin_amdgcn_mfma_f32_16x16x4f32(cv.y, bv.y, gd, 0, 0, 0);
+      gd = __builtin_amdgcn_mfma_f32_16x16x4f32(cv.z, bv.z, gd, 0, 0, 0);
+      gd = __builtin_amdgcn_mfma_f32_16x16x4f32(cv.w, bv.w, gd, 0, 0, 0);
+    }
+    // lane: column j = lane%16, rows s = 4 kg + r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_gp[wave * 256 + (4 * kg + r) * 16 + pl] = gd[r];
+    __syncthreads();
+  }
   for (int si = tid >> 4; si < Sp; si += NT >> 4)
     for (int j = tid & 15; j < Sp; j += 16) {
       float* m = s_m + si * Sp + j;
-      *m = (j <= si && si < S) ? s_dt[j] * __expf(s_cum[si] - s_cum[j]) * *m : 0.f;
+      float gsj;
+      if constexpr (FUSED) {             // the waves' partials, in wave order
+        gsj = s_gp[si * 16 + j];
+#pragma unroll
+        for (int q = 1; q < P / 16; ++q) gsj += s_gp[q * 256 + si * 16 + j];
+      } else {
+        gsj = *m;
+      }
+      *m = (j <= si && si < S) ? s_dt[j] * __expf(s_cum[si] - s_cum[j]) * gsj : 0.f;
     }
   __syncthreads();
 
@@ -406,7 +507,7 @@ __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const fl
   T* y = static_cast<T*>(a.y) + (static_cast<int64_t>(b) * S) * (H * P) + h * P + wave * 16 + 4 * kg;
   for (int s0 = 0; s0 < Sp; s0 += kSC) {
     f32x4 d = {0.f, 0.f, 0.f, 0.f};
-    const float* crow = s_c + (s0 + pl) * BP + (CTX ? 4 * kg : kg * KS);
+    const float* crow = s_c + (s0 + pl) * BP + 4 * kg;
 #pragma unroll
     for (int t = 0; t < KS; t += 4) {
       const float4 cv = *reinterpret_cast<const float4*>(crow + kStride * t);
@@ -504,26 +605,33 @@ hipError_t launch_t(const MambaArgs& a, void* ws, hipStream_t st) {
                                                static_cast<int>(bytes))
                          : hipSuccess;
   };
+  // the XCD-aware grid: 8 * ceil(units / 8) workgroups
+  const dim3 grid(static_cast<unsigned>((a.B * a.H + 7) / 8 * 8));
+  // one launch (FUSED) where it applies, else the group kernel and the scan
+#define TT_SCAN(PP, NN, WW, CTX, FUSED)                                                         \
+  {                                                                                             \
+    hipError_t e = allow(reinterpret_cast<const void*>(&mamba_scan_kernel<T, PP, NN, WW, CTX, FUSED>), lds_s); \
+    if (e != hipSuccess) return e;                                                              \
+    hipLaunchKernelGGL((mamba_scan_kernel<T, PP, NN, WW, CTX, FUSED>), grid, dim3(4 * PP), lds_s, \
+                       st, a, ws_bc, ws_g);                                                     \
+    return hipGetLastError();                                                                   \
+  }
 #define TT_MAMBA(PP, NN, WW)                                                                    \
   if (a.P == PP && a.N == NN && a.W == WW) {                                                    \
-    const void* scan = a.ssm_state_out                                                          \
-        ? reinterpret_cast<const void*>(&mamba_scan_kernel<T, PP, NN, WW, true>)                \
-        : reinterpret_cast<const void*>(&mamba_scan_kernel<T, PP, NN, WW, false>);              \
+    if constexpr (4 * PP == 2 * NN) {                                                           \
+      if (mamba_fused(a.S, PP, NN)) {                                                           \
+        if (a.ssm_state_out) TT_SCAN(PP, NN, WW, true, true)                                    \
+        TT_SCAN(PP, NN, WW, false, true)                                                        \
+      }                                                                                         \
+    }                                                                                           \
     hipError_t e = allow(reinterpret_cast<const void*>(&mamba_group_kernel<T, NN, WW>), lds_g); \
-    if (e == hipSuccess) e = allow(scan, lds_s);                                                \
     if (e != hipSuccess) return e;                                                              \
     hipLaunchKernelGGL((mamba_group_kernel<T, NN, WW>), dim3(static_cast<unsigned>(a.B * a.G)), \
                        blk, lds_g, st, a, ws_bc, ws_g);                                         \
     e = hipGetLastError();                                                                      \
     if (e != hipSuccess) return e;                                                              \
-    const dim3 grid(static_cast<unsigned>(a.B * a.H));                                          \
-    if (a.ssm_state_out)                                                                        \
-      hipLaunchKernelGGL((mamba_scan_kernel<T, PP, NN, WW, true>), grid, dim3(4 * PP), lds_s,   \
-                         st, a, ws_bc, ws_g);                                                   \
-    else                                                                                        \
-      hipLaunchKernelGGL((mamba_scan_kernel<T, PP, NN, WW, false>), grid, dim3(4 * PP), lds_s,  \
-                         st, a, ws_bc, ws_g);                                                   \
-    return hipGetLastError();                                                                   \
+    if (a.ssm_state_out) TT_SCAN(PP, NN, WW, true, false)                                       \
+    TT_SCAN(PP, NN, WW, false, false)                                                           \
   }
 #define TT_MAMBA_W(PP, NN) TT_MAMBA(PP, NN, 2) TT_MAMBA(PP, NN, 3) TT_MAMBA(PP, NN, 4)
   TT_MAMBA_W(64, 128)
@@ -532,10 +640,13 @@ hipError_t launch_t(const MambaArgs& a, void* ws, hipStream_t st) {
   TT_MAMBA_W(32, 64)
 #undef TT_MAMBA_W
 #undef TT_MAMBA
+#undef TT_SCAN
   return hipErrorInvalidValue;
 }
 
 }  // namespace
+
+bool mamba_fused(int S, int P, int N) { return S <= kSC && 4 * P == 2 * N; }
 
 bool mamba_supported(int P, int N, int W) {
   return (P == 64 || P == 32) && (N == 128 || N == 64) && W >= 2 && W <= 4;
@@ -543,11 +654,13 @@ bool mamba_supported(int P, int N, int W) {
 
 size_t mamba_lds_bytes(int S, int P, int N) {
   // the scan kernel: the x window (S + 3 rows at most) and outputs (S
-  // rounded up to 16), B and C rows, dt, cum and M; the group kernel needs
+  // rounded up to 16), B and C rows (S rounded up), dt, cum, M and, in the
+  // one-launch form, the waves' partial G tiles; the group kernel needs
   // (2S + 3) (2N + 4) floats, checked separately
   const size_t Sp = (S + 15) / 16 * 16;
-  return (static_cast<size_t>(S + 3 + Sp) * (P + 4) + static_cast<size_t>(S + Sp) * (N + 4) +
-          3 * Sp + Sp * Sp) * sizeof(float);
+  const size_t gp = mamba_fused(S, P, N) ? static_cast<size_t>(P / 16) * 256 : 0;
+  return (static_cast<size_t>(S + 3 + Sp) * (P + 4) + 2 * Sp * (N + 4) + 3 * Sp + Sp * Sp + gp) *
+         sizeof(float);
 }
 
 size_t mamba_group_lds_bytes(int S, int N) {

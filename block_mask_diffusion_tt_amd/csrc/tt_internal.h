@@ -95,6 +95,8 @@ struct MambaArgs {
 };
 
 bool mamba_supported(int P, int N, int W);
+// whether one launch does the whole layer (no group kernel, workspace unused)
+bool mamba_fused(int S, int P, int N);
 size_t mamba_lds_bytes(int S, int P, int N);
 size_t mamba_group_lds_bytes(int S, int N);
 size_t mamba_workspace_bytes(int B, int S, int G, int N);

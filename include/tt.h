@@ -540,7 +540,8 @@ tt_status tt_generate(const tt_attn_shape* shape, int32_t n_layers, int32_t n_bl
  * All device pointers.  fp32 arithmetic throughout; y rounded to nearest
  * even for bf16.  The workspace (tt_mamba_workspace_size bytes, 16-byte
  * aligned, no initialisation) holds the B/C conv outputs and C.B products
- * the heads of a group share.  Errors: TT_ERR_INVALID_ARG (NULL required
+ * the heads of a group share; it is left untouched where one kernel does
+ * the whole layer (S <= 16 and N = 2P), but must still be passed.  Errors: TT_ERR_INVALID_ARG (NULL required
  * pointer, bad sizes, G not dividing H, misaligned state or y),
  * TT_ERR_UNSUPPORTED (P, N or W outside the sets above), TT_ERR_WORKSPACE,
  * TT_ERR_HIP.
