@@ -351,9 +351,11 @@ __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const fl
   const int C = H * P + 2 * G * N;
   constexpr int XP = P + 4;              // LDS row strides (rows start 4 banks apart)
   constexpr int BP = N + 4;
+  // FUSED with P = 64: the x conv runs from registers (no x window in LDS)
+  constexpr bool kXinRegs = FUSED && P == 64;
   extern __shared__ float lds[];
   float* s_win = lds;                    // [S + W-1][XP]  x inputs
-  float* s_x = s_win + (S + W - 1) * XP; // [Sp][XP]       conv outputs of the head's x
+  float* s_x = s_win + (kXinRegs ? 0 : (S + W - 1) * XP); // [Sp][XP] conv outputs of the head's x
   float* s_b = s_x + Sp * XP;            // [Sp][BP]       the group's B
   float* s_c = s_b + Sp * BP;            // [Sp][BP]       the group's C
   float* s_dt = s_c + Sp * BP;           // [Sp] dt_s
@@ -401,21 +403,57 @@ __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const fl
     const int cb = H * P + (tid < N ? g * N + tid : G * N + g * N + (tid - N));
     Taps<KW> tb;
     tb.load(a.conv_w, a.conv_b, cb);
-    uint32_t w[RD::kWn];
-    uint32_t vb[kRows];
-    RD::issue_x(w, xbc, cst, C, h, S, 0);
+    // x, P = 64: wave w convolves slots 4w .. 4w+3 of channel c = lane from
+    // its own registers (window rows 4w .. 4w+2+W, clamped onto the last),
+    // so the x window needs no LDS; the row pointers are uniform and a load
+    // needs no address arithmetic of its own; rows below W-1 (wave 0 only)
+    // come from the conv state
+    constexpr int kXR = 4 + KW - 1;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t xw[kXinRegs ? kXR : 1];
+    uint32_t w[kXinRegs ? 1 : RD::kWn];
+    if constexpr (kXinRegs) {
+      const int c = h * P + lane;
 #pragma unroll
-    for (int u = 0; u < kRows; ++u) {
-      const int r = min(u, S + KW - 2);
-      const int t = r - (KW - 1);
-      const T* src = t < 0 ? cst + static_cast<int64_t>(cb) * (KW - 1) + r
-                           : xbc + static_cast<int64_t>(t) * C + cb;
-      vb[u] = ld_raw(src);
+      for (int u = 0; u < kXR; ++u) {
+        const int r = min(4 * wv + u, S + KW - 2);
+        const T* src;
+        if (u < KW - 1)
+          src = r < KW - 1 ? cst + static_cast<int64_t>(c) * (KW - 1) + r
+                           : xbc + static_cast<int64_t>(r - (KW - 1)) * C + c;
+        else
+          src = xbc + static_cast<int64_t>(r - (KW - 1)) * C + c;
+        xw[u] = ld_raw(src);
+      }
+    } else {
+      RD::issue_x(w, xbc, cst, C, h, S, 0);
+    }
+    // B/C window: rows u < W-1 from the conv state, the others slot
+    // min(u - (W-1), S-1) of the block (uniform row pointers)
+    uint32_t vb[kRows];
+    const T* cs_ch = cst + static_cast<int64_t>(cb) * (KW - 1);
+#pragma unroll
+    for (int u = 0; u < KW - 1; ++u) vb[u] = ld_raw(cs_ch + u);
+#pragma unroll
+    for (int u = KW - 1; u < kRows; ++u) {
+      const T* row = xbc + static_cast<int64_t>(min(u - (KW - 1), S - 1)) * C;
+      vb[u] = ld_raw(row + cb);
     }
     __builtin_amdgcn_sched_barrier(0);
     load_state();
     __builtin_amdgcn_sched_barrier(0);
-    RD::commit_x(w, s_win, S, 0, XP);
+    if constexpr (kXinRegs) {
+      // slots past S are stored as 0 (the zero padding of s_x)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float acc = tp.bias;
+#pragma unroll
+        for (int j = 0; j < KW; ++j) acc = fmaf(tp.w[j], raw_f32<T>(xw[q + j]), acc);
+        s_x[(4 * wv + q) * XP + lane] = 4 * wv + q < S ? silu(acc) : 0.f;
+      }
+    } else {
+      RD::commit_x(w, s_win, S, 0, XP);
+    }
     // conv + SiLU of the channel; slots past S are stored as 0
     float* dst = tid < N ? s_b + tid : s_c + (tid - N);
 #pragma unroll
@@ -463,8 +501,10 @@ __global__ __launch_bounds__(4 * P) void mamba_scan_kernel(MambaArgs a, const fl
     }
   }
   __syncthreads();
-  conv_window<KW, NT, P>(s_win, XP, S, tp, s_x, XP);
-  for (int i = tid; i < (Sp - S) * XP; i += NT) s_x[S * XP + i] = 0.f;
+  if constexpr (!kXinRegs) {
+    conv_window<KW, NT, P>(s_win, XP, S, tp, s_x, XP);
+    for (int i = tid; i < (Sp - S) * XP; i += NT) s_x[S * XP + i] = 0.f;
+  }
   if constexpr (FUSED) {
     // this wave's part of G = C B^T (16 x 16, Sp = 16): D[s][j] over the
     // entries n in [wave KW4, wave KW4 + KW4), lane group kg taking KQ
@@ -658,8 +698,10 @@ size_t mamba_lds_bytes(int S, int P, int N) {
   // one-launch form, the waves' partial G tiles; the group kernel needs
   // (2S + 3) (2N + 4) floats, checked separately
   const size_t Sp = (S + 15) / 16 * 16;
-  const size_t gp = mamba_fused(S, P, N) ? static_cast<size_t>(P / 16) * 256 : 0;
-  return (static_cast<size_t>(S + 3 + Sp) * (P + 4) + 2 * Sp * (N + 4) + 3 * Sp + Sp * Sp + gp) *
+  const bool fused = mamba_fused(S, P, N);
+  const size_t gp = fused ? static_cast<size_t>(P / 16) * 256 : 0;
+  const size_t win = fused && P == 64 ? 0 : static_cast<size_t>(S + 3);   // x window rows
+  return (static_cast<size_t>(win + Sp) * (P + 4) + 2 * Sp * (N + 4) + 3 * Sp + Sp * Sp + gp) *
          sizeof(float);
 }
 
