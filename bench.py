@@ -390,9 +390,9 @@ def main():
         # Mamba-2 seeded block scan (one layer): the denoiser's form (reads the
         # seed) and the context tower's (also writes the final states)
         mb = mamba_inputs(tt, B, S)
-        us_mamba = timed(lambda r: tt.mamba_block_scan(*mb["args"], **mb["kw"]))
+        us_mamba = timed(lambda r: tt.mamba_block_scan(*mb["args"](r), **mb["kw"]))
         us_mamba_ctx = timed(lambda r: tt.mamba_block_scan(
-            *mb["args"], **mb["kw"], conv_state_out=mb["cso"], ssm_state_out=mb["sso"]))
+            *mb["args"](r), **mb["kw"], conv_state_out=mb["cso"], ssm_state_out=mb["sso"]))
         del mb["args"], mb["cso"], mb["sso"]
         # weighted adaLN-single sublayer (one layer) at width Hq*d: its three
         # kernels alone, then the whole sublayer over this workload's contexts
@@ -485,7 +485,8 @@ def main():
             "f1_ctx_advance": {"calls": "tt_ctx_advance + a 4*B-byte length reset copy",
                                "us_per_call": round(us_adv, 2)},
             "f4_mamba_scan": dict(row(us_mamba, mb["bytes"], "tt_mamba_block_scan, seed read "
-                                      "(denoiser), one layer"), shape=mb["desc"]),
+                                      "(denoiser), one layer, seeds rotated over "
+                                      f"{MAMBA_SETS} sets (read from HBM)"), shape=mb["desc"]),
             "f4_mamba_scan_ctx": row(us_mamba_ctx, mb["bytes_ctx"],
                                      "tt_mamba_block_scan with the final states written "
                                      "(context tower), one layer"),
@@ -551,6 +552,9 @@ def denoise_loop(tt, w, kc, vc, qb, kb, vb, ada_w, ada_b, ada_t, logits, start, 
 
 
 MAMBA = dict(H=64, P=64, N=128, G=8, W=4)   # assumed layer sizes (the pages give none)
+# seed states the Mamba rows rotate over (4 x 134 MB: more than the 256 MB
+# last-level cache holds, so every call reads its seed from HBM)
+MAMBA_SETS = 4
 
 
 def sublayer_inputs(tt, B, S, Hq, Hkv, d, max_len):
@@ -576,7 +580,8 @@ def sublayer_inputs(tt, B, S, Hq, Hkv, d, max_len):
 def mamba_inputs(tt, B, S):
     """Seeded synthetic inputs of one Mamba-2 layer's block scan at the bench's
     batch and block: 64 heads of 64 channels, d_state 128, 8 groups, conv
-    width 4 (bf16 activations and conv state, fp32 SSM state and parameters)."""
+    width 4 (bf16 activations and conv state, fp32 SSM state and parameters).
+    `args(r)` gives the call's arguments with seed state set r % MAMBA_SETS."""
     import torch
 
     import synth
@@ -586,7 +591,7 @@ def mamba_inputs(tt, B, S):
     xbc = synth.normal((B, S, C), 1.0, 801, bf, dev)
     dt_raw = synth.normal((B, S, H), 1.0, 802, f32, dev) - 1.0
     cs = synth.normal((B, C, W - 1), 1.0, 803, bf, dev)
-    ss = synth.normal((B, H, P, N), 1.0, 804, f32, dev)
+    ss = [synth.normal((B, H, P, N), 1.0, 804 + 10 * i, f32, dev) for i in range(MAMBA_SETS)]
     conv_w = synth.normal((C, W), 0.5, 805, f32, dev)
     conv_b = synth.normal((C,), 0.1, 806, f32, dev)
     A_log = torch.log(torch.linspace(1.0, 16.0, H, device=dev))
@@ -598,10 +603,10 @@ def mamba_inputs(tt, B, S):
     conv_state = B * C * (W - 1) * 2
     rest = B * S * C * 2 + B * S * H * 4 + B * S * H * P * 2 + C * W * 4 + C * 4 + 3 * H * 4
     ws = torch.empty(tt.mamba_workspace_size(shape), dtype=torch.uint8, device=dev)
-    return {"args": (shape, xbc, dt_raw, cs, ss, conv_w, A_log, y, ws),
+    return {"args": lambda r: (shape, xbc, dt_raw, cs, ss[r % MAMBA_SETS], conv_w, A_log, y, ws),
             "kw": dict(conv_b=conv_b, dt_bias=dt_bias, D=D),
             # the context tower's form writes its states to second buffers
-            "cso": torch.empty_like(cs), "sso": torch.empty_like(ss),
+            "cso": torch.empty_like(cs), "sso": torch.empty_like(ss[0]),
             "bytes": state + conv_state + rest,
             "bytes_ctx": 2 * state + 2 * conv_state + rest,
             "desc": {"batch": B, "block": S, **MAMBA, "dtype": "bf16 (fp32 state)"}}
