@@ -142,3 +142,36 @@ def test_full_size_sampled():
     y, _, _ = run(c)
     seqs = [0, 33, 63]
     close(y[seqs], ref(c, seqs), BF16, "full size")
+
+
+def _mshapes(seed, n):
+    """Seeded shapes: the four (P, N) pairs in turn (N = 2P takes the
+    one-launch form for S <= 16), S on both sides of 16, head counts whose
+    sequence x head units leave the XCD-aware grid partly idle, every conv
+    width, both dtypes, and the final states on every other case."""
+    rng = np.random.default_rng(seed)
+    pn = [(64, 128), (32, 64), (64, 64), (32, 128)]
+    out = []
+    for i in range(n):
+        P, N = pn[i % 4]
+        S = int(rng.integers(1, 17)) if i < n - 2 else int(rng.integers(17, 65))
+        H = int(rng.choice([4, 8, 12]))
+        G = int(rng.choice([g for g in (1, 2, 4) if H % g == 0]))
+        out.append((int(rng.integers(1, 6)), S, H, P, N, G, int(rng.integers(2, 5)),
+                    BF16 if rng.random() < 0.6 else F32, bool(i % 2)))
+    return out
+
+
+@pytest.mark.parametrize("B,S,H,P,N,G,W,dtype,states", _mshapes(2026, 8))
+def test_random_shapes(B, S, H, P, N, G, W, dtype, states):
+    c = mcase(B, S, H, P, N, G, W=W, dtype=dtype, seed=100 + B * 97 + S * 13 + H + W)
+    say("mamba random", B, S, H, P, N, G, W, dtype, "states" if states else "")
+    if states:
+        y_ref, conv_ref, ssm_ref = ref(c, return_state=True)
+        y, cso, sso = run(c, states_out=True, in_place=False)
+        np.testing.assert_array_equal(np64(cso), conv_ref)
+        close(sso, ssm_ref, F32, "random final SSM state")
+    else:
+        y_ref = ref(c)
+        y, _, _ = run(c)
+    close(y, y_ref, dtype, f"random B={B} S={S} H={H} P={P} N={N} G={G} W={W}")
