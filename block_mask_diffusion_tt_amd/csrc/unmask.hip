@@ -324,6 +324,12 @@ struct Chunk;
 template <>
 struct Chunk<uint16_t> {
   uint4 r[4];
+  // a whole pass of 16-byte aligned tokens: unconditional loads, no branch
+  __device__ __forceinline__ void load_full(const uint16_t* x, int base) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      r[u] = *reinterpret_cast<const uint4*>(x + base + 8 * (static_cast<int>(threadIdx.x) + kThreads * u));
+  }
   __device__ __forceinline__ void load(const uint16_t* x, int base, int end, int vec_ok) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -353,6 +359,14 @@ struct Chunk<uint16_t> {
 template <>
 struct Chunk<float> {
   float4 r[8];
+  __device__ __forceinline__ void load_full(const float* x, int base) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int g = base + 8 * (static_cast<int>(threadIdx.x) + kThreads * u);
+      r[2 * u] = *reinterpret_cast<const float4*>(x + g);
+      r[2 * u + 1] = *reinterpret_cast<const float4*>(x + g + 4);
+    }
+  }
   __device__ __forceinline__ void load(const float* x, int base, int end, int vec_ok) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -378,7 +392,8 @@ struct Chunk<float> {
 
 // Streams one slice [split*split_len, +split_len) of one masked row in passes
 // of 8192 tokens, the next pass's loads in flight while the current one is
-// processed.  Per pass: the workgroup maximum (one barrier), the running
+// processed (whole aligned passes; a partial or unaligned pass is loaded and
+// processed on its own).  Per pass: the workgroup maximum (one barrier), the running
 // reference M = max so far (Z rescaled when it grows), Z += exp2((x - M) c),
 // and the Gumbel-max candidates x >= M - cand_margin(M): the token holding
 // M was itself a candidate when it arrived, and it outscores every token
@@ -405,12 +420,9 @@ __global__ __launch_bounds__(kThreads) void rowsample_kernel(
   float M = -FLT_MAX, z = 0.f;
   float key = -INFINITY, key2 = -INFINITY, lx = 0.f;
   int idx = INT_MAX;
-  const int npass = (end - beg + kChunk - 1) / kChunk;
-  Chunk<T> cur, nxt;
-  cur.load(x, beg, end, vec_ok);
-  for (int k = 0; k < npass; ++k) {
-    const int cb = beg + k * kChunk;
-    if (k + 1 < npass) nxt.load(x, cb + kChunk, end, vec_ok);
+  // one pass over the tokens a chunk holds (cb: its first token)
+  int pass = 0;
+  auto process = [&](const Chunk<T>& cur, int cb) {
     float tm = -FLT_MAX;
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) tm = fmaxf(tm, cur.get(i));
@@ -418,10 +430,11 @@ __global__ __launch_bounds__(kThreads) void rowsample_kernel(
     for (int off = 32; off >= 1; off >>= 1) tm = fmaxf(tm, __shfl_xor(tm, off));
     // two slots, alternating: a slot is rewritten only after the next
     // barrier, which every thread passes after reading it
-    if (lane == 0) s_cmax[k & 1][wave] = tm;
+    if (lane == 0) s_cmax[pass & 1][wave] = tm;
     __syncthreads();
-    const float C = fmaxf(fmaxf(s_cmax[k & 1][0], s_cmax[k & 1][1]),
-                          fmaxf(s_cmax[k & 1][2], s_cmax[k & 1][3]));
+    const float C = fmaxf(fmaxf(s_cmax[pass & 1][0], s_cmax[pass & 1][1]),
+                          fmaxf(s_cmax[pass & 1][2], s_cmax[pass & 1][3]));
+    ++pass;
     if (C > M) {   // workgroup-uniform
       z *= fast_exp2((M - C) * c);
       M = C;
@@ -454,7 +467,32 @@ __global__ __launch_bounds__(kThreads) void rowsample_kernel(
       const float sc = l + tau * gumbel32(noise_word(rk, t));
       merge_best(key, key2, idx, lx, sc, -INFINITY, t, l);
     }
-    cur = nxt;
+  };
+  // whole passes of 16-byte aligned tokens: two register buffers taken in
+  // turn, the next pass's loads issued before the current pass is processed.
+  // No copy between the buffers and no branch around a load (the last
+  // pass's fetch repeats its own addresses, in bounds and unused): a copy or
+  // a branchy load made the compiler wait for the next pass's loads before
+  // processing the current one, so each pass paid a full memory round trip.
+  const int nfull = vec_ok ? (end - beg) / kChunk : 0;
+  if (nfull > 0) {
+    Chunk<T> ca, cbf;
+    ca.load_full(x, beg);
+    for (int k = 0;;) {
+      cbf.load_full(x, beg + (k + 1 < nfull ? k + 1 : k) * kChunk);
+      process(ca, beg + k * kChunk);
+      if (++k == nfull) break;
+      ca.load_full(x, beg + (k + 1 < nfull ? k + 1 : k) * kChunk);
+      process(cbf, beg + k * kChunk);
+      if (++k == nfull) break;
+    }
+  }
+  // the rest: a partial last pass, or every pass of a row whose tokens are
+  // not 16-byte aligned (tokens at or past `end` read as -inf)
+  for (int cb = beg + nfull * kChunk; cb < end; cb += kChunk) {
+    Chunk<T> cur;
+    cur.load(x, cb, end, vec_ok);
+    process(cur, cb);
   }
   // fixed-shape trees: Z and the best pair over the wave, then the four waves
 #pragma unroll
