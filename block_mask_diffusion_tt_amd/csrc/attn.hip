@@ -171,7 +171,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // need not keep it.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-               :: "v"(off), "s"(base), "s"(lds) : "memory");
+               :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 
 // Waits until at most N vector memory operations of this wave are in flight.

@@ -57,7 +57,7 @@ enum { kEpiQkv = 0, kEpiGate = 1 };
 // explicit.  No register result.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(off), "s"(base), "s"(lds) : "memory");
+               :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 
 // Waits until at most N vector memory operations of this wave are in flight.
