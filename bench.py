@@ -394,14 +394,15 @@ def main():
         del f3
         f3_us = (us_ln, us_qkv, us_o, us_sub)
         return us_ada, us_sample, us_unmask, us_ctx, us_adv, loop, gen, us_mamba, us_mamba_ctx, mb, f3_us
-    # The per-row timings and the reference streams run before the warm-up
+    # The reference streams and the per-row timings run before the warm-up
     # steps: from an idle GPU the clocks need about 35 ms of work to reach
     # their sustained level, more than a short warm-up gives, and these
-    # measurements are over a second of GPU work.  They leave the timed
+    # measurements are over a second of GPU work, ending with attention
+    # calls.  They leave the timed
     # steps' inputs as they were (their block states, the cache rows past
     # each context and their buffers are their own).
-    rows_data = None if args.no_rows else collect_rows()
     streams = None if args.no_rows else reference_streams()
+    rows_data = None if args.no_rows else collect_rows()
     calibration_copy(args)
     for i in range(args.warmup):
         step(i, False)
@@ -435,6 +436,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
         "step_ms_p10_p50_p90": pct(step_ms),
+        "step_ms_blocks": [round(float(v), 4) for v in step_ms],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -454,7 +456,7 @@ def main():
                      "launch_ms_p10_p50_p90": pct(attn_ms)},
     }
     if streams is not None:
-        streams["when"] = "before the warm-up steps, after the per-row timings"
+        streams["when"] = "before the per-row timings and the warm-up steps"
         result["roofline"]["reference_streams"] = streams
     # algorithmic bytes of the other rows: adaLN reads W, bias and the table
     # and writes every layer's vectors; unmasking reads the masked rows'

@@ -301,6 +301,28 @@ def test_timestep_embedding_special_values():
     np.testing.assert_allclose(e[:, :128] ** 2 + e[:, 128:] ** 2, 1.0, atol=1e-14)
 
 
+# Structure of the sinusoid, checked without its formula: the angle-addition
+# identities hold for every pair (so each pair is (cos, sin) of one angle that
+# is linear in t), and the angular frequencies recovered from the phase at a
+# small t form one geometric progression from 1000 down by a factor of
+# 10000 per 128 pairs (max period 10000, argument scale 1000).
+def test_timestep_embedding_angle_addition_and_frequencies():
+    rng = np.random.default_rng(7)
+    t1, t2 = rng.uniform(0, 0.5, 16), rng.uniform(0, 0.5, 16)
+    a, b, ab = (oracle.timestep_embedding(t1), oracle.timestep_embedding(t2),
+                oracle.timestep_embedding(t1 + t2))
+    ca, sa, cb, sb = a[:, :128], a[:, 128:], b[:, :128], b[:, 128:]
+    np.testing.assert_allclose(ab[:, :128], ca * cb - sa * sb, atol=1e-12)
+    np.testing.assert_allclose(ab[:, 128:], sa * cb + ca * sb, atol=1e-12)
+    t = 1e-6   # every phase 1000 t f_i stays below pi
+    e = oracle.timestep_embedding([t])[0]
+    omega = np.arctan2(e[128:], e[:128]) / t
+    assert abs(omega[0] - 1000.0) < 1e-6
+    ratio = omega[1:] / omega[:-1]
+    np.testing.assert_allclose(ratio, 10000.0 ** (-1.0 / 128), rtol=1e-9)
+    assert abs(omega[-1] / omega[0] - 10000.0 ** (-127.0 / 128)) < 1e-9
+
+
 def test_adaln_single_pins():
     B, E, width, nl = 3, 6, 4, 2
     emb = _rand((B, E), 111, 2.0)
