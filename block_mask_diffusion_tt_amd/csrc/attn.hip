@@ -858,36 +858,47 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(KParams p) {
 // ------------------------------------------------------------------ merge
 // o = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c, combined in chunk
 // order; lse = ln2 * (M + log2 sum); out = residual + gate * o.
+// 8 consecutive output-type values as one 16-byte access for bf16 (two for
+// fp32): each 16-byte piece of an output row is written by one instruction,
+// so the lines a wave writes arrive whole (two 8-byte stores per piece made
+// the memory side fetch the output's lines before writing them).
 template <typename OutT>
-__device__ __forceinline__ void store4(OutT* dst, float a, float b, float c, float d);
+__device__ __forceinline__ void load8(const OutT* src, float (&v)[8]);
 
 template <>
-__device__ __forceinline__ void store4<float>(float* dst, float a, float b, float c, float d) {
-  *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
-}
-
-template <>
-__device__ __forceinline__ void store4<uint16_t>(uint16_t* dst, float a, float b, float c, float d) {
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-  bf16x4 v = {static_cast<__bf16>(a), static_cast<__bf16>(b), static_cast<__bf16>(c),
-              static_cast<__bf16>(d)};
-  *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, v);
-}
-
-template <typename OutT>
-__device__ __forceinline__ void load4(const OutT* src, float (&v)[4]);
-
-template <>
-__device__ __forceinline__ void load4<float>(const float* src, float (&v)[4]) {
-  const float4 x = *reinterpret_cast<const float4*>(src);
+__device__ __forceinline__ void load8<float>(const float* src, float (&v)[8]) {
+  const float4 x = reinterpret_cast<const float4*>(src)[0], y = reinterpret_cast<const float4*>(src)[1];
   v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
 }
 
 template <>
-__device__ __forceinline__ void load4<uint16_t>(const uint16_t* src, float (&v)[4]) {
-  const uint2 x = *reinterpret_cast<const uint2*>(src);
-  v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xffff0000u);
-  v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xffff0000u);
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* src, float (&v)[8]) {
+  const uint4 x = *reinterpret_cast<const uint4*>(src);
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <typename OutT>
+__device__ __forceinline__ void store8(OutT* dst, const float (&v)[8]);
+
+template <>
+__device__ __forceinline__ void store8<float>(float* dst, const float (&v)[8]) {
+  reinterpret_cast<float4*>(dst)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(dst)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+template <>
+__device__ __forceinline__ void store8<uint16_t>(uint16_t* dst, const float (&v)[8]) {
+  typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+  bf16x8v b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = static_cast<__bf16>(v[i]);
+  *reinterpret_cast<uint4*>(dst) = __builtin_bit_cast(uint4, b);
 }
 
 // N consecutive partial values from element offset `off`: fp16 partials
@@ -938,6 +949,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MParams p) {
   constexpr int Q = kMergeQuads;         // 16-byte loads per thread per chunk
   constexpr int TPR = D / CPT;           // threads per row
   constexpr bool kMany = NB >= 16;
+  static_assert(CPT == 8, "the epilogue moves 8 channels per thread");
   const int grp = blockIdx.y;  // (b, g, rb)
   const int rb = grp % p.RB;
   const int g = (grp / p.RB) % p.Hkv;
@@ -963,11 +975,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MParams p) {
     for (int q = 0; q < Q; ++q) {
       const float4 x = *reinterpret_cast<const float4*>(gp + 4 * q);
       gv[4 * q] = x.x; gv[4 * q + 1] = x.y; gv[4 * q + 2] = x.z; gv[4 * q + 3] = x.w;
-      float r4[4];
-      load4<OutT>(rp + 4 * q, r4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rv[4 * q + i] = r4[i];
     }
+    load8<OutT>(rp, rv);
   }
   // chunk c contributes 2^(m_c - M) l_c o_c, M the largest m_c; its stored
   // partial is o_c 2^-k_c (fp16 for bf16 output, fp32 for fp32 output).
@@ -1029,29 +1038,26 @@ __global__ __launch_bounds__(256) void merge_kernel(MParams p) {
   const float* gp = p.gate ? p.gate + (static_cast<int64_t>(b) * p.Hq + h) * D + c0 : nullptr;
   const OutT* rp = p.residual ? static_cast<const OutT*>(p.residual) + orow * D + c0 : nullptr;
   OutT* op = static_cast<OutT*>(p.out) + orow * D + c0;
+  float v[CPT];
 #pragma unroll
-  for (int q = 0; q < Q; ++q) {
-    float v[4] = {o[4 * q] * inv, o[4 * q + 1] * inv, o[4 * q + 2] * inv, o[4 * q + 3] * inv};
-    if (gp) {
-      if constexpr (!kMany) {
+  for (int i = 0; i < CPT; ++i) v[i] = o[i] * inv;
+  if (gp) {
+    if constexpr (!kMany) {
+#pragma unroll
+      for (int q = 0; q < Q; ++q) {
         const float4 x = *reinterpret_cast<const float4*>(gp + 4 * q);
         gv[4 * q] = x.x; gv[4 * q + 1] = x.y; gv[4 * q + 2] = x.z; gv[4 * q + 3] = x.w;
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] *= gv[4 * q + i];
     }
-    if (rp) {
-      if constexpr (!kMany) {
-        float r4[4];
-        load4<OutT>(rp + 4 * q, r4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rv[4 * q + i] = r4[i];
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] += rv[4 * q + i];
-    }
-    store4<OutT>(op + 4 * q, v[0], v[1], v[2], v[3]);
+    for (int i = 0; i < CPT; ++i) v[i] *= gv[i];
   }
+  if (rp) {
+    if constexpr (!kMany) load8<OutT>(rp, rv);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) v[i] += rv[i];
+  }
+  store8<OutT>(op, v);
   if (p.lse && c0 == 0) p.lse[orow] = 0.6931471805599453f * (M + log2f(L));
 }
 
