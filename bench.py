@@ -63,7 +63,7 @@ def parse():
                     help="sweep32k: timed denoise loops per (S, gamma) cell, after one untimed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
-                    help="skip the per-row timings after the timed region (counter runs)")
+                    help="skip the per-row timings and reference streams (counter runs)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=24)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="run one plain device copy of this many MiB before timing (its "
