@@ -168,10 +168,12 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // flight before any LDS read (it cannot tell the pipeline stages apart); the
 // stage waits below are explicit.  The instruction has no register result.
 // Marked non-temporal: the context K/V is read once per layer, so the caches
-// need not keep it.
+// need not keep it.  M0 is not in the clobber list: the compiler reserves it
+// and warns that such a clobber is not honoured; instead the build fails if
+// the compiler itself uses M0 anywhere in this file's kernels.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-               :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
+               :: "v"(off), "s"(base), "s"(lds) : "memory");
 }
 
 // Waits until at most N vector memory operations of this wave are in flight.

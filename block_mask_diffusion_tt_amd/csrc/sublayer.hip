@@ -54,10 +54,12 @@ enum { kEpiQkv = 0, kEpiGate = 1 };
 // base plus a per-lane byte offset: lane i writes LDS bytes
 // [lds + 16 i, lds + 16 i + 16).  In asm so that the compiler does not wait
 // for the copies in flight before every LDS read; the stage waits are
-// explicit.  No register result.
+// explicit.  No register result.  M0 is not in the clobber list (the
+// compiler reserves it and warns that such a clobber is not honoured); the
+// build fails if the compiler itself uses M0 in this file's kernels.
 __device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
+               :: "v"(off), "s"(base), "s"(lds) : "memory");
 }
 
 // Waits until at most N vector memory operations of this wave are in flight.
