@@ -425,6 +425,7 @@ def main():
     def pct(x):
         return [round(float(v), 4) for v in np.percentile(np.asarray(x), [10, 50, 90])]
     per_launch, step_bytes = algorithmic_bytes(w, B * S)
+    attn_flops = 4 * S * Hq * d * sum(L + S for L in lens)
     qtok_s = B * S / (ms * 1e-3)
     attn_gbps = per_launch / (attn_avg * 1e-3) / 1e9
     result = {
@@ -453,7 +454,13 @@ def main():
                      "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": counted_traffic() if w["name"] == "ctx8k" else None,
                      "bytes_per_launch": per_launch, "mean_launch_ms": round(attn_avg, 4),
-                     "launch_ms_p10_p50_p90": pct(attn_ms)},
+                     "launch_ms_p10_p50_p90": pct(attn_ms),
+                     # the co-bound: the same launches' matrix products
+                     # (QK^T and PV over every context and block key)
+                     "mfma_co_bound": {"flops_per_launch": attn_flops,
+                                       "tflops": round(attn_flops / (attn_avg * 1e-3) / 1e12, 1),
+                                       "peak_tflops": MFMA_BF16_TFLOPS,
+                                       "frac": round(attn_flops / (attn_avg * 1e-3) / 1e12 / MFMA_BF16_TFLOPS, 4)}},
     }
     if streams is not None:
         streams["when"] = "before the per-row timings and the warm-up steps"
