@@ -80,11 +80,12 @@ ATTN_KERNELS = ("attn_bf16_kernel<128, 8>", "merge_kernel<unsigned short, 128, 2
 
 
 def attn_source_hash():
-    """Hash of the attention kernel's sources: the counters describe that code only."""
+    """Hash of the attention kernel's sources and of the build script (its
+    compiler flags): the counters describe that code only."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("attn.hip", "tt_internal.h"):
-        with open(os.path.join(ROOT, "block_mask_diffusion_tt_amd", "csrc", f), "rb") as fh:
+    for f in ("csrc/attn.hip", "csrc/tt_internal.h", "build.py"):
+        with open(os.path.join(ROOT, "block_mask_diffusion_tt_amd", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
